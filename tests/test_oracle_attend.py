@@ -1,0 +1,103 @@
+"""Pins for the oracle's decode attention and top-k (CPU only).
+
+Attention over the packed cache is the textbook scaled-dot-product softmax
+over logits from codes (keys) and MSE-decoded values, with the most recent
+tokens optionally kept exact (blog.hotdry.top, engineering configuration:
+keep the latest 128-256 tokens in full precision).
+"""
+import math
+
+import numpy as np
+import pytest
+from scipy import special
+
+from oracle import tq_oracle as o
+
+
+def _setup(N=96, T=8, d=32, G=4, seed=0):
+    rng = np.random.default_rng(seed)
+    kq = o.Quantizer(d, 3, seed=1)
+    vq = o.Quantizer(d, 3, seed=2)
+    K = rng.standard_normal((N, d)) * 3
+    V = rng.standard_normal((N, d))
+    q = rng.standard_normal((G, d))
+    ki, kb, kn, kg = o.encode_prod(kq, K)
+    vi, vn = o.encode_mse(vq, V)
+    kt = rng.standard_normal((T, d))
+    vt = rng.standard_normal((T, d))
+    return kq, vq, q, (ki, kb, kn, kg), (vi, vn), kt, vt
+
+
+def test_attend_equals_dense_textbook_attention():
+    kq, vq, q, (ki, kb, kn, kg), (vi, vn), kt, vt = _setup()
+    out = o.attend(kq, vq, q, ki, kb, kn, kg, vi, vn, kt, vt)
+    # dense: decoded keys and values as matrices, scipy softmax
+    Kd = np.concatenate([o.decode_prod(kq, ki, kb, kn, kg), kt])
+    Vd = np.concatenate([o.decode_mse(vq, vi, vn), vt])
+    p = special.softmax(q @ Kd.T / math.sqrt(q.shape[1]), axis=1)
+    assert np.max(np.abs(out - p @ Vd)) < 1e-12
+
+
+def test_attend_without_tail_and_custom_scale():
+    kq, vq, q, (ki, kb, kn, kg), (vi, vn), _, _ = _setup(seed=1)
+    out = o.attend(kq, vq, q, ki, kb, kn, kg, vi, vn, scale=0.05)
+    Kd = o.decode_prod(kq, ki, kb, kn, kg)
+    Vd = o.decode_mse(vq, vi, vn)
+    p = special.softmax(0.05 * q @ Kd.T, axis=1)
+    assert np.max(np.abs(out - p @ Vd)) < 1e-12
+
+
+def test_attend_zero_scale_is_mean():
+    kq, vq, q, (ki, kb, kn, kg), (vi, vn), kt, vt = _setup(seed=2)
+    out = o.attend(kq, vq, q, ki, kb, kn, kg, vi, vn, kt, vt, scale=0.0)
+    Vd = np.concatenate([o.decode_mse(vq, vi, vn), vt])
+    assert np.max(np.abs(out - Vd.mean(0)[None])) < 1e-12
+
+
+def test_attend_dominant_logit_picks_its_value():
+    kq, vq, q, (ki, kb, kn, kg), (vi, vn), kt, vt = _setup(seed=3)
+    kt2 = kt.copy()
+    kt2[5] = q[0] * 1e3          # one tail key aligned with query 0, huge logit
+    out = o.attend(kq, vq, q[:1], ki, kb, kn, kg, vi, vn, kt2, vt)
+    assert np.max(np.abs(out[0] - vt[5])) < 1e-9
+
+
+def test_attend_softmax_is_shift_invariant_and_rows_sum_to_one():
+    kq, vq, q, (ki, kb, kn, kg), (vi, vn), kt, vt = _setup(seed=4)
+    ones = np.ones_like(vt)
+    vones_i, vones_n = o.encode_mse(vq, np.ones((len(vi), q.shape[1])))
+    out = o.attend(kq, vq, q, ki, kb, kn, kg, vones_i, vones_n, kt, ones)
+    # values all equal to the MSE decode of the all-ones vector / ones
+    dec = o.decode_mse(vq, vones_i, vones_n)[0]
+    assert np.all(out.min(0) >= np.minimum(dec, 1).min() - 1e-12)
+
+
+def test_topk_matches_full_sort_and_tie_order():
+    rng = np.random.default_rng(5)
+    lg = rng.standard_normal((7, 500))
+    lg[3, 10] = lg[3, 20] = lg[3].max() + 1.0          # a tie at the top
+    s, i = o.topk(lg, 10)
+    for r in range(7):
+        order = sorted(range(500), key=lambda j: (-lg[r, j], j))[:10]
+        assert list(i[r]) == order
+        assert np.array_equal(s[r], lg[r, order])
+    assert list(i[3, :2]) == [10, 20]
+
+
+def test_scores_gqa_head_mapping():
+    rng = np.random.default_rng(6)
+    qz = o.Quantizer(16, 3, seed=0)
+    B, Hkv, G, N, d = 2, 3, 2, 40, 16
+    X = rng.standard_normal((B, Hkv, N, d))
+    q = rng.standard_normal((B, Hkv * G, d))
+    enc = [[o.encode_prod(qz, X[b, h]) for h in range(Hkv)] for b in range(B)]
+    idx = np.array([[e[0] for e in r] for r in enc])
+    bits = np.array([[e[1] for e in r] for r in enc])
+    nrm = np.array([[e[2] for e in r] for r in enc])
+    gam = np.array([[e[3] for e in r] for r in enc])
+    out = o.scores_gqa(qz, q, idx, bits, nrm, gam)
+    for b in range(B):
+        for h in range(Hkv * G):
+            kv = h // G
+            ref = q[b, h] @ o.decode_prod(qz, idx[b, kv], bits[b, kv], nrm[b, kv], gam[b, kv]).T
+            assert np.max(np.abs(out[b, h] - ref)) < 1e-10 * np.abs(ref).max()

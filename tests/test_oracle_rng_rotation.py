@@ -1,0 +1,120 @@
+"""Pins for the oracle's random streams and rotation (CPU only).
+
+Rotation: QR of a Gaussian matrix (a2a-mcp.org, 什麼是TurboQuant？, stage 1,
+random orthogonal rotation); after rotation the coordinates of a unit vector
+are near Gaussian (wiselychen, TurboQuant+ section: kurtosis 900.4 -> 2.9).
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import tq_oracle as o
+
+
+def test_splitmix64_published_first_output(golden):
+    want = int(golden["books"]["splitmix64_seed0"]["values"][0], 16)
+    assert int(o.splitmix64(0, 1)[0]) == want
+
+
+def test_splitmix64_counter_based():
+    # output k of a stream = output 0 of the stream started k*GAMMA later
+    a = o.splitmix64(12345, 10)
+    gamma = 0x9E3779B97F4A7C15
+    for k in range(10):
+        assert int(a[k]) == int(o.splitmix64((12345 + k * gamma) % 2 ** 64, 1)[0])
+
+
+def test_uniform_open_interval_and_moments():
+    u = o.uniforms(7, 200000)
+    assert u.min() > 0.0 and u.max() < 1.0
+    assert abs(u.mean() - 0.5) < 4 * math.sqrt(1 / 12 / u.size)
+
+
+def test_box_muller_moments():
+    z = o.normals(3, 1, 2_000_000)
+    se = 1 / math.sqrt(z.size)
+    assert abs(z.mean()) < 4 * se
+    assert abs(z.var() - 1.0) < 4 * math.sqrt(2) * se
+    # fourth moment of a Gaussian is 3; kurtosis SE ~ sqrt(24/n)
+    k = np.mean(z ** 4) / np.mean(z ** 2) ** 2
+    assert abs(k - 3.0) < 4 * math.sqrt(24 / z.size)
+
+
+def test_streams_are_distinct():
+    g = o.normals(0, o.TAG_ROTATION, 1000)
+    s = o.normals(0, o.TAG_QJL, 1000)
+    g1 = o.normals(1, o.TAG_ROTATION, 1000)
+    assert abs(np.corrcoef(g, s)[0, 1]) < 0.15 and abs(np.corrcoef(g, g1)[0, 1]) < 0.15
+
+
+@pytest.mark.parametrize("d", [3, 16, 128, 200])
+def test_rotation_orthogonal(d):
+    pi = o.rotation(d, 0)
+    assert np.max(np.abs(pi.T @ pi - np.eye(d))) < 1e-12
+    p32 = pi.astype(np.float32).astype(np.float64)
+    assert np.max(np.abs(p32.T @ p32 - np.eye(d))) < 1e-6
+
+
+@pytest.mark.parametrize("d", [4, 128])
+def test_rotation_is_positive_diagonal_qr_factor(d):
+    # Pi is THE orthogonal factor of G = Pi R with R upper triangular and a
+    # positive diagonal: Pi^T G must be such an R.
+    g = o.normals(0, o.TAG_ROTATION, d * d).reshape(d, d)
+    r = o.rotation(d, 0).T @ g
+    assert np.max(np.abs(np.tril(r, -1))) < 1e-10 * np.abs(r).max()
+    assert np.all(np.diag(r) > 0)
+
+
+def test_rotation_seed_changes_matrix():
+    assert np.max(np.abs(o.rotation(16, 0) - o.rotation(16, 1))) > 0.1
+
+
+def test_rotated_uniform_coordinates_kurtosis():
+    # A coordinate of a uniform point on S^{d-1} has kurtosis 3d/(d+2).
+    d, n = 128, 40000
+    rng = np.random.default_rng(0)
+    u = rng.standard_normal((n, d))
+    u /= np.linalg.norm(u, axis=1, keepdims=True)
+    y = u @ o.rotation(d, 0).T
+    k = np.mean(y ** 4) / np.mean(y ** 2) ** 2
+    assert abs(k - 3 * d / (d + 2)) < 0.03
+
+
+def test_rotation_gaussianises_outlier_channels(golden):
+    # Gaussian data with 4 channels scaled x20 (the tiny key workload): the
+    # pooled kurtosis is large before rotation and near-Gaussian after it
+    # (the page reports 900.4 -> 2.9 on real activations).
+    pv = golden["pages"]["kurtosis_after_rotation"]
+    d, n = 128, 20000
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((n, d))
+    x[:, rng.choice(d, 4, replace=False)] *= 20.0
+    before = np.mean(x ** 4) / np.mean(x ** 2) ** 2
+    u = x / np.linalg.norm(x, axis=1, keepdims=True)
+    y = u @ o.rotation(d, 0).T
+    after = np.mean(y ** 4) / np.mean(y ** 2) ** 2
+    # shape only: the page's 2.9 is on its own data; ours must land near the
+    # same Gaussian value, within 0.15 of the page's number.
+    assert before > 50
+    assert abs(after - pv["after"]) < 0.15 and abs(after - pv["gaussian"]) < 0.1
+
+
+def test_beta_law_matches_sampled_coordinates():
+    # (x+1)/2 ~ Beta((d-1)/2, (d-1)/2) for a coordinate of a uniform unit vector.
+    from scipy import stats
+    d = 12
+    rng = np.random.default_rng(2)
+    u = rng.standard_normal((100000, d))
+    u /= np.linalg.norm(u, axis=1, keepdims=True)
+    ks = stats.kstest(u[:, 0], lambda x: o.beta_cdf(x, d))
+    assert ks.pvalue > 1e-3
+
+
+def test_beta_density_normalised_and_moment():
+    from scipy import integrate
+    for d in (3, 5, 128, 200):
+        mass, _ = integrate.quad(lambda x: o.beta_density(x, d), -1, 1, limit=200)
+        second, _ = integrate.quad(lambda x: x * x * o.beta_density(x, d), -1, 1, limit=200)
+        assert abs(mass - 1) < 1e-9
+        assert abs(second - 1.0 / d) < 1e-9
