@@ -1,0 +1,108 @@
+"""Comparison helpers for the GPU-vs-oracle parity tests.
+
+Tolerances (the method's parity bar):
+  codes   bit-exact, except an MSE index whose oracle rotated coordinate lies
+          within 1e-5 of a decision threshold may take the adjacent index,
+          and a QJL bit whose oracle projection |z| < 1e-5 * gamma may flip;
+          at most 1e-4 of all coded coordinates may differ.  When an index
+          differs, the oracle's QJL bits and gamma are recomputed from the
+          GPU's indices before they are compared (cascade rule).
+  norms, gammas   1e-5 relative.
+  logits  |gpu - oracle| <= 1e-3 * max(|oracle|, ||q|| n / sqrt(d)), on
+          identical codes (the GPU's codes fed to the oracle).
+  attention output, per row: |gpu - oracle| <= 1e-3 * max(|oracle_e|, ||oracle_row|| / sqrt(d)).
+"""
+import math
+
+import numpy as np
+
+from oracle import tq_oracle as o
+
+BAND = 1e-5
+MAX_FLIP_FRAC = 1e-4
+
+
+def to_u32(t):
+    return t.detach().cpu().numpy().view(np.uint32)
+
+
+def check_prod_codes(qz, x, codes, norms, gammas):
+    """qz: oracle Quantizer; x float64 [N, d]; GPU outputs as numpy.  Returns
+    (idx_gpu, bits_gpu, stats)."""
+    d = qz.d
+    bp, c, t = qz.codebook("prod")
+    N = x.shape[0]
+    idx_g, bits_g = o.unpack_prod(codes.reshape(N, -1), bp, d)
+    idx_o, bits_o, n_o, g_o = o.encode_prod(qz, x)
+    nz = n_o > 0
+    y = np.zeros_like(x)
+    y[nz] = (x[nz] / n_o[nz, None]) @ qz.pi.T
+    dist = np.min(np.abs(y[..., None] - t), axis=-1)
+    bad_idx = idx_g != idx_o
+    assert np.all(np.abs(idx_g - idx_o)[bad_idx] == 1), "index differs by more than one level"
+    assert np.all(dist[bad_idx] < BAND), f"index flips outside the band: {np.sum(dist[bad_idx] >= BAND)}"
+    # cascade rule: recompute sketch and gamma from the GPU's indices where they differ
+    rows = np.any(bad_idx, axis=1)
+    bits_ref = bits_o.copy()
+    g_ref = g_o.copy()
+    _, _, z_all = o.qjl_from_indices(qz, x, idx_o)
+    if rows.any():
+        b2, g2, z2 = o.qjl_from_indices(qz, x[rows], idx_g[rows])
+        bits_ref[rows] = b2
+        g_ref[rows] = g2
+        z_all[rows] = z2
+    bad_bit = bits_g != bits_ref
+    zb = np.abs(z_all) < BAND * g_ref[:, None]
+    assert np.all(zb[bad_bit]), f"QJL bits flipped outside the band: {np.sum(~zb[bad_bit])}"
+    flips = int(bad_idx.sum() + bad_bit.sum())
+    assert flips <= MAX_FLIP_FRAC * N * (d + qz.m) + 0.5, f"{flips} flipped coordinates"
+    assert np.allclose(norms, n_o, rtol=1e-5, atol=1e-30)
+    pos = g_ref > 0
+    assert np.all(gammas[~pos] == 0)
+    if pos.any():
+        assert np.max(np.abs(gammas[pos] - g_ref[pos]) / g_ref[pos]) < 1e-5
+    return idx_g, bits_g, {"index_flips": int(bad_idx.sum()), "bit_flips": int(bad_bit.sum())}
+
+
+def check_mse_codes(qz, x, codes, norms):
+    d = qz.d
+    bp, c, t = qz.codebook("mse")
+    N = x.shape[0]
+    idx_g = o.unpack_mse(codes, N, bp, d)
+    idx_o, n_o = o.encode_mse(qz, x)
+    nz = n_o > 0
+    y = np.zeros_like(x)
+    y[nz] = (x[nz] / n_o[nz, None]) @ qz.pi.T
+    dist = np.min(np.abs(y[..., None] - t), axis=-1)
+    bad = idx_g != idx_o
+    assert np.all(np.abs(idx_g - idx_o)[bad] == 1)
+    assert np.all(dist[bad] < BAND), f"index flips outside the band: {np.sum(dist[bad] >= BAND)}"
+    assert bad.sum() <= MAX_FLIP_FRAC * N * d + 0.5
+    assert np.allclose(norms, n_o, rtol=1e-5, atol=1e-30)
+    # padding tokens of the last block must be zero bits
+    nb = (N + 31) // 32
+    if N % 32:
+        w = codes.reshape(nb, bp, d)[-1]
+        assert np.all((w >> np.uint32(N % 32)) == 0)
+    return idx_g, {"index_flips": int(bad.sum())}
+
+
+def check_logits(gpu, ref, qnorm, knorm, d, rel=1e-3):
+    """gpu/ref [Q, N]; qnorm [Q]; knorm [N]."""
+    floor = qnorm[:, None] * knorm[None, :] / math.sqrt(d)
+    tol = rel * np.maximum(np.abs(ref), floor)
+    err = np.abs(gpu - ref)
+    worst = float(np.max(err / np.maximum(np.maximum(np.abs(ref), floor), 1e-30)))
+    assert np.all(err <= tol + 1e-30), f"logit error {worst:.3g} (relative to the floor) exceeds {rel}"
+    return worst
+
+
+def check_attention(gpu, ref, rel=1e-3):
+    """gpu/ref [R, d]."""
+    d = ref.shape[1]
+    floor = np.linalg.norm(ref, axis=1, keepdims=True) / math.sqrt(d)
+    tol = rel * np.maximum(np.abs(ref), floor)
+    err = np.abs(gpu - ref)
+    worst = float(np.max(err / np.maximum(np.maximum(np.abs(ref), floor), 1e-30)))
+    assert np.all(err <= tol + 1e-30), f"attention error {worst:.3g} exceeds {rel}"
+    return worst

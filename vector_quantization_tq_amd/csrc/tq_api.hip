@@ -1,0 +1,333 @@
+// C ABI of libtq (declared in include/tq.h): argument checks, the quantizer
+// object and its device tables, and kernel launches.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/tq.h"
+#include "tq_internal.h"
+#include "tq_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(TQ_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Walsh masks in the order the kernels use (odd subsets of the index bits).
+const int kMasks[4][8] = {{1}, {1, 2}, {1, 2, 4, 7}, {1, 2, 4, 8, 7, 11, 13, 14}};
+
+bool fill_codebook(int d, int bp, tq::Codebook& cb) {
+  const int K = 1 << bp;
+  std::vector<double> c(K), t(K - 1);
+  if (tq::codebook(d, K, c.data(), t.data()) != 0) return false;
+  cb.bp = bp;
+  cb.levels = K;
+  cb.nterms = K / 2;
+  for (int k = 0; k < K; ++k) cb.c[k] = static_cast<float>(c[k]);
+  for (int k = 0; k < K - 1; ++k) cb.t[k] = static_cast<float>(t[k]);
+  // coefficients in the +-1 basis: coef_S = mean_idx c[idx] prod_{p in S} s_p
+  double csum = 0;
+  for (int i = 0; i < cb.nterms; ++i) {
+    const int mk = kMasks[bp - 1][i];
+    double a = 0;
+    for (int idx = 0; idx < K; ++idx) {
+      double sgn = 1;
+      for (int p = 0; p < bp; ++p)
+        if (mk & (1 << p)) sgn *= ((idx >> p) & 1) ? 1.0 : -1.0;
+      a += c[idx] * sgn;
+    }
+    a /= K;
+    cb.mask[i] = mk;
+    cb.coef[i] = static_cast<float>(a);
+    csum += a;
+  }
+  cb.coef_sum = static_cast<float>(csum);
+  // the expansion must reproduce the codebook (symmetric => odd subsets only)
+  for (int idx = 0; idx < K; ++idx) {
+    double v = 0;
+    for (int i = 0; i < cb.nterms; ++i) {
+      double sgn = 1;
+      for (int p = 0; p < bp; ++p)
+        if (cb.mask[i] & (1 << p)) sgn *= ((idx >> p) & 1) ? 1.0 : -1.0;
+      v += static_cast<double>(cb.coef[i]) * sgn;
+    }
+    if (std::fabs(v - c[idx]) > 1e-6 * (std::fabs(c[idx]) + 1e-3)) return false;
+  }
+  return true;
+}
+
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = true;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) { ok = false; return; }
+    if (prev != dev && hipSetDevice(dev) != hipSuccess) ok = false;
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+int check_quantizer(const tq_quantizer* q) {
+  if (!q) return fail(TQ_EINVAL, "quantizer is NULL");
+  return TQ_OK;
+}
+
+int check_mode(const tq_quantizer* q, int mode) {
+  if (mode != TQ_PROD && mode != TQ_MSE) return fail(TQ_EINVAL, "mode must be TQ_PROD or TQ_MSE");
+  if (q->cb[mode].bp < 1) return fail(TQ_EINVAL, "prod mode needs bits >= 2 (bits=%d)", q->bits);
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tq_version(void) { return 1; }
+
+const char* tq_last_error(void) { return g_last_error.c_str(); }
+
+int tq_host_normals(uint64_t seed, int tag, int64_t n, double* out) {
+  if (n < 0 || (n > 0 && !out)) return fail(TQ_EINVAL, "bad n or NULL output");
+  tq::normals(seed, tag, n, out);
+  return TQ_OK;
+}
+
+int tq_host_rotation(int d, uint64_t seed, double* pi_out) {
+  if (d < 3 || d > 1024 || !pi_out) return fail(TQ_EINVAL, "need 3 <= d <= 1024 and an output array");
+  tq::rotation(d, seed, pi_out);
+  return TQ_OK;
+}
+
+int tq_host_qjl_matrix(int m, int d, uint64_t seed, double* s_out) {
+  if (m < 1 || d < 1 || !s_out) return fail(TQ_EINVAL, "need m, d >= 1 and an output array");
+  tq::qjl_matrix(m, d, seed, s_out);
+  return TQ_OK;
+}
+
+int tq_host_codebook(int d, int levels, double* centroids, double* thresholds) {
+  if (d < 3 || d > 1024) return fail(TQ_EINVAL, "need 3 <= d <= 1024");
+  if (levels != 2 && levels != 4 && levels != 8 && levels != 16) return fail(TQ_EINVAL, "levels must be 2, 4, 8 or 16");
+  if (!centroids || !thresholds) return fail(TQ_EINVAL, "NULL output");
+  if (tq::codebook(d, levels, centroids, thresholds) != 0) return fail(TQ_EINVAL, "codebook failed");
+  return TQ_OK;
+}
+
+tq_quantizer* tq_make_quantizer(int d, int bits, uint64_t seed) {
+  if (d < 3 || d > 1024) { fail(TQ_EINVAL, "d=%d out of [3, 1024]", d); return nullptr; }
+  if (bits < 1 || bits > 4) { fail(TQ_EINVAL, "bits=%d out of [1, 4]", bits); return nullptr; }
+  tq_quantizer* q = new (std::nothrow) tq_quantizer();
+  if (!q) { fail(TQ_ENOMEM, "host allocation failed"); return nullptr; }
+  q->d = d;
+  q->bits = bits;
+  q->m = d;
+  q->seed = seed;
+  q->pi.resize(static_cast<size_t>(d) * d);
+  q->s.resize(static_cast<size_t>(q->m) * d);
+  tq::rotation(d, seed, q->pi.data());
+  tq::qjl_matrix(q->m, d, seed, q->s.data());
+  if (bits >= 2 && !fill_codebook(d, bits - 1, q->cb[TQ_PROD])) { fail(TQ_EINVAL, "prod codebook failed"); delete q; return nullptr; }
+  if (!fill_codebook(d, bits, q->cb[TQ_MSE])) { fail(TQ_EINVAL, "mse codebook failed"); delete q; return nullptr; }
+
+  std::vector<float> pi32(q->pi.size()), s32(q->s.size()), sp32(q->s.size());
+  for (size_t i = 0; i < q->pi.size(); ++i) pi32[i] = static_cast<float>(q->pi[i]);
+  for (size_t i = 0; i < q->s.size(); ++i) s32[i] = static_cast<float>(q->s[i]);
+  for (int r = 0; r < q->m; ++r)
+    for (int j = 0; j < d; ++j) {   // S' = S Pi^T: S'[r][j] = sum_k S[r][k] Pi[j][k]
+      double a = 0;
+      for (int k = 0; k < d; ++k) a += q->s[static_cast<size_t>(r) * d + k] * q->pi[static_cast<size_t>(j) * d + k];
+      sp32[static_cast<size_t>(r) * d + j] = static_cast<float>(a);
+    }
+  hipError_t e = hipGetDevice(&q->device);
+  if (e != hipSuccess) { hip_fail(e, "hipGetDevice"); delete q; return nullptr; }
+  // raise the dynamic-LDS limit of the large encode tiles; if the runtime
+  // refuses, launches that need more than the default report the error
+  if (tq::set_kernel_attributes() != hipSuccess) (void)hipGetLastError();
+  const size_t bp = pi32.size() * sizeof(float), bs = s32.size() * sizeof(float);
+  if ((e = hipMalloc(&q->d_pi, bp)) != hipSuccess || (e = hipMalloc(&q->d_s, bs)) != hipSuccess ||
+      (e = hipMalloc(&q->d_sp, bs)) != hipSuccess) {
+    hip_fail(e, "hipMalloc");
+    tq_free_quantizer(q);
+    return nullptr;
+  }
+  if ((e = hipMemcpy(q->d_pi, pi32.data(), bp, hipMemcpyHostToDevice)) != hipSuccess ||
+      (e = hipMemcpy(q->d_s, s32.data(), bs, hipMemcpyHostToDevice)) != hipSuccess ||
+      (e = hipMemcpy(q->d_sp, sp32.data(), bs, hipMemcpyHostToDevice)) != hipSuccess) {
+    hip_fail(e, "hipMemcpy");
+    tq_free_quantizer(q);
+    return nullptr;
+  }
+  return q;
+}
+
+void tq_free_quantizer(tq_quantizer* q) {
+  if (!q) return;
+  if (q->d_pi || q->d_s || q->d_sp) {
+    DeviceGuard g(q->device);
+    if (q->d_pi) (void)hipFree(q->d_pi);
+    if (q->d_s) (void)hipFree(q->d_s);
+    if (q->d_sp) (void)hipFree(q->d_sp);
+  }
+  delete q;
+}
+
+int tq_quantizer_info(const tq_quantizer* q, int* d, int* bits, int* m) {
+  if (int r = check_quantizer(q)) return r;
+  if (d) *d = q->d;
+  if (bits) *bits = q->bits;
+  if (m) *m = q->m;
+  return TQ_OK;
+}
+
+int64_t tq_code_words(const tq_quantizer* q, int mode, int64_t nseq, int64_t n) {
+  if (check_quantizer(q) || check_mode(q, mode)) return -1;
+  if (nseq < 0 || n < 0) return fail(TQ_EINVAL, "negative size");
+  const int bp = q->cb[mode].bp;
+  if (mode == TQ_PROD) return nseq * n * ((q->d + 31) / 32) * (bp + 1);
+  return nseq * ((n + 31) / 32) * bp * q->d;
+}
+
+int tq_encode(const tq_quantizer* q, int mode, const void* x, int dtype, int64_t nseq, int64_t n, uint32_t* codes,
+              float* norms, float* gammas, void* stream) {
+  if (int r = check_quantizer(q)) return r;
+  if (int r = check_mode(q, mode)) return r;
+  if (dtype != TQ_F32 && dtype != TQ_BF16) return fail(TQ_EINVAL, "dtype must be TQ_F32 or TQ_BF16");
+  if (nseq < 0 || n < 0) return fail(TQ_EINVAL, "negative size");
+  if (nseq * n == 0) return TQ_OK;
+  if (!x || !codes || !norms || (mode == TQ_PROD && !gammas)) return fail(TQ_EINVAL, "NULL array argument");
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(norms, 16) || (gammas && !aligned(gammas, 16)))
+    return fail(TQ_EINVAL, "device pointers must be 16-byte aligned");
+  if (q->d > 256) return fail(TQ_EUNSUPPORTED, "encode supports d <= 256 (d=%d)", q->d);
+  if (nseq > 65535) return fail(TQ_EUNSUPPORTED, "nseq > 65535");
+  DeviceGuard g(q->device);
+  if (!g.ok) return fail(TQ_EHIP, "cannot select the quantizer's device");
+  hipError_t e = tq::launch_encode(q, mode, x, dtype, nseq, n, codes, norms, gammas, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : hip_fail(e, "encode launch");
+}
+
+int tq_decode(const tq_quantizer* q, int mode, const uint32_t* codes, const float* norms, const float* gammas,
+              int64_t nseq, int64_t n, float* x_out, void* stream) {
+  if (int r = check_quantizer(q)) return r;
+  if (int r = check_mode(q, mode)) return r;
+  if (nseq < 0 || n < 0) return fail(TQ_EINVAL, "negative size");
+  if (nseq * n == 0) return TQ_OK;
+  if (!codes || !norms || !x_out || (mode == TQ_PROD && !gammas)) return fail(TQ_EINVAL, "NULL array argument");
+  if (!aligned(codes, 16) || !aligned(norms, 16) || !aligned(x_out, 16) || (gammas && !aligned(gammas, 16)))
+    return fail(TQ_EINVAL, "device pointers must be 16-byte aligned");
+  if (nseq > 65535) return fail(TQ_EUNSUPPORTED, "nseq > 65535");
+  DeviceGuard g(q->device);
+  if (!g.ok) return fail(TQ_EHIP, "cannot select the quantizer's device");
+  hipError_t e = tq::launch_decode(q, mode, codes, norms, gammas, nseq, n, x_out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : hip_fail(e, "decode launch");
+}
+
+static int check_heads(int B, int Hq, int Hkv) {
+  if (B < 1 || Hq < 1 || Hkv < 1) return fail(TQ_EINVAL, "B, Hq, Hkv must be >= 1");
+  if (Hq % Hkv) return fail(TQ_EINVAL, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  return TQ_OK;
+}
+
+int64_t tq_scores_workspace_bytes(const tq_quantizer* q, int B, int Hq, int Hkv, int64_t n, int topk) {
+  if (check_quantizer(q) || check_heads(B, Hq, Hkv)) return -1;
+  if (q->cb[TQ_PROD].bp < 1) return fail(TQ_EINVAL, "scores need a prod quantizer (bits >= 2)");
+  if (topk > 0) return tq::topk_ws_bytes(q, B, Hq, Hkv, n, topk);
+  return tq::scores_ws_bytes(q, B, Hq, Hkv);
+}
+
+int tq_scores(const tq_quantizer* q, const void* queries, int q_dtype, int B, int Hq, int Hkv, const uint32_t* codes,
+              const float* norms, const float* gammas, int64_t n, int topk, float* out, int64_t* out_idx,
+              void* workspace, int64_t ws_bytes, void* stream) {
+  if (int r = check_quantizer(q)) return r;
+  if (int r = check_heads(B, Hq, Hkv)) return r;
+  if (q->cb[TQ_PROD].bp < 1) return fail(TQ_EINVAL, "scores need a prod quantizer (bits >= 2)");
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return fail(TQ_EINVAL, "q_dtype must be TQ_F32 or TQ_BF16");
+  if (n < 0) return fail(TQ_EINVAL, "negative n");
+  if (topk < 0 || topk > 32) return fail(TQ_EINVAL, "topk must be in [0, 32]");
+  if (topk > 0 && n < topk) return fail(TQ_EINVAL, "topk (%d) larger than n (%lld)", topk, static_cast<long long>(n));
+  if (n == 0) return TQ_OK;
+  if (!queries || !codes || !norms || !gammas || !out || (topk > 0 && !out_idx))
+    return fail(TQ_EINVAL, "NULL array argument");
+  if (!aligned(queries, 16) || !aligned(codes, 16) || !aligned(norms, 16) || !aligned(gammas, 16) ||
+      !aligned(out, 16) || (out_idx && !aligned(out_idx, 16)))
+    return fail(TQ_EINVAL, "device pointers must be 16-byte aligned");
+  if (q->d > 256) return fail(TQ_EUNSUPPORTED, "scores support d <= 256 (d=%d)", q->d);
+  const int64_t need = tq_scores_workspace_bytes(q, B, Hq, Hkv, n, topk);
+  if (need < 0) return TQ_EINVAL;
+  if (!workspace || ws_bytes < need)
+    return fail(TQ_EWORKSPACE, "workspace of %lld bytes needed", static_cast<long long>(need));
+  if (!aligned(workspace, 256)) return fail(TQ_EINVAL, "workspace must be 256-byte aligned");
+  if (static_cast<int64_t>(B) * Hkv * ((Hq / Hkv + 3) / 4) > 65535) return fail(TQ_EUNSUPPORTED, "too many groups");
+  DeviceGuard g(q->device);
+  if (!g.ok) return fail(TQ_EHIP, "cannot select the quantizer's device");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = topk > 0 ? tq::launch_topk(q, queries, q_dtype, B, Hq, Hkv, codes, norms, gammas, n, topk, out, out_idx,
+                                            workspace, st)
+                          : tq::launch_scores(q, queries, q_dtype, B, Hq, Hkv, codes, norms, gammas, n, out, workspace, st);
+  if (e == hipErrorNotSupported) return fail(TQ_EUNSUPPORTED, "shape not supported by the scores kernels");
+  return e == hipSuccess ? TQ_OK : hip_fail(e, "scores launch");
+}
+
+int64_t tq_attend_workspace_bytes(const tq_quantizer* kq, const tq_quantizer* vq, int B, int Hq, int Hkv, int64_t n_comp,
+                                  int n_tail) {
+  if (check_quantizer(kq) || check_quantizer(vq) || check_heads(B, Hq, Hkv)) return -1;
+  if (kq->d != vq->d) return fail(TQ_EINVAL, "key and value quantizers differ in d");
+  if (n_comp < 0 || n_tail < 0) return fail(TQ_EINVAL, "negative size");
+  return tq::attend_ws_bytes(kq, vq, B, Hq, Hkv, n_comp, n_tail);
+}
+
+int tq_attend_decode(const tq_quantizer* kq, const tq_quantizer* vq, const void* queries, int q_dtype, int B, int Hq,
+                     int Hkv, const uint32_t* kcodes, const float* knorms, const float* kgammas, const uint32_t* vcodes,
+                     const float* vnorms, int64_t n_comp, const uint16_t* k_tail, const uint16_t* v_tail, int n_tail,
+                     float scale, float* out, void* workspace, int64_t ws_bytes, void* stream) {
+  if (int r = check_quantizer(kq)) return r;
+  if (int r = check_quantizer(vq)) return r;
+  if (int r = check_heads(B, Hq, Hkv)) return r;
+  if (kq->d != vq->d) return fail(TQ_EINVAL, "key and value quantizers differ in d");
+  if (kq->cb[TQ_PROD].bp < 1) return fail(TQ_EINVAL, "keys need a prod quantizer (bits >= 2)");
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return fail(TQ_EINVAL, "q_dtype must be TQ_F32 or TQ_BF16");
+  if (n_comp < 0 || n_tail < 0) return fail(TQ_EINVAL, "negative size");
+  if (n_comp + n_tail < 1) return fail(TQ_EINVAL, "empty cache (n_comp + n_tail == 0)");
+  if (!queries || !out) return fail(TQ_EINVAL, "NULL queries or output");
+  if (n_comp > 0 && (!kcodes || !knorms || !kgammas || !vcodes || !vnorms)) return fail(TQ_EINVAL, "NULL cache array");
+  if (n_tail > 0 && (!k_tail || !v_tail)) return fail(TQ_EINVAL, "NULL tail array");
+  const void* ptrs[] = {queries, out, kcodes, knorms, kgammas, vcodes, vnorms, k_tail, v_tail};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, 16)) return fail(TQ_EINVAL, "device pointers must be 16-byte aligned");
+  if (kq->d != 128) return fail(TQ_EUNSUPPORTED, "attend supports d = 128 (d=%d)", kq->d);
+  const int64_t need = tq_attend_workspace_bytes(kq, vq, B, Hq, Hkv, n_comp, n_tail);
+  if (need < 0) return TQ_EINVAL;
+  if (!workspace || ws_bytes < need)
+    return fail(TQ_EWORKSPACE, "workspace of %lld bytes needed", static_cast<long long>(need));
+  if (!aligned(workspace, 256)) return fail(TQ_EINVAL, "workspace must be 256-byte aligned");
+  if (!(scale > 0.f)) scale = 1.f / std::sqrt(static_cast<float>(kq->d));
+  DeviceGuard g(kq->device);
+  if (!g.ok) return fail(TQ_EHIP, "cannot select the quantizer's device");
+  hipError_t e = tq::launch_attend(kq, vq, queries, q_dtype, B, Hq, Hkv, kcodes, knorms, kgammas, vcodes, vnorms, n_comp,
+                                   k_tail, v_tail, n_tail, scale, out, workspace, static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return fail(TQ_EUNSUPPORTED, "shape not supported by the attention kernels");
+  return e == hipSuccess ? TQ_OK : hip_fail(e, "attend launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,44 @@
+// Internal declarations shared by the libtq sources (not part of the ABI).
+#pragma once
+
+#include <cstdint>
+#include <vector>
+
+namespace tq {
+
+// host precompute (tq_host.cpp)
+void normals(uint64_t seed, int tag, int64_t n, double* out);
+void rotation(int d, uint64_t seed, double* pi);
+void qjl_matrix(int m, int d, uint64_t seed, double* s);
+int codebook(int d, int K, double* centroids, double* thresholds);
+
+constexpr int kMaxLevels = 16;
+constexpr int kMaxTerms = 8;
+
+// One codebook as the kernels see it (passed by value as a kernel argument).
+// The centroid of an index is also written in the +-1 (Walsh) basis of its
+// bits: with s_p = 2*bit_p - 1, c[idx] = sum_t coef[t] * prod_{p in mask[t]} s_p,
+// and prod_{p in mask} s_p = 2*XOR_{p in mask} bit_p - 1 for odd |mask|.  A
+// symmetric codebook has only odd-size masks, 2^(bp-1) of them.
+struct Codebook {
+  int bp = 0;      // index bits (0 = codebook unavailable)
+  int levels = 0;  // 2^bp
+  int nterms = 0;  // 2^(bp-1)
+  float c[kMaxLevels] = {};
+  float t[kMaxLevels] = {};   // thresholds, levels-1 used
+  int mask[kMaxTerms] = {};
+  float coef[kMaxTerms] = {};
+  float coef_sum = 0.f;       // sum of coef (the centroid of "all bits 0" is -coef_sum)
+};
+
+}  // namespace tq
+
+struct tq_quantizer {
+  int d = 0, bits = 0, m = 0, device = 0;
+  uint64_t seed = 0;
+  std::vector<double> pi, s;          // host float64 copies (row major)
+  tq::Codebook cb[2];                 // [TQ_PROD], [TQ_MSE]
+  float* d_pi = nullptr;              // [d][d]   y = Pi x
+  float* d_s = nullptr;               // [m][d]   QJL matrix
+  float* d_sp = nullptr;              // [m][d]   S' = S Pi^T (acts on rotated residuals)
+};
