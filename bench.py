@@ -1,0 +1,287 @@
+"""Benchmark of the TurboQuant hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa|long|decode|search]
+
+One step = one pass of the whole hot path over one batch of synthetic input
+already resident in HBM: encode the keys (prod codes) and values (mse codes),
+rotate/project the queries, compute the logits from the packed keys, and run
+decode attention (softmax . V) over the packed cache.  The default workload is
+the GQA decode layer (batch 8, 8 KV heads, 32 query heads, 32768 tokens,
+d = 128, 3-bit keys and values).
+
+Printed: one JSON line.  `value` is the packed-cache bandwidth of the logits
+kernel (packed key bytes / kernel time); encode keys/s and the attention
+kernel are reported beside it.  Kernel times come from HIP events recorded on
+the stream the kernels run on, over the timed steps.  Code buffers alternate
+between two copies so that every scan reads codes written a full step (more
+than 1 GB of other traffic) earlier, i.e. from HBM, not from the 256 MB
+last-level cache.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+FP32_MFMA_PEAK_TFLOPS = 157.3
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gqa", choices=["gqa", "long", "decode", "search"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def bf16_tensor(torch, u16, dev):
+    import numpy as np
+    return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+class Timer:
+    """Per-kernel HIP-event timing on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pending = []
+        self.acc = {}
+        self.count = {}
+
+    def mark(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def span(self, name, a, b):
+        self.pending.append((name, a, b))
+
+    def collect(self):
+        for name, a, b in self.pending:
+            self.acc[name] = self.acc.get(name, 0.0) + a.elapsed_time(b)
+            self.count[name] = self.count.get(name, 0) + 1
+        self.pending = []
+
+    def avg_ms(self, name):
+        return self.acc[name] / self.count[name]
+
+
+def cpu_baseline_gqa(wl, steps_note):
+    """The oracle as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import tq_oracle as o
+    oq = o.Quantizer(128, 3, 0)
+    # sample: the first 16384 keys of each of the first 4 (batch, KV head) groups
+    nk = 16384
+    keys = wl.arrays["k"][0, :4, :nk].reshape(-1, 128).astype(np.float64)
+    qs = wl.arrays["q"][0, :16].astype(np.float64)        # the 4 query heads of each of the 4 groups
+    t0 = time.perf_counter()
+    idx, bits, nrm, gam = o.encode_prod(oq, keys)
+    t1 = time.perf_counter()
+    reps = 0
+    t2 = time.perf_counter()
+    while True:
+        for h in range(4):
+            sl = slice(h * nk, (h + 1) * nk)
+            o.scores(oq, qs[4 * h:4 * h + 4], idx[sl], bits[sl], nrm[sl], gam[sl])
+        reps += 1
+        if time.perf_counter() - t2 > 10.0:
+            break
+    t3 = time.perf_counter()
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    packed = 4 * nk * o.record_bytes("prod", 128, 3)
+    return {
+        "value": packed * reps / (t3 - t2) / 1e9,
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"float64 numpy oracle: logits of 4 query heads x {nk} keys for 4 (batch, KV head) groups, "
+                  f"{reps} passes in {t3 - t2:.1f} s; encode of the same {4 * nk} keys took {t1 - t0:.2f} s "
+                  f"({4 * nk / (t1 - t0):.0f} keys/s)",
+        "encode_keys_per_s": 4 * nk / (t1 - t0),
+    }
+
+
+def run_gqa(args, torch, dev, tq, wl_fn, name, bits, n_tail=0):
+    import numpy as np
+    wl = wl_fn()
+    B, Hkv, Hq, N = wl.meta["B"], wl.meta["Hkv"], wl.meta["Hq"], wl.meta["N"]
+    d = wl.d
+    n_comp = N - n_tail
+    k_all = bf16_tensor(torch, wl.arrays["k_bf16"], dev).view(B * Hkv, N, d)
+    v_all = bf16_tensor(torch, wl.arrays["v_bf16"], dev).view(B * Hkv, N, d)
+    q = bf16_tensor(torch, wl.arrays["q_bf16"], dev)
+    k = k_all[:, :n_comp].contiguous()
+    v = v_all[:, :n_comp].contiguous()
+    k_tail = k_all[:, n_comp:].contiguous().view(B, Hkv, n_tail, d) if n_tail else None
+    v_tail = v_all[:, n_comp:].contiguous().view(B, Hkv, n_tail, d) if n_tail else None
+    qz = tq.Quantizer(d, bits, 0)
+    nseq = B * Hkv
+    copies = []
+    for _ in range(2):
+        ck = torch.empty(qz.code_words(tq.TQ_PROD, nseq, n_comp), dtype=torch.int32, device=dev)
+        kn = torch.empty(nseq * n_comp, dtype=torch.float32, device=dev)
+        kg = torch.empty(nseq * n_comp, dtype=torch.float32, device=dev)
+        cv = torch.empty(qz.code_words(tq.TQ_MSE, nseq, n_comp), dtype=torch.int32, device=dev)
+        vn = torch.empty(nseq * n_comp, dtype=torch.float32, device=dev)
+        copies.append((ck, kn, kg, cv, vn))
+    logits = torch.empty((B, Hq, n_comp), dtype=torch.float32, device=dev)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    ws_s = torch.empty(tq.scores_workspace_bytes(qz, B, Hq, Hkv, n_comp), dtype=torch.uint8, device=dev)
+    attend_ok = True
+    try:
+        ws_a = torch.empty(max(tq.attend_workspace_bytes(qz, qz, B, Hq, Hkv, n_comp, n_tail), 256), dtype=torch.uint8,
+                           device=dev)
+    except Exception:
+        attend_ok = False
+    # fill both copies once
+    for c in copies:
+        tq.tq_encode(qz, tq.TQ_PROD, k, out=(c[0], c[1], c[2]))
+        tq.tq_encode(qz, tq.TQ_MSE, v, out=(c[3], c[4], None))
+    if attend_ok:
+        try:
+            c = copies[0]
+            tq.tq_attend_decode(qz, qz, q, c[0], c[1], c[2], c[3], c[4], Hkv, n_comp, k_tail, v_tail, 0.0, out=out,
+                                workspace=ws_a)
+        except tq.TQError:
+            attend_ok = False
+    torch.cuda.synchronize()
+
+    timer = Timer(torch)
+
+    def step(i, timed):
+        w = copies[i % 2]          # written now
+        r = copies[(i + 1) % 2]    # written one step ago
+        e0 = timer.mark()
+        tq.tq_encode(qz, tq.TQ_PROD, k, out=(w[0], w[1], w[2]))
+        e1 = timer.mark()
+        tq.tq_encode(qz, tq.TQ_MSE, v, out=(w[3], w[4], None))
+        e2 = timer.mark()
+        tq.tq_query_prep(qz, q, Hkv, workspace=ws_s)
+        e3 = timer.mark()
+        tq.tq_scores_from_prep(qz, B, Hq, Hkv, r[0], r[1], r[2], n_comp, ws_s, out=logits)
+        e4 = timer.mark()
+        if attend_ok:
+            tq.tq_attend_decode(qz, qz, q, r[0], r[1], r[2], r[3], r[4], Hkv, n_comp, k_tail, v_tail, 0.0, out=out,
+                                workspace=ws_a)
+        e5 = timer.mark()
+        if timed:
+            timer.span("encode_keys", e0, e1)
+            timer.span("encode_values", e1, e2)
+            timer.span("query_prep", e2, e3)
+            timer.span("scores", e3, e4)
+            if attend_ok:
+                timer.span("attend", e4, e5)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    timer.collect()
+
+    nkeys = nseq * n_comp
+    rec_k = 4 * ((d + 31) // 32) * bits + 8          # packed key bytes per key (codes + norm + gamma)
+    rec_v = (bits * d) // 8 + 4                       # packed value bytes per token (codes + norm)
+    G = Hq // Hkv
+    scores_ms = timer.avg_ms("scores")
+    scores_alg = nkeys * (rec_k + 4 * G)              # read packed keys, write fp32 logits
+    packed_gbs = nkeys * rec_k / (scores_ms * 1e-3) / 1e9
+    enc_ms = timer.avg_ms("encode_keys")
+    enc_flop = nkeys * 4.0 * d * d                    # Pi x and S' rho per key
+    res = {
+        "metric": "packed-KV logits GB/s (% of HBM peak) + encode keys/s, d=128 3-bit, 1 MI355X",
+        "value": round(packed_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round((t1 - t0) * 1e3 / args.steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8",
+        "data": "synthetic",
+        "config": {"workload": name, "batch": B, "kv_heads": Hkv, "q_heads": Hq, "tokens": N, "tail_bf16": n_tail,
+                   "d": d, "bits_keys": bits, "bits_values": bits, "key_mode": "prod (b-1 MSE + 1 QJL)",
+                   "value_mode": "mse"},
+        "packed_pct_of_hbm_peak": round(100 * packed_gbs / HBM_PEAK_GBS, 1),
+        "encode_keys_per_s": round(nkeys / (enc_ms * 1e-3), 0),
+        "kernels_ms": {k2: round(timer.avg_ms(k2), 4) for k2 in timer.acc},
+        "roofline": {
+            "kernel": "scores_kernel (tq_scores_from_prep)",
+            "bound": "hbm",
+            "achieved": round(scores_alg / (scores_ms * 1e-3) / 1e9, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(scores_alg / (scores_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": scores_alg,
+            "bytes_per_key": rec_k + 4 * G,
+        },
+        "roofline_encode": {
+            "kernel": "encode_kernel (tq_encode, prod)",
+            "bound": "mfma",
+            "achieved": round(enc_flop / (enc_ms * 1e-3) / 1e12, 2),
+            "peak": FP32_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(enc_flop / (enc_ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
+            "flop_per_key": 4 * d * d,
+        },
+    }
+    if attend_ok:
+        at_ms = timer.avg_ms("attend")
+        at_bytes = nkeys * (rec_k + rec_v) + (nseq * n_tail * d * 2 * 2)
+        res["roofline_attend"] = {
+            "kernel": "tq_attend_decode (all its launches)",
+            "bound": "hbm",
+            "achieved": round(at_bytes / (at_ms * 1e-3) / 1e9, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(at_bytes / (at_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes_per_launch": at_bytes,
+        }
+    return res, wl
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU sharding is "
+              "described in DESIGN.md, not implemented.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from vector_quantization_tq_amd import tq
+    from vector_quantization_tq_amd import workloads as W
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    if args.workload == "gqa":
+        res, wl = run_gqa(args, torch, dev, tq, W.gqa_layer, "gqa-decode-layer b8 kv8 q32 n32768 d128 3-bit", 3)
+        if not args.no_cpu_baseline:
+            res["cpu_baseline"] = cpu_baseline_gqa(wl, args.steps)
+    elif args.workload == "long":
+        res, wl = run_gqa(args, torch, dev, tq, W.long_context, "long-context b1 kv8 q32 n131072 tail256 d128 4-bit", 4,
+                          n_tail=256)
+    else:
+        raise SystemExit(f"workload {args.workload} is not wired into bench.py yet")
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

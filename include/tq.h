@@ -151,6 +151,19 @@ int tq_decode(const tq_quantizer* q, int mode, const uint32_t* codes, const floa
  *              (1 <= topk <= 32)
  *   workspace: device scratch of at least tq_scores_workspace_bytes(...) */
 int64_t tq_scores_workspace_bytes(const tq_quantizer* q, int B, int Hq, int Hkv, int64_t n, int topk);
+
+/* The two halves of tq_scores (topk == 0), for callers that score several
+ * caches with the same queries or time the scan alone:
+ * tq_query_prep rotates and projects the queries once and writes the
+ * query-side MFMA operands into `workspace` (a2a how-to-implement: the query
+ * is pre-rotated once); tq_scores_from_prep streams the packed keys against
+ * them.  The workspace must not change between the two calls. */
+int tq_query_prep(const tq_quantizer* q, const void* queries, int q_dtype, int B, int Hq, int Hkv, void* workspace,
+                  int64_t ws_bytes, void* stream);
+int tq_scores_from_prep(const tq_quantizer* q, int B, int Hq, int Hkv, const uint32_t* codes, const float* norms,
+                        const float* gammas, int64_t n, float* logits, const void* workspace, int64_t ws_bytes,
+                        void* stream);
+
 int tq_scores(const tq_quantizer* q, const void* queries, int q_dtype, int B, int Hq, int Hkv,
               const uint32_t* codes, const float* norms, const float* gammas, int64_t n, int topk,
               float* out, int64_t* out_idx, void* workspace, int64_t ws_bytes, void* stream);

@@ -289,6 +289,51 @@ int tq_scores(const tq_quantizer* q, const void* queries, int q_dtype, int B, in
   return e == hipSuccess ? TQ_OK : hip_fail(e, "scores launch");
 }
 
+int tq_query_prep(const tq_quantizer* q, const void* queries, int q_dtype, int B, int Hq, int Hkv, void* workspace,
+                  int64_t ws_bytes, void* stream) {
+  if (int r = check_quantizer(q)) return r;
+  if (int r = check_heads(B, Hq, Hkv)) return r;
+  if (q->cb[TQ_PROD].bp < 1) return fail(TQ_EINVAL, "scores need a prod quantizer (bits >= 2)");
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return fail(TQ_EINVAL, "q_dtype must be TQ_F32 or TQ_BF16");
+  if (!queries) return fail(TQ_EINVAL, "NULL queries");
+  if (!aligned(queries, 16)) return fail(TQ_EINVAL, "device pointers must be 16-byte aligned");
+  if (q->d > 256) return fail(TQ_EUNSUPPORTED, "scores support d <= 256 (d=%d)", q->d);
+  const int64_t need = tq::scores_ws_bytes(q, B, Hq, Hkv);
+  if (!workspace || ws_bytes < need)
+    return fail(TQ_EWORKSPACE, "workspace of %lld bytes needed", static_cast<long long>(need));
+  if (!aligned(workspace, 256)) return fail(TQ_EINVAL, "workspace must be 256-byte aligned");
+  if (static_cast<int64_t>(B) * Hkv * ((Hq / Hkv + 3) / 4) * 4 > 0x7fffffff) return fail(TQ_EUNSUPPORTED, "too many queries");
+  DeviceGuard g(q->device);
+  if (!g.ok) return fail(TQ_EHIP, "cannot select the quantizer's device");
+  hipError_t e = tq::launch_query_prep_ws(q, queries, q_dtype, B, Hq, Hkv, workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : hip_fail(e, "query prep launch");
+}
+
+int tq_scores_from_prep(const tq_quantizer* q, int B, int Hq, int Hkv, const uint32_t* codes, const float* norms,
+                        const float* gammas, int64_t n, float* logits, const void* workspace, int64_t ws_bytes,
+                        void* stream) {
+  if (int r = check_quantizer(q)) return r;
+  if (int r = check_heads(B, Hq, Hkv)) return r;
+  if (q->cb[TQ_PROD].bp < 1) return fail(TQ_EINVAL, "scores need a prod quantizer (bits >= 2)");
+  if (n < 0) return fail(TQ_EINVAL, "negative n");
+  if (n == 0) return TQ_OK;
+  if (!codes || !norms || !gammas || !logits) return fail(TQ_EINVAL, "NULL array argument");
+  if (!aligned(codes, 16) || !aligned(norms, 16) || !aligned(gammas, 16) || !aligned(logits, 16))
+    return fail(TQ_EINVAL, "device pointers must be 16-byte aligned");
+  if (q->d > 256) return fail(TQ_EUNSUPPORTED, "scores support d <= 256 (d=%d)", q->d);
+  const int64_t need = tq::scores_ws_bytes(q, B, Hq, Hkv);
+  if (!workspace || ws_bytes < need)
+    return fail(TQ_EWORKSPACE, "workspace of %lld bytes needed", static_cast<long long>(need));
+  if (!aligned(workspace, 256)) return fail(TQ_EINVAL, "workspace must be 256-byte aligned");
+  if (static_cast<int64_t>(B) * Hkv * ((Hq / Hkv + 3) / 4) > 65535) return fail(TQ_EUNSUPPORTED, "too many groups");
+  DeviceGuard g(q->device);
+  if (!g.ok) return fail(TQ_EHIP, "cannot select the quantizer's device");
+  hipError_t e = tq::launch_scores_scan(q, B, Hq, Hkv, codes, norms, gammas, n, logits, workspace,
+                                        static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return fail(TQ_EUNSUPPORTED, "shape not supported by the scores kernels");
+  return e == hipSuccess ? TQ_OK : hip_fail(e, "scores launch");
+}
+
 int64_t tq_attend_workspace_bytes(const tq_quantizer* kq, const tq_quantizer* vq, int B, int Hq, int Hkv, int64_t n_comp,
                                   int n_tail) {
   if (check_quantizer(kq) || check_quantizer(vq) || check_heads(B, Hq, Hkv)) return -1;

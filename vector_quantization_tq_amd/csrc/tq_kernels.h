@@ -15,6 +15,10 @@ hipError_t launch_decode(const tq_quantizer* q, int mode, const uint32_t* codes,
                          int64_t nseq, int64_t n, float* out, hipStream_t st);
 
 int64_t scores_ws_bytes(const tq_quantizer* q, int B, int Hq, int Hkv);
+hipError_t launch_query_prep_ws(const tq_quantizer* q, const void* queries, int q_dtype, int B, int Hq, int Hkv,
+                                void* ws, hipStream_t st);
+hipError_t launch_scores_scan(const tq_quantizer* q, int B, int Hq, int Hkv, const uint32_t* codes, const float* norms,
+                              const float* gammas, int64_t n, float* out, const void* ws, hipStream_t st);
 hipError_t launch_scores(const tq_quantizer* q, const void* queries, int q_dtype, int B, int Hq, int Hkv,
                          const uint32_t* codes, const float* norms, const float* gammas, int64_t n, float* out,
                          void* ws, hipStream_t st);

@@ -155,71 +155,200 @@ __global__ void __launch_bounds__(256) query_prep_kernel(const void* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Scores: grid (key blocks, groups * row tiles); 4 waves, each wave handles
-// kTilesPerWave tiles of 16 keys.  Lane l: key (l & 15) of the tile, word
-// group (l >> 4) of each 128-coordinate chunk.
+// Scores: grid (blocks per group, groups * row tiles), 4 independent waves
+// per block.  A wave takes batches of 64 consecutive keys (4 MFMA tiles of
+// 16): batch k of the group goes to wave (k mod waves-per-group).  The packed
+// words of a batch are one contiguous run; they travel from HBM straight into
+// a ring of kRing LDS slots owned by the wave (global_load_lds, no registers
+// held while in flight), together with the batch's norms and gammas.  The
+// wave consumes slot i while the next kRing-1 batches are in flight, reading
+// the words back in the MFMA operand layout.  The 4 x 64 logits of a batch are
+// staged in LDS and leave as one 256-byte run per query row.
+//
+// Vector-memory waits are explicit: the counter (vmcnt) retires in issue
+// order, so waiting for batch i means allowing every younger load and store
+// of this wave to stay outstanding.
 // ---------------------------------------------------------------------------
-constexpr int kTilesPerWave = 8;
-constexpr int kKeysPerBlock = 4 * kTilesPerWave * 16;
+#ifndef TQ_SCORES_WAVES
+#define TQ_SCORES_WAVES 4096
+#endif
+#ifndef TQ_SCORES_RING
+#define TQ_SCORES_RING 2
+#endif
+constexpr int kTargetWaves = TQ_SCORES_WAVES;   // resident waves aimed at (256 CUs x 4 SIMDs x 4)
+constexpr int kRing = TQ_SCORES_RING;
+constexpr int kBatchKeys = 64;
 
-template <int BP, int C>
+// s_waitcnt immediate that waits for vmcnt <= N only (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+template <int N>
+__device__ __forceinline__ void wait_vm_upto(int n) {   // runtime n in [0, N]
+  if constexpr (N > 0) {
+    if (n >= N) { wait_vm<N>(); return; }
+    wait_vm_upto<N - 1>(n);
+  } else {
+    wait_vm<0>();
+  }
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+template <int WPK>
+struct DmaPlan {
+  // bytes per lane per load; the 12-byte form places lanes 16 bytes apart in LDS, so it is not used
+  static constexpr int SZ = (WPK % 4 == 0) ? 16 : 4;
+  static constexpr int WPL = SZ / 4;                                            // words per lane per load
+  static constexpr int NC = WPK / WPL;                                          // loads for the packed words
+  static constexpr int L = NC + 2;                                              // + norms + gammas
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ lds_void* to_lds(void* p) {
+  return reinterpret_cast<lds_void*>(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)));
+}
+
+// issue the loads of one batch (keys k0 .. k0+63 of a sequence of n keys) into an LDS slot
+template <int WPK>
+__device__ __forceinline__ void issue_batch(uint32_t* slot, const uint32_t* __restrict__ cbase,
+                                            const float* __restrict__ nb, const float* __restrict__ gb, int64_t k0,
+                                            int64_t n, int lane) {
+  using P = DmaPlan<WPK>;
+  const int64_t limit = (n - k0) * WPK;        // valid words from this batch's start (> 0)
+#pragma unroll
+  for (int i = 0; i < P::NC; ++i) {
+    int64_t off = static_cast<int64_t>(i) * 64 * P::WPL + lane * P::WPL;
+    if (off + P::WPL > limit) off = limit - P::WPL;   // past the end: re-read the last valid words
+    const uint32_t* src = cbase + k0 * WPK + off;
+    lds_void* dst = to_lds(slot + i * 64 * P::WPL);
+    if constexpr (P::SZ == 16) {
+      __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+    } else {
+      __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+    }
+  }
+  int64_t kk = k0 + lane;
+  if (kk >= n) kk = n - 1;
+  float* ng = reinterpret_cast<float*>(slot + kBatchKeys * WPK);
+  __builtin_amdgcn_global_load_lds(nb + kk, to_lds(ng), 4, 0, 0);
+  __builtin_amdgcn_global_load_lds(gb + kk, to_lds(ng + kBatchKeys), 4, 0, 0);
+}
+
+template <int BP, int GW>
 __global__ void __launch_bounds__(256) scores_kernel(const uint32_t* __restrict__ codes, const float* __restrict__ norms,
-                                                     const float* __restrict__ gammas, int64_t n, int d, int Hq,
-                                                     int Hkv, int G, int RT, const uint8_t* __restrict__ wsA,
+                                                     const float* __restrict__ gammas, int64_t n, int Hq, int Hkv,
+                                                     int G, int RT, const uint8_t* __restrict__ wsA,
                                                      const float* __restrict__ wsC, float* __restrict__ out) {
   constexpr int T = (1 << (BP - 1)) + 1;
   constexpr int W = BP + 1;
+  constexpr int C = (GW + 3) / 4;
+  constexpr int WPK = GW * W;                                   // packed words per key
+  constexpr int SLOTW = kBatchKeys * WPK + 2 * kBatchKeys;      // words per ring slot
+  constexpr int WAVEW = kRing * SLOTW + 4 * kBatchKeys;         // + logit staging
+  using P = DmaPlan<WPK>;
+  constexpr int L = P::L;
+  __shared__ __attribute__((aligned(16))) uint32_t lds[4 * WAVEW];
+
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t* ring = lds + wave * WAVEW;
+  float* lout = reinterpret_cast<float*>(ring + kRing * SLOTW);
+
   const int gy = blockIdx.y;
   const int grp = gy / RT, rt = gy - grp * RT;
   const int b = grp / Hkv, kvh = grp - b * Hkv;
-  const int qi = lane >> 4;
-  const int Gw = (d + 31) >> 5;
+  const int qi = lane >> 4, j = lane & 15, g = lane >> 4;
 
+  const uint32_t* cbase = codes + static_cast<int64_t>(grp) * n * WPK;
+  const float* nb = norms + static_cast<int64_t>(grp) * n;
+  const float* gb = gammas + static_cast<int64_t>(grp) * n;
+  const int64_t nbatch = (n + kBatchKeys - 1) / kBatchKeys;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 4;
+  const int64_t first = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  if (first >= nbatch) return;
+  const int nbw = static_cast<int>((nbatch - first + stride - 1) / stride);   // batches of this wave
+
+  // prologue: fill the ring
+#pragma unroll
+  for (int s2 = 0; s2 < kRing; ++s2)
+    if (s2 < nbw) issue_batch<WPK>(ring + s2 * SLOTW, cbase, nb, gb, (first + s2 * stride) * kBatchKeys, n, lane);
+
+  // query-side operands (L2 resident)
   v8i A[T][C];
   const v8i* ap = reinterpret_cast<const v8i*>(wsA + static_cast<int64_t>(gy) * T * C * 2048);
 #pragma unroll
   for (int t = 0; t < T; ++t)
 #pragma unroll
     for (int c = 0; c < C; ++c) A[t][c] = ap[(t * C + c) * 64 + lane];
-  const float* cs = wsC + (static_cast<int64_t>(gy) * 4 + qi) * 16;
-  const float cM = cs[0], cQ = cs[1];
-  const float sM0 = cs[2], sM1 = cs[3], sM2 = cs[4], sM3 = cs[5];
-  const float sQ0 = cs[6], sQ1 = cs[7], sQ2 = cs[8], sQ3 = cs[9];
-  const int qg = rt * 4 + qi;
-  float* orow = (qg < G) ? out + (static_cast<int64_t>(b) * Hq + kvh * G + qg) * n : nullptr;
+  float cs[10];
+  {
+    const float* cp = wsC + (static_cast<int64_t>(gy) * 4 + qi) * 16;
+#pragma unroll
+    for (int i = 0; i < 10; ++i) cs[i] = cp[i];
+  }
+  // output row of lane l in the store phase: query (l >> 4), keys 4*(l & 15) .. +3
+  const int sqg = rt * 4 + (lane >> 4);
+  float* srow = (sqg < G) ? out + (static_cast<int64_t>(b) * Hq + kvh * G + sqg) * n : nullptr;
+  const bool vec_store = (n & 3) == 0;
+  const int S = vec_store ? 1 : 4;   // store instructions per batch (all but the last batch)
 
-  const uint32_t* cbase = codes + static_cast<int64_t>(grp) * n * Gw * W;
-  const float* nb = norms + static_cast<int64_t>(grp) * n;
-  const float* gb = gammas + static_cast<int64_t>(grp) * n;
-  const int64_t kstart = static_cast<int64_t>(blockIdx.x) * kKeysPerBlock + wave * (kTilesPerWave * 16);
-
-  for (int tile = 0; tile < kTilesPerWave; ++tile) {
-    const int64_t k0 = kstart + tile * 16;
-    if (k0 >= n) break;
-    const int64_t key = k0 + (lane & 15);
-    const bool kv = key < n;
-    v4f accM = {0.f, 0.f, 0.f, 0.f}, accQ = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-      const int gg = 4 * c + (lane >> 4);
-      uint32_t w[5] = {0u, 0u, 0u, 0u, 0u};
-      if (kv && gg < Gw) {
-        const uint32_t* wp = cbase + (key * Gw + gg) * W;
-#pragma unroll
-        for (int p = 0; p < W; ++p) w[p] = wp[p];
-      }
-#pragma unroll
-      for (int t = 0; t < T - 1; ++t) {
-        accM = mfma_fp8_fp4(A[t][c], bits_to_fp4(walsh_word<BP>(w, t)), accM);
-      }
-      accQ = mfma_fp8_fp4(A[T - 1][c], bits_to_fp4(w[BP]), accQ);
+  for (int i = 0; i < nbw; ++i) {
+    const int64_t k0 = (first + static_cast<int64_t>(i) * stride) * kBatchKeys;
+    uint32_t* slot = ring + (i % kRing) * SLOTW;
+    const float* lng = reinterpret_cast<const float*>(slot + kBatchKeys * WPK);
+    // wait for this batch: younger ops are the loads of later batches already issued
+    // and the stores of the previous kRing-1 iterations
+    {
+      const int cl = min(kRing - 1, nbw - 1 - i);
+      const int cst = min(i, kRing - 1);
+      wait_vm_upto<(kRing - 1) * (L + 4)>(cl * L + cst * S);
     }
-    pin(accM);
-    pin(accQ);
-    const float mse = fmaf(accM[0], sM0, fmaf(accM[1], sM1, fmaf(accM[2], sM2, fmaf(accM[3], sM3, cM))));
-    const float qjl = fmaf(accQ[0], sQ0, fmaf(accQ[1], sQ1, fmaf(accQ[2], sQ2, fmaf(accQ[3], sQ3, cQ))));
-    if (kv && orow) orow[key] = fmaf(nb[key], mse, gb[key] * qjl);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int kk = 16 * u + j;   // key of this lane within the batch
+      v4f accM = {0.f, 0.f, 0.f, 0.f}, accQ = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const int gg = 4 * c + g;
+        uint32_t w[5] = {0u, 0u, 0u, 0u, 0u};
+        if (gg < GW) {
+#pragma unroll
+          for (int p = 0; p < W; ++p) w[p] = slot[(kk * GW + gg) * W + p];
+        }
+#pragma unroll
+        for (int t = 0; t < T - 1; ++t) accM = mfma_fp8_fp4(A[t][c], bits_to_fp4(walsh_word<BP>(w, t)), accM);
+        accQ = mfma_fp8_fp4(A[T - 1][c], bits_to_fp4(w[BP]), accQ);
+      }
+      pin(accM);
+      pin(accQ);
+      const float mse = fmaf(accM[0], cs[2], fmaf(accM[1], cs[3], fmaf(accM[2], cs[4], fmaf(accM[3], cs[5], cs[0]))));
+      const float qjl = fmaf(accQ[0], cs[6], fmaf(accQ[1], cs[7], fmaf(accQ[2], cs[8], fmaf(accQ[3], cs[9], cs[1]))));
+      lout[qi * kBatchKeys + kk] = fmaf(lng[kk], mse, lng[kBatchKeys + kk] * qjl);
+    }
+    __builtin_amdgcn_wave_barrier();
+    {
+      typedef float f4 __attribute__((ext_vector_type(4)));
+      const f4 v = *reinterpret_cast<const f4*>(lout + (lane >> 4) * kBatchKeys + 4 * (lane & 15));
+      const int64_t key = k0 + 4 * (lane & 15);
+      if (srow) {
+        if (vec_store && key + 4 <= n) {
+          __builtin_nontemporal_store(v, reinterpret_cast<f4*>(srow + key));
+        } else {
+          if (key + 0 < n) srow[key + 0] = v.x;
+          if (key + 1 < n) srow[key + 1] = v.y;
+          if (key + 2 < n) srow[key + 2] = v.z;
+          if (key + 3 < n) srow[key + 3] = v.w;
+        }
+      }
+    }
+    // every LDS read of this slot (and of the staging area) has returned before
+    // the slot is refilled and the staging area rewritten
+    wait_lgkm0();
+    __builtin_amdgcn_wave_barrier();
+    if (i + kRing < nbw)
+      issue_batch<WPK>(slot, cbase, nb, gb, (first + static_cast<int64_t>(i + kRing) * stride) * kBatchKeys, n, lane);
   }
 }
 
@@ -244,9 +373,8 @@ hipError_t launch_query_prep(const tq_quantizer* q, const void* queries, int q_d
   return hipGetLastError();
 }
 
-hipError_t launch_scores(const tq_quantizer* q, const void* queries, int q_dtype, int B, int Hq, int Hkv,
-                         const uint32_t* codes, const float* norms, const float* gammas, int64_t n, float* out,
-                         void* ws, hipStream_t st) {
+hipError_t launch_query_prep_ws(const tq_quantizer* q, const void* queries, int q_dtype, int B, int Hq, int Hkv,
+                                void* ws, hipStream_t st) {
   const int G = Hq / Hkv;
   const int RT = (G + 3) / 4;
   const int T = q->cb[0].nterms + 1;
@@ -254,19 +382,45 @@ hipError_t launch_scores(const tq_quantizer* q, const void* queries, int q_dtype
   const int64_t groups = static_cast<int64_t>(B) * Hkv * RT;
   uint8_t* wsA = static_cast<uint8_t*>(ws);
   float* wsC = reinterpret_cast<float*>(wsA + groups * T * C * 2048);
-  hipError_t e = launch_query_prep(q, queries, q_dtype, B, Hq, Hkv, wsA, wsC, st);
-  if (e != hipSuccess) return e;
-  dim3 grid(static_cast<unsigned>((n + kKeysPerBlock - 1) / kKeysPerBlock), static_cast<unsigned>(groups));
+  return launch_query_prep(q, queries, q_dtype, B, Hq, Hkv, wsA, wsC, st);
+}
+
+hipError_t launch_scores_scan(const tq_quantizer* q, int B, int Hq, int Hkv, const uint32_t* codes, const float* norms,
+                              const float* gammas, int64_t n, float* out, const void* ws, hipStream_t st) {
+  const int G = Hq / Hkv;
+  const int RT = (G + 3) / 4;
+  const int T = q->cb[0].nterms + 1;
+  const int C = (q->d + 127) / 128;
+  const int64_t groups = static_cast<int64_t>(B) * Hkv * RT;
+  const uint8_t* wsA = static_cast<const uint8_t*>(ws);
+  const float* wsC = reinterpret_cast<const float*>(wsA + groups * T * C * 2048);
+  const int64_t nbatch = (n + kBatchKeys - 1) / kBatchKeys;
+  int64_t bx = (kTargetWaves / 4 + groups - 1) / groups;
+  const int64_t need = (nbatch + 3) / 4;
+  if (bx > need) bx = need;
+  if (bx < 1) bx = 1;
+  dim3 grid(static_cast<unsigned>(bx), static_cast<unsigned>(groups));
   const int bp = q->cb[0].bp;
-#define TQ_SC(BPV, CV)                                                                                           \
-  if (bp == BPV && C == CV) {                                                                                    \
-    hipLaunchKernelGGL((scores_kernel<BPV, CV>), grid, dim3(256), 0, st, codes, norms, gammas, n, q->d, Hq, Hkv, G, \
-                       RT, wsA, wsC, out);                                                                       \
+  const int gw = (q->d + 31) / 32;
+#define TQ_SC(BPV, GWV)                                                                                          \
+  if (bp == BPV && gw == GWV) {                                                                                  \
+    hipLaunchKernelGGL((scores_kernel<BPV, GWV>), grid, dim3(256), 0, st, codes, norms, gammas, n, Hq, Hkv, G, RT, \
+                       wsA, wsC, out);                                                                           \
     return hipGetLastError();                                                                                    \
   }
-  TQ_SC(1, 1) TQ_SC(2, 1) TQ_SC(3, 1) TQ_SC(1, 2) TQ_SC(2, 2) TQ_SC(3, 2)
+#define TQ_SC_ALL(GWV) TQ_SC(1, GWV) TQ_SC(2, GWV) TQ_SC(3, GWV)
+  TQ_SC_ALL(1) TQ_SC_ALL(2) TQ_SC_ALL(3) TQ_SC_ALL(4) TQ_SC_ALL(5) TQ_SC_ALL(6) TQ_SC_ALL(7) TQ_SC_ALL(8)
+#undef TQ_SC_ALL
 #undef TQ_SC
-  return hipErrorInvalidValue;
+  return hipErrorNotSupported;
+}
+
+hipError_t launch_scores(const tq_quantizer* q, const void* queries, int q_dtype, int B, int Hq, int Hkv,
+                         const uint32_t* codes, const float* norms, const float* gammas, int64_t n, float* out,
+                         void* ws, hipStream_t st) {
+  hipError_t e = launch_query_prep_ws(q, queries, q_dtype, B, Hq, Hkv, ws, st);
+  if (e != hipSuccess) return e;
+  return launch_scores_scan(q, B, Hq, Hkv, codes, norms, gammas, n, out, ws, st);
 }
 
 }  // namespace tq

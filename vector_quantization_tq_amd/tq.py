@@ -22,7 +22,8 @@ TQ_F32, TQ_BF16 = 0, 1
 EXPORTS = [
     "tq_version", "tq_last_error", "tq_host_normals", "tq_host_rotation", "tq_host_qjl_matrix", "tq_host_codebook",
     "tq_make_quantizer", "tq_free_quantizer", "tq_quantizer_info", "tq_code_words", "tq_encode", "tq_decode",
-    "tq_scores_workspace_bytes", "tq_scores", "tq_attend_workspace_bytes", "tq_attend_decode",
+    "tq_scores_workspace_bytes", "tq_query_prep", "tq_scores_from_prep", "tq_scores", "tq_attend_workspace_bytes",
+    "tq_attend_decode",
 ]
 
 
@@ -60,6 +61,8 @@ def lib() -> ctypes.CDLL:
         "tq_decode": (c_i, [c_p, c_i, c_p, c_p, c_p, c_i64, c_i64, c_p, c_p]),
         "tq_scores_workspace_bytes": (c_i64, [c_p, c_i, c_i, c_i, c_i64, c_i]),
         "tq_scores": (c_i, [c_p, c_p, c_i, c_i, c_i, c_i, c_p, c_p, c_p, c_i64, c_i, c_p, c_p, c_p, c_i64, c_p]),
+        "tq_query_prep": (c_i, [c_p, c_p, c_i, c_i, c_i, c_i, c_p, c_i64, c_p]),
+        "tq_scores_from_prep": (c_i, [c_p, c_i, c_i, c_i, c_p, c_p, c_p, c_i64, c_p, c_p, c_i64, c_p]),
         "tq_attend_workspace_bytes": (c_i64, [c_p, c_p, c_i, c_i, c_i, c_i64, c_i]),
         "tq_attend_decode": (c_i, [c_p, c_p, c_p, c_i, c_i, c_i, c_i, c_p, c_p, c_p, c_p, c_p, c_i64, c_p, c_p, c_i,
                                    c_f, c_p, c_p, c_i64, c_p]),
@@ -238,6 +241,29 @@ def tq_scores(qz: Quantizer, q, codes, norms, gammas, Hkv: int, n: int, topk: in
                            topk, _ptr(out), _ptr(out_idx) if topk else None, _ptr(workspace), workspace.numel(),
                            _stream()))
     return (out, out_idx) if topk else out
+
+
+def tq_query_prep(qz: Quantizer, q, Hkv: int, workspace=None):
+    """Rotate/project the queries [B, Hq, d] once; returns the workspace."""
+    torch = _torch()
+    _need_cuda(q)
+    B, Hq = q.shape[0], q.shape[1]
+    if workspace is None:
+        workspace = torch.empty(max(scores_workspace_bytes(qz, B, Hq, Hkv, 1, 0), 256), dtype=torch.uint8,
+                                device=q.device)
+    _check(lib().tq_query_prep(qz.handle, _ptr(q), _dtype_code(q), B, Hq, Hkv, _ptr(workspace), workspace.numel(),
+                               _stream()))
+    return workspace
+
+
+def tq_scores_from_prep(qz: Quantizer, B: int, Hq: int, Hkv: int, codes, norms, gammas, n: int, workspace, out=None):
+    torch = _torch()
+    _need_cuda(codes, norms, gammas, workspace)
+    if out is None:
+        out = torch.empty((B, Hq, n), dtype=torch.float32, device=codes.device)
+    _check(lib().tq_scores_from_prep(qz.handle, B, Hq, Hkv, _ptr(codes), _ptr(norms), _ptr(gammas), n, _ptr(out),
+                                     _ptr(workspace), workspace.numel(), _stream()))
+    return out
 
 
 def attend_workspace_bytes(kq: Quantizer, vq: Quantizer, B: int, Hq: int, Hkv: int, n_comp: int, n_tail: int) -> int:
