@@ -11,6 +11,10 @@ Tolerances (the method's parity bar):
   logits  |gpu - oracle| <= 1e-3 * max(|oracle|, ||q|| n / sqrt(d)), on
           identical codes (the GPU's codes fed to the oracle).
   attention output, per row: |gpu - oracle| <= 1e-3 * max(|oracle_e|, ||oracle_row|| / sqrt(d)).
+  top-k   indices distinct and in range, scores non-increasing, each score
+          within the logit tolerance of the oracle's logit at that index; the
+          set equals the oracle's top k except for swaps among keys whose
+          oracle scores lie within the logit tolerance of the oracle's k-th.
 """
 import math
 
@@ -106,3 +110,28 @@ def check_attention(gpu, ref, rel=1e-3):
     worst = float(np.max(err / np.maximum(np.maximum(np.abs(ref), floor), 1e-30)))
     assert np.all(err <= tol + 1e-30), f"attention error {worst:.3g} exceeds {rel}"
     return worst
+
+
+def check_topk(gpu_s, gpu_i, ref, qnorm, knorm, d, rel=1e-3):
+    """gpu_s/gpu_i [Q, k] (GPU top-k); ref [Q, N] oracle logits on identical
+    codes; qnorm [Q]; knorm [N].  Returns the number of allowed swaps."""
+    Q, k = gpu_i.shape
+    N = ref.shape[1]
+    swaps = 0
+    ref_s, ref_i = o.topk(ref, k)
+    for r in range(Q):
+        gi = gpu_i[r].astype(np.int64)
+        assert np.all((gi >= 0) & (gi < N)), "top-k index out of range"
+        assert len(set(gi.tolist())) == k, "top-k indices repeat"
+        assert np.all(np.diff(gpu_s[r]) <= 0), "top-k scores not in descending order"
+        tol_all = rel * np.maximum(np.abs(ref[r]), qnorm[r] * knorm / math.sqrt(d))
+        err = np.abs(gpu_s[r] - ref[r, gi])
+        assert np.all(err <= tol_all[gi] + 1e-30), f"query {r}: top-k score off its oracle logit"
+        kth = ref_i[r, -1]
+        gset, rset = set(gi.tolist()), set(ref_i[r].tolist())
+        for i in gset - rset:      # chosen by the GPU, not by the oracle
+            assert ref[r, i] >= ref[r, kth] - tol_all[i] - tol_all[kth], f"query {r}: key {i} is not a top-{k} key"
+        for i in rset - gset:      # chosen by the oracle, missed by the GPU
+            assert ref[r, i] <= ref[r, kth] + tol_all[i] + tol_all[kth], f"query {r}: top-{k} key {i} missed"
+        swaps += len(gset - rset)
+    return swaps

@@ -101,3 +101,23 @@ def test_scores_gqa_head_mapping():
             kv = h // G
             ref = q[b, h] @ o.decode_prod(qz, idx[b, kv], bits[b, kv], nrm[b, kv], gam[b, kv]).T
             assert np.max(np.abs(out[b, h] - ref)) < 1e-10 * np.abs(ref).max()
+
+
+def test_topk_parity_helper_accepts_ties_and_rejects_wrong_keys():
+    """The top-k comparison used by the GPU tests: the oracle's own answer
+    passes, a swap inside the tolerance passes, a clearly worse key fails."""
+    from tests import parity as P
+    rng = np.random.default_rng(3)
+    ref = rng.standard_normal((2, 500))
+    ref[0, 7] = ref[0, 9] = 5.0            # a tie at the boundary of the top 2 ...
+    ref[0, 3] = 6.0
+    s, i = o.topk(ref, 2)
+    qn, kn = np.ones(2), np.ones(500)
+    assert P.check_topk(s.astype(np.float32), i, ref, qn, kn, 16) == 0
+    i2 = i.copy()
+    i2[0, 1] = 9                           # ... may resolve either way
+    assert P.check_topk(ref[np.arange(2)[:, None], i2].astype(np.float32), i2, ref, qn, kn, 16) == 1
+    i3 = i.copy()
+    i3[1, 1] = int(np.argmin(ref[1]))      # the worst key is no top-2 key
+    with pytest.raises(AssertionError):
+        P.check_topk(ref[np.arange(2)[:, None], i3].astype(np.float32), i3, ref, qn, kn, 16)

@@ -32,17 +32,6 @@ namespace {
 constexpr int kStep = 128;          // tokens per step
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <int BP>
-__device__ __forceinline__ uint32_t walsh_word_a(const uint32_t (&w)[5], int t) {
-  constexpr int masks[4][8] = {{1}, {1, 2}, {1, 2, 4, 7}, {1, 2, 4, 8, 7, 11, 13, 14}};
-  const int mk = masks[BP - 1][t];
-  uint32_t r = 0u;
-#pragma unroll
-  for (int p = 0; p < BP; ++p)
-    if (mk & (1 << p)) r ^= w[p];
-  return r;
-}
-
 // Fixed-point limbs of x in [0, 16): x ~ l0 + l1/16 + l2/256 + l3/4096 with
 // every limb a small integer (|l| <= 16), exact in fp8 E4M3.  Byte k of the
 // result is limb k.  The matrix core sums the products of a row in groups of 8,
@@ -154,7 +143,7 @@ __global__ void __launch_bounds__(256) attend_chunk_kernel(
       }
       v4f aM = {0.f, 0.f, 0.f, 0.f}, aQ = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < TK - 1; ++t) aM = mfma_fp8_fp4(AK[t], bits_to_fp4(walsh_word_a<BPK>(w, t)), aM);
+      for (int t = 0; t < TK - 1; ++t) aM = mfma_fp8_fp4(AK[t], bits_to_fp4(walsh_word<BPK>(w, t)), aM);
       aQ = mfma_fp8_fp4(AK[TK - 1], bits_to_fp4(w[BPK]), aQ);
       pin(aM);
       pin(aQ);
@@ -245,7 +234,7 @@ __global__ void __launch_bounds__(256) attend_chunk_kernel(
           for (int p = 0; p < BPV; ++p) w[p] = wp[p * d];
         }
 #pragma unroll
-        for (int t = 0; t < NV; ++t) acc[t][ct] = mfma_fp8_fp4(A, bits_to_fp4(walsh_word_a<BPV>(w, t)), acc[t][ct]);
+        for (int t = 0; t < NV; ++t) acc[t][ct] = mfma_fp8_fp4(A, bits_to_fp4(walsh_word<BPV>(w, t)), acc[t][ct]);
       }
 #pragma unroll
       for (int t = 0; t < NV; ++t) {
@@ -393,13 +382,6 @@ hipError_t launch_attend(const tq_quantizer* kq, const tq_quantizer* vq, const v
   hipLaunchKernelGGL(attend_merge_kernel, dim3(static_cast<unsigned>(B * Hq)), dim3(128), 0, st, queries, q_dtype, Hq, Hkv,
                      G, RT, nch, part, k_tail, v_tail, n_tail, sl, vq->d_pi, out);
   return hipGetLastError();
-}
-
-int64_t topk_ws_bytes(const tq_quantizer*, int, int, int, int64_t, int) { return 256; }
-
-hipError_t launch_topk(const tq_quantizer*, const void*, int, int, int, int, const uint32_t*, const float*, const float*,
-                       int64_t, int, float*, int64_t*, void*, hipStream_t) {
-  return hipErrorNotSupported;
 }
 
 }  // namespace tq

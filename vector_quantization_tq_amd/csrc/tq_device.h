@@ -74,6 +74,22 @@ __device__ __forceinline__ v8i bits_to_fp4(uint32_t w) {
   return b;
 }
 
+// The codebook of b' index bits is symmetric, so its centroids expand over
+// the odd Walsh functions of the bits: c[idx] = sum_t coef_t (2 x_t - 1) with
+// x_t the XOR of the index bits in mask t.  Word t of a packed group is that
+// XOR taken over 32 coordinates at once (masks in the host's coefficient
+// order).
+template <int BP>
+__device__ __forceinline__ uint32_t walsh_word(const uint32_t (&w)[5], int t) {
+  constexpr int masks[4][8] = {{1}, {1, 2}, {1, 2, 4, 7}, {1, 2, 4, 8, 7, 11, 13, 14}};
+  const int mk = masks[BP - 1][t];
+  uint32_t r = 0u;
+#pragma unroll
+  for (int p = 0; p < BP; ++p)
+    if (mk & (1 << p)) r ^= w[p];
+  return r;
+}
+
 // value of a set bit at element slot s = (K % 32) / 8
 __host__ __device__ __forceinline__ float fp4_slot_value(int s) { return s == 0 ? 0.5f : (s == 1 ? 1.f : 2.f); }
 

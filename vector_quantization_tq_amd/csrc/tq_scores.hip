@@ -28,23 +28,6 @@
 
 namespace tq {
 
-namespace {
-
-template <int BP>
-__device__ __forceinline__ uint32_t walsh_word(const uint32_t (&w)[5], int t) {
-  // Walsh masks of the odd subsets of the index bits, in the order the host
-  // computes the coefficients
-  constexpr int masks[4][8] = {{1}, {1, 2}, {1, 2, 4, 7}, {1, 2, 4, 8, 7, 11, 13, 14}};
-  const int mk = masks[BP - 1][t];
-  uint32_t r = 0u;
-#pragma unroll
-  for (int p = 0; p < BP; ++p)
-    if (mk & (1 << p)) r ^= w[p];
-  return r;
-}
-
-}  // namespace
-
 // ---------------------------------------------------------------------------
 // Query prep: one workgroup per query slot (group, row tile, query-in-tile).
 // Writes the fp8 A operands [group*RT + rt][term][chunk][lane][32 bytes] and

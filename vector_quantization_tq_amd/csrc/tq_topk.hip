@@ -1,0 +1,348 @@
+// Top-k inner-product search straight from packed keys: the unbiased score of
+// blog.hotdry.top "TurboQuant vector-search compression" (QJL section) for
+// every (query, key) pair, of which only the k best per query leave the chip
+// (a2a-mcp.org "什麼是TurboQuant？", benchmark section: top-k recall of a
+// vector search over d = 200 embeddings).
+//
+// With hundreds of queries sharing every key this is bound by the matrix core,
+// not by HBM.  A workgroup owns up to 16 queries of one key sequence (4 row
+// tiles of the query-operand layout, one per wave, held in registers) and a
+// slice of that sequence's keys.  Keys pass through LDS 64 at a time, read
+// once from memory for all four waves, with the next batch in flight in
+// registers while the current one is scored.  Each lane scores one key of a
+// 16-key tile for one query and keeps the KK best (score, index) pairs it has
+// seen in registers, ordered by score descending, then index ascending.  At
+// the end the 16 lanes of a query hand their sorted lists to a tournament
+// (shuffles within the 16 lanes) that emits the slice's top k.  Workgroups
+// that share a key slice sit on one XCD so the slice is reused from that
+// XCD's L2.  A second kernel merges the slices of each query the same way.
+//
+// The arithmetic of a score is the logits kernel's, term for term, so a top-k
+// score equals the corresponding logit bit for bit.
+#include "tq_device.h"
+#include "tq_kernels.h"
+
+namespace tq {
+
+namespace {
+
+constexpr int kTopBlockKeys = 64;
+constexpr int kTopTargetBlocks = 4096;
+
+// (s, i) ranks before (t, j): higher score, ties to the lower index
+__device__ __forceinline__ bool ranks_before(float s, int i, float t, int j) { return s > t || (s == t && i < j); }
+
+// insert into a list sorted by ranks_before; the last entry falls off
+template <int KK>
+__device__ __forceinline__ void list_insert(float s, int i, float (&ls)[KK], int (&li)[KK]) {
+#pragma unroll
+  for (int k = 0; k < KK; ++k) {
+    const bool b = ranks_before(s, i, ls[k], li[k]);
+    const float ts = b ? ls[k] : s;
+    const int ti = b ? li[k] : i;
+    ls[k] = b ? s : ls[k];
+    li[k] = b ? i : li[k];
+    s = ts;
+    i = ti;
+  }
+}
+
+template <int KK>
+__device__ __forceinline__ void list_init(float (&ls)[KK], int (&li)[KK]) {
+#pragma unroll
+  for (int k = 0; k < KK; ++k) {
+    ls[k] = -INFINITY;
+    li[k] = 0x7fffffff;
+  }
+}
+
+// Tournament over the sorted lists of WIDTH consecutive lanes (a power of two
+// <= 64, aligned): round r finds the r-th best pair of their union on every
+// lane of the group; the writer lane stores it at position r.
+template <int KK, int WIDTH>
+__device__ __forceinline__ void tournament(const float (&ls)[KK], const int (&li)[KK], int topk, bool writer,
+                                           float* out_s, int* out_i, int64_t* out_i64) {
+  int head = 0;
+  for (int r = 0; r < topk; ++r) {
+    float s = -INFINITY;
+    int i = 0x7fffffff;
+#pragma unroll
+    for (int k = 0; k < KK; ++k) {
+      if (k == head) {
+        s = ls[k];
+        i = li[k];
+      }
+    }
+    float bs = s;
+    int bi = i;
+#pragma unroll
+    for (int off = WIDTH / 2; off > 0; off >>= 1) {
+      const float os = __shfl_xor(bs, off);
+      const int oi = __shfl_xor(bi, off);
+      if (ranks_before(os, oi, bs, bi)) {
+        bs = os;
+        bi = oi;
+      }
+    }
+    // the lane whose head won moves on (a key sits in one list only, so one
+    // lane matches, unless all that is left are fillers)
+    if (s == bs && i == bi) ++head;
+    if (writer) {
+      if (out_s) out_s[r] = bs;
+      if (out_i) out_i[r] = bi;
+      if (out_i64) out_i64[r] = bi;
+    }
+  }
+}
+
+}  // namespace
+
+struct TopkPlan {
+  int RT;               // row tiles (4 queries each) per key sequence
+  int64_t rg_per_seq;   // row groups (4 row tiles) per key sequence
+  int64_t rg_count;     // all row groups
+  int64_t slices;       // key slices per sequence
+  int64_t slice_keys;   // keys per slice (a multiple of the batch)
+};
+
+static TopkPlan topk_plan(int B, int Hq, int Hkv, int64_t n) {
+  TopkPlan p;
+  const int G = Hq / Hkv;
+  p.RT = (G + 3) / 4;
+  p.rg_per_seq = (p.RT + 3) / 4;
+  p.rg_count = static_cast<int64_t>(B) * Hkv * p.rg_per_seq;
+  int64_t s = (kTopTargetBlocks + p.rg_count - 1) / p.rg_count;
+  const int64_t max_s = (n + kTopBlockKeys - 1) / kTopBlockKeys;
+  if (s > max_s) s = max_s;
+  if (s < 1) s = 1;
+  const int64_t per = n > 0 ? (n + s - 1) / s : 1;
+  p.slice_keys = (per + kTopBlockKeys - 1) / kTopBlockKeys * kTopBlockKeys;
+  p.slices = (n + p.slice_keys - 1) / p.slice_keys;
+  return p;
+}
+
+static int64_t topk_prep_bytes(const tq_quantizer* q, int B, int Hq, int Hkv) {
+  return (scores_ws_bytes(q, B, Hq, Hkv) + 255) / 256 * 256;
+}
+
+int64_t topk_ws_bytes(const tq_quantizer* q, int B, int Hq, int Hkv, int64_t n, int topk) {
+  const TopkPlan p = topk_plan(B, Hq, Hkv, n);
+  // candidates [row group][slice][16 queries][topk]: float scores, then int indices
+  return topk_prep_bytes(q, B, Hq, Hkv) + p.rg_count * p.slices * 16 * topk * 8 + 256;
+}
+
+template <int BP, int GW, int KK>
+__global__ void __launch_bounds__(256) topk_scan_kernel(const uint32_t* __restrict__ codes,
+                                                        const float* __restrict__ norms,
+                                                        const float* __restrict__ gammas, int64_t n, int RT,
+                                                        int64_t rg_per_seq, int64_t rg_count, int64_t slices,
+                                                        int64_t slice_keys, int topk, const uint8_t* __restrict__ wsA,
+                                                        const float* __restrict__ wsC, float* __restrict__ cand_s,
+                                                        int* __restrict__ cand_i) {
+  constexpr int T = (1 << (BP - 1)) + 1;
+  constexpr int W = BP + 1;
+  constexpr int C = (GW + 3) / 4;
+  constexpr int WPK = GW * W;                      // packed words per key
+  constexpr int BW = kTopBlockKeys * WPK;          // words of a batch
+  constexpr int BUFW = BW + 2 * kTopBlockKeys;     // + norms + gammas
+  constexpr int PER = (BW + 255) / 256;            // staged words per thread
+  __shared__ __attribute__((aligned(16))) uint32_t buf[2][BUFW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // workgroup -> (row group, slice); consecutive workgroups go round-robin over
+  // the 8 XCDs, so XCD x takes slices x, x+8, ... with all row groups of each
+  const int64_t L = blockIdx.x;
+  const int64_t x = L & 7, jx = L >> 3;
+  const int64_t rg = jx % rg_count;
+  const int64_t slice = x + 8 * (jx / rg_count);
+  if (slice >= slices) return;   // uniform over the workgroup
+  const int64_t seq = rg / rg_per_seq;
+  const int rt = static_cast<int>((rg - seq * rg_per_seq) * 4) + wave;
+  const bool active = rt < RT;   // uniform over the wave
+  const int64_t gy = seq * RT + rt;
+  const int qi = lane >> 4, jj = lane & 15, g = lane >> 4;
+
+  v8i A[T][C];
+  float cs[10];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int c = 0; c < C; ++c) A[t][c] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 10; ++i) cs[i] = 0.f;
+  if (active) {
+    const v8i* ap = reinterpret_cast<const v8i*>(wsA + gy * T * C * 2048);
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int c = 0; c < C; ++c) A[t][c] = ap[(t * C + c) * 64 + lane];
+    const float* cp = wsC + (gy * 4 + qi) * 16;
+#pragma unroll
+    for (int i = 0; i < 10; ++i) cs[i] = cp[i];
+  }
+
+  float ls[KK];
+  int li[KK];
+  list_init<KK>(ls, li);
+
+  const uint32_t* cbase = codes + seq * n * WPK;
+  const float* nb = norms + seq * n;
+  const float* gb = gammas + seq * n;
+  const int64_t k_begin = slice * slice_keys;
+  const int64_t k_end = min(n, k_begin + slice_keys);
+  const int nbat = static_cast<int>((k_end - k_begin + kTopBlockKeys - 1) / kTopBlockKeys);
+
+  uint32_t stage[PER];
+  float stage_ng = 0.f;
+  auto fetch = [&](int bi) {
+    const int64_t k0 = k_begin + static_cast<int64_t>(bi) * kTopBlockKeys;
+    const int64_t valid = (min(k_end, k0 + kTopBlockKeys) - k0) * WPK;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int idx = e * 256 + tid;
+      stage[e] = (idx < valid) ? cbase[k0 * WPK + idx] : 0u;
+    }
+    if (tid < 2 * kTopBlockKeys) {
+      const int kk = tid & (kTopBlockKeys - 1);
+      const float* src = tid < kTopBlockKeys ? nb : gb;
+      stage_ng = (k0 + kk < k_end) ? src[k0 + kk] : 0.f;
+    }
+  };
+  auto commit = [&](int slot) {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int idx = e * 256 + tid;
+      if (idx < BW) buf[slot][idx] = stage[e];
+    }
+    if (tid < 2 * kTopBlockKeys) reinterpret_cast<float*>(buf[slot] + BW)[tid] = stage_ng;
+  };
+
+  fetch(0);
+  commit(0);
+  __syncthreads();
+  for (int bi = 0; bi < nbat; ++bi) {
+    const int slot = bi & 1;
+    if (bi + 1 < nbat) fetch(bi + 1);   // in flight while this batch is scored
+    if (active) {
+      const uint32_t* kw = buf[slot];
+      const float* kn = reinterpret_cast<const float*>(kw + BW);
+      const int64_t k0 = k_begin + static_cast<int64_t>(bi) * kTopBlockKeys;
+      const int nk = static_cast<int>(min(static_cast<int64_t>(kTopBlockKeys), k_end - k0));
+#pragma unroll
+      for (int u = 0; u < kTopBlockKeys / 16; ++u) {
+        const int kk = 16 * u + jj;
+        v4f aM = {0.f, 0.f, 0.f, 0.f}, aQ = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+          const int gg = 4 * c + g;
+          uint32_t w[5] = {0u, 0u, 0u, 0u, 0u};
+          if (gg < GW) {
+#pragma unroll
+            for (int p = 0; p < W; ++p) w[p] = kw[(kk * GW + gg) * W + p];
+          }
+#pragma unroll
+          for (int t = 0; t < T - 1; ++t) aM = mfma_fp8_fp4(A[t][c], bits_to_fp4(walsh_word<BP>(w, t)), aM);
+          aQ = mfma_fp8_fp4(A[T - 1][c], bits_to_fp4(w[BP]), aQ);
+        }
+        pin(aM);
+        pin(aQ);
+        const float mse = fmaf(aM[0], cs[2], fmaf(aM[1], cs[3], fmaf(aM[2], cs[4], fmaf(aM[3], cs[5], cs[0]))));
+        const float qjl = fmaf(aQ[0], cs[6], fmaf(aQ[1], cs[7], fmaf(aQ[2], cs[8], fmaf(aQ[3], cs[9], cs[1]))));
+        const float s = fmaf(kn[kk], mse, kn[kTopBlockKeys + kk] * qjl);
+        const int key = static_cast<int>(k0) + kk;
+        if (kk < nk && ranks_before(s, key, ls[KK - 1], li[KK - 1])) list_insert<KK>(s, key, ls, li);
+      }
+    }
+    // the other slot was last read before the previous barrier
+    if (bi + 1 < nbat) commit(slot ^ 1);
+    __syncthreads();
+  }
+
+  if (!active) return;   // no barrier follows
+  const int64_t q16 = wave * 4 + qi;
+  const int64_t base = ((rg * slices + slice) * 16 + q16) * topk;
+  tournament<KK, 16>(ls, li, topk, jj == 0, cand_s + base, cand_i + base, nullptr);
+}
+
+// One wave per query: merge the slices' candidate lists into the final top k.
+template <int KK>
+__global__ void __launch_bounds__(64) topk_merge_kernel(const float* __restrict__ cand_s,
+                                                        const int* __restrict__ cand_i, int64_t slices, int Hq,
+                                                        int Hkv, int64_t rg_per_seq, int topk,
+                                                        float* __restrict__ out, int64_t* __restrict__ out_idx) {
+  const int lane = threadIdx.x;
+  const int64_t bh = blockIdx.x;   // b * Hq + h
+  const int G = Hq / Hkv;
+  const int64_t b = bh / Hq;
+  const int h = static_cast<int>(bh - b * Hq);
+  const int kvh = h / G, qg = h - kvh * G;
+  const int rt = qg >> 2, qi = qg & 3;
+  const int64_t seq = b * Hkv + kvh;
+  const int64_t rg = seq * rg_per_seq + (rt >> 2);
+  const int64_t q16 = (rt & 3) * 4 + qi;
+  float ls[KK];
+  int li[KK];
+  list_init<KK>(ls, li);
+  for (int64_t sl = lane; sl < slices; sl += 64) {
+    const int64_t base = ((rg * slices + sl) * 16 + q16) * topk;
+    for (int k = 0; k < topk; ++k) {
+      const float s = cand_s[base + k];
+      const int i = cand_i[base + k];
+      if (!ranks_before(s, i, ls[KK - 1], li[KK - 1])) break;   // the slice's list is sorted
+      list_insert<KK>(s, i, ls, li);
+    }
+  }
+  tournament<KK, 64>(ls, li, topk, lane == 0, out + bh * topk, nullptr, out_idx + bh * topk);
+}
+
+hipError_t launch_topk(const tq_quantizer* q, const void* queries, int q_dtype, int B, int Hq, int Hkv,
+                       const uint32_t* codes, const float* norms, const float* gammas, int64_t n, int topk, float* out,
+                       int64_t* out_idx, void* ws, hipStream_t st) {
+  if (topk < 1 || topk > 32 || n >= 0x7fffffff) return hipErrorNotSupported;
+  const TopkPlan p = topk_plan(B, Hq, Hkv, n);
+  const int T = q->cb[0].nterms + 1;
+  const int Cc = (q->d + 127) / 128;
+  const int64_t row_tiles = static_cast<int64_t>(B) * Hkv * p.RT;
+  // whole rounds of 8 slices so that each XCD's workgroups share slices
+  const int64_t blocks = (p.slices + 7) / 8 * 8 * p.rg_count;
+  if (blocks > 0x7fffffff) return hipErrorNotSupported;
+  hipError_t e = launch_query_prep_ws(q, queries, q_dtype, B, Hq, Hkv, ws, st);
+  if (e != hipSuccess) return e;
+  const uint8_t* wsA = static_cast<const uint8_t*>(ws);
+  const float* wsC = reinterpret_cast<const float*>(wsA + row_tiles * T * Cc * 2048);
+  float* cs = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + topk_prep_bytes(q, B, Hq, Hkv));
+  int* ci = reinterpret_cast<int*>(cs + p.rg_count * p.slices * 16 * topk);
+  const int bp = q->cb[0].bp;
+  const int gw = (q->d + 31) / 32;
+  const bool big = topk > 16;
+  bool launched = false;
+#define TQ_TK(BPV, GWV)                                                                                            \
+  if (!launched && bp == BPV && gw == GWV) {                                                                       \
+    if (big)                                                                                                       \
+      hipLaunchKernelGGL((topk_scan_kernel<BPV, GWV, 32>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,  \
+                         codes, norms, gammas, n, p.RT, p.rg_per_seq, p.rg_count, p.slices, p.slice_keys, topk, wsA, \
+                         wsC, cs, ci);                                                                             \
+    else                                                                                                           \
+      hipLaunchKernelGGL((topk_scan_kernel<BPV, GWV, 16>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,  \
+                         codes, norms, gammas, n, p.RT, p.rg_per_seq, p.rg_count, p.slices, p.slice_keys, topk, wsA, \
+                         wsC, cs, ci);                                                                             \
+    launched = true;                                                                                               \
+  }
+#define TQ_TK_ALL(GWV) TQ_TK(1, GWV) TQ_TK(2, GWV) TQ_TK(3, GWV)
+  TQ_TK_ALL(1) TQ_TK_ALL(2) TQ_TK_ALL(3) TQ_TK_ALL(4) TQ_TK_ALL(5) TQ_TK_ALL(6) TQ_TK_ALL(7) TQ_TK_ALL(8)
+#undef TQ_TK_ALL
+#undef TQ_TK
+  if (!launched) return hipErrorNotSupported;
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 mgrid(static_cast<unsigned>(static_cast<int64_t>(B) * Hq));
+  if (big)
+    hipLaunchKernelGGL((topk_merge_kernel<32>), mgrid, dim3(64), 0, st, cs, ci, p.slices, Hq, Hkv, p.rg_per_seq, topk,
+                       out, out_idx);
+  else
+    hipLaunchKernelGGL((topk_merge_kernel<16>), mgrid, dim3(64), 0, st, cs, ci, p.slices, Hq, Hkv, p.rg_per_seq, topk,
+                       out, out_idx);
+  return hipGetLastError();
+}
+
+}  // namespace tq
