@@ -3,23 +3,34 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa|long|decode|search]
 
 One step = one pass of the whole hot path over one batch of synthetic input
-already resident in HBM: encode the keys (prod codes) and values (mse codes),
+already resident in HBM.  For the default workload (the GQA decode layer:
+batch 8, 8 KV heads, 32 query heads, 32768 tokens, d = 128, 3-bit keys and
+values) that is: encode the keys (prod codes) and values (mse codes),
 rotate/project the queries, compute the logits from the packed keys, and run
-decode attention (softmax . V) over the packed cache.  The default workload is
-the GQA decode layer (batch 8, 8 KV heads, 32 query heads, 32768 tokens,
-d = 128, 3-bit keys and values).
+decode attention (softmax . V) over the packed cache.  `long` is the same
+step on the 131072-token cache with a 256-token bf16 tail (4-bit); `decode`
+is encode + logits of the single-layer decode workload (32 heads x 8192
+keys, one query per head); `search` is encode + fused top-10 of the
+1,000,000 x 200 vector-search workload (1000 queries).
 
-Printed: one JSON line.  `value` is the packed-cache bandwidth of the logits
-kernel (packed key bytes / kernel time); encode keys/s and the attention
-kernel are reported beside it.  Kernel times come from HIP events recorded on
-the stream the kernels run on, over the timed steps.  Code buffers alternate
-between two copies so that every scan reads codes written a full step (more
-than 1 GB of other traffic) earlier, i.e. from HBM, not from the 256 MB
-last-level cache.
+Printed: one JSON line.  For gqa/long/decode `value` is the packed-cache
+bandwidth of the logits kernel (packed key bytes / kernel time); encode
+keys/s and the attention kernel are reported beside it.  Kernel times come
+from HIP events recorded on the stream the kernels run on (the library
+launches on torch's current stream, where the events are recorded too), over
+the timed steps.  Code buffers alternate between two copies so that every
+scan reads codes written a full step (more than 1 GB of other traffic)
+earlier, i.e. from HBM, not from the 256 MB last-level cache.
+
+`roofline.traffic` is the HBM traffic of one logits launch measured with the
+FETCH_SIZE and WRITE_SIZE counters (profiles/scores_kernel_gqa_traffic.txt,
+each scaled by what the counter reads for a copy kernel of known size); it is
+null when the kernel sources have changed since those counters were taken.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -32,6 +43,12 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 FP32_MFMA_PEAK_TFLOPS = 157.3
+FP8_MFMA_PEAK_TFLOPS = 5000.0
+METRIC = "packed-KV logits GB/s (% of HBM peak) + encode keys/s, d=128 3-bit, 1 MI355X"
+# sources whose compiled code the logits kernel is made of
+SCORES_SOURCES = ["vector_quantization_tq_amd/csrc/tq_scores.hip", "vector_quantization_tq_amd/csrc/tq_device.h",
+                  "vector_quantization_tq_amd/build.py"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scores_kernel_gqa_traffic.txt")
 
 
 def parse():
@@ -40,8 +57,45 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gqa", choices=["gqa", "long", "decode", "search"])
+    ap.add_argument("--bits", type=int, default=None, help="bits for the decode/search workloads (default 3 / 4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a 256 MiB device copy 3 times (the known-size kernel for counter scaling)")
     return ap.parse_args()
+
+
+def sources_sha256(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per logits launch from the counter summary, or None when it is
+    missing or was taken on other kernel sources."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("source_sha256") != sources_sha256(SCORES_SOURCES):
+            return None
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def copy_calibration(torch, dev):
+    x = torch.ones(64 << 20, dtype=torch.float32, device=dev)   # 256 MiB
+    y = torch.empty_like(x)
+    for _ in range(3):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    del x, y
 
 
 def bf16_tensor(torch, u16, dev):
@@ -205,7 +259,7 @@ def run_gqa(args, torch, dev, tq, wl_fn, name, bits, n_tail=0):
     enc_ms = timer.avg_ms("encode_keys")
     enc_flop = nkeys * 4.0 * d * d                    # Pi x and S' rho per key
     res = {
-        "metric": "packed-KV logits GB/s (% of HBM peak) + encode keys/s, d=128 3-bit, 1 MI355X",
+        "metric": METRIC,
         "value": round(packed_gbs, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -230,7 +284,7 @@ def run_gqa(args, torch, dev, tq, wl_fn, name, bits, n_tail=0):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(scores_alg / (scores_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic() if name.startswith("gqa") else None,
             "algorithmic_bytes_per_launch": scores_alg,
             "bytes_per_key": rec_k + 4 * G,
         },
@@ -259,6 +313,135 @@ def run_gqa(args, torch, dev, tq, wl_fn, name, bits, n_tail=0):
     return res, wl
 
 
+def _timed_loop(args, torch, step):
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, True)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def _common(args, ms_step, config, value, unit, metric=METRIC):
+    return {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "u8", "data": "synthetic", "config": config}
+
+
+def run_decode(args, torch, dev, tq, W):
+    """Single-layer decode: encode 32 x 8192 keys, then the logits of one query
+    per head (the logits are launch-bound at this size)."""
+    bits = args.bits or 3
+    wl = W.decode_layer(bits)
+    H, N, d = 32, 8192, 128
+    k = bf16_tensor(torch, wl.arrays["k_bf16"], dev).view(H, N, d)
+    q = bf16_tensor(torch, wl.arrays["q_bf16"], dev).view(1, H, d)
+    qz = tq.Quantizer(d, bits, 0)
+    copies = []
+    for _ in range(2):
+        copies.append((torch.empty(qz.code_words(tq.TQ_PROD, H, N), dtype=torch.int32, device=dev),
+                       torch.empty(H * N, dtype=torch.float32, device=dev),
+                       torch.empty(H * N, dtype=torch.float32, device=dev)))
+        tq.tq_encode(qz, tq.TQ_PROD, k, out=copies[-1])
+    logits = torch.empty((1, H, N), dtype=torch.float32, device=dev)
+    ws = torch.empty(tq.scores_workspace_bytes(qz, 1, H, H, N), dtype=torch.uint8, device=dev)
+    timer = Timer(torch)
+
+    def step(i, timed):
+        w, r = copies[i % 2], copies[(i + 1) % 2]
+        e0 = timer.mark()
+        tq.tq_encode(qz, tq.TQ_PROD, k, out=w)
+        e1 = timer.mark()
+        tq.tq_query_prep(qz, q, H, workspace=ws)
+        e2 = timer.mark()
+        tq.tq_scores_from_prep(qz, 1, H, H, r[0], r[1], r[2], N, ws, out=logits)
+        e3 = timer.mark()
+        if timed:
+            timer.span("encode_keys", e0, e1)
+            timer.span("query_prep", e1, e2)
+            timer.span("scores", e2, e3)
+
+    el = _timed_loop(args, torch, step)
+    timer.collect()
+    rec_k = 4 * ((d + 31) // 32) * bits + 8
+    sc = timer.avg_ms("scores")
+    enc = timer.avg_ms("encode_keys")
+    gbs = H * N * rec_k / (sc * 1e-3) / 1e9
+    res = _common(args, el * 1e3 / args.steps,
+                  {"workload": f"decode-layer 32 heads x 8192 keys d128 {bits}-bit, 1 query per head"},
+                  round(gbs, 1), "GB/s")
+    res["encode_keys_per_s"] = round(H * N / (enc * 1e-3), 0)
+    res["kernels_ms"] = {k2: round(timer.avg_ms(k2), 4) for k2 in timer.acc}
+    res["roofline"] = {"kernel": "scores_kernel", "bound": "hbm",
+                       "achieved": round(H * N * (rec_k + 4) / (sc * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                       "unit": "GB/s", "frac": round(H * N * (rec_k + 4) / (sc * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                       "traffic": None, "note": "launch-bound: the packed keys are %.1f MB" % (H * N * rec_k / 1e6)}
+    return res
+
+
+def run_search(args, torch, dev, tq, W):
+    """Vector search: encode the 1,000,000 x 200 database, then the fused top-10
+    of 1000 queries straight from the codes."""
+    bits = args.bits or 4
+    wl = W.vector_search(bits)
+    n, d, nq, k = 1_000_000, 200, 1000, 10
+    x = torch.from_numpy(wl.arrays["x"]).to(dev)
+    q = torch.from_numpy(wl.arrays["q"][None]).to(dev)
+    qz = tq.Quantizer(d, bits, 0)
+    copies = []
+    for _ in range(2):
+        copies.append((torch.empty(qz.code_words(tq.TQ_PROD, 1, n), dtype=torch.int32, device=dev),
+                       torch.empty(n, dtype=torch.float32, device=dev),
+                       torch.empty(n, dtype=torch.float32, device=dev)))
+        tq.tq_encode(qz, tq.TQ_PROD, x, out=copies[-1])
+    out_s = torch.empty((1, nq, k), dtype=torch.float32, device=dev)
+    out_i = torch.empty((1, nq, k), dtype=torch.int64, device=dev)
+    ws = torch.empty(tq.scores_workspace_bytes(qz, 1, nq, 1, n, k), dtype=torch.uint8, device=dev)
+    timer = Timer(torch)
+
+    def step(i, timed):
+        w, r = copies[i % 2], copies[(i + 1) % 2]
+        e0 = timer.mark()
+        tq.tq_encode(qz, tq.TQ_PROD, x, out=w)
+        e1 = timer.mark()
+        tq.tq_scores(qz, q, r[0], r[1], r[2], 1, n, topk=k, out=out_s, out_idx=out_i, workspace=ws)
+        e2 = timer.mark()
+        if timed:
+            timer.span("encode_keys", e0, e1)
+            timer.span("topk", e1, e2)
+
+    el = _timed_loop(args, torch, step)
+    timer.collect()
+    # recall@10 of the codes against the exact float32 top 10 (context)
+    exact = torch.topk(torch.matmul(q[0], x.t()), k, dim=1).indices
+    got = out_i[0]
+    recall = float((got[:, :, None] == exact[:, None, :]).any(dim=2).float().mean())
+    tk = timer.avg_ms("topk")
+    enc = timer.avg_ms("encode_keys")
+    gw = (d + 31) // 32
+    rec_k = 4 * gw * bits + 8
+    alg_flop = 2.0 * n * nq * (d + d)                     # MSE and QJL inner products, m = d
+    T = (1 << (bits - 2)) + 1
+    issued = (nq + 3) // 4 * ((n + 15) // 16) * T * ((d + 127) // 128) * 2 * 16 * 16 * 128
+    res = _common(args, el * 1e3 / args.steps,
+                  {"workload": f"vector-search 1000000 x 200 fp32, 1000 queries, top-10, {bits}-bit"},
+                  round(nq / (tk * 1e-3), 1), "queries/s", metric="top-10 queries/s from packed codes, 1 MI355X")
+    res["dtype"] = "fp8 x fp4 MFMA, f32 accumulate"
+    res["scan_gb_per_s"] = round(n * rec_k / (tk * 1e-3) / 1e9, 1)
+    res["encode_keys_per_s"] = round(n / (enc * 1e-3), 0)
+    res["recall_at_10_vs_exact_fp32"] = round(recall, 4)
+    res["kernels_ms"] = {k2: round(timer.avg_ms(k2), 4) for k2 in timer.acc}
+    res["roofline"] = {"kernel": "topk_scan_kernel + merge (tq_scores, topk=10)", "bound": "mfma",
+                       "achieved": round(alg_flop / (tk * 1e-3) / 1e12, 2), "peak": FP8_MFMA_PEAK_TFLOPS,
+                       "unit": "TFLOP/s", "frac": round(alg_flop / (tk * 1e-3) / 1e12 / FP8_MFMA_PEAK_TFLOPS, 4),
+                       "traffic": None, "algorithmic_flop_per_launch": alg_flop,
+                       "issued_mfma_flop_per_launch": issued,
+                       "issued_mfma_tflops": round(issued / (tk * 1e-3) / 1e12, 1)}
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -271,6 +454,8 @@ def main():
     from vector_quantization_tq_amd import workloads as W
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
     if args.workload == "gqa":
         res, wl = run_gqa(args, torch, dev, tq, W.gqa_layer, "gqa-decode-layer b8 kv8 q32 n32768 d128 3-bit", 3)
         if not args.no_cpu_baseline:
@@ -278,9 +463,11 @@ def main():
     elif args.workload == "long":
         res, wl = run_gqa(args, torch, dev, tq, W.long_context, "long-context b1 kv8 q32 n131072 tail256 d128 4-bit", 4,
                           n_tail=256)
+    elif args.workload == "decode":
+        res = run_decode(args, torch, dev, tq, W)
     else:
-        raise SystemExit(f"workload {args.workload} is not wired into bench.py yet")
-    print(json.dumps(res))
+        res = run_search(args, torch, dev, tq, W)
+    print(json.dumps(res), flush=True)
 
 
 if __name__ == "__main__":
