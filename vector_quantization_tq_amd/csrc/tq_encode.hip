@@ -11,6 +11,8 @@
 // decisions are taken on fp32-accurate values.  One workgroup encodes a tile
 // of 64 vectors; each of its 4 waves owns 16 vectors (rows) and all output
 // columns, so a wave only ever reads back its own rows from LDS.
+#include <algorithm>
+
 #include "tq_device.h"
 #include "tq_kernels.h"
 
@@ -210,6 +212,335 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(const void* __restrict
   }
 }
 
+// ---------------------------------------------------------------------------
+// Tile encoder for d <= 128 (the head dimensions of attention caches).
+//
+// Wave w owns the 32-coordinate group w: the rows 32w..32w+31 of Pi and of S'
+// stay in its registers for the whole kernel (B operands of the fp32
+// 16x16x4 MFMA), so the only operand read per MFMA is the x (or rho) tile,
+// which sits once in LDS for all four waves.  The contraction index is
+// permuted (lane-group q takes k = q*KS + s) so that a lane's A values for
+// four consecutive steps are one 16-byte LDS read.  Workgroups are
+// persistent over 64-vector tiles and fetch the next tile into registers
+// while the current one is encoded.
+//
+// prod (keys): C[vector][coordinate]; an index bit plane of 16 coordinates
+// of 4 vectors is one ballot, so each packed word is assembled from two
+// ballots.  rho = y - c[idx] goes to a second LDS tile for the QJL product.
+// mse (values): the operands are swapped, C[coordinate][vector], so a ballot
+// gives 16 tokens of 4 coordinates: the token-major words of the value
+// layout come out the same way.
+// ---------------------------------------------------------------------------
+constexpr int kEncRows = 64;
+
+// LK: how a tile is loaded: 0 element by element (any d), 1 bf16 and 2 fp32 in
+// 16-byte chunks fetched one tile ahead (rows a multiple of 16 bytes).
+template <int KS, int LK, bool PROD>
+__global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restrict__ x, int dtype, int64_t nseq,
+                                                             int64_t n, int d, const float* __restrict__ pi,
+                                                             const float* __restrict__ sp, Codebook cb,
+                                                             uint32_t* __restrict__ codes, float* __restrict__ norms,
+                                                             float* __restrict__ gammas) {
+  constexpr int KP = 4 * KS;   // padded contraction length
+  constexpr int LD = KP + 4;   // LDS row stride in floats (16-byte aligned, conflict-free 16-byte reads)
+  __shared__ __attribute__((aligned(16))) float xs[kEncRows * LD];
+  __shared__ __attribute__((aligned(16))) float rs[kEncRows * LD];
+  __shared__ float nrm2[2][kEncRows];   // by tile parity: read while the next tile is committed
+  __shared__ float part2[4][kEncRows];
+  __shared__ float cen[kMaxLevels];
+  __shared__ uint32_t ost[2][1024];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r16 = lane & 15, q = lane >> 4;
+  const int bp = cb.bp;
+  const int G = (d + 31) >> 5;
+  const int W = bp + 1;                    // prod words per group
+  const int WPK = G * W;
+  constexpr bool prod = PROD;
+  constexpr bool VEC = LK != 0;
+  constexpr int PREN = LK == 2 ? KS / 4 : KS / 8 > 0 ? KS / 8 : 1;   // 16-byte chunks per thread
+  const int64_t tps = (n + kEncRows - 1) / kEncRows;   // tiles per sequence
+  const int64_t total = nseq * tps;
+  const int64_t nb = (n + 31) >> 5;                      // mse blocks per sequence
+
+  // stationary operands: row j of Pi / S' at k = q*KS + s
+  float bP[2][KS], bS[2][PROD ? KS : 1];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int j = 32 * w + 16 * ct + r16;
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) {
+      const int k = q * KS + s2;
+      const bool in = j < d && k < d;
+      bP[ct][s2] = in ? pi[static_cast<int64_t>(j) * d + k] : 0.f;
+      if constexpr (PROD) bS[ct][s2] = in ? sp[static_cast<int64_t>(j) * d + k] : 0.f;
+    }
+  }
+  for (int e = tid; e < kEncRows * LD; e += 256) {
+    xs[e] = 0.f;
+    rs[e] = 0.f;
+  }
+  if (tid < kMaxLevels) cen[tid] = tid < cb.levels ? cb.c[tid] : 0.f;
+
+  // loader role: row = tid / 4, four threads per row
+  const int lrow = tid >> 2, part = tid & 3;
+  constexpr int esz = LK == 1 ? 2 : 4;
+  const int CH = d * esz / 16;             // 16-byte chunks per row (VEC)
+  uint4 pre[PREN];
+  auto tile_of = [&](int64_t t, int64_t& seq, int64_t& v0, int& rows) {
+    seq = t / tps;
+    v0 = (t - seq * tps) * kEncRows;
+    rows = static_cast<int>(min(static_cast<int64_t>(kEncRows), n - v0));
+  };
+  auto fetch = [&](int64_t t) {
+    if constexpr (VEC) {
+      int64_t seq, v0;
+      int rows;
+      tile_of(t, seq, v0, rows);
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(x) +
+                                                        ((seq * n + v0 + lrow) * d) * esz);
+#pragma unroll
+      for (int j = 0; j < PREN; ++j) {
+        const int c = part + 4 * j;
+        if (lrow < rows && c < CH) pre[j] = src[c];
+      }
+    }
+  };
+  auto commit = [&](int64_t t, float* nrm) {
+    int64_t seq, v0;
+    int rows;
+    tile_of(t, seq, v0, rows);
+    float ss = 0.f;
+    float* xr = xs + lrow * LD;
+    if (lrow < rows) {
+      if constexpr (VEC) {
+#pragma unroll
+        for (int j = 0; j < PREN; ++j) {
+          const int c = part + 4 * j;
+          if (c < CH) {
+            const uint4 v = pre[j];
+            const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+            if constexpr (esz == 2) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float lo = __uint_as_float(u[e] << 16), hi = __uint_as_float(u[e] & 0xFFFF0000u);
+                xr[8 * c + 2 * e] = lo;
+                xr[8 * c + 2 * e + 1] = hi;
+                ss = fmaf(lo, lo, ss);
+                ss = fmaf(hi, hi, ss);
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float f = __uint_as_float(u[e]);
+                xr[4 * c + e] = f;
+                ss = fmaf(f, f, ss);
+              }
+            }
+          }
+        }
+      } else {
+        const int64_t off = (seq * n + v0 + lrow) * d;
+        for (int col = part; col < d; col += 4) {
+          const float f = load_elem(x, dtype, off + col);
+          xr[col] = f;
+          ss = fmaf(f, f, ss);
+        }
+      }
+    } else {
+      for (int col = part; col < d; col += 4) xr[col] = 0.f;
+    }
+    ss += __shfl_xor(ss, 1);
+    ss += __shfl_xor(ss, 2);
+    if (part == 0) nrm[lrow] = lrow < rows ? sqrtf(ss) : 0.f;
+  };
+  auto store = [&](int64_t t, int buf) {
+    int64_t seq, v0;
+    int rows;
+    tile_of(t, seq, v0, rows);
+    if constexpr (PROD) {
+      uint32_t* dst = codes + (seq * n + v0) * WPK;
+      for (int e = tid; e < rows * WPK; e += 256) dst[e] = ost[buf][e];
+    } else {
+      const int nblk = (rows + 31) >> 5;
+      uint32_t* dst = codes + ((seq * nb + (v0 >> 5)) * bp) * d;
+      for (int e = tid; e < nblk * bp * d; e += 256) dst[e] = ost[buf][e];
+    }
+  };
+
+  int64_t t = blockIdx.x;
+  if (t < total) fetch(t);
+  __syncthreads();   // zero fill done before the first commit
+  int it = 0;
+  for (; t < total; t += gridDim.x, ++it) {
+    const int buf = it & 1;
+    float* nrm = nrm2[buf];
+    commit(t, nrm);
+    const int64_t tn = t + gridDim.x;
+    if (tn < total) fetch(tn);   // in flight while this tile is encoded
+    __syncthreads();
+    if (it > 0) store(t - gridDim.x, buf ^ 1);
+
+    int64_t seq, v0;
+    int rows;
+    tile_of(t, seq, v0, rows);
+
+    // Two halves of 32 vectors each keep the accumulators to 2 x 2 tiles.
+    // acc[h2][ct]: row tile 2h + h2, column tile ct of this wave's group.
+    auto contract = [&](const float* src, const float (&bm)[2][KS], int h, bool swap, v4f (&acc)[2][2]) {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) acc[h2][ct] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s4 = 0; s4 < KS / 4; ++s4) {
+        float4 a[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+          a[h2] = *reinterpret_cast<const float4*>(src + (32 * h + 16 * h2 + r16) * LD + q * KS + 4 * s4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const float av = e == 0 ? a[h2].x : e == 1 ? a[h2].y : e == 2 ? a[h2].z : a[h2].w;
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+              acc[h2][ct] = swap ? mfma_f32(bm[ct][4 * s4 + e], av, acc[h2][ct])
+                                 : mfma_f32(av, bm[ct][4 * s4 + e], acc[h2][ct]);
+          }
+      }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) pin(acc[h2][ct]);
+    };
+    // packed word of vector (or coordinate) row 4q + i from two 16-bit halves
+    auto halves = [&](uint64_t m0, uint64_t m1) {
+      return static_cast<uint32_t>((m0 >> (16 * q)) & 0xFFFFu) | (static_cast<uint32_t>((m1 >> (16 * q)) & 0xFFFFu) << 16);
+    };
+
+    if constexpr (PROD) {
+#pragma unroll 1
+      for (int h = 0; h < 2; ++h) {
+        v4f acc[2][2];
+        contract(xs, bP, h, false, acc);
+        // lane holds vector 32h + 16h2 + 4q + i, coordinate 32w + 16ct + r16
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int vbase = 32 * h + 16 * h2 + 4 * q;
+          float inv[4], r2[4];
+          uint32_t idxs[2][4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float nv = nrm[vbase + i];
+            inv[i] = nv > 0.f ? 1.f / nv : 0.f;
+            r2[i] = 0.f;
+          }
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) {
+            const int c = 32 * w + 16 * ct + r16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float y = acc[h2][ct][i] * inv[i];
+              int idx = 0;
+              for (int k = 0; k < cb.levels - 1; ++k) idx += (cb.t[k] < y) ? 1 : 0;
+              const float rho = c < d ? y - cen[idx] : 0.f;
+              r2[i] = fmaf(rho, rho, r2[i]);
+              if (c < KP) rs[(vbase + i) * LD + c] = rho;
+              idxs[ct][i] = c < d ? static_cast<uint32_t>(idx) : 0u;
+            }
+          }
+          if (w < G) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              for (int p = 0; p < bp; ++p) {
+                const uint64_t m0 = __ballot((idxs[0][i] >> p) & 1u);
+                const uint64_t m1 = __ballot((idxs[1][i] >> p) & 1u);
+                if (r16 == 0) ost[buf][(vbase + i) * WPK + w * W + p] = halves(m0, m1);
+              }
+          }
+          // partial ||rho||^2 over this wave's 32 coordinates
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float v = r2[i];
+            v += __shfl_xor(v, 1);
+            v += __shfl_xor(v, 2);
+            v += __shfl_xor(v, 4);
+            v += __shfl_xor(v, 8);
+            if (r16 == 0) part2[w][vbase + i] = v;
+          }
+        }
+      }
+      __syncthreads();
+
+      // ---- QJL: z = S' rho, bit = [z >= 0] (all ones for a zero vector) ----
+#pragma unroll 1
+      for (int h = 0; h < 2; ++h) {
+        v4f acc[2][2];
+        contract(rs, bS, h, false, acc);
+        if (w < G) {
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const int vbase = 32 * h + 16 * h2 + 4 * q;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const bool zero = !(nrm[vbase + i] > 0.f);
+              const uint64_t m0 = __ballot((32 * w + r16 < d) && (acc[h2][0][i] >= 0.f || zero));
+              const uint64_t m1 = __ballot((32 * w + 16 + r16 < d) && (acc[h2][1][i] >= 0.f || zero));
+              if (r16 == 0) ost[buf][(vbase + i) * WPK + w * W + bp] = halves(m0, m1);
+            }
+          }
+        }
+      }
+      if (tid < rows) {
+        const float nv = nrm[tid];
+        norms[seq * n + v0 + tid] = nv;
+        gammas[seq * n + v0 + tid] = nv * sqrtf(part2[0][tid] + part2[1][tid] + part2[2][tid] + part2[3][tid]);
+      }
+    } else {
+      // operands swapped: lane holds coordinate 32w + 16ct + 4q + i, token
+      // 32h + 16h2 + r16; half h is the 32-token block h of the tile
+#pragma unroll 1
+      for (int h = 0; h < 2; ++h) {
+        v4f acc[2][2];
+        contract(xs, bP, h, true, acc);
+        uint32_t idxs[2][2][4];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int tk = 32 * h + 16 * h2 + r16;
+          const float nv = nrm[tk];
+          const float inv = nv > 0.f ? 1.f / nv : 0.f;
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float y = acc[h2][ct][i] * inv;
+              int idx = 0;
+              for (int k = 0; k < cb.levels - 1; ++k) idx += (cb.t[k] < y) ? 1 : 0;
+              idxs[h2][ct][i] = (tk < rows && 32 * w + 16 * ct + 4 * q + i < d) ? static_cast<uint32_t>(idx) : 0u;
+            }
+        }
+        if (w < G) {
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              for (int p = 0; p < bp; ++p) {
+                const uint64_t m0 = __ballot((idxs[0][ct][i] >> p) & 1u);
+                const uint64_t m1 = __ballot((idxs[1][ct][i] >> p) & 1u);
+                const int c = 32 * w + 16 * ct + 4 * q + i;
+                if (r16 == 0 && c < d) ost[buf][(h * bp + p) * d + c] = halves(m0, m1);
+              }
+        }
+      }
+      if (tid < rows) norms[seq * n + v0 + tid] = nrm[tid];
+      __syncthreads();   // every wave is done with the x tile before the next commit
+    }
+  }
+  __syncthreads();
+  if (it > 0) store(t - gridDim.x, (it - 1) & 1);
+}
+
 // Decode: one workgroup per 8 vectors; plain fp32 FMAs (not on the hot path).
 __global__ void __launch_bounds__(256) decode_kernel(const uint32_t* __restrict__ codes, const float* __restrict__ norms,
                                                      const float* __restrict__ gammas, int64_t n, int d, int m, int mode,
@@ -287,8 +618,48 @@ size_t encode_lds_bytes(int d) {
   return sizeof(float) * (kTileRows * (DP + 1) + kTileRows + kMaxLevels) + 2 * kTileRows * DP;
 }
 
+static int encode_tile_blocks() {
+  static int blocks = [] {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      cus = 256;
+    return 2 * cus;   // two resident workgroups per CU (LDS and registers)
+  }();
+  return blocks;
+}
+
+template <int KS, int LK>
+hipError_t launch_encode_tile_lk(const tq_quantizer* q, int mode, const void* x, int dtype, int64_t nseq, int64_t n,
+                                 uint32_t* codes, float* norms, float* gammas, hipStream_t st) {
+  const int64_t tiles = nseq * ((n + kEncRows - 1) / kEncRows);
+  const dim3 grid(static_cast<unsigned>(std::min<int64_t>(tiles, encode_tile_blocks())));
+  if (mode == 0)
+    hipLaunchKernelGGL((encode_tile_kernel<KS, LK, true>), grid, dim3(256), 0, st, x, dtype, nseq, n, q->d, q->d_pi,
+                       q->d_sp, q->cb[0], codes, norms, gammas);
+  else
+    hipLaunchKernelGGL((encode_tile_kernel<KS, LK, false>), grid, dim3(256), 0, st, x, dtype, nseq, n, q->d, q->d_pi,
+                       q->d_sp, q->cb[1], codes, norms, gammas);
+  return hipGetLastError();
+}
+
+template <int KS>
+hipError_t launch_encode_tile(const tq_quantizer* q, int mode, const void* x, int dtype, int64_t nseq, int64_t n,
+                              uint32_t* codes, float* norms, float* gammas, hipStream_t st) {
+  const int esz = dtype == 1 ? 2 : 4;
+  if ((q->d * esz) % 16 != 0)
+    return launch_encode_tile_lk<KS, 0>(q, mode, x, dtype, nseq, n, codes, norms, gammas, st);
+  if (dtype == 1) return launch_encode_tile_lk<KS, 1>(q, mode, x, dtype, nseq, n, codes, norms, gammas, st);
+  return launch_encode_tile_lk<KS, 2>(q, mode, x, dtype, nseq, n, codes, norms, gammas, st);
+}
+
 hipError_t launch_encode(const tq_quantizer* q, int mode, const void* x, int dtype, int64_t nseq, int64_t n,
                          uint32_t* codes, float* norms, float* gammas, hipStream_t st) {
+  if (q->d <= 128) {
+    if (q->d <= 32) return launch_encode_tile<8>(q, mode, x, dtype, nseq, n, codes, norms, gammas, st);
+    if (q->d <= 64) return launch_encode_tile<16>(q, mode, x, dtype, nseq, n, codes, norms, gammas, st);
+    return launch_encode_tile<32>(q, mode, x, dtype, nseq, n, codes, norms, gammas, st);
+  }
   const int nt = (q->d + 15) / 16;
   switch (nt) {
 #define TQ_NT_CASE(N) \
