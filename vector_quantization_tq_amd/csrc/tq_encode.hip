@@ -213,79 +213,109 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(const void* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// Tile encoder for d <= 128 (the head dimensions of attention caches).
+// Tile encoder for d <= 128 (the head dimensions of attention caches), on the
+// fp16 16x16x32 MFMA with split operands.
 //
-// Wave w owns the 32-coordinate group w: the rows 32w..32w+31 of Pi and of S'
-// stay in its registers for the whole kernel (B operands of the fp32
-// 16x16x4 MFMA), so the only operand read per MFMA is the x (or rho) tile,
-// which sits once in LDS for all four waves.  The contraction index is
-// permuted (lane-group q takes k = q*KS + s) so that a lane's A values for
-// four consecutive steps are one 16-byte LDS read.  Workgroups are
-// persistent over 64-vector tiles and fetch the next tile into registers
-// while the current one is encoded.
+// The matrix core accumulates fp16 products at fp32 accuracy, so a float
+// operand written as hi + lo (two fp16 numbers, 22 significant bits)
+// reproduces a float product to about 2^-22.  The rotation is
+// x . (Pi_hi + Pi_lo) (bf16 keys are exact in fp16 after a power-of-two row
+// scale; fp32 keys add x_lo . Pi_hi), the QJL projection is
+// rho_hi . S'_hi + rho_lo . S'_hi + rho_hi . S'_lo.  Pi is scaled by 2^8 and
+// rho by 2^14 before splitting so that the lo parts stay normal numbers.
 //
-// prod (keys): C[vector][coordinate]; an index bit plane of 16 coordinates
-// of 4 vectors is one ballot, so each packed word is assembled from two
-// ballots.  rho = y - c[idx] goes to a second LDS tile for the QJL product.
+// Wave w owns the 32-coordinate group w: its rows of Pi_hi/lo and S'_hi/lo
+// stay in registers as B operands for the whole kernel; the x (or rho) tile
+// sits once in LDS for all four waves, and each lane reads its 8 consecutive
+// contraction values as one 16-byte load.  Workgroups are persistent over
+// 64-vector tiles and fetch the next tile into registers while the current
+// one is encoded.
+//
+// prod (keys): C[vector][coordinate]; an index bit plane of 16 coordinates of
+// 4 vectors is one ballot, so a packed word is assembled from two ballots.
 // mse (values): the operands are swapped, C[coordinate][vector], so a ballot
-// gives 16 tokens of 4 coordinates: the token-major words of the value
-// layout come out the same way.
+// gives 16 tokens of 4 coordinates: the token-major value words come out the
+// same way.
 // ---------------------------------------------------------------------------
 constexpr int kEncRows = 64;
+constexpr float kPiScale = 256.f;       // 2^8
+constexpr float kRhoScale = 16384.f;    // 2^14
 
-// LK: how a tile is loaded: 0 element by element (any d), 1 bf16 and 2 fp32 in
-// 16-byte chunks fetched one tile ahead (rows a multiple of 16 bytes).
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ v4f mfma_f16(const v8h& a, const v8h& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// LK: how a tile is loaded: 0 element by element (any d, either dtype),
+// 1 bf16 and 2 fp32 in 16-byte chunks fetched one tile ahead.
 template <int KS, int LK, bool PROD>
 __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restrict__ x, int dtype, int64_t nseq,
                                                              int64_t n, int d, const float* __restrict__ pi,
                                                              const float* __restrict__ sp, Codebook cb,
                                                              uint32_t* __restrict__ codes, float* __restrict__ norms,
                                                              float* __restrict__ gammas) {
-  constexpr int KP = 4 * KS;   // padded contraction length
-  constexpr int LD = KP + 4;   // LDS row stride in floats (16-byte aligned, conflict-free 16-byte reads)
-  __shared__ __attribute__((aligned(16))) float xs[kEncRows * LD];
-  __shared__ __attribute__((aligned(16))) float rs[kEncRows * LD];
-  __shared__ float nrm2[2][kEncRows];   // by tile parity: read while the next tile is committed
+  constexpr int KP = 32 * KS;            // padded contraction length
+  constexpr int LDH = KP + 8;            // LDS row stride in halves (16-byte rows, conflict-free reads)
+  constexpr bool XLO = LK != 1;          // fp32 keys need x_lo (bf16 keys are exact in fp16)
+  constexpr int PREN = LK == 2 ? KS * 2 : LK == 1 ? KS : 1;   // 16-byte chunks per loader thread
+  constexpr int EPT = KP / 4;            // elements per loader thread (scalar path)
+  __shared__ __attribute__((aligned(16))) _Float16 xh[kEncRows * LDH];
+  __shared__ __attribute__((aligned(16))) _Float16 xl[XLO ? kEncRows * LDH : 8];
+  __shared__ __attribute__((aligned(16))) _Float16 rh[PROD ? kEncRows * LDH : 8];
+  __shared__ __attribute__((aligned(16))) _Float16 rl[PROD ? kEncRows * LDH : 8];
+  __shared__ float scl2[2][kEncRows];    // 2^-(row scale + 8) / n, by tile parity
+  __shared__ float nrm2[2][kEncRows];    // n, by tile parity
   __shared__ float part2[4][kEncRows];
-  __shared__ float cen[kMaxLevels];
   __shared__ uint32_t ost[2][1024];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, q = lane >> 4;
   const int bp = cb.bp;
   const int G = (d + 31) >> 5;
-  const int W = bp + 1;                    // prod words per group
+  const int W = bp + 1;                  // prod words per group
   const int WPK = G * W;
-  constexpr bool prod = PROD;
-  constexpr bool VEC = LK != 0;
-  constexpr int PREN = LK == 2 ? KS / 4 : KS / 8 > 0 ? KS / 8 : 1;   // 16-byte chunks per thread
   const int64_t tps = (n + kEncRows - 1) / kEncRows;   // tiles per sequence
   const int64_t total = nseq * tps;
   const int64_t nb = (n + 31) >> 5;                      // mse blocks per sequence
 
-  // stationary operands: row j of Pi / S' at k = q*KS + s
-  float bP[2][KS], bS[2][PROD ? KS : 1];
+  // stationary operands: lane (r16, q) holds row 32w + 16ct + r16, columns
+  // 32s + 8q .. +7 of Pi (and S'), split into hi + lo
+  v8h bPh[2][KS], bPl[2][KS], bSh[2][PROD ? KS : 1], bSl[2][PROD ? KS : 1];
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
     const int j = 32 * w + 16 * ct + r16;
 #pragma unroll
-    for (int s2 = 0; s2 < KS; ++s2) {
-      const int k = q * KS + s2;
-      const bool in = j < d && k < d;
-      bP[ct][s2] = in ? pi[static_cast<int64_t>(j) * d + k] : 0.f;
-      if constexpr (PROD) bS[ct][s2] = in ? sp[static_cast<int64_t>(j) * d + k] : 0.f;
+    for (int s2 = 0; s2 < KS; ++s2)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int k = 32 * s2 + 8 * q + e;
+        const bool in = j < d && k < d;
+        const float vp = in ? pi[static_cast<int64_t>(j) * d + k] * kPiScale : 0.f;
+        const _Float16 ph = static_cast<_Float16>(vp);
+        bPh[ct][s2][e] = ph;
+        bPl[ct][s2][e] = static_cast<_Float16>(vp - static_cast<float>(ph));
+        if constexpr (PROD) {
+          const float vs = in ? sp[static_cast<int64_t>(j) * d + k] * kPiScale : 0.f;
+          const _Float16 sh = static_cast<_Float16>(vs);
+          bSh[ct][s2][e] = sh;
+          bSl[ct][s2][e] = static_cast<_Float16>(vs - static_cast<float>(sh));
+        }
+      }
+  }
+  for (int e = tid; e < kEncRows * LDH; e += 256) {
+    xh[e] = static_cast<_Float16>(0.f);
+    if constexpr (XLO) xl[e] = static_cast<_Float16>(0.f);
+    if constexpr (PROD) {
+      rh[e] = static_cast<_Float16>(0.f);
+      rl[e] = static_cast<_Float16>(0.f);
     }
   }
-  for (int e = tid; e < kEncRows * LD; e += 256) {
-    xs[e] = 0.f;
-    rs[e] = 0.f;
-  }
-  if (tid < kMaxLevels) cen[tid] = tid < cb.levels ? cb.c[tid] : 0.f;
 
   // loader role: row = tid / 4, four threads per row
   const int lrow = tid >> 2, part = tid & 3;
   constexpr int esz = LK == 1 ? 2 : 4;
-  const int CH = d * esz / 16;             // 16-byte chunks per row (VEC)
+  const int CH = d * esz / 16;           // 16-byte chunks per row (vector paths)
   uint4 pre[PREN];
   auto tile_of = [&](int64_t t, int64_t& seq, int64_t& v0, int& rows) {
     seq = t / tps;
@@ -293,7 +323,7 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
     rows = static_cast<int>(min(static_cast<int64_t>(kEncRows), n - v0));
   };
   auto fetch = [&](int64_t t) {
-    if constexpr (VEC) {
+    if constexpr (LK != 0) {
       int64_t seq, v0;
       int rows;
       tile_of(t, seq, v0, rows);
@@ -306,53 +336,78 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
       }
     }
   };
-  auto commit = [&](int64_t t, float* nrm) {
+  // element e of this thread's share of the row (column col(e)), as float
+  auto commit = [&](int64_t t, float* scl, float* nrm) {
     int64_t seq, v0;
     int rows;
     tile_of(t, seq, v0, rows);
-    float ss = 0.f;
-    float* xr = xs + lrow * LD;
-    if (lrow < rows) {
-      if constexpr (VEC) {
+    float v[EPT];
+    int cols[EPT];
+    int cnt = 0;
+    if constexpr (LK == 1) {
 #pragma unroll
-        for (int j = 0; j < PREN; ++j) {
-          const int c = part + 4 * j;
-          if (c < CH) {
-            const uint4 v = pre[j];
-            const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-            if constexpr (esz == 2) {
+      for (int j = 0; j < PREN; ++j) {
+        const int c = part + 4 * j;
+        const uint32_t u[4] = {pre[j].x, pre[j].y, pre[j].z, pre[j].w};
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float lo = __uint_as_float(u[e] << 16), hi = __uint_as_float(u[e] & 0xFFFF0000u);
-                xr[8 * c + 2 * e] = lo;
-                xr[8 * c + 2 * e + 1] = hi;
-                ss = fmaf(lo, lo, ss);
-                ss = fmaf(hi, hi, ss);
-              }
-            } else {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float f = __uint_as_float(u[e]);
-                xr[4 * c + e] = f;
-                ss = fmaf(f, f, ss);
-              }
-            }
-          }
-        }
-      } else {
-        const int64_t off = (seq * n + v0 + lrow) * d;
-        for (int col = part; col < d; col += 4) {
-          const float f = load_elem(x, dtype, off + col);
-          xr[col] = f;
-          ss = fmaf(f, f, ss);
+        for (int e = 0; e < 4; ++e) {
+          v[8 * j + 2 * e] = (lrow < rows && c < CH) ? __uint_as_float(u[e] << 16) : 0.f;
+          v[8 * j + 2 * e + 1] = (lrow < rows && c < CH) ? __uint_as_float(u[e] & 0xFFFF0000u) : 0.f;
+          cols[8 * j + 2 * e] = 8 * c + 2 * e;
+          cols[8 * j + 2 * e + 1] = 8 * c + 2 * e + 1;
         }
       }
+      cnt = EPT;
+    } else if constexpr (LK == 2) {
+#pragma unroll
+      for (int j = 0; j < PREN; ++j) {
+        const int c = part + 4 * j;
+        const uint32_t u[4] = {pre[j].x, pre[j].y, pre[j].z, pre[j].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[4 * j + e] = (lrow < rows && c < CH) ? __uint_as_float(u[e]) : 0.f;
+          cols[4 * j + e] = 4 * c + e;
+        }
+      }
+      cnt = EPT;
     } else {
-      for (int col = part; col < d; col += 4) xr[col] = 0.f;
+      const int64_t off = (seq * n + v0 + lrow) * d;
+#pragma unroll
+      for (int j = 0; j < EPT; ++j) {
+        const int col = part + 4 * j;
+        v[j] = (lrow < rows && col < d) ? load_elem(x, dtype, off + col) : 0.f;
+        cols[j] = col;
+      }
+      cnt = EPT;
+    }
+    float ss = 0.f, mx = 0.f;
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      ss = fmaf(v[j], v[j], ss);
+      mx = fmaxf(mx, fabsf(v[j]));
     }
     ss += __shfl_xor(ss, 1);
     ss += __shfl_xor(ss, 2);
-    if (part == 0) nrm[lrow] = lrow < rows ? sqrtf(ss) : 0.f;
+    mx = fmaxf(mx, __shfl_xor(mx, 1));
+    mx = fmaxf(mx, __shfl_xor(mx, 2));
+    // power-of-two row scale putting the largest element in [2^14, 2^15)
+    const int sig = mx > 0.f ? 14 - ilogbf(mx) : 0;
+    _Float16* hr = xh + lrow * LDH;
+    _Float16* lr = xl + lrow * LDH;
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      if (j < cnt && cols[j] < d) {
+        const float sv = ldexpf(v[j], sig);
+        const _Float16 h = static_cast<_Float16>(sv);
+        hr[cols[j]] = h;
+        if constexpr (XLO) lr[cols[j]] = static_cast<_Float16>(sv - static_cast<float>(h));
+      }
+    }
+    if (part == 0) {
+      const float nv = lrow < rows ? sqrtf(ss) : 0.f;
+      nrm[lrow] = nv;
+      scl[lrow] = nv > 0.f ? ldexpf(1.f / nv, -(sig + 8)) : 0.f;
+    }
   };
   auto store = [&](int64_t t, int buf) {
     int64_t seq, v0;
@@ -367,6 +422,43 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
       for (int e = tid; e < nblk * bp * d; e += 256) dst[e] = ost[buf][e];
     }
   };
+  // acc[h2][ct] (+)= rows 32h + 16h2 .. of src times this wave's columns;
+  // SWAP puts the stationary operand first (C[coordinate][vector])
+  auto contract = [&](const _Float16* src, const v8h (&bm)[2][KS], int h, bool swap, v4f (&acc)[2][2]) {
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) {
+      v8h a[2];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+        a[h2] = *reinterpret_cast<const v8h*>(src + (32 * h + 16 * h2 + r16) * LDH + 32 * s2 + 8 * q);
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+          acc[h2][ct] = swap ? mfma_f16(bm[ct][s2], a[h2], acc[h2][ct]) : mfma_f16(a[h2], bm[ct][s2], acc[h2][ct]);
+    }
+  };
+  auto zero_acc = [&](v4f (&acc)[2][2]) {
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) acc[h2][ct] = (v4f){0.f, 0.f, 0.f, 0.f};
+  };
+  auto pin_acc = [&](v4f (&acc)[2][2]) {
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) pin(acc[h2][ct]);
+  };
+  // packed word of row 4q + i of a ballot pair (low 16 bits, high 16 bits)
+  auto halves = [&](uint64_t m0, uint64_t m1) {
+    return static_cast<uint32_t>((m0 >> (16 * q)) & 0xFFFFu) | (static_cast<uint32_t>((m1 >> (16 * q)) & 0xFFFFu) << 16);
+  };
+  auto bucket = [&](float y) {
+    int idx = 0;
+    for (int k = 0; k < cb.levels - 1; ++k) idx += (cb.t[k] < y) ? 1 : 0;
+    return idx;
+  };
 
   int64_t t = blockIdx.x;
   if (t < total) fetch(t);
@@ -374,8 +466,9 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
   int it = 0;
   for (; t < total; t += gridDim.x, ++it) {
     const int buf = it & 1;
+    float* scl = scl2[buf];
     float* nrm = nrm2[buf];
-    commit(t, nrm);
+    commit(t, scl, nrm);
     const int64_t tn = t + gridDim.x;
     if (tn < total) fetch(tn);   // in flight while this tile is encoded
     __syncthreads();
@@ -385,68 +478,38 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
     int rows;
     tile_of(t, seq, v0, rows);
 
-    // Two halves of 32 vectors each keep the accumulators to 2 x 2 tiles.
-    // acc[h2][ct]: row tile 2h + h2, column tile ct of this wave's group.
-    auto contract = [&](const float* src, const float (&bm)[2][KS], int h, bool swap, v4f (&acc)[2][2]) {
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) acc[h2][ct] = (v4f){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s4 = 0; s4 < KS / 4; ++s4) {
-        float4 a[2];
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-          a[h2] = *reinterpret_cast<const float4*>(src + (32 * h + 16 * h2 + r16) * LD + q * KS + 4 * s4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            const float av = e == 0 ? a[h2].x : e == 1 ? a[h2].y : e == 2 ? a[h2].z : a[h2].w;
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
-              acc[h2][ct] = swap ? mfma_f32(bm[ct][4 * s4 + e], av, acc[h2][ct])
-                                 : mfma_f32(av, bm[ct][4 * s4 + e], acc[h2][ct]);
-          }
-      }
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) pin(acc[h2][ct]);
-    };
-    // packed word of vector (or coordinate) row 4q + i from two 16-bit halves
-    auto halves = [&](uint64_t m0, uint64_t m1) {
-      return static_cast<uint32_t>((m0 >> (16 * q)) & 0xFFFFu) | (static_cast<uint32_t>((m1 >> (16 * q)) & 0xFFFFu) << 16);
-    };
-
     if constexpr (PROD) {
 #pragma unroll 1
       for (int h = 0; h < 2; ++h) {
         v4f acc[2][2];
-        contract(xs, bP, h, false, acc);
+        zero_acc(acc);
+        contract(xh, bPh, h, false, acc);
+        contract(xh, bPl, h, false, acc);
+        if constexpr (XLO) contract(xl, bPh, h, false, acc);
+        pin_acc(acc);
         // lane holds vector 32h + 16h2 + 4q + i, coordinate 32w + 16ct + r16
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           const int vbase = 32 * h + 16 * h2 + 4 * q;
-          float inv[4], r2[4];
+          float r2[4];
           uint32_t idxs[2][4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float nv = nrm[vbase + i];
-            inv[i] = nv > 0.f ? 1.f / nv : 0.f;
-            r2[i] = 0.f;
-          }
+          for (int i = 0; i < 4; ++i) r2[i] = 0.f;
 #pragma unroll
           for (int ct = 0; ct < 2; ++ct) {
             const int c = 32 * w + 16 * ct + r16;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const float y = acc[h2][ct][i] * inv[i];
-              int idx = 0;
-              for (int k = 0; k < cb.levels - 1; ++k) idx += (cb.t[k] < y) ? 1 : 0;
-              const float rho = c < d ? y - cen[idx] : 0.f;
+              const float y = acc[h2][ct][i] * scl[vbase + i];
+              const int idx = bucket(y);
+              const float rho = c < d ? y - cb.c[idx] : 0.f;
               r2[i] = fmaf(rho, rho, r2[i]);
-              if (c < KP) rs[(vbase + i) * LD + c] = rho;
+              if (c < KP) {
+                const float sr = rho * kRhoScale;
+                const _Float16 hh = static_cast<_Float16>(sr);
+                rh[(vbase + i) * LDH + c] = hh;
+                rl[(vbase + i) * LDH + c] = static_cast<_Float16>(sr - static_cast<float>(hh));
+              }
               idxs[ct][i] = c < d ? static_cast<uint32_t>(idx) : 0u;
             }
           }
@@ -473,11 +536,15 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
       }
       __syncthreads();
 
-      // ---- QJL: z = S' rho, bit = [z >= 0] (all ones for a zero vector) ----
+      // ---- QJL: z = S' rho (scaled), bit = [z >= 0] (all ones for a zero vector) ----
 #pragma unroll 1
       for (int h = 0; h < 2; ++h) {
         v4f acc[2][2];
-        contract(rs, bS, h, false, acc);
+        zero_acc(acc);
+        contract(rh, bSh, h, false, acc);
+        contract(rl, bSh, h, false, acc);
+        contract(rh, bSl, h, false, acc);
+        pin_acc(acc);
         if (w < G) {
 #pragma unroll
           for (int h2 = 0; h2 < 2; ++h2) {
@@ -498,25 +565,26 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
         gammas[seq * n + v0 + tid] = nv * sqrtf(part2[0][tid] + part2[1][tid] + part2[2][tid] + part2[3][tid]);
       }
     } else {
-      // operands swapped: lane holds coordinate 32w + 16ct + 4q + i, token
-      // 32h + 16h2 + r16; half h is the 32-token block h of the tile
+      // lane holds coordinate 32w + 16ct + 4q + i, token 32h + 16h2 + r16;
+      // half h is the 32-token block h of the tile
 #pragma unroll 1
       for (int h = 0; h < 2; ++h) {
         v4f acc[2][2];
-        contract(xs, bP, h, true, acc);
+        zero_acc(acc);
+        contract(xh, bPh, h, true, acc);
+        contract(xh, bPl, h, true, acc);
+        if constexpr (XLO) contract(xl, bPh, h, true, acc);
+        pin_acc(acc);
         uint32_t idxs[2][2][4];
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           const int tk = 32 * h + 16 * h2 + r16;
-          const float nv = nrm[tk];
-          const float inv = nv > 0.f ? 1.f / nv : 0.f;
+          const float sc = scl[tk];
 #pragma unroll
           for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const float y = acc[h2][ct][i] * inv;
-              int idx = 0;
-              for (int k = 0; k < cb.levels - 1; ++k) idx += (cb.t[k] < y) ? 1 : 0;
+              const int idx = bucket(acc[h2][ct][i] * sc);
               idxs[h2][ct][i] = (tk < rows && 32 * w + 16 * ct + 4 * q + i < d) ? static_cast<uint32_t>(idx) : 0u;
             }
         }
@@ -656,9 +724,9 @@ hipError_t launch_encode_tile(const tq_quantizer* q, int mode, const void* x, in
 hipError_t launch_encode(const tq_quantizer* q, int mode, const void* x, int dtype, int64_t nseq, int64_t n,
                          uint32_t* codes, float* norms, float* gammas, hipStream_t st) {
   if (q->d <= 128) {
-    if (q->d <= 32) return launch_encode_tile<8>(q, mode, x, dtype, nseq, n, codes, norms, gammas, st);
-    if (q->d <= 64) return launch_encode_tile<16>(q, mode, x, dtype, nseq, n, codes, norms, gammas, st);
-    return launch_encode_tile<32>(q, mode, x, dtype, nseq, n, codes, norms, gammas, st);
+    if (q->d <= 32) return launch_encode_tile<1>(q, mode, x, dtype, nseq, n, codes, norms, gammas, st);
+    if (q->d <= 64) return launch_encode_tile<2>(q, mode, x, dtype, nseq, n, codes, norms, gammas, st);
+    return launch_encode_tile<4>(q, mode, x, dtype, nseq, n, codes, norms, gammas, st);
   }
   const int nt = (q->d + 15) / 16;
   switch (nt) {
