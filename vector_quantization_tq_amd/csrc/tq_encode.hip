@@ -248,8 +248,8 @@ __device__ __forceinline__ v4f mfma_f16(const v8h& a, const v8h& b, const v4f& c
 }
 
 // LK: how a tile is loaded: 0 element by element (any d, either dtype),
-// 1 bf16 and 2 fp32 in 16-byte chunks fetched one tile ahead.
-template <int KS, int LK, bool PROD>
+// 1 bf16 and 2 fp32 in 16-byte chunks fetched one tile ahead.  BP: index bits.
+template <int KS, int LK, bool PROD, int BP>
 __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restrict__ x, int dtype, int64_t nseq,
                                                              int64_t n, int d, const float* __restrict__ pi,
                                                              const float* __restrict__ sp, Codebook cb,
@@ -271,7 +271,8 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, q = lane >> 4;
-  const int bp = cb.bp;
+  constexpr int bp = BP;
+  constexpr int NT = (1 << BP) - 1;      // thresholds
   const int G = (d + 31) >> 5;
   const int W = bp + 1;                  // prod words per group
   const int WPK = G * W;
@@ -454,9 +455,23 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
   auto halves = [&](uint64_t m0, uint64_t m1) {
     return static_cast<uint32_t>((m0 >> (16 * q)) & 0xFFFFu) | (static_cast<uint32_t>((m1 >> (16 * q)) & 0xFFFFu) << 16);
   };
-  auto bucket = [&](float y) {
+  // idx = #{t_k < y}; the centroid telescopes over the same comparisons
+  float th[NT], dc[NT];
+#pragma unroll
+  for (int k2 = 0; k2 < NT; ++k2) {
+    th[k2] = cb.t[k2];
+    dc[k2] = cb.c[k2 + 1] - cb.c[k2];
+  }
+  const float c0 = cb.c[0];
+  auto bucket = [&](float y, float& cv) {
     int idx = 0;
-    for (int k = 0; k < cb.levels - 1; ++k) idx += (cb.t[k] < y) ? 1 : 0;
+    cv = c0;
+#pragma unroll
+    for (int k2 = 0; k2 < NT; ++k2) {
+      const bool above = th[k2] < y;
+      idx += above ? 1 : 0;
+      cv += above ? dc[k2] : 0.f;
+    }
     return idx;
   };
 
@@ -501,8 +516,9 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const float y = acc[h2][ct][i] * scl[vbase + i];
-              const int idx = bucket(y);
-              const float rho = c < d ? y - cb.c[idx] : 0.f;
+              float cv;
+              const int idx = bucket(y, cv);
+              const float rho = c < d ? y - cv : 0.f;
               r2[i] = fmaf(rho, rho, r2[i]);
               if (c < KP) {
                 const float sr = rho * kRhoScale;
@@ -516,6 +532,7 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
           if (w < G) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
+              #pragma unroll
               for (int p = 0; p < bp; ++p) {
                 const uint64_t m0 = __ballot((idxs[0][i] >> p) & 1u);
                 const uint64_t m1 = __ballot((idxs[1][i] >> p) & 1u);
@@ -584,7 +601,8 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
           for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const int idx = bucket(acc[h2][ct][i] * sc);
+              float cv;
+              const int idx = bucket(acc[h2][ct][i] * sc, cv);
               idxs[h2][ct][i] = (tk < rows && 32 * w + 16 * ct + 4 * q + i < d) ? static_cast<uint32_t>(idx) : 0u;
             }
         }
@@ -593,6 +611,7 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
           for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
+              #pragma unroll
               for (int p = 0; p < bp; ++p) {
                 const uint64_t m0 = __ballot((idxs[0][ct][i] >> p) & 1u);
                 const uint64_t m1 = __ballot((idxs[1][ct][i] >> p) & 1u);
@@ -697,36 +716,51 @@ static int encode_tile_blocks() {
   return blocks;
 }
 
-template <int KS, int LK>
-hipError_t launch_encode_tile_lk(const tq_quantizer* q, int mode, const void* x, int dtype, int64_t nseq, int64_t n,
-                                 uint32_t* codes, float* norms, float* gammas, hipStream_t st) {
+template <int LK, bool PROD>
+hipError_t launch_encode_tile_m(const tq_quantizer* q, const void* x, int dtype, int64_t nseq, int64_t n,
+                                uint32_t* codes, float* norms, float* gammas, hipStream_t st) {
   const int64_t tiles = nseq * ((n + kEncRows - 1) / kEncRows);
   const dim3 grid(static_cast<unsigned>(std::min<int64_t>(tiles, encode_tile_blocks())));
-  if (mode == 0)
-    hipLaunchKernelGGL((encode_tile_kernel<KS, LK, true>), grid, dim3(256), 0, st, x, dtype, nseq, n, q->d, q->d_pi,
-                       q->d_sp, q->cb[0], codes, norms, gammas);
-  else
-    hipLaunchKernelGGL((encode_tile_kernel<KS, LK, false>), grid, dim3(256), 0, st, x, dtype, nseq, n, q->d, q->d_pi,
-                       q->d_sp, q->cb[1], codes, norms, gammas);
+  const Codebook& cb = q->cb[PROD ? 0 : 1];
+#define TQ_ENC(BPV)                                                                                                 \
+  case BPV:                                                                                                         \
+    hipLaunchKernelGGL((encode_tile_kernel<4, LK, PROD, BPV>), grid, dim3(256), 0, st, x, dtype, nseq, n, q->d,     \
+                       q->d_pi, q->d_sp, cb, codes, norms, gammas);                                               \
+    break;
+  switch (cb.bp) {
+    TQ_ENC(1) TQ_ENC(2) TQ_ENC(3)
+    case 4:
+      if constexpr (!PROD) {
+        hipLaunchKernelGGL((encode_tile_kernel<4, LK, PROD, 4>), grid, dim3(256), 0, st, x, dtype, nseq, n, q->d,
+                           q->d_pi, q->d_sp, cb, codes, norms, gammas);
+        break;
+      }
+      return hipErrorNotSupported;
+    default: return hipErrorNotSupported;
+  }
+#undef TQ_ENC
   return hipGetLastError();
 }
 
-template <int KS>
+template <int LK>
+hipError_t launch_encode_tile_lk(const tq_quantizer* q, int mode, const void* x, int dtype, int64_t nseq, int64_t n,
+                                 uint32_t* codes, float* norms, float* gammas, hipStream_t st) {
+  return mode == 0 ? launch_encode_tile_m<LK, true>(q, x, dtype, nseq, n, codes, norms, gammas, st)
+                   : launch_encode_tile_m<LK, false>(q, x, dtype, nseq, n, codes, norms, gammas, st);
+}
+
 hipError_t launch_encode_tile(const tq_quantizer* q, int mode, const void* x, int dtype, int64_t nseq, int64_t n,
                               uint32_t* codes, float* norms, float* gammas, hipStream_t st) {
   const int esz = dtype == 1 ? 2 : 4;
-  if ((q->d * esz) % 16 != 0)
-    return launch_encode_tile_lk<KS, 0>(q, mode, x, dtype, nseq, n, codes, norms, gammas, st);
-  if (dtype == 1) return launch_encode_tile_lk<KS, 1>(q, mode, x, dtype, nseq, n, codes, norms, gammas, st);
-  return launch_encode_tile_lk<KS, 2>(q, mode, x, dtype, nseq, n, codes, norms, gammas, st);
+  if ((q->d * esz) % 16 != 0) return launch_encode_tile_lk<0>(q, mode, x, dtype, nseq, n, codes, norms, gammas, st);
+  if (dtype == 1) return launch_encode_tile_lk<1>(q, mode, x, dtype, nseq, n, codes, norms, gammas, st);
+  return launch_encode_tile_lk<2>(q, mode, x, dtype, nseq, n, codes, norms, gammas, st);
 }
 
 hipError_t launch_encode(const tq_quantizer* q, int mode, const void* x, int dtype, int64_t nseq, int64_t n,
                          uint32_t* codes, float* norms, float* gammas, hipStream_t st) {
   if (q->d <= 128) {
-    if (q->d <= 32) return launch_encode_tile<1>(q, mode, x, dtype, nseq, n, codes, norms, gammas, st);
-    if (q->d <= 64) return launch_encode_tile<2>(q, mode, x, dtype, nseq, n, codes, norms, gammas, st);
-    return launch_encode_tile<4>(q, mode, x, dtype, nseq, n, codes, norms, gammas, st);
+    return launch_encode_tile(q, mode, x, dtype, nseq, n, codes, norms, gammas, st);
   }
   const int nt = (q->d + 15) / 16;
   switch (nt) {
