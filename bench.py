@@ -105,26 +105,54 @@ def bf16_tensor(torch, u16, dev):
 
 
 class Timer:
-    """Per-kernel HIP-event timing on the current stream."""
+    """Per-kernel HIP events on the stream the library launches on (torch's
+    current stream).  The events are created without the system-scope fence
+    (hipEventDisableSystemFence): a timing event then records its timestamp in
+    stream order without flushing the caches for the host, so it does not add
+    a cache write-back to the interval it brackets."""
+
+    FLAGS = 0x20000000   # hipEventDisableSystemFence
 
     def __init__(self, torch):
+        import ctypes
         self.torch = torch
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
         self.pending = []
         self.acc = {}
         self.count = {}
+        self.pool = []
+
+    def _event(self):
+        if self.pool:
+            return self.pool.pop()
+        e = self.ct.c_void_p()
+        if self.hip.hipEventCreateWithFlags(self.ct.byref(e), self.ct.c_uint(self.FLAGS)) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        return e
 
     def mark(self):
-        e = self.torch.cuda.Event(enable_timing=True)
-        e.record()
+        e = self._event()
+        stream = self.ct.c_void_p(self.torch.cuda.current_stream().cuda_stream)
+        if self.hip.hipEventRecord(e, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
         return e
 
     def span(self, name, a, b):
         self.pending.append((name, a, b))
 
     def collect(self):
+        ms = self.ct.c_float()
         for name, a, b in self.pending:
-            self.acc[name] = self.acc.get(name, 0.0) + a.elapsed_time(b)
+            if self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            self.acc[name] = self.acc.get(name, 0.0) + ms.value
             self.count[name] = self.count.get(name, 0) + 1
+        seen = {}
+        for _, a, b in self.pending:
+            seen[a.value] = a
+            seen[b.value] = b
+        self.pool.extend(seen.values())
         self.pending = []
 
     def avg_ms(self, name):

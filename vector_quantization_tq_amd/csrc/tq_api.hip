@@ -160,6 +160,12 @@ tq_quantizer* tq_make_quantizer(int d, int bits, uint64_t seed) {
       for (int k = 0; k < d; ++k) a += q->s[static_cast<size_t>(r) * d + k] * q->pi[static_cast<size_t>(j) * d + k];
       sp32[static_cast<size_t>(r) * d + j] = static_cast<float>(a);
     }
+  const int dm = d + q->m;
+  std::vector<float> qt32(static_cast<size_t>(d) * dm);
+  for (int k = 0; k < d; ++k) {
+    for (int j = 0; j < d; ++j) qt32[static_cast<size_t>(k) * dm + j] = pi32[static_cast<size_t>(j) * d + k];
+    for (int r = 0; r < q->m; ++r) qt32[static_cast<size_t>(k) * dm + d + r] = s32[static_cast<size_t>(r) * d + k];
+  }
   hipError_t e = hipGetDevice(&q->device);
   if (e != hipSuccess) { hip_fail(e, "hipGetDevice"); delete q; return nullptr; }
   // raise the dynamic-LDS limit of the large encode tiles; if the runtime
@@ -167,14 +173,16 @@ tq_quantizer* tq_make_quantizer(int d, int bits, uint64_t seed) {
   if (tq::set_kernel_attributes() != hipSuccess) (void)hipGetLastError();
   const size_t bp = pi32.size() * sizeof(float), bs = s32.size() * sizeof(float);
   if ((e = hipMalloc(&q->d_pi, bp)) != hipSuccess || (e = hipMalloc(&q->d_s, bs)) != hipSuccess ||
-      (e = hipMalloc(&q->d_sp, bs)) != hipSuccess) {
+      (e = hipMalloc(&q->d_sp, bs)) != hipSuccess ||
+      (e = hipMalloc(&q->d_qt, qt32.size() * sizeof(float))) != hipSuccess) {
     hip_fail(e, "hipMalloc");
     tq_free_quantizer(q);
     return nullptr;
   }
   if ((e = hipMemcpy(q->d_pi, pi32.data(), bp, hipMemcpyHostToDevice)) != hipSuccess ||
       (e = hipMemcpy(q->d_s, s32.data(), bs, hipMemcpyHostToDevice)) != hipSuccess ||
-      (e = hipMemcpy(q->d_sp, sp32.data(), bs, hipMemcpyHostToDevice)) != hipSuccess) {
+      (e = hipMemcpy(q->d_sp, sp32.data(), bs, hipMemcpyHostToDevice)) != hipSuccess ||
+      (e = hipMemcpy(q->d_qt, qt32.data(), qt32.size() * sizeof(float), hipMemcpyHostToDevice)) != hipSuccess) {
     hip_fail(e, "hipMemcpy");
     tq_free_quantizer(q);
     return nullptr;
@@ -184,11 +192,12 @@ tq_quantizer* tq_make_quantizer(int d, int bits, uint64_t seed) {
 
 void tq_free_quantizer(tq_quantizer* q) {
   if (!q) return;
-  if (q->d_pi || q->d_s || q->d_sp) {
+  if (q->d_pi || q->d_s || q->d_sp || q->d_qt) {
     DeviceGuard g(q->device);
     if (q->d_pi) (void)hipFree(q->d_pi);
     if (q->d_s) (void)hipFree(q->d_s);
     if (q->d_sp) (void)hipFree(q->d_sp);
+    if (q->d_qt) (void)hipFree(q->d_qt);
   }
   delete q;
 }

@@ -79,6 +79,31 @@ int64_t attend_ws_bytes(const tq_quantizer* kq, const tq_quantizer*, int B, int 
   return prep + groups * nch * 4 * kPartStride * 4 + 256;
 }
 
+// s_waitcnt immediate that waits for vmcnt == 0 only (gfx9 encoding)
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
+
+typedef __attribute__((address_space(3))) void lds_ptr_t;
+__device__ __forceinline__ lds_ptr_t* as_lds(const void* p) {
+  return reinterpret_cast<lds_ptr_t*>(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)));
+}
+
+// Copy `words` 32-bit words (a multiple of 4) from src to LDS dst by 16-byte
+// DMA loads (global -> LDS, no registers), spread over the 4 waves; words at
+// or past `limit` (a multiple of 4, > 0) re-read the last valid 16 bytes.
+__device__ __forceinline__ void dma16(uint32_t* dst, const uint32_t* src, int words, int limit, int wave, int lane) {
+  for (int i = wave; i * 256 < words; i += 4) {
+    int off = i * 256 + lane * 4;
+    if (off + 4 > limit) off = limit - 4;
+    __builtin_amdgcn_global_load_lds(src + off, as_lds(dst + i * 256), 16, 0, 0);
+  }
+}
+// 64 floats of a per-token array, one per lane, index clamped to [0, n-1]
+__device__ __forceinline__ void dma_tok(float* dst, const float* src, int64_t t0, int64_t n, int lane) {
+  int64_t t = t0 + lane;
+  if (t >= n) t = n - 1;
+  __builtin_amdgcn_global_load_lds(src + t, as_lds(dst), 4, 0, 0);
+}
+
 template <int BPK, int BPV>
 __global__ void __launch_bounds__(256) attend_chunk_kernel(
     const uint32_t* __restrict__ kcodes, const float* __restrict__ knorms, const float* __restrict__ kgammas,
@@ -88,17 +113,46 @@ __global__ void __launch_bounds__(256) attend_chunk_kernel(
   constexpr int d = 128;
   constexpr int TK = (1 << (BPK - 1)) + 1;   // key MFMA terms (Walsh + QJL)
   constexpr int WK = BPK + 1;                // key words per 32-coordinate group
+  constexpr int WPK = 4 * WK;                // key words per token
   constexpr int NV = 1 << (BPV - 1);         // value Walsh terms
+  constexpr int KW = kStep * WPK;            // key words of a step
+  constexpr int VW = 4 * BPV * d;            // value words of a step (4 blocks of 32 tokens)
+  constexpr int SLOT = KW + VW + 3 * kStep;  // + key norms, key gammas, value norms
+  __shared__ __attribute__((aligned(16))) uint32_t stage[2][SLOT];
   __shared__ float sc[4][kStep];             // scaled logits (base 2)
   __shared__ __attribute__((aligned(16))) uint32_t av[64 * 8];   // value A operand (fp8 limbs)
   __shared__ float qst[4][4];                // per query: rescale factor, E
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int gy = blockIdx.y;
-  const int grp = gy / RT, rt = gy - grp * RT;
+  const int grp = gy / RT;
   const int64_t c0 = static_cast<int64_t>(blockIdx.x) * chunk;
   const int64_t c1 = min(n, c0 + chunk);
   const int qi = lane >> 4, j = lane & 15, g = lane >> 4;
+
+  const uint32_t* kb = kcodes + static_cast<int64_t>(grp) * n * WPK;
+  const float* knb = knorms + static_cast<int64_t>(grp) * n;
+  const float* kgb = kgammas + static_cast<int64_t>(grp) * n;
+  const int64_t nbk = (n + 31) >> 5;
+  const uint32_t* vb = vcodes + static_cast<int64_t>(grp) * nbk * BPV * d;
+  const float* vnb = vnorms + static_cast<int64_t>(grp) * n;
+
+  // stage the packed keys, values and per-token norms of the step at t0
+  auto issue = [&](int64_t t0, int buf) {
+    uint32_t* sl = stage[buf];
+    const int kv = static_cast<int>(min(static_cast<int64_t>(kStep), n - t0)) * WPK;
+    dma16(sl, kb + t0 * WPK, KW, kv, wave, lane);
+    const int64_t b0 = t0 >> 5;
+    const int vv = static_cast<int>(min(static_cast<int64_t>(4), nbk - b0)) * BPV * d;
+    dma16(sl + KW, vb + b0 * BPV * d, VW, vv, wave, lane);
+    float* nz = reinterpret_cast<float*>(sl + KW + VW);
+    if (wave < 2) {
+      dma_tok(nz + 64 * wave, knb, t0 + 64 * wave, n, lane);
+      dma_tok(nz + kStep + 64 * wave, kgb, t0 + 64 * wave, n, lane);
+    } else {
+      dma_tok(nz + 2 * kStep + 64 * (wave - 2), vnb, t0 + 64 * (wave - 2), n, lane);
+    }
+  };
 
   v8i AK[TK];
   {
@@ -112,14 +166,8 @@ __global__ void __launch_bounds__(256) attend_chunk_kernel(
 #pragma unroll
     for (int i = 0; i < 10; ++i) cs[i] = cp[i];
   }
-  const uint32_t* kb = kcodes + static_cast<int64_t>(grp) * n * 4 * WK;
-  const float* knb = knorms + static_cast<int64_t>(grp) * n;
-  const float* kgb = kgammas + static_cast<int64_t>(grp) * n;
-  const int64_t nbk = (n + 31) >> 5;
-  const uint32_t* vb = vcodes + static_cast<int64_t>(grp) * nbk * BPV * d;
-  const float* vnb = vnorms + static_cast<int64_t>(grp) * n;
 
-  // running softmax state of query `wave` (softmax phase) -- kept by every lane of that wave
+  // running softmax state of query `wave` (softmax phase), uniform over that wave
   float m_run = -INFINITY, l_run = 0.f, w_run = 0.f;
   int e_run = 0;
   // value accumulators: [Walsh term][column tile of this wave]; rows 4q+limb, column 16ct+j
@@ -128,19 +176,21 @@ __global__ void __launch_bounds__(256) attend_chunk_kernel(
   for (int t = 0; t < NV; ++t) acc[t][0] = acc[t][1] = (v4f){0.f, 0.f, 0.f, 0.f};
   int e_acc = 0;   // scale exponent the accumulators are in (per query, same in every wave)
 
-  for (int64_t t0 = c0; t0 < c1; t0 += kStep) {
+  if (c0 < c1) issue(c0, 0);
+  int buf = 0;
+  for (int64_t t0 = c0; t0 < c1; t0 += kStep, buf ^= 1) {
+    wait_vm0();        // this wave's part of the step's data has landed in LDS
+    __syncthreads();   // ... and every wave's; the other slot is free again
+    if (t0 + kStep < c1) issue(t0 + kStep, buf ^ 1);
+    const uint32_t* sl = stage[buf];
+    const float* kns = reinterpret_cast<const float*>(sl + KW + VW);
     // ---------------- K phase: logits of tokens t0 + 32*wave .. +31 ----------------
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int tt = 32 * wave + 16 * u + j;   // token within the step
-      const int64_t key = t0 + tt;
-      const bool kv = key < c1;
       uint32_t w[5] = {0u, 0u, 0u, 0u, 0u};
-      if (kv) {
-        const uint32_t* wp = kb + (key * 4 + g) * WK;
 #pragma unroll
-        for (int p = 0; p < WK; ++p) w[p] = wp[p];
-      }
+      for (int p = 0; p < WK; ++p) w[p] = sl[(tt * 4 + g) * WK + p];
       v4f aM = {0.f, 0.f, 0.f, 0.f}, aQ = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int t = 0; t < TK - 1; ++t) aM = mfma_fp8_fp4(AK[t], bits_to_fp4(walsh_word<BPK>(w, t)), aM);
@@ -150,7 +200,7 @@ __global__ void __launch_bounds__(256) attend_chunk_kernel(
       const float mse = fmaf(aM[0], cs[2], fmaf(aM[1], cs[3], fmaf(aM[2], cs[4], fmaf(aM[3], cs[5], cs[0]))));
       const float qjl = fmaf(aQ[0], cs[6], fmaf(aQ[1], cs[7], fmaf(aQ[2], cs[8], fmaf(aQ[3], cs[9], cs[1]))));
       float s = -INFINITY;
-      if (kv) s = fmaf(knb[key], mse, kgb[key] * qjl) * scale_log2;
+      if (t0 + tt < c1) s = fmaf(kns[tt], mse, kns[kStep + tt] * qjl) * scale_log2;
       sc[qi][tt] = s;
     }
     __syncthreads();
@@ -159,21 +209,16 @@ __global__ void __launch_bounds__(256) attend_chunk_kernel(
       const int q = wave;
       const int ta = 2 * lane, tb = 2 * lane + 1;
       const float sa = sc[q][ta], sb = sc[q][tb];
-      float mx = fmaxf(sa, sb);
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      const float mx = wave_max(fmaxf(sa, sb));
       const float m_new = fmaxf(m_run, mx);
       const float alpha = exp2f(m_run - m_new);   // 0 on the first step
       const float pa = exp2f(sa - m_new), pb = exp2f(sb - m_new);
-      const float na = (t0 + ta < c1) ? vnb[t0 + ta] : 0.f;
-      const float nb2 = (t0 + tb < c1) ? vnb[t0 + tb] : 0.f;
+      const float* vns = kns + 2 * kStep;
+      const float na = (t0 + ta < c1) ? vns[ta] : 0.f;
+      const float nb2 = (t0 + tb < c1) ? vns[tb] : 0.f;
       const float wa = pa * na, wb = pb * nb2;
-      float ps = pa + pb, wm = fmaxf(wa, wb);
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        ps += __shfl_xor(ps, off);
-        wm = fmaxf(wm, __shfl_xor(wm, off));
-      }
+      const float ps = wave_sum(pa + pb);
+      const float wm = wave_max(fmaxf(wa, wb));
       l_run = fmaf(l_run, alpha, ps);
       m_run = m_new;
       // the A values are w / (fp4 slot value >= 0.5): 2 * max lands in [8, 16)
@@ -208,9 +253,7 @@ __global__ void __launch_bounds__(256) attend_chunk_kernel(
 #pragma unroll
         for (int lb = 0; lb < 4; ++lb) avb[(4 * q + lb + 16 * gg) * 32 + e] = static_cast<uint8_t>(limbs >> (8 * lb));
       }
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) wq_sum += __shfl_xor(wq_sum, off);
-      w_run = fmaf(w_run, alpha, wq_sum);
+      w_run = fmaf(w_run, alpha, wave_sum(wq_sum));
     }
     __syncthreads();
     // ---------------- V phase: wave owns coordinates 32*wave .. +31 ----------------
@@ -223,16 +266,14 @@ __global__ void __launch_bounds__(256) attend_chunk_kernel(
         acc[t][0] *= rs;
         acc[t][1] *= rs;
       }
-      const int64_t blk = (t0 >> 5) + g;   // 32-token block of this lane group
+      // lane group g reads the 32-token block g of the step; blocks past the
+      // end hold re-read words, which meet zero weights
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         const int col = 32 * wave + 16 * ct + j;
         uint32_t w[5] = {0u, 0u, 0u, 0u, 0u};
-        if (blk < nbk) {
-          const uint32_t* wp = vb + (blk * BPV) * d + col;
 #pragma unroll
-          for (int p = 0; p < BPV; ++p) w[p] = wp[p * d];
-        }
+        for (int p = 0; p < BPV; ++p) w[p] = sl[KW + (g * BPV + p) * d + col];
 #pragma unroll
         for (int t = 0; t < NV; ++t) acc[t][ct] = mfma_fp8_fp4(A, bits_to_fp4(walsh_word<BPV>(w, t)), acc[t][ct]);
       }
@@ -242,12 +283,12 @@ __global__ void __launch_bounds__(256) attend_chunk_kernel(
         pin(acc[t][1]);
       }
     }
-    __syncthreads();
   }
 
   // ---------------- chunk result ----------------
   // value part: sum_t w_t c[idx] = sum_S coef_S (2 sum_t w_t b_S - sum_t w_t);
   // the softmax state of query q lives in wave q: publish it
+  __syncthreads();
   if (lane == 0) {
     qst[wave][2] = w_run;
     qst[wave][3] = l_run;
@@ -273,7 +314,10 @@ __global__ void __launch_bounds__(256) attend_chunk_kernel(
   }
 }
 
-// one workgroup (128 threads) per (batch, query head)
+// One workgroup (256 threads) per (batch, query head): combine the chunk
+// partials (max-shifted), add the exact bf16 tail, rotate back once and
+// normalise.  Each output coordinate is shared by two threads (halves of the
+// chunk list / of the rotation's inner dimension / of the tail).
 __global__ void __launch_bounds__(256) attend_merge_kernel(const void* __restrict__ queries, int q_dtype, int Hq,
                                                            int Hkv, int G, int RT, int64_t nchunk,
                                                            const float* __restrict__ part,
@@ -284,66 +328,74 @@ __global__ void __launch_bounds__(256) attend_merge_kernel(const void* __restric
   constexpr int d = 128;
   __shared__ float qv[d];
   __shared__ float accs[d];
+  __shared__ float half2[2][d];
   __shared__ float red[8];
-  __shared__ float ts[512];   // tail logits (n_tail <= 512)
-  const int tid = threadIdx.x;
+  __shared__ float ts[512];   // tail logits, then tail weights (n_tail <= 512)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i = tid & (d - 1), hf = tid >> 7;
   const int bh = blockIdx.x;
   const int b = bh / Hq, h = bh - b * Hq;
   const int kvh = h / G, qg = h - kvh * G;
   const int rt = qg >> 2, qi = qg & 3;
   const int64_t gy = (static_cast<int64_t>(b) * Hkv + kvh) * RT + rt;
+  const float* pq = part + (gy * nchunk * 4 + qi) * kPartStride;   // chunk c at pq + c * 4 * kPartStride
+  const int64_t cstride = 4 * kPartStride;
   if (tid < d) qv[tid] = load_elem(queries, q_dtype, static_cast<int64_t>(bh) * d + tid);
-  // global max over chunks and tail
+  __syncthreads();
+  // maxima: chunks, then the tail logits (one wave per tail token, lanes over coordinates)
   float mloc = -INFINITY;
-  for (int64_t c = tid; c < nchunk; c += blockDim.x)
-    mloc = fmaxf(mloc, part[((gy * nchunk + c) * 4 + qi) * kPartStride + 128]);
-  __syncthreads();
+  for (int64_t c = tid; c < nchunk; c += 256) mloc = fmaxf(mloc, pq[c * cstride + 128]);
   const int64_t toff = (static_cast<int64_t>(b) * Hkv + kvh) * n_tail;
-  for (int t = tid; t < n_tail; t += blockDim.x) {
+  for (int t = wave; t < n_tail; t += 4) {
     const uint16_t* kt = k_tail + (toff + t) * d;
-    float s = 0.f;
-    for (int k = 0; k < d; ++k) s = fmaf(qv[k], bf16_to_f32(kt[k]), s);
-    ts[t] = s * scale_log2;
-    mloc = fmaxf(mloc, ts[t]);
+    const float sdot = wave_sum(fmaf(qv[lane], bf16_to_f32(kt[lane]), qv[lane + 64] * bf16_to_f32(kt[lane + 64])));
+    if (lane == 0) ts[t] = sdot * scale_log2;
+    mloc = fmaxf(mloc, sdot * scale_log2);
   }
-  for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
-  if ((tid & 63) == 0) red[tid >> 6] = mloc;
+  mloc = wave_max(mloc);
+  if (lane == 0) red[wave] = mloc;
   __syncthreads();
-  float M = -INFINITY;
-  for (int w = 0; w < static_cast<int>(blockDim.x >> 6); ++w) M = fmaxf(M, red[w]);
-  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   // denominators
   float lsum = 0.f;
-  for (int64_t c = tid; c < nchunk; c += blockDim.x) {
-    const float* pc = part + ((gy * nchunk + c) * 4 + qi) * kPartStride;
-    lsum += pc[129] * exp2f(pc[128] - M);
+  for (int64_t c = tid; c < nchunk; c += 256) lsum = fmaf(pq[c * cstride + 129], exp2f(pq[c * cstride + 128] - M), lsum);
+  for (int t = tid; t < n_tail; t += 256) {
+    const float pt = exp2f(ts[t] - M);
+    ts[t] = pt;
+    lsum += pt;
   }
-  for (int t = tid; t < n_tail; t += blockDim.x) {
-    const float p = exp2f(ts[t] - M);
-    ts[t] = p;
-    lsum += p;
-  }
-  for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off);
-  if ((tid & 63) == 0) red[tid >> 6] = lsum;
+  lsum = wave_sum(lsum);
   __syncthreads();
-  float L = 0.f;
-  for (int w = 0; w < static_cast<int>(blockDim.x >> 6); ++w) L += red[w];
-  // rotated-frame accumulator of the compressed part
-  if (tid < d) {
-    float a = 0.f;
-    for (int64_t c = 0; c < nchunk; ++c) {
-      const float* pc = part + ((gy * nchunk + c) * 4 + qi) * kPartStride;
-      a = fmaf(pc[tid], exp2f(pc[128] - M), a);
+  if (lane == 0) red[4 + wave] = lsum;
+  // rotated-frame accumulator of the compressed part: chunks split by parity
+  {
+    float a0 = 0.f, a1 = 0.f;
+    int64_t c = hf;
+    for (; c + 2 < nchunk; c += 4) {
+      a0 = fmaf(pq[c * cstride + i], exp2f(pq[c * cstride + 128] - M), a0);
+      a1 = fmaf(pq[(c + 2) * cstride + i], exp2f(pq[(c + 2) * cstride + 128] - M), a1);
     }
-    accs[tid] = a;
+    for (; c < nchunk; c += 2) a0 = fmaf(pq[c * cstride + i], exp2f(pq[c * cstride + 128] - M), a0);
+    half2[hf][i] = a0 + a1;
   }
   __syncthreads();
-  if (tid < d) {
-    float o = 0.f;
-    for (int jj = 0; jj < d; ++jj) o = fmaf(piv[static_cast<int64_t>(jj) * d + tid], accs[jj], o);   // Pi^T acc
-    for (int t = 0; t < n_tail; ++t) o = fmaf(ts[t], bf16_to_f32(v_tail[(toff + t) * d + tid]), o);
-    out[static_cast<int64_t>(bh) * d + tid] = o / L;
+  const float L = (red[4] + red[5]) + (red[6] + red[7]);
+  if (tid < d) accs[i] = half2[0][i] + half2[1][i];
+  __syncthreads();
+  // Pi^T acc (inner dimension split between the two halves), then the tail values
+  {
+    float o0 = 0.f, o1 = 0.f;
+    const int j0 = hf * (d / 2);
+#pragma unroll 4
+    for (int jj = 0; jj < d / 2; jj += 2) {
+      o0 = fmaf(piv[static_cast<int64_t>(j0 + jj) * d + i], accs[j0 + jj], o0);
+      o1 = fmaf(piv[static_cast<int64_t>(j0 + jj + 1) * d + i], accs[j0 + jj + 1], o1);
+    }
+    for (int t = hf; t < n_tail; t += 2) o0 = fmaf(ts[t], bf16_to_f32(v_tail[(toff + t) * d + i]), o0);
+    half2[hf][i] = o0 + o1;
   }
+  __syncthreads();
+  if (tid < d) out[static_cast<int64_t>(bh) * d + i] = (half2[0][i] + half2[1][i]) / L;
 }
 
 hipError_t launch_attend(const tq_quantizer* kq, const tq_quantizer* vq, const void* queries, int q_dtype, int B, int Hq,
@@ -379,7 +431,7 @@ hipError_t launch_attend(const tq_quantizer* kq, const tq_quantizer* vq, const v
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(attend_merge_kernel, dim3(static_cast<unsigned>(B * Hq)), dim3(128), 0, st, queries, q_dtype, Hq, Hkv,
+  hipLaunchKernelGGL(attend_merge_kernel, dim3(static_cast<unsigned>(B * Hq)), dim3(256), 0, st, queries, q_dtype, Hq, Hkv,
                      G, RT, nch, part, k_tail, v_tail, n_tail, sl, vq->d_pi, out);
   return hipGetLastError();
 }

@@ -18,50 +18,6 @@ __device__ __forceinline__ float load_elem(const void* p, int dtype, int64_t i) 
 }
 
 // --------------------------------------------------------------------------
-// OCP FP8 E4M3 (bias 7, max 448, subnormal step 2^-9), round to nearest even.
-// Used to split query-side operands into limbs; decode is exact so each
-// residual is exact in float.
-// --------------------------------------------------------------------------
-__device__ __forceinline__ float e4m3_value(uint32_t b) {
-  uint32_t e = (b >> 3) & 15u, m = b & 7u;
-  float v = e == 0 ? ldexpf(static_cast<float>(m), -9) : ldexpf(static_cast<float>(8u + m), static_cast<int>(e) - 10);
-  return (b & 0x80u) ? -v : v;
-}
-
-__device__ __forceinline__ uint32_t e4m3_encode(float x) {
-  uint32_t sign = x < 0.f ? 0x80u : 0u;
-  float a = fabsf(x);
-  if (!(a > 0.f)) return 0u;
-  if (a >= 448.f) return sign | 0x7Eu;
-  int ex;
-  frexpf(a, &ex);              // a = f * 2^ex, f in [0.5, 1)
-  int e = ex - 1 + 7;           // biased exponent of a
-  uint32_t code;
-  if (e <= 0) {                 // subnormal: step 2^-9
-    float q = rintf(ldexpf(a, 9));   // round half to even
-    code = static_cast<uint32_t>(q); // 0..8 (8 == min normal 2^-6)
-  } else {
-    float q = rintf(ldexpf(a, 3 - (ex - 1)));   // mantissa with 3 fraction bits, in [8, 16]
-    uint32_t mq = static_cast<uint32_t>(q);
-    if (mq == 16u) { mq = 8u; ++e; }
-    code = (static_cast<uint32_t>(e) << 3) | (mq - 8u);
-    if (code > 0x7Eu) code = 0x7Eu;
-  }
-  return sign | code;
-}
-
-// Limb k (k = 0..3) of x: x ~ sum_k 2^(-4k) limb_k with limb values fp8.
-__device__ __forceinline__ uint32_t e4m3_limb(float x, int k) {
-  float r = x;
-  uint32_t b = e4m3_encode(r);
-  for (int i = 0; i < k; ++i) {
-    r = (r - e4m3_value(b)) * 16.f;
-    b = e4m3_encode(r);
-  }
-  return b;
-}
-
-// --------------------------------------------------------------------------
 // A 32-bit word of bits (one bit per coordinate or per token) as the fp4
 // (E2M1) B operand of the 16x16x128 f8f6f4 MFMA: 4 dwords of 8 nibbles.
 // Dword s holds bit 4i+s of w in nibble i (value 0.5 / 1 / 2 / 2 for
@@ -88,6 +44,40 @@ __device__ __forceinline__ uint32_t walsh_word(const uint32_t (&w)[5], int t) {
   for (int p = 0; p < BP; ++p)
     if (mk & (1 << p)) r ^= w[p];
   return r;
+}
+
+// Wave-wide reductions over all 64 lanes without the LDS permute path: DPP
+// within rows of 16 (quad swaps, then row rotations by 4 and 8), then the
+// four row results through scalar reads.  Every lane must be active; the
+// result is uniform.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_f<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp_f<0x124>(v);   // row_ror:4
+  v += dpp_f<0x128>(v);   // row_ror:8
+  return v;
+}
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x124>(v));
+  v = fmaxf(v, dpp_f<0x128>(v));
+  return v;
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row_sum16(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = row_max16(v);
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
 // value of a set bit at element slot s = (K % 32) / 8

@@ -41,4 +41,5 @@ struct tq_quantizer {
   float* d_pi = nullptr;              // [d][d]   y = Pi x
   float* d_s = nullptr;               // [m][d]   QJL matrix
   float* d_sp = nullptr;              // [m][d]   S' = S Pi^T (acts on rotated residuals)
+  float* d_qt = nullptr;              // [d][d+m] column k of Pi then of S (query transform, k-major)
 };

@@ -35,9 +35,9 @@ namespace tq {
 //   {cM, cQ, sM0..3, sQ0..3}: logit = n (sum_k sM_k C_M,k + cM) + gamma (sum_k sQ_k C_Q,k + cQ)
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) query_prep_kernel(const void* __restrict__ queries, int q_dtype, int Hq, int Hkv,
-                                                         int G, int RT, int d, int m, const float* __restrict__ pi,
-                                                         const float* __restrict__ s, Codebook cb, int C,
-                                                         uint8_t* __restrict__ wsA, float* __restrict__ wsC) {
+                                                         int G, int RT, int d, int m, const float* __restrict__ qt,
+                                                         Codebook cb, int C, uint8_t* __restrict__ wsA,
+                                                         float* __restrict__ wsC) {
   extern __shared__ float sm[];
   float* qv = sm;           // [d]
   float* qh = qv + d;       // [d]   Pi q
@@ -56,21 +56,63 @@ __global__ void __launch_bounds__(256) query_prep_kernel(const void* __restrict_
     for (int j = tid; j < d; j += blockDim.x) qv[j] = load_elem(queries, q_dtype, qoff + j);
   }
   __syncthreads();
+  // [Pi q, S q] from the k-major table: wave w takes the contraction slice
+  // k in [w KQ, (w+1) KQ), lane the 4 consecutive outputs 4 lane + 256 r;
+  // the loads of a slice are independent 16-byte reads (indices clamped, no
+  // branches), partial sums meet in LDS
   float lmax_h = 0.f, lmax_s = 0.f, lsum_h = 0.f, lsum_s = 0.f;
-  if (valid) {
-    for (int j = tid; j < d; j += blockDim.x) {
-      float a = 0.f;
-      for (int k = 0; k < d; ++k) a = fmaf(pi[static_cast<int64_t>(j) * d + k], qv[k], a);
-      qh[j] = a;
-      lmax_h = fmaxf(lmax_h, fabsf(a));
-      lsum_h += a;
+  const int dm = d + m;
+  float* pw = sq + m;   // [4][dm] partial sums
+  {
+    const int wave = tid >> 6, lane = tid & 63;
+    const int KQ = (d + 3) / 4;
+    const int k0 = min(d, wave * KQ), k1 = min(d, k0 + KQ);
+    for (int ob = 0; ob < dm; ob += 256) {
+      const int o = ob + 4 * lane;
+      float a[4] = {0.f, 0.f, 0.f, 0.f};
+      if (valid && (dm & 3) == 0) {
+        const int oc = min(o, dm - 4);
+        for (int kk = k0; kk < k1; kk += 16) {
+          // 16 loads in flight before the first use
+          float4 v[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u)
+            v[u] = *reinterpret_cast<const float4*>(qt + static_cast<int64_t>(min(kk + u, k1 - 1)) * dm + oc);
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            const float qk = kk + u < k1 ? qv[min(kk + u, k1 - 1)] : 0.f;
+            a[0] = fmaf(v[u].x, qk, a[0]);
+            a[1] = fmaf(v[u].y, qk, a[1]);
+            a[2] = fmaf(v[u].z, qk, a[2]);
+            a[3] = fmaf(v[u].w, qk, a[3]);
+          }
+        }
+      } else if (valid) {
+#pragma unroll 4
+        for (int kk = k0; kk < k1; ++kk) {
+          const float qk = qv[kk];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a[e] = fmaf(qt[static_cast<int64_t>(kk) * dm + min(o + e, dm - 1)], qk, a[e]);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (o + e < dm) pw[wave * dm + o + e] = a[e];
     }
-    for (int r = tid; r < m; r += blockDim.x) {
-      float a = 0.f;
-      for (int k = 0; k < d; ++k) a = fmaf(s[static_cast<int64_t>(r) * d + k], qv[k], a);
-      sq[r] = a;
-      lmax_s = fmaxf(lmax_s, fabsf(a));
-      lsum_s += a;
+  }
+  __syncthreads();
+  if (valid) {
+    for (int o = tid; o < dm; o += blockDim.x) {
+      const float a = (pw[o] + pw[dm + o]) + (pw[2 * dm + o] + pw[3 * dm + o]);
+      if (o < d) {
+        qh[o] = a;
+        lmax_h = fmaxf(lmax_h, fabsf(a));
+        lsum_h += a;
+      } else {
+        sq[o - d] = a;
+        lmax_s = fmaxf(lmax_s, fabsf(a));
+        lsum_s += a;
+      }
     }
   }
   // block reductions (max and sum of both vectors)
@@ -104,30 +146,31 @@ __global__ void __launch_bounds__(256) query_prep_kernel(const void* __restrict_
   const int E_m = vmax_m > 0.f ? 7 - ilogbf(vmax_m) : 0;
   const int E_q = vmax_q > 0.f ? 7 - ilogbf(vmax_q) : 0;
 
-  // A operand bytes of this query: rows 4*qi .. 4*qi+3 (limbs), lane-groups 0..3
+  // A operand bytes of this query: rows 4*qi .. 4*qi+3 (limbs), lane-groups
+  // 0..3.  One thread per (term, chunk, lane-group, element) writes the 4 limbs
+  // of its value: limb k carries the next 4 significant bits, each rounded to
+  // fp8 E4M3 by the hardware conversion (round to nearest even), so every
+  // residual is exact in float.
   const int64_t tile_bytes = 64 * 32;
   uint8_t* base = wsA + static_cast<int64_t>(gy) * T * C * tile_bytes;
-  for (int t = 0; t < T; ++t) {
+  for (int idx = tid; idx < T * C * 128; idx += blockDim.x) {
+    const int t = idx / (C * 128), c = (idx >> 7) - t * C, ge = idx & 127;
+    const int g = ge >> 5, e = ge & 31;
     const bool is_q = t == T - 1;
-    const float coef = is_q ? alpha2 : 2.f * cb.coef[t];
-    const int E = is_q ? E_q : E_m;
-    for (int c = 0; c < C; ++c) {
-      for (int e2 = tid; e2 < 16 * 32; e2 += blockDim.x) {
-        const int li = e2 >> 5, e = e2 & 31;        // li: 4 limbs x 4 lane-groups
-        const int limb = li & 3, g = li >> 2;
-        const int lane = 4 * qi + limb + 16 * g;
-        uint32_t byte = 0u;
-        if (valid) {
-          const int k = a_elem_to_k(g, e);
-          const int coord = c * 128 + 32 * (k >> 5) + k_to_bit(k);
-          const int lim = is_q ? m : d;
-          if (coord < lim) {
-            const float v = coef * (is_q ? sq[coord] : qh[coord]) / fp4_slot_value((k & 31) >> 3);
-            byte = e4m3_limb(ldexpf(v, E), limb);
-          }
-        }
-        base[(static_cast<int64_t>(t) * C + c) * tile_bytes + lane * 32 + e] = static_cast<uint8_t>(byte);
-      }
+    const int k = a_elem_to_k(g, e);
+    const int coord = c * 128 + 32 * (k >> 5) + k_to_bit(k);
+    float x = 0.f;
+    if (valid && coord < (is_q ? m : d)) {
+      const float coef = is_q ? alpha2 : 2.f * cb.coef[t];
+      const float v = coef * (is_q ? sq[coord] : qh[coord]) / fp4_slot_value((k & 31) >> 3);
+      x = ldexpf(v, is_q ? E_q : E_m);
+    }
+    uint8_t* dst = base + (static_cast<int64_t>(t) * C + c) * tile_bytes + (4 * qi + 16 * g) * 32 + e;
+#pragma unroll
+    for (int limb = 0; limb < 4; ++limb) {
+      const uint32_t byte = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.f, 0, false)) & 0xFFu;
+      dst[limb * 32] = static_cast<uint8_t>(byte);
+      x = (x - __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(byte), 0)) * 16.f;
     }
   }
   if (tid < 16) {
@@ -354,10 +397,10 @@ hipError_t launch_query_prep(const tq_quantizer* q, const void* queries, int q_d
   const int G = Hq / Hkv;
   const int RT = (G + 3) / 4;
   const int C = (q->d + 127) / 128;
-  const size_t lds = sizeof(float) * (2 * q->d + q->m);
+  const size_t lds = sizeof(float) * (2 * q->d + q->m + 4 * (q->d + q->m));
   dim3 grid(static_cast<unsigned>(static_cast<int64_t>(B) * Hkv * RT * 4));
-  hipLaunchKernelGGL(query_prep_kernel, grid, dim3(256), lds, st, queries, q_dtype, Hq, Hkv, G, RT, q->d, q->m, q->d_pi,
-                     q->d_s, q->cb[0], C, wsA, wsC);
+  hipLaunchKernelGGL(query_prep_kernel, grid, dim3(256), lds, st, queries, q_dtype, Hq, Hkv, G, RT, q->d, q->m, q->d_qt,
+                     q->cb[0], C, wsA, wsC);
   return hipGetLastError();
 }
 
