@@ -79,8 +79,21 @@ int64_t attend_ws_bytes(const tq_quantizer* kq, const tq_quantizer*, int B, int 
   return prep + groups * nch * 4 * kPartStride * 4 + 256;
 }
 
-// s_waitcnt immediate that waits for vmcnt == 0 only (gfx9 encoding)
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
+// s_waitcnt immediate that waits for vmcnt <= N only (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+template <int N>
+__device__ __forceinline__ void wait_vm_upto(int n) {   // runtime n in [0, N]
+  if constexpr (N > 0) {
+    if (n >= N) { wait_vm<N>(); return; }
+    wait_vm_upto<N - 1>(n);
+  } else {
+    wait_vm<0>();
+  }
+}
 
 typedef __attribute__((address_space(3))) void lds_ptr_t;
 __device__ __forceinline__ lds_ptr_t* as_lds(const void* p) {
@@ -118,7 +131,8 @@ __global__ void __launch_bounds__(256) attend_chunk_kernel(
   constexpr int KW = kStep * WPK;            // key words of a step
   constexpr int VW = 4 * BPV * d;            // value words of a step (4 blocks of 32 tokens)
   constexpr int SLOT = KW + VW + 3 * kStep;  // + key norms, key gammas, value norms
-  __shared__ __attribute__((aligned(16))) uint32_t stage[2][SLOT];
+  constexpr int NSLOT = 3;                   // steps s, s+1, s+2 staged at once
+  __shared__ __attribute__((aligned(16))) uint32_t stage[NSLOT][SLOT];
   __shared__ float sc[4][kStep];             // scaled logits (base 2)
   __shared__ __attribute__((aligned(16))) uint32_t av[64 * 8];   // value A operand (fp8 limbs)
   __shared__ float qst[4][4];                // per query: rescale factor, E
@@ -176,12 +190,18 @@ __global__ void __launch_bounds__(256) attend_chunk_kernel(
   for (int t = 0; t < NV; ++t) acc[t][0] = acc[t][1] = (v4f){0.f, 0.f, 0.f, 0.f};
   int e_acc = 0;   // scale exponent the accumulators are in (per query, same in every wave)
 
+  // DMA instructions this wave issues per step (the same for every step)
+  constexpr int KI = KW / 256, VI = VW / 256;
+  const int per_step = (KI + 3 - wave) / 4 + (VI + 3 - wave) / 4 + (wave < 2 ? 2 : 1);
   if (c0 < c1) issue(c0, 0);
+  if (c0 + kStep < c1) issue(c0 + kStep, 1);
   int buf = 0;
-  for (int64_t t0 = c0; t0 < c1; t0 += kStep, buf ^= 1) {
-    wait_vm0();        // this wave's part of the step's data has landed in LDS
-    __syncthreads();   // ... and every wave's; the other slot is free again
-    if (t0 + kStep < c1) issue(t0 + kStep, buf ^ 1);
+  for (int64_t t0 = c0; t0 < c1; t0 += kStep, buf = buf == NSLOT - 1 ? 0 : buf + 1) {
+    // this wave's part of step t0 has landed once at most the next step's
+    // loads are outstanding (the counter retires in issue order) ...
+    wait_vm_upto<8>(t0 + kStep < c1 ? per_step : 0);
+    __syncthreads();   // ... and every wave's; the slot of step t0 - kStep is free again
+    if (t0 + 2 * kStep < c1) issue(t0 + 2 * kStep, buf == 0 ? NSLOT - 1 : buf - 1);
     const uint32_t* sl = stage[buf];
     const float* kns = reinterpret_cast<const float*>(sl + KW + VW);
     // ---------------- K phase: logits of tokens t0 + 32*wave .. +31 ----------------

@@ -247,6 +247,42 @@ __device__ __forceinline__ v4f mfma_f16(const v8h& a, const v8h& b, const v4f& c
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// Binary search of the sorted thresholds: bit L of idx = #{t_k < y} is
+// decided by one comparison against the threshold that splits the cells
+// still possible, picked from the candidates by the bits above L with
+// branch-free selects.  Each comparison is also that bit plane's lane mask.
+template <int BP, int L>
+__device__ __forceinline__ float pick_threshold(const float (&th)[(1 << BP) - 1], const bool (&bit)[BP]) {
+  constexpr int NC = 1 << (BP - 1 - L);
+  float c[NC];
+#pragma unroll
+  for (int u = 0; u < NC; ++u) c[u] = th[u * (2 << L) + (1 << L) - 1];
+#pragma unroll
+  for (int j = 0; (1 << j) < NC; ++j)
+#pragma unroll
+    for (int u = 0; u < (NC >> (j + 1)); ++u) c[u] = bit[L + 1 + j] ? c[2 * u + 1] : c[2 * u];
+  return c[0];
+}
+
+template <int BP, int L>
+__device__ __forceinline__ void decide_bits(float y, const float (&th)[(1 << BP) - 1], bool (&bit)[BP]) {
+  bit[L] = pick_threshold<BP, L>(th, bit) < y;
+  if constexpr (L > 0) decide_bits<BP, L - 1>(y, th, bit);
+}
+
+// c[idx] from the bits, by a select tree over the 2^BP centroids
+template <int BP>
+__device__ __forceinline__ float pick_centroid(const float (&cen)[1 << BP], const bool (&bit)[BP]) {
+  float c[1 << BP];
+#pragma unroll
+  for (int u = 0; u < (1 << BP); ++u) c[u] = cen[u];
+#pragma unroll
+  for (int j = 0; j < BP; ++j)
+#pragma unroll
+    for (int u = 0; u < ((1 << BP) >> (j + 1)); ++u) c[u] = bit[j] ? c[2 * u + 1] : c[2 * u];
+  return c[0];
+}
+
 // LK: how a tile is loaded: 0 element by element (any d, either dtype),
 // 1 bf16 and 2 fp32 in 16-byte chunks fetched one tile ahead.  BP: index bits.
 template <int KS, int LK, bool PROD, int BP>
@@ -455,25 +491,13 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
   auto halves = [&](uint64_t m0, uint64_t m1) {
     return static_cast<uint32_t>((m0 >> (16 * q)) & 0xFFFFu) | (static_cast<uint32_t>((m1 >> (16 * q)) & 0xFFFFu) << 16);
   };
-  // idx = #{t_k < y}; the centroid telescopes over the same comparisons
-  float th[NT], dc[NT];
+  float th[NT], cen[NT + 1];
 #pragma unroll
-  for (int k2 = 0; k2 < NT; ++k2) {
-    th[k2] = cb.t[k2];
-    dc[k2] = cb.c[k2 + 1] - cb.c[k2];
-  }
-  const float c0 = cb.c[0];
-  auto bucket = [&](float y, float& cv) {
-    int idx = 0;
-    cv = c0;
+  for (int k2 = 0; k2 < NT; ++k2) th[k2] = cb.t[k2];
 #pragma unroll
-    for (int k2 = 0; k2 < NT; ++k2) {
-      const bool above = th[k2] < y;
-      idx += above ? 1 : 0;
-      cv += above ? dc[k2] : 0.f;
-    }
-    return idx;
-  };
+  for (int k2 = 0; k2 <= NT; ++k2) cen[k2] = cb.c[k2];
+  // row sum over the 16 lanes of a row of the C layout (one DPP row)
+  auto sum16 = [&](float v) { return row_sum16(v); };
 
   int64_t t = blockIdx.x;
   if (t < total) fetch(t);
@@ -506,48 +530,36 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           const int vbase = 32 * h + 16 * h2 + 4 * q;
-          float r2[4];
-          uint32_t idxs[2][4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) r2[i] = 0.f;
+          for (int i = 0; i < 4; ++i) {
+            const float sc = scl[vbase + i];
+            bool bits[2][BP];
+            float r2 = 0.f;
 #pragma unroll
-          for (int ct = 0; ct < 2; ++ct) {
-            const int c = 32 * w + 16 * ct + r16;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float y = acc[h2][ct][i] * scl[vbase + i];
-              float cv;
-              const int idx = bucket(y, cv);
-              const float rho = c < d ? y - cv : 0.f;
-              r2[i] = fmaf(rho, rho, r2[i]);
+            for (int ct = 0; ct < 2; ++ct) {
+              const int c = 32 * w + 16 * ct + r16;
+              const float y = acc[h2][ct][i] * sc;
+              decide_bits<BP, BP - 1>(y, th, bits[ct]);
+              const float rho = c < d ? y - pick_centroid<BP>(cen, bits[ct]) : 0.f;
+              r2 = fmaf(rho, rho, r2);
               if (c < KP) {
                 const float sr = rho * kRhoScale;
                 const _Float16 hh = static_cast<_Float16>(sr);
                 rh[(vbase + i) * LDH + c] = hh;
                 rl[(vbase + i) * LDH + c] = static_cast<_Float16>(sr - static_cast<float>(hh));
               }
-              idxs[ct][i] = c < d ? static_cast<uint32_t>(idx) : 0u;
             }
-          }
-          if (w < G) {
+            if (w < G) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              #pragma unroll
-              for (int p = 0; p < bp; ++p) {
-                const uint64_t m0 = __ballot((idxs[0][i] >> p) & 1u);
-                const uint64_t m1 = __ballot((idxs[1][i] >> p) & 1u);
+              for (int p = 0; p < BP; ++p) {
+                const uint64_t m0 = __ballot(bits[0][p] && 32 * w + r16 < d);
+                const uint64_t m1 = __ballot(bits[1][p] && 32 * w + 16 + r16 < d);
                 if (r16 == 0) ost[buf][(vbase + i) * WPK + w * W + p] = halves(m0, m1);
               }
-          }
-          // partial ||rho||^2 over this wave's 32 coordinates
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float v = r2[i];
-            v += __shfl_xor(v, 1);
-            v += __shfl_xor(v, 2);
-            v += __shfl_xor(v, 4);
-            v += __shfl_xor(v, 8);
-            if (r16 == 0) part2[w][vbase + i] = v;
+            }
+            // partial ||rho||^2 over this wave's 32 coordinates
+            r2 = sum16(r2);
+            if (r16 == 0) part2[w][vbase + i] = r2;
           }
         }
       }
@@ -592,32 +604,25 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
         contract(xh, bPl, h, true, acc);
         if constexpr (XLO) contract(xl, bPh, h, true, acc);
         pin_acc(acc);
-        uint32_t idxs[2][2][4];
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const int tk = 32 * h + 16 * h2 + r16;
-          const float sc = scl[tk];
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              float cv;
-              const int idx = bucket(acc[h2][ct][i] * sc, cv);
-              idxs[h2][ct][i] = (tk < rows && 32 * w + 16 * ct + 4 * q + i < d) ? static_cast<uint32_t>(idx) : 0u;
-            }
-        }
+        // lane holds coordinate 32w + 16ct + 4q + i, token 32h + 16h2 + r16
+        const float sc0 = scl[32 * h + r16], sc1 = scl[32 * h + 16 + r16];
+        const bool tok0 = 32 * h + r16 < rows, tok1 = 32 * h + 16 + r16 < rows;
         if (w < G) {
 #pragma unroll
           for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              #pragma unroll
-              for (int p = 0; p < bp; ++p) {
-                const uint64_t m0 = __ballot((idxs[0][ct][i] >> p) & 1u);
-                const uint64_t m1 = __ballot((idxs[1][ct][i] >> p) & 1u);
-                const int c = 32 * w + 16 * ct + 4 * q + i;
+            for (int i = 0; i < 4; ++i) {
+              const int c = 32 * w + 16 * ct + 4 * q + i;
+              bool b0[BP], b1[BP];
+              decide_bits<BP, BP - 1>(acc[0][ct][i] * sc0, th, b0);
+              decide_bits<BP, BP - 1>(acc[1][ct][i] * sc1, th, b1);
+#pragma unroll
+              for (int p = 0; p < BP; ++p) {
+                const uint64_t m0 = __ballot(b0[p] && tok0);
+                const uint64_t m1 = __ballot(b1[p] && tok1);
                 if (r16 == 0 && c < d) ost[buf][(h * bp + p) * d + c] = halves(m0, m1);
               }
+            }
         }
       }
       if (tid < rows) norms[seq * n + v0 + tid] = nrm[tid];
