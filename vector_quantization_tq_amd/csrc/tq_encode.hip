@@ -431,13 +431,27 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
     const int sig = mx > 0.f ? 14 - ilogbf(mx) : 0;
     _Float16* hr = xh + lrow * LDH;
     _Float16* lr = xl + lrow * LDH;
+    if constexpr (LK == 1) {
+      // a 16-byte chunk of 8 bf16 values becomes one 16-byte row segment
 #pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-      if (j < cnt && cols[j] < d) {
-        const float sv = ldexpf(v[j], sig);
-        const _Float16 h = static_cast<_Float16>(sv);
-        hr[cols[j]] = h;
-        if constexpr (XLO) lr[cols[j]] = static_cast<_Float16>(sv - static_cast<float>(h));
+      for (int j = 0; j < PREN; ++j) {
+        const int c = part + 4 * j;
+        if (c < CH) {
+          v8h hv;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) hv[e] = static_cast<_Float16>(ldexpf(v[8 * j + e], sig));
+          *reinterpret_cast<v8h*>(hr + 8 * c) = hv;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < EPT; ++j) {
+        if (j < cnt && cols[j] < d) {
+          const float sv = ldexpf(v[j], sig);
+          const _Float16 h = static_cast<_Float16>(sv);
+          hr[cols[j]] = h;
+          if constexpr (XLO) lr[cols[j]] = static_cast<_Float16>(sv - static_cast<float>(h));
+        }
       }
     }
     if (part == 0) {
@@ -491,11 +505,23 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
   auto halves = [&](uint64_t m0, uint64_t m1) {
     return static_cast<uint32_t>((m0 >> (16 * q)) & 0xFFFFu) | (static_cast<uint32_t>((m1 >> (16 * q)) & 0xFFFFu) << 16);
   };
-  float th[NT], cen[NT + 1];
+  // The codebook is symmetric (the middle threshold is 0 and c[K-1-i] = -c[i]
+  // exactly), so idx = #{t_k < y} is K/2 + j for y > 0 and K/2 - 1 - j
+  // otherwise, with j = #{positive t_k < |y|}: the top bit is the sign and the
+  // low bits are j, complemented for y <= 0.  Only the positive halves of the
+  // tables are kept; the centroids pre-scaled for the residual.
+  constexpr int KH = 1 << (BP - 1);      // centroids per half
+  float thp[KH > 1 ? KH - 1 : 1], cenS[KH];
 #pragma unroll
-  for (int k2 = 0; k2 < NT; ++k2) th[k2] = cb.t[k2];
+  for (int k2 = 0; k2 + 1 < KH; ++k2) thp[k2] = cb.t[KH + k2];
 #pragma unroll
-  for (int k2 = 0; k2 <= NT; ++k2) cen[k2] = cb.c[k2];
+  for (int k2 = 0; k2 < KH; ++k2) cenS[k2] = cb.c[KH + k2] * kRhoScale;
+  // sign and magnitude bits of y: pos = [y > 0], jb = bits of j
+  auto classify = [&](float y, bool& pos, bool (&jb)[BP > 1 ? BP - 1 : 1]) {
+    pos = y > 0.f;
+    if constexpr (BP > 1) decide_bits<BP - 1, BP - 2>(fabsf(y), thp, jb);
+    else jb[0] = false;
+  };
   // row sum over the 16 lanes of a row of the C layout (one DPP row)
   auto sum16 = [&](float v) { return row_sum16(v); };
 
@@ -533,31 +559,41 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float sc = scl[vbase + i];
-            bool bits[2][BP];
+            const float scS = sc * kRhoScale;
+            bool pos[2], jb[2][BP > 1 ? BP - 1 : 1];
             float r2 = 0.f;
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct) {
               const int c = 32 * w + 16 * ct + r16;
-              const float y = acc[h2][ct][i] * sc;
-              decide_bits<BP, BP - 1>(y, th, bits[ct]);
-              const float rho = c < d ? y - pick_centroid<BP>(cen, bits[ct]) : 0.f;
-              r2 = fmaf(rho, rho, r2);
+              const float a = acc[h2][ct][i];
+              classify(a * sc, pos[ct], jb[ct]);
+              // rho * 2^14 = y 2^14 - c[idx] 2^14 in one rounding
+              float cabs;
+              if constexpr (BP > 1) cabs = pick_centroid<BP - 1>(cenS, jb[ct]);
+              else cabs = cenS[0];
+              const float rs = c < d ? fmaf(a, scS, pos[ct] ? -cabs : cabs) : 0.f;
+              r2 = fmaf(rs, rs, r2);
               if (c < KP) {
-                const float sr = rho * kRhoScale;
-                const _Float16 hh = static_cast<_Float16>(sr);
+                const _Float16 hh = static_cast<_Float16>(rs);
                 rh[(vbase + i) * LDH + c] = hh;
-                rl[(vbase + i) * LDH + c] = static_cast<_Float16>(sr - static_cast<float>(hh));
+                rl[(vbase + i) * LDH + c] = static_cast<_Float16>(rs - static_cast<float>(hh));
               }
             }
             if (w < G) {
+              const bool ok0 = 32 * w + r16 < d, ok1 = 32 * w + 16 + r16 < d;
+              {
+                const uint64_t m0 = __ballot(pos[0] && ok0);
+                const uint64_t m1 = __ballot(pos[1] && ok1);
+                if (r16 == 0) ost[buf][(vbase + i) * WPK + w * W + BP - 1] = halves(m0, m1);
+              }
 #pragma unroll
-              for (int p = 0; p < BP; ++p) {
-                const uint64_t m0 = __ballot(bits[0][p] && 32 * w + r16 < d);
-                const uint64_t m1 = __ballot(bits[1][p] && 32 * w + 16 + r16 < d);
+              for (int p = 0; p + 1 < BP; ++p) {
+                const uint64_t m0 = __ballot((jb[0][p] == pos[0]) && ok0);
+                const uint64_t m1 = __ballot((jb[1][p] == pos[1]) && ok1);
                 if (r16 == 0) ost[buf][(vbase + i) * WPK + w * W + p] = halves(m0, m1);
               }
             }
-            // partial ||rho||^2 over this wave's 32 coordinates
+            // partial ||rho||^2 (x 2^28) over this wave's 32 coordinates
             r2 = sum16(r2);
             if (r16 == 0) part2[w][vbase + i] = r2;
           }
@@ -591,7 +627,8 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
       if (tid < rows) {
         const float nv = nrm[tid];
         norms[seq * n + v0 + tid] = nv;
-        gammas[seq * n + v0 + tid] = nv * sqrtf(part2[0][tid] + part2[1][tid] + part2[2][tid] + part2[3][tid]);
+        gammas[seq * n + v0 + tid] =
+            nv * sqrtf(part2[0][tid] + part2[1][tid] + part2[2][tid] + part2[3][tid]) * (1.f / kRhoScale);
       }
     } else {
       // lane holds coordinate 32w + 16ct + 4q + i, token 32h + 16h2 + r16;
@@ -613,13 +650,15 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int c = 32 * w + 16 * ct + 4 * q + i;
-              bool b0[BP], b1[BP];
-              decide_bits<BP, BP - 1>(acc[0][ct][i] * sc0, th, b0);
-              decide_bits<BP, BP - 1>(acc[1][ct][i] * sc1, th, b1);
+              bool p0, p1, j0[BP > 1 ? BP - 1 : 1], j1[BP > 1 ? BP - 1 : 1];
+              classify(acc[0][ct][i] * sc0, p0, j0);
+              classify(acc[1][ct][i] * sc1, p1, j1);
 #pragma unroll
               for (int p = 0; p < BP; ++p) {
-                const uint64_t m0 = __ballot(b0[p] && tok0);
-                const uint64_t m1 = __ballot(b1[p] && tok1);
+                const bool c0b = p == BP - 1 ? p0 : (j0[p < BP - 1 ? p : 0] == p0);
+                const bool c1b = p == BP - 1 ? p1 : (j1[p < BP - 1 ? p : 0] == p1);
+                const uint64_t m0 = __ballot(c0b && tok0);
+                const uint64_t m1 = __ballot(c1b && tok1);
                 if (r16 == 0 && c < d) ost[buf][(h * bp + p) * d + c] = halves(m0, m1);
               }
             }
