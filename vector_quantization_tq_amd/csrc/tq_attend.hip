@@ -336,8 +336,9 @@ __global__ void __launch_bounds__(256) attend_chunk_kernel(
 
 // One workgroup (256 threads) per (batch, query head): combine the chunk
 // partials (max-shifted), add the exact bf16 tail, rotate back once and
-// normalise.  Each output coordinate is shared by two threads (halves of the
-// chunk list / of the rotation's inner dimension / of the tail).
+// normalise.  Sums over chunks and over tail tokens are spread over 8 slices
+// of 32 threads, each thread carrying 4 consecutive coordinates with 16-byte
+// loads; the slices meet in LDS.
 __global__ void __launch_bounds__(256) attend_merge_kernel(const void* __restrict__ queries, int q_dtype, int Hq,
                                                            int Hkv, int G, int RT, int64_t nchunk,
                                                            const float* __restrict__ part,
@@ -348,11 +349,13 @@ __global__ void __launch_bounds__(256) attend_merge_kernel(const void* __restric
   constexpr int d = 128;
   __shared__ float qv[d];
   __shared__ float accs[d];
+  __shared__ __attribute__((aligned(16))) float sl8[8][d];
   __shared__ float half2[2][d];
   __shared__ float red[8];
   __shared__ float ts[512];   // tail logits, then tail weights (n_tail <= 512)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = tid & (d - 1), hf = tid >> 7;
+  const int slc = tid >> 5, u4 = 4 * (tid & 31);   // slice, first coordinate of this thread's quad
   const int bh = blockIdx.x;
   const int b = bh / Hq, h = bh - b * Hq;
   const int kvh = h / G, qg = h - kvh * G;
@@ -366,11 +369,25 @@ __global__ void __launch_bounds__(256) attend_merge_kernel(const void* __restric
   float mloc = -INFINITY;
   for (int64_t c = tid; c < nchunk; c += 256) mloc = fmaxf(mloc, pq[c * cstride + 128]);
   const int64_t toff = (static_cast<int64_t>(b) * Hkv + kvh) * n_tail;
-  for (int t = wave; t < n_tail; t += 4) {
-    const uint16_t* kt = k_tail + (toff + t) * d;
-    const float sdot = wave_sum(fmaf(qv[lane], bf16_to_f32(kt[lane]), qv[lane + 64] * bf16_to_f32(kt[lane + 64])));
-    if (lane == 0) ts[t] = sdot * scale_log2;
-    mloc = fmaxf(mloc, sdot * scale_log2);
+  // one thread per tail token: its 256-byte key row as 16 independent 16-byte loads
+  for (int t = tid; t < n_tail; t += 256) {
+    const uint4* kt = reinterpret_cast<const uint4*>(k_tail + (toff + t) * d);
+    uint4 kr[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) kr[c] = kt[c];
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const uint32_t wv[4] = {kr[c].x, kr[c].y, kr[c].z, kr[c].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s0 = fmaf(qv[8 * c + 2 * e], __uint_as_float(wv[e] << 16), s0);
+        s1 = fmaf(qv[8 * c + 2 * e + 1], __uint_as_float(wv[e] & 0xFFFF0000u), s1);
+      }
+    }
+    const float sl = (s0 + s1) * scale_log2;
+    ts[t] = sl;
+    mloc = fmaxf(mloc, sl);
   }
   mloc = wave_max(mloc);
   if (lane == 0) red[wave] = mloc;
@@ -387,35 +404,78 @@ __global__ void __launch_bounds__(256) attend_merge_kernel(const void* __restric
   lsum = wave_sum(lsum);
   __syncthreads();
   if (lane == 0) red[4 + wave] = lsum;
-  // rotated-frame accumulator of the compressed part: chunks split by parity
+  // rotated-frame accumulator of the compressed part: chunk c goes to slice
+  // c mod 8; 8 chunks of a slice are loaded before any is used
   {
-    float a0 = 0.f, a1 = 0.f;
-    int64_t c = hf;
-    for (; c + 2 < nchunk; c += 4) {
-      a0 = fmaf(pq[c * cstride + i], exp2f(pq[c * cstride + 128] - M), a0);
-      a1 = fmaf(pq[(c + 2) * cstride + i], exp2f(pq[(c + 2) * cstride + 128] - M), a1);
+    float4 a = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t c0 = slc; c0 < nchunk; c0 += 64) {
+      float mc[8];
+      float4 pc[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int64_t c = min(c0 + 8 * k, nchunk - 1);
+        mc[k] = pq[c * cstride + 128];
+        pc[k] = *reinterpret_cast<const float4*>(pq + c * cstride + u4);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float wk = c0 + 8 * k < nchunk ? exp2f(mc[k] - M) : 0.f;
+        a.x = fmaf(pc[k].x, wk, a.x);
+        a.y = fmaf(pc[k].y, wk, a.y);
+        a.z = fmaf(pc[k].z, wk, a.z);
+        a.w = fmaf(pc[k].w, wk, a.w);
+      }
     }
-    for (; c < nchunk; c += 2) a0 = fmaf(pq[c * cstride + i], exp2f(pq[c * cstride + 128] - M), a0);
-    half2[hf][i] = a0 + a1;
+    *reinterpret_cast<float4*>(&sl8[slc][u4]) = a;
   }
   __syncthreads();
   const float L = (red[4] + red[5]) + (red[6] + red[7]);
-  if (tid < d) accs[i] = half2[0][i] + half2[1][i];
-  __syncthreads();
-  // Pi^T acc (inner dimension split between the two halves), then the tail values
-  {
-    float o0 = 0.f, o1 = 0.f;
-    const int j0 = hf * (d / 2);
-#pragma unroll 4
-    for (int jj = 0; jj < d / 2; jj += 2) {
-      o0 = fmaf(piv[static_cast<int64_t>(j0 + jj) * d + i], accs[j0 + jj], o0);
-      o1 = fmaf(piv[static_cast<int64_t>(j0 + jj + 1) * d + i], accs[j0 + jj + 1], o1);
-    }
-    for (int t = hf; t < n_tail; t += 2) o0 = fmaf(ts[t], bf16_to_f32(v_tail[(toff + t) * d + i]), o0);
-    half2[hf][i] = o0 + o1;
+  if (tid < d) {
+    float v = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v += sl8[k][i];
+    accs[i] = v;
   }
   __syncthreads();
-  if (tid < d) out[static_cast<int64_t>(bh) * d + i] = (half2[0][i] + half2[1][i]) / L;
+  // tail values: token t goes to slice t mod 8 (weights ts[] already in place)
+  {
+    float4 a = {0.f, 0.f, 0.f, 0.f};
+    for (int t0 = slc; t0 < n_tail; t0 += 64) {
+      uint2 raw[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        raw[k] = *reinterpret_cast<const uint2*>(v_tail + (toff + min(t0 + 8 * k, n_tail - 1)) * d + u4);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float pt = t0 + 8 * k < n_tail ? ts[min(t0 + 8 * k, n_tail - 1)] : 0.f;
+        a.x = fmaf(pt, __uint_as_float(raw[k].x << 16), a.x);
+        a.y = fmaf(pt, __uint_as_float(raw[k].x & 0xFFFF0000u), a.y);
+        a.z = fmaf(pt, __uint_as_float(raw[k].y << 16), a.z);
+        a.w = fmaf(pt, __uint_as_float(raw[k].y & 0xFFFF0000u), a.w);
+      }
+    }
+    *reinterpret_cast<float4*>(&sl8[slc][u4]) = a;
+  }
+  // Pi^T acc (inner dimension split between the two halves), 16 loads in flight
+  {
+    float o[4] = {0.f, 0.f, 0.f, 0.f};
+    const int j0 = hf * (d / 2);
+    for (int jj = 0; jj < d / 2; jj += 16) {
+      float pv[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) pv[k] = piv[static_cast<int64_t>(j0 + jj + k) * d + i];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) o[k & 3] = fmaf(pv[k], accs[j0 + jj + k], o[k & 3]);
+    }
+    half2[hf][i] = (o[0] + o[1]) + (o[2] + o[3]);
+  }
+  __syncthreads();
+  if (tid < d) {
+    float tv = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) tv += sl8[k][i];
+    out[static_cast<int64_t>(bh) * d + i] = (half2[0][i] + half2[1][i] + tv) / L;
+  }
 }
 
 hipError_t launch_attend(const tq_quantizer* kq, const tq_quantizer* vq, const void* queries, int q_dtype, int B, int Hq,
