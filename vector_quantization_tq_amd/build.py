@@ -23,6 +23,9 @@ def hipcc_flags():
     return ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
             # keep the compiler from forming packed fp32 ops (v_pk_*_f32)
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # matrix-core accumulators in ordinary VGPRs: the kernels scale and
+            # read them with vector ALU ops, which cannot address AGPRs
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
 
 
