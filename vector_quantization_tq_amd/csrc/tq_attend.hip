@@ -38,7 +38,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 // aligned to the largest product of the group, so limbs that are integers on
 // one common scale keep those group sums exact whatever the spread of the
 // weights (per-element floating limbs would lose the small ones).
-__device__ __forceinline__ uint32_t fixed_limbs4(float x) {
+__device__ __forceinline__ uint32_t fixed_limbs4(float x, float& xq) {
   const float l0 = rintf(x);
   float r = (x - l0) * 16.f;
   const float l1 = rintf(r);
@@ -46,6 +46,7 @@ __device__ __forceinline__ uint32_t fixed_limbs4(float x) {
   const float l2 = rintf(r);
   r = (r - l2) * 16.f;
   const float l3 = rintf(r);
+  xq = l0 + (l1 + (l2 + l3 * (1.f / 16.f)) * (1.f / 16.f)) * (1.f / 16.f);   // exact: 16-bit fixed point
   const int b01 = __builtin_amdgcn_cvt_pk_fp8_f32(l0, l1, 0, false);
   const int b23 = __builtin_amdgcn_cvt_pk_fp8_f32(l2, l3, 0, false);
   return (static_cast<uint32_t>(b01) & 0xFFFFu) | (static_cast<uint32_t>(b23) << 16);
@@ -193,6 +194,20 @@ __global__ void __launch_bounds__(256) attend_chunk_kernel(
   // DMA instructions this wave issues per step (the same for every step)
   constexpr int KI = KW / 256, VI = VW / 256;
   const int per_step = (KI + 3 - wave) / 4 + (VI + 3 - wave) / 4 + (wave < 2 ? 2 : 1);
+  // softmax tokens of this lane: tA and tB = tA + 4, whose value-MFMA A bytes
+  // are adjacent (K and K + 1 in the same fp4 slot), so each limb of the pair
+  // is one 16-bit LDS write.  token = 32(K/32) + 4(K%8) + (K%32)/8.
+  const int tA = 8 * (lane >> 2) + (lane & 3), tB = tA + 4;
+  int a_off;       // byte offset of tA's limb 0 in the A tile, minus 32 * 4q
+  float a_inv, a_slot;
+  {
+    const int hh = tA >> 5, rem = tA & 31;
+    const int K = 32 * hh + 8 * (rem & 3) + (rem >> 2);
+    const int gg = (K & 63) >> 4, e = 16 * (K >> 6) + (K & 15);
+    a_off = 16 * gg * 32 + e;
+    a_slot = fp4_slot_value((K & 31) >> 3);
+    a_inv = 1.f / a_slot;   // 2, 1 or 0.5: exact
+  }
   if (c0 < c1) issue(c0, 0);
   if (c0 + kStep < c1) issue(c0 + kStep, 1);
   int buf = 0;
@@ -227,15 +242,14 @@ __global__ void __launch_bounds__(256) attend_chunk_kernel(
     // ---------------- softmax phase: wave q handles query q ----------------
     {
       const int q = wave;
-      const int ta = 2 * lane, tb = 2 * lane + 1;
-      const float sa = sc[q][ta], sb = sc[q][tb];
+      const float sa = sc[q][tA], sb = sc[q][tB];
       const float mx = wave_max(fmaxf(sa, sb));
       const float m_new = fmaxf(m_run, mx);
       const float alpha = exp2f(m_run - m_new);   // 0 on the first step
       const float pa = exp2f(sa - m_new), pb = exp2f(sb - m_new);
       const float* vns = kns + 2 * kStep;
-      const float na = (t0 + ta < c1) ? vns[ta] : 0.f;
-      const float nb2 = (t0 + tb < c1) ? vns[tb] : 0.f;
+      const float na = (t0 + tA < c1) ? vns[tA] : 0.f;
+      const float nb2 = (t0 + tB < c1) ? vns[tB] : 0.f;
       const float wa = pa * na, wb = pb * nb2;
       const float ps = wave_sum(pa + pb);
       const float wm = wave_max(fmaxf(wa, wb));
@@ -251,28 +265,15 @@ __global__ void __launch_bounds__(256) attend_chunk_kernel(
       // A operand of the value MFMA: rows 4q + limb, K = token slot.  The
       // weight sum that enters the Walsh constant term is taken over the
       // quantised weights, so that sum_t w_t (2 b_t - 1) is exact for them.
-      float wq_sum = 0.f;
+      float qa, qb;
+      const uint32_t la = fixed_limbs4(ldexpf(wa * a_inv, e_new), qa);
+      const uint32_t lb = fixed_limbs4(ldexpf(wb * a_inv, e_new), qb);
+      const float wq_sum = ldexpf(qa + qb, -e_new) * a_slot;
+      uint8_t* avb = reinterpret_cast<uint8_t*>(av) + 4 * q * 32 + a_off;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int tk = 2 * lane + h;
-        const float wt = h ? wb : wa;
-        // token -> K: token = 32(K/32) + 4(K%8) + (K%32)/8; K -> (lane-group, element)
-        const int hh = tk >> 5, rem = tk & 31;
-        const int K = 32 * hh + 8 * (rem & 3) + (rem >> 2);
-        const int gg = (K & 63) >> 4, e = 16 * (K >> 6) + (K & 15);
-        const float v = ldexpf(wt / fp4_slot_value((K & 31) >> 3), e_new);
-        const uint32_t limbs = fixed_limbs4(v);
-        {
-          float rec = 0.f;
-#pragma unroll
-          for (int lb = 3; lb >= 0; --lb)
-            rec = fmaf(rec, 1.f / 16.f, __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(limbs >> (8 * lb)), 0));
-          wq_sum = fmaf(ldexpf(rec, -e_new), fp4_slot_value((K & 31) >> 3), wq_sum);
-        }
-        uint8_t* avb = reinterpret_cast<uint8_t*>(av);
-#pragma unroll
-        for (int lb = 0; lb < 4; ++lb) avb[(4 * q + lb + 16 * gg) * 32 + e] = static_cast<uint8_t>(limbs >> (8 * lb));
-      }
+      for (int lb2 = 0; lb2 < 4; ++lb2)
+        *reinterpret_cast<uint16_t*>(avb + lb2 * 32) =
+            static_cast<uint16_t>(((la >> (8 * lb2)) & 0xFFu) | (((lb >> (8 * lb2)) & 0xFFu) << 8));
       w_run = fmaf(w_run, alpha, wave_sum(wq_sum));
     }
     __syncthreads();
