@@ -118,11 +118,11 @@ __device__ __forceinline__ void dma_tok(float* dst, const float* src, int64_t t0
   __builtin_amdgcn_global_load_lds(src + t, as_lds(dst), 4, 0, 0);
 }
 
-template <int BPK, int BPV>
-__global__ void __launch_bounds__(256) attend_chunk_kernel(
+template <int BPK, int BPV, int NSLOT>
+__device__ __forceinline__ void attend_chunk_body(
     const uint32_t* __restrict__ kcodes, const float* __restrict__ knorms, const float* __restrict__ kgammas,
     const uint32_t* __restrict__ vcodes, const float* __restrict__ vnorms, int64_t n, int64_t chunk, int G, int RT,
-    float scale_log2, const uint8_t* __restrict__ wsA, const float* __restrict__ wsC, Codebook vcb,
+    float scale_log2, const uint8_t* __restrict__ wsA, const float* __restrict__ wsC, const Codebook& vcb,
     float* __restrict__ part) {
   constexpr int d = 128;
   constexpr int TK = (1 << (BPK - 1)) + 1;   // key MFMA terms (Walsh + QJL)
@@ -132,7 +132,7 @@ __global__ void __launch_bounds__(256) attend_chunk_kernel(
   constexpr int KW = kStep * WPK;            // key words of a step
   constexpr int VW = 4 * BPV * d;            // value words of a step (4 blocks of 32 tokens)
   constexpr int SLOT = KW + VW + 3 * kStep;  // + key norms, key gammas, value norms
-  constexpr int NSLOT = 3;                   // steps s, s+1, s+2 staged at once
+  static_assert(NSLOT == 2 || NSLOT == 3, "staging ring of 2 or 3 steps");
   __shared__ __attribute__((aligned(16))) uint32_t stage[NSLOT][SLOT];
   __shared__ float sc[4][kStep];             // scaled logits (base 2)
   __shared__ __attribute__((aligned(16))) uint32_t av[64 * 8];   // value A operand (fp8 limbs)
@@ -208,15 +208,23 @@ __global__ void __launch_bounds__(256) attend_chunk_kernel(
     a_slot = fp4_slot_value((K & 31) >> 3);
     a_inv = 1.f / a_slot;   // 2, 1 or 0.5: exact
   }
-  if (c0 < c1) issue(c0, 0);
-  if (c0 + kStep < c1) issue(c0 + kStep, 1);
+  // prefetch depth NSLOT - 1: steps s+1 .. s+NSLOT-1 are in flight while step s is used
+  constexpr int P = NSLOT - 1;
+#pragma unroll
+  for (int k = 0; k < P; ++k)
+    if (c0 + k * kStep < c1) issue(c0 + k * kStep, k);
   int buf = 0;
   for (int64_t t0 = c0; t0 < c1; t0 += kStep, buf = buf == NSLOT - 1 ? 0 : buf + 1) {
-    // this wave's part of step t0 has landed once at most the next step's
-    // loads are outstanding (the counter retires in issue order) ...
-    wait_vm_upto<8>(t0 + kStep < c1 ? per_step : 0);
+    // this wave's part of step t0 has landed once at most the loads of the
+    // later steps already issued are outstanding (the counter retires in
+    // issue order) ...
+    {
+      const int64_t later = (c1 - t0 - 1) / kStep;   // steps after t0 in this chunk
+      const int ahead = static_cast<int>(min(static_cast<int64_t>(P - 1), later));
+      wait_vm_upto<8>(ahead * per_step);
+    }
     __syncthreads();   // ... and every wave's; the slot of step t0 - kStep is free again
-    if (t0 + 2 * kStep < c1) issue(t0 + 2 * kStep, buf == 0 ? NSLOT - 1 : buf - 1);
+    if (t0 + P * kStep < c1) issue(t0 + P * kStep, buf == 0 ? NSLOT - 1 : buf - 1);
     const uint32_t* sl = stage[buf];
     const float* kns = reinterpret_cast<const float*>(sl + KW + VW);
     // ---------------- K phase: logits of tokens t0 + 32*wave .. +31 ----------------
@@ -333,6 +341,16 @@ __global__ void __launch_bounds__(256) attend_chunk_kernel(
     pbase[threadIdx.x * kPartStride + 128] = qst[threadIdx.x][0];
     pbase[threadIdx.x * kPartStride + 129] = qst[threadIdx.x][3];
   }
+}
+
+template <int BPK, int BPV>
+__global__ void __launch_bounds__(256) attend_chunk_kernel(
+    const uint32_t* __restrict__ kcodes, const float* __restrict__ knorms, const float* __restrict__ kgammas,
+    const uint32_t* __restrict__ vcodes, const float* __restrict__ vnorms, int64_t n, int64_t chunk, int G, int RT,
+    float scale_log2, const uint8_t* __restrict__ wsA, const float* __restrict__ wsC, Codebook vcb,
+    float* __restrict__ part) {
+  attend_chunk_body<BPK, BPV, 3>(kcodes, knorms, kgammas, vcodes, vnorms, n, chunk, G, RT, scale_log2, wsA, wsC, vcb,
+                                 part);
 }
 
 // One workgroup (256 threads) per (batch, query head): combine the chunk
