@@ -80,27 +80,6 @@ int64_t attend_ws_bytes(const tq_quantizer* kq, const tq_quantizer*, int B, int 
   return prep + groups * nch * 4 * kPartStride * 4 + 256;
 }
 
-// s_waitcnt immediate that waits for vmcnt <= N only (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-template <int N>
-__device__ __forceinline__ void wait_vm_upto(int n) {   // runtime n in [0, N]
-  if constexpr (N > 0) {
-    if (n >= N) { wait_vm<N>(); return; }
-    wait_vm_upto<N - 1>(n);
-  } else {
-    wait_vm<0>();
-  }
-}
-
-typedef __attribute__((address_space(3))) void lds_ptr_t;
-__device__ __forceinline__ lds_ptr_t* as_lds(const void* p) {
-  return reinterpret_cast<lds_ptr_t*>(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)));
-}
-
 // Copy `words` 32-bit words (a multiple of 4) from src to LDS dst by 16-byte
 // DMA loads (global -> LDS, no registers), spread over the 4 waves; words at
 // or past `limit` (a multiple of 4, > 0) re-read the last valid 16 bytes.

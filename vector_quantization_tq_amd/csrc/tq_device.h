@@ -80,6 +80,30 @@ __device__ __forceinline__ float wave_max(float v) {
   return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
+// s_waitcnt immediate that waits for vmcnt <= N only (gfx9 encoding; the
+// counter retires vector-memory operations in issue order)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+template <int N>
+__device__ __forceinline__ void wait_vm_upto(int n) {   // runtime n in [0, N]
+  if constexpr (N > 0) {
+    if (n >= N) { wait_vm<N>(); return; }
+    wait_vm_upto<N - 1>(n);
+  } else {
+    wait_vm<0>();
+  }
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// LDS destination of the global -> LDS DMA loads
+typedef __attribute__((address_space(3))) void lds_ptr_t;
+__device__ __forceinline__ lds_ptr_t* as_lds(const void* p) {
+  return reinterpret_cast<lds_ptr_t*>(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)));
+}
+
 // value of a set bit at element slot s = (K % 32) / 8
 __host__ __device__ __forceinline__ float fp4_slot_value(int s) { return s == 0 ? 0.5f : (s == 1 ? 1.f : 2.f); }
 

@@ -210,23 +210,6 @@ constexpr int kTargetWaves = TQ_SCORES_WAVES;   // resident waves aimed at (256 
 constexpr int kRing = TQ_SCORES_RING;
 constexpr int kBatchKeys = 64;
 
-// s_waitcnt immediate that waits for vmcnt <= N only (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-template <int N>
-__device__ __forceinline__ void wait_vm_upto(int n) {   // runtime n in [0, N]
-  if constexpr (N > 0) {
-    if (n >= N) { wait_vm<N>(); return; }
-    wait_vm_upto<N - 1>(n);
-  } else {
-    wait_vm<0>();
-  }
-}
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-
 template <int WPK>
 struct DmaPlan {
   // bytes per lane per load; the 12-byte form places lanes 16 bytes apart in LDS, so it is not used
@@ -235,11 +218,6 @@ struct DmaPlan {
   static constexpr int NC = WPK / WPL;                                          // loads for the packed words
   static constexpr int L = NC + 2;                                              // + norms + gammas
 };
-
-typedef __attribute__((address_space(3))) void lds_void;
-__device__ __forceinline__ lds_void* to_lds(void* p) {
-  return reinterpret_cast<lds_void*>(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)));
-}
 
 // issue the loads of one batch (keys k0 .. k0+63 of a sequence of n keys) into an LDS slot
 template <int WPK>
@@ -253,7 +231,7 @@ __device__ __forceinline__ void issue_batch(uint32_t* slot, const uint32_t* __re
     int64_t off = static_cast<int64_t>(i) * 64 * P::WPL + lane * P::WPL;
     if (off + P::WPL > limit) off = limit - P::WPL;   // past the end: re-read the last valid words
     const uint32_t* src = cbase + k0 * WPK + off;
-    lds_void* dst = to_lds(slot + i * 64 * P::WPL);
+    lds_ptr_t* dst = as_lds(slot + i * 64 * P::WPL);
     if constexpr (P::SZ == 16) {
       __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
     } else {
@@ -263,8 +241,8 @@ __device__ __forceinline__ void issue_batch(uint32_t* slot, const uint32_t* __re
   int64_t kk = k0 + lane;
   if (kk >= n) kk = n - 1;
   float* ng = reinterpret_cast<float*>(slot + kBatchKeys * WPK);
-  __builtin_amdgcn_global_load_lds(nb + kk, to_lds(ng), 4, 0, 0);
-  __builtin_amdgcn_global_load_lds(gb + kk, to_lds(ng + kBatchKeys), 4, 0, 0);
+  __builtin_amdgcn_global_load_lds(nb + kk, as_lds(ng), 4, 0, 0);
+  __builtin_amdgcn_global_load_lds(gb + kk, as_lds(ng + kBatchKeys), 4, 0, 0);
 }
 
 template <int BP, int GW>

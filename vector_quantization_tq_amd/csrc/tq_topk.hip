@@ -145,8 +145,8 @@ __global__ void __launch_bounds__(256) topk_scan_kernel(const uint32_t* __restri
   constexpr int WPK = GW * W;                      // packed words per key
   constexpr int BW = kTopBlockKeys * WPK;          // words of a batch
   constexpr int BUFW = BW + 2 * kTopBlockKeys;     // + norms + gammas
-  constexpr int PER = (BW + 255) / 256;            // staged words per thread
-  __shared__ __attribute__((aligned(16))) uint32_t buf[2][BUFW];
+  constexpr int NS = 3;                            // batches b, b+1, b+2 staged at once
+  __shared__ __attribute__((aligned(16))) uint32_t buf[NS][BUFW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // workgroup -> (row group, slice); consecutive workgroups go round-robin over
@@ -192,38 +192,47 @@ __global__ void __launch_bounds__(256) topk_scan_kernel(const uint32_t* __restri
   const int64_t k_end = min(n, k_begin + slice_keys);
   const int nbat = static_cast<int>((k_end - k_begin + kTopBlockKeys - 1) / kTopBlockKeys);
 
-  uint32_t stage[PER];
-  float stage_ng = 0.f;
-  auto fetch = [&](int bi) {
+  // batch bi of the slice goes HBM -> LDS by dword DMA (no registers, no
+  // alignment assumptions); past the slice end the last valid word is re-read
+  const int wave_dma = (WPK + 3 - wave) / 4 + (wave >= 2 ? 1 : 0);   // DMA instructions per batch
+  auto issue = [&](int bi, int slot) {
     const int64_t k0 = k_begin + static_cast<int64_t>(bi) * kTopBlockKeys;
-    const int64_t valid = (min(k_end, k0 + kTopBlockKeys) - k0) * WPK;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int idx = e * 256 + tid;
-      stage[e] = (idx < valid) ? cbase[k0 * WPK + idx] : 0u;
+    const int valid = static_cast<int>(min(k_end, k0 + kTopBlockKeys) - k0);
+    uint32_t* dst = buf[slot];
+    const uint32_t* src = cbase + k0 * WPK;
+    for (int i = wave; i < WPK; i += 4) {
+      int off = i * 64 + lane;
+      if (off >= valid * WPK) off = valid * WPK - 1;
+      __builtin_amdgcn_global_load_lds(src + off, as_lds(dst + i * 64), 4, 0, 0);
     }
-    if (tid < 2 * kTopBlockKeys) {
-      const int kk = tid & (kTopBlockKeys - 1);
-      const float* src = tid < kTopBlockKeys ? nb : gb;
-      stage_ng = (k0 + kk < k_end) ? src[k0 + kk] : 0.f;
+    if (wave >= 2) {
+      const float* arr = wave == 2 ? nb : gb;
+      int64_t t = k0 + lane;
+      if (t >= k0 + valid) t = k0 + valid - 1;
+      __builtin_amdgcn_global_load_lds(arr + t, as_lds(dst + BW + (wave - 2) * kTopBlockKeys), 4, 0, 0);
     }
-  };
-  auto commit = [&](int slot) {
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int idx = e * 256 + tid;
-      if (idx < BW) buf[slot][idx] = stage[e];
-    }
-    if (tid < 2 * kTopBlockKeys) reinterpret_cast<float*>(buf[slot] + BW)[tid] = stage_ng;
   };
 
-  fetch(0);
-  commit(0);
-  __syncthreads();
-  for (int bi = 0; bi < nbat; ++bi) {
-    const int slot = bi & 1;
-    if (bi + 1 < nbat) fetch(bi + 1);   // in flight while this batch is scored
+  constexpr int P = NS - 1;   // batches in flight ahead of the one being scored
+#pragma unroll
+  for (int k = 0; k < P; ++k)
+    if (k < nbat) issue(k, k);
+  int slot = 0;
+  for (int bi = 0; bi < nbat; ++bi, slot = slot == NS - 1 ? 0 : slot + 1) {
+    wait_vm_upto<16>(min(P - 1, nbat - 1 - bi) * wave_dma);   // this wave's loads of batch bi landed
+    __syncthreads();                                          // ... and every wave's; slot of bi-1 free
+    if (bi + P < nbat) issue(bi + P, slot == 0 ? NS - 1 : slot - 1);
     if (active) {
+      // A key can only enter the query's top k if it ranks at least level with
+      // the query's current k-th best.  The largest of the 16 lanes' own k-th
+      // best scores is a lower bound of that (the lane alone holds k scores at
+      // least as large), so keys below it are skipped without touching the
+      // lists: insertions become rare.
+      float kth = ls[0];
+#pragma unroll
+      for (int k = 1; k < KK; ++k)
+        if (k == topk - 1) kth = ls[k];
+      const float tau = row_max16(kth);
       const uint32_t* kw = buf[slot];
       const float* kn = reinterpret_cast<const float*>(kw + BW);
       const int64_t k0 = k_begin + static_cast<int64_t>(bi) * kTopBlockKeys;
@@ -250,12 +259,14 @@ __global__ void __launch_bounds__(256) topk_scan_kernel(const uint32_t* __restri
         const float qjl = fmaf(aQ[0], cs[6], fmaf(aQ[1], cs[7], fmaf(aQ[2], cs[8], fmaf(aQ[3], cs[9], cs[1]))));
         const float s = fmaf(kn[kk], mse, kn[kTopBlockKeys + kk] * qjl);
         const int key = static_cast<int>(k0) + kk;
-        if (kk < nk && ranks_before(s, key, ls[KK - 1], li[KK - 1])) list_insert<KK>(s, key, ls, li);
+        const bool ins = kk < nk && s >= tau && ranks_before(s, key, ls[KK - 1], li[KK - 1]);
+        // wave-uniform gate: the insertion (selects over the whole list) only
+        // runs when some lane of the wave has a key to insert
+        if (__ballot(ins) != 0ull) {
+          if (ins) list_insert<KK>(s, key, ls, li);
+        }
       }
     }
-    // the other slot was last read before the previous barrier
-    if (bi + 1 < nbat) commit(slot ^ 1);
-    __syncthreads();
   }
 
   if (!active) return;   // no barrier follows
