@@ -34,11 +34,13 @@ def _bf16(u16):
     return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).to(_dev()).view(torch.bfloat16)
 
 
-def _run_case(k, v, q, B, Hkv, Hq, n_comp, n_tail, bits, scale=0.0, groups=None, kseed=0, vseed=1):
-    """k, v: torch bf16 [B*Hkv, N, d]; q: torch [B, Hq, d]."""
+def _run_case(k, v, q, B, Hkv, Hq, n_comp, n_tail, bits, scale=0.0, groups=None, kseed=0, vseed=1, vbits=None):
+    """k, v: torch bf16 [B*Hkv, N, d]; q: torch [B, Hq, d]; bits for keys
+    (vbits for values, default the same)."""
     d = k.shape[-1]
+    vbits = bits if vbits is None else vbits
     gk, ok = _pair(d, bits, kseed)
-    gv, ov = _pair(d, bits, vseed)
+    gv, ov = _pair(d, vbits, vseed)
     kc = k[:, :n_comp].contiguous()
     vc = v[:, :n_comp].contiguous()
     kcodes, kn, kg = tq.tq_encode(gk, tq.TQ_PROD, kc) if n_comp else (torch.empty(4, dtype=torch.int32, device=_dev()),
@@ -66,7 +68,7 @@ def _run_case(k, v, q, B, Hkv, Hq, n_comp, n_tail, bits, scale=0.0, groups=None,
         s = b * Hkv + h
         if n_comp:
             ki, kb = o.unpack_prod(kw[s * perk:(s + 1) * perk].reshape(n_comp, -1), bits - 1, d)
-            vi = o.unpack_mse(vw[s * perv:(s + 1) * perv], n_comp, bits, d)
+            vi = o.unpack_mse(vw[s * perv:(s + 1) * perv], n_comp, vbits, d)
         else:
             ki = np.zeros((0, d), dtype=np.int64); kb = np.zeros((0, d), dtype=np.uint8); vi = ki
         sl = slice(s * n_comp, (s + 1) * n_comp)
@@ -118,4 +120,14 @@ def test_attend_full_size_sampled(name):
     q = _bf16(wl.arrays["q_bf16"])
     groups = [(0, 0), (B - 1, Hkv - 1)]
     w = _run_case(k, v, q, B, Hkv, Hq, N - tail, tail, wl.bits, groups=groups, kseed=0, vseed=0)
+    print("worst relative error", w)
+
+
+@pytest.mark.parametrize("kbits,vbits", [(4, 2), (2, 4), (3, 1), (4, 3)])
+def test_attend_asymmetric_bits(kbits, vbits):
+    """Keys and values at different bit widths (each quantizer owns its own
+    codebook); the chunk kernel is instantiated per (key bits, value bits)."""
+    print(f"case: attend asymmetric K {kbits}-bit V {vbits}-bit", flush=True)
+    k, v, q = _gqa_inputs(1, 4, 16, 2000, 128, seed=kbits * 10 + vbits)
+    w = _run_case(k, v, q, 1, 4, 16, 1900, 100, kbits, vbits=vbits)
     print("worst relative error", w)
