@@ -306,6 +306,15 @@ def scores_gqa(qz: Quantizer, q, idx, bits01, norms, gammas):
     return out
 
 
+def scores_mse(qz: Quantizer, q, idx, norms):
+    """MSE-only keys ([hotdry] accuracy tuning section: a mode without the
+    QJL correction, which can rank better in some settings): all b bits go to
+    the Lloyd-Max index and the logit is n <Pi q, c[idx]> = <q, decode_mse>."""
+    _, c, _ = qz.codebook("mse")
+    q_rot = np.asarray(q, dtype=np.float64) @ qz.pi.T
+    return (c[idx] @ q_rot.T).T * np.asarray(norms, dtype=np.float64)[None, :]
+
+
 # ---------------------------------------------------------------------------
 # 7. Decode attention over the packed cache (R13: the pages do not spell the
 #    softmax out; the standard scaled dot product is taken, scale 1/sqrt(d)
@@ -317,11 +326,15 @@ def scores_gqa(qz: Quantizer, q, idx, bits01, norms, gammas):
 def attend(kq: Quantizer, vq: Quantizer, q, k_idx, k_bits, k_norms, k_gammas,
            v_idx, v_norms, k_tail=None, v_tail=None, scale=None):
     """q [Hg, d] queries of one KV head; compressed keys/values [N, ...];
-    tails [T, d] (float).  Returns out [Hg, d]."""
+    tails [T, d] (float).  Returns out [Hg, d].  k_bits = None: MSE-only keys
+    (logits from scores_mse)."""
     q = np.asarray(q, dtype=np.float64)
     d = q.shape[1]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    logit = scores(kq, q, k_idx, k_bits, k_norms, k_gammas)
+    if k_bits is None:
+        logit = scores_mse(kq, q, k_idx, k_norms)
+    else:
+        logit = scores(kq, q, k_idx, k_bits, k_norms, k_gammas)
     vals = decode_mse(vq, v_idx, v_norms)
     if k_tail is not None and len(k_tail):
         logit = np.concatenate([logit, q @ np.asarray(k_tail, dtype=np.float64).T], axis=1)
@@ -356,6 +369,8 @@ def topk(logits, k: int):
 #      groups of 32 coordinates; word (g, p) holds bit p of the index of
 #      coordinates 32g..32g+31 (bit i <-> coordinate 32g+i) for p < b', and
 #      the QJL bits of rows 32g..32g+31 for p = b' (m = d).  Unused bits 0.
+#    mse keys, token major: uint32 [N][G][b] (the prod layout without the
+#      QJL plane, b = all bits to the index); norms only.
 #    mse (values), 32-token blocks, coordinate major: uint32 words
 #      [ceil(N/32)][b'][d]; word (blk, p, j) holds bit p of the index of
 #      coordinate j of tokens 32blk..32blk+31 (bit i <-> token 32blk+i).
@@ -397,6 +412,28 @@ def unpack_prod(words, bp: int, d: int):
     return idx, planes[:, bp, :d].copy()
 
 
+def pack_mse_keys(idx, bp: int, d: int) -> np.ndarray:
+    """MSE-only keys, token major: uint32 [N][G][b'] (the prod layout without
+    the QJL plane)."""
+    n = idx.shape[0]
+    G = (d + 31) // 32
+    planes = np.zeros((n, bp, G * 32), dtype=np.uint8)
+    for p in range(bp):
+        planes[:, p, :d] = (idx >> p) & 1
+    return np.ascontiguousarray(_bits_to_words(planes).transpose(0, 2, 1))
+
+
+def unpack_mse_keys(words, bp: int, d: int):
+    words = np.asarray(words, dtype=np.uint32)
+    n = words.shape[0]
+    G = (d + 31) // 32
+    planes = _words_to_bits(np.ascontiguousarray(words.reshape(n, G, bp).transpose(0, 2, 1)))
+    idx = np.zeros((n, d), dtype=np.int64)
+    for p in range(bp):
+        idx |= planes[:, p, :d].astype(np.int64) << p
+    return idx
+
+
 def pack_mse(idx, bp: int, d: int) -> np.ndarray:
     n = idx.shape[0]
     nb = (n + 31) // 32
@@ -426,4 +463,6 @@ def record_bytes(mode: str, d: int, bits: int) -> int:
     G = (d + 31) // 32
     if mode == "prod":
         return 4 * G * bits + 8
+    if mode == "mse_keys":
+        return 4 * G * bits + 4
     return (bits * d) // 8 + 4

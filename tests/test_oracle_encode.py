@@ -219,3 +219,20 @@ def test_record_size_matches_page_compression_ratios(golden):
     pv = golden["pages"]["compression_vs_fp16"]["values"]
     for bits in (2, 3):
         assert abs(256 / o.record_bytes("prod", 128, bits) - pv[str(bits)]) < 0.05
+
+
+@pytest.mark.parametrize("d,bits", [(16, 2), (128, 3), (200, 4), (48, 1)])
+def test_mse_keys_scores_equal_inner_product_with_decode_and_pack_roundtrip(d, bits):
+    """MSE-only keys: the logit from indices equals <q, decode_mse(code)>
+    (two routes), and the token-major packing round-trips."""
+    rng = np.random.default_rng(d + bits)
+    qz = o.Quantizer(d, bits, 3)
+    x = rng.standard_normal((50, d)) * rng.uniform(0.5, 4.0, (50, 1))
+    q = rng.standard_normal((7, d))
+    idx, nrm = o.encode_mse(qz, x)
+    ref = q @ o.decode_mse(qz, idx, nrm).T
+    np.testing.assert_allclose(o.scores_mse(qz, q, idx, nrm), ref, rtol=1e-10, atol=1e-10 * np.abs(ref).max())
+    w = o.pack_mse_keys(idx, bits, d)
+    assert w.shape == (50, (d + 31) // 32, bits)
+    assert np.array_equal(o.unpack_mse_keys(w.reshape(50, -1), bits, d), idx)
+    assert o.record_bytes("mse_keys", d, bits) == w[0].nbytes + 4
