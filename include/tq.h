@@ -7,7 +7,9 @@
  *   [hotdry]  blog.hotdry.top, "TurboQuant vector-search compression":
  *             sections "随机旋转与标量量化" (random rotation + scalar
  *             quantisation), "QJL 残差校正" (QJL residual correction),
- *             "工程配置参数清单" (engineering configuration)
+ *             "工程配置参数清单" (engineering configuration), "精度调优与
+ *             监控要点" (accuracy tuning and monitoring: an MSE-only mode
+ *             without the QJL correction, for workloads where it ranks better)
  *   [a2a]     a2a-mcp.org, "什麼是TurboQuant？": sections "第一階段" (stage 1:
  *             rotation + Lloyd-Max), "第二階段" (stage 2: QJL), "如何實作
  *             TurboQuant" (how to implement: precompute codebooks, quantise at
@@ -37,6 +39,9 @@
  *                 32g..32g+31 (bit i <-> coordinate 32g+i); word (g, b-1) holds
  *                 the QJL sign bits of projections 32g..32g+31 (1 = non-negative).
  *                 Plus float norms [nseq][n] and float gammas [nseq][n].
+ *   mse keys:     uint32 words [nseq][n][G][b]: the prod layout with all b
+ *                 words holding index bits (word (g, p) = bit p of the b-bit
+ *                 index), no QJL plane.  Plus float norms [nseq][n] only.
  *   mse (values): uint32 words [nseq][ceil(n/32)][b][d].  Word (blk, p, j)
  *                 holds bit p of the index of coordinate j of tokens
  *                 32blk..32blk+31 (bit i <-> token 32blk+i); bits of padding
@@ -62,8 +67,9 @@ enum {
   TQ_EWORKSPACE = -5     /* workspace smaller than the size query returned */
 };
 
-enum { TQ_PROD = 0, /* keys: (bits-1)-bit Lloyd-Max index + 1-bit QJL sketch */
-       TQ_MSE = 1   /* values: bits-bit Lloyd-Max index only */ };
+enum { TQ_PROD = 0,     /* keys: (bits-1)-bit Lloyd-Max index + 1-bit QJL sketch */
+       TQ_MSE = 1,      /* values: bits-bit Lloyd-Max index only */
+       TQ_MSE_KEYS = 2  /* keys without QJL: bits-bit index, token-major ([hotdry] accuracy tuning) */ };
 
 enum { TQ_F32 = 0, TQ_BF16 = 1 };
 
@@ -117,6 +123,15 @@ void tq_free_quantizer(tq_quantizer* q);
 /* d, bits, m of a quantizer (any output pointer may be NULL). */
 int tq_quantizer_info(const tq_quantizer* q, int* d, int* bits, int* m);
 
+/* Which key encoding the scoring calls (tq_scores, tq_query_prep,
+ * tq_scores_from_prep, tq_attend_decode as kq) read from this quantizer:
+ * TQ_PROD (the default; needs bits >= 2) or TQ_MSE_KEYS ([hotdry] accuracy
+ * tuning section: the MSE-only mode, logit(q, i) = n_i <Pi q, c_b[index_i]>
+ * with the bits-bit codebook).  Not thread-safe against concurrent calls on
+ * the same quantizer; a query-prep workspace is only valid for the key mode
+ * it was written under.  Returns TQ_EINVAL for any other value. */
+int tq_set_key_mode(tq_quantizer* q, int key_mode);
+
 /* Number of uint32 code words for nseq sequences of n vectors in `mode`. */
 int64_t tq_code_words(const tq_quantizer* q, int mode, int64_t nseq, int64_t n);
 
@@ -127,13 +142,15 @@ int64_t tq_code_words(const tq_quantizer* q, int mode, int64_t nseq, int64_t n);
  * A zero vector gets y = 0, index = levels/2 - 1, gamma = 0, all QJL bits 1.
  *   x:      [nseq][n][d] of dtype (TQ_F32 or TQ_BF16)
  *   codes:  tq_code_words(q, mode, nseq, n) uint32 words, layout above
- *   norms:  [nseq][n] float;  gammas: [nseq][n] float (prod) or NULL (mse)
+ *   norms:  [nseq][n] float;  gammas: [nseq][n] float (prod), NULL or
+ *           ignored (TQ_MSE, TQ_MSE_KEYS: those use the bits-bit codebook)
  * nseq*n may be 0 (no launch). */
 int tq_encode(const tq_quantizer* q, int mode, const void* x, int dtype, int64_t nseq, int64_t n,
               uint32_t* codes, float* norms, float* gammas, void* stream);
 
 /* Decode ([hotdry] QJL section): prod: x~ = n Pi^T c[index] +
- * gamma sqrt(pi/2)/m S^T sigma, sigma = +-1; mse: x^ = n Pi^T c[index].
+ * gamma sqrt(pi/2)/m S^T sigma, sigma = +-1; mse and mse keys:
+ * x^ = n Pi^T c[index].
  * x_out: [nseq][n][d] float. */
 int tq_decode(const tq_quantizer* q, int mode, const uint32_t* codes, const float* norms,
               const float* gammas, int64_t nseq, int64_t n, float* x_out, void* stream);
@@ -144,7 +161,9 @@ int tq_decode(const tq_quantizer* q, int mode, const uint32_t* codes, const floa
  *   logit(q, i) = n_i <Pi q, c[index_i]> + gamma_i sqrt(pi/2)/m <S q, sigma_i>
  *   queries: [B][Hq][d] (q_dtype TQ_F32 or TQ_BF16); query head h reads KV
  *            head h / (Hq/Hkv) (Hq a multiple of Hkv)
- *   codes/norms/gammas: the prod encoding of [B*Hkv] sequences of n keys
+ *   codes/norms/gammas: the encoding of [B*Hkv] sequences of n keys in the
+ *            quantizer's key mode (tq_set_key_mode); with TQ_MSE_KEYS the
+ *            logit has no QJL term and gammas may be NULL
  *   topk == 0: out = logits [B][Hq][n] float, out_idx unused (may be NULL)
  *   topk  > 0: out = the topk largest logits per query [B][Hq][topk] float,
  *              descending, ties by lower index; out_idx [B][Hq][topk] int64
@@ -171,12 +190,13 @@ int tq_scores(const tq_quantizer* q, const void* queries, int q_dtype, int B, in
 /* Decode-step attention over a packed cache with an optional exact tail
  * ([hotdry] engineering configuration: recent 128-256 tokens kept in full
  * precision, older tokens compressed).  For each query head h of batch b:
- *   s_i = scale * logit(q, i) for compressed tokens (prod keys of kq),
+ *   s_i = scale * logit(q, i) for compressed tokens (keys of kq in its key
+ *         mode; kgammas may be NULL for TQ_MSE_KEYS),
  *   s_i = scale * <q, k_tail_i> for tail tokens (bf16 keys),
  *   p = softmax(s) (max-subtracted, float),
  *   out = sum_i p_i v_i, v_i = n_i Pi_v^T c_v[index_i] (mse values of vq) or
  *         the bf16 tail value.
- *   queries [B][Hq][d]; kcodes/knorms/kgammas: prod encoding of [B*Hkv]
+ *   queries [B][Hq][d]; kcodes/knorms/kgammas: key encoding of [B*Hkv]
  *   sequences of n_comp keys; vcodes/vnorms: mse encoding of the same;
  *   k_tail, v_tail: [B][Hkv][n_tail][d] bf16 (NULL if n_tail == 0);
  *   out: [B][Hq][d] float.  scale <= 0 selects 1/sqrt(d).

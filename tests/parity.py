@@ -1,7 +1,8 @@
 """Comparison helpers for the GPU-vs-oracle parity tests.
 
 Tolerances (the method's parity bar):
-  codes   bit-exact, except an MSE index whose oracle rotated coordinate lies
+  codes   bit-exact (all layouts: prod keys, MSE-only keys, values), except
+          an MSE index whose oracle rotated coordinate lies
           within 1e-5 of a decision threshold may take the adjacent index,
           and a QJL bit whose oracle projection |z| < 1e-5 * gamma may flip;
           at most 1e-4 of all coded coordinates may differ.  When an index
@@ -88,6 +89,30 @@ def check_mse_codes(qz, x, codes, norms):
     if N % 32:
         w = codes.reshape(nb, bp, d)[-1]
         assert np.all((w >> np.uint32(N % 32)) == 0)
+    return idx_g, {"index_flips": int(bad.sum())}
+
+
+def check_mse_key_codes(qz, x, codes, norms):
+    """MSE-only keys (token major, all bits to the index): the mse-values
+    rules (band, flip budget, norms); unused bits of the last group are 0."""
+    d = qz.d
+    bp, c, t = qz.codebook("mse")
+    N = x.shape[0]
+    G = (d + 31) // 32
+    words = codes.reshape(N, G, bp)
+    idx_g = o.unpack_mse_keys(words.reshape(N, -1), bp, d)
+    idx_o, n_o = o.encode_mse(qz, x)
+    nz = n_o > 0
+    y = np.zeros_like(x)
+    y[nz] = (x[nz] / n_o[nz, None]) @ qz.pi.T
+    dist = np.min(np.abs(y[..., None] - t), axis=-1)
+    bad = idx_g != idx_o
+    assert np.all(np.abs(idx_g - idx_o)[bad] == 1)
+    assert np.all(dist[bad] < BAND), f"index flips outside the band: {np.sum(dist[bad] >= BAND)}"
+    assert bad.sum() <= MAX_FLIP_FRAC * N * d + 0.5
+    assert np.allclose(norms, n_o, rtol=1e-5, atol=1e-30)
+    if d % 32:
+        assert np.all((words[:, -1, :] >> np.uint32(d % 32)) == 0), "bits past d must be 0"
     return idx_g, {"index_flips": int(bad.sum())}
 
 

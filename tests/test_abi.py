@@ -86,6 +86,7 @@ def test_quantizer_argument_errors():
     assert L.tq_scores(None, None, 0, 1, 1, 1, None, None, None, 1, 0, None, None, None, 0, None) == tq.TQ_EINVAL
     assert L.tq_attend_decode(None, None, None, 0, 1, 1, 1, None, None, None, None, None, 1, None, None, 0,
                               0.0, None, None, 0, None) == tq.TQ_EINVAL
+    assert L.tq_set_key_mode(None, tq.TQ_MSE_KEYS) == tq.TQ_EINVAL
     assert L.tq_code_words(None, 0, 1, 1) < 0
     assert L.tq_scores_workspace_bytes(None, 1, 1, 1, 1, 0) < 0
 
@@ -95,3 +96,4 @@ def test_layout_sizes_match_oracle_records():
     for d, bits in [(128, 2), (128, 3), (128, 4), (200, 2), (200, 4)]:
         G = (d + 31) // 32
         assert 4 * G * bits + 8 == o.record_bytes("prod", d, bits)
+        assert 4 * G * bits + 4 == o.record_bytes("mse_keys", d, bits)

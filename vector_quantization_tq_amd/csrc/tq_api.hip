@@ -96,8 +96,15 @@ int check_quantizer(const tq_quantizer* q) {
 }
 
 int check_mode(const tq_quantizer* q, int mode) {
-  if (mode != TQ_PROD && mode != TQ_MSE) return fail(TQ_EINVAL, "mode must be TQ_PROD or TQ_MSE");
-  if (q->cb[mode].bp < 1) return fail(TQ_EINVAL, "prod mode needs bits >= 2 (bits=%d)", q->bits);
+  if (mode != TQ_PROD && mode != TQ_MSE && mode != TQ_MSE_KEYS)
+    return fail(TQ_EINVAL, "mode must be TQ_PROD, TQ_MSE or TQ_MSE_KEYS");
+  if (q->cb[mode == TQ_PROD ? 0 : 1].bp < 1) return fail(TQ_EINVAL, "prod mode needs bits >= 2 (bits=%d)", q->bits);
+  return TQ_OK;
+}
+
+// the quantizer's key encoding is readable by the scoring kernels
+int check_keys(const tq_quantizer* q) {
+  if (tq::key_codebook(q).bp < 1) return fail(TQ_EINVAL, "prod keys need bits >= 2 (bits=%d)", q->bits);
   return TQ_OK;
 }
 
@@ -210,12 +217,20 @@ int tq_quantizer_info(const tq_quantizer* q, int* d, int* bits, int* m) {
   return TQ_OK;
 }
 
+int tq_set_key_mode(tq_quantizer* q, int key_mode) {
+  if (int r = check_quantizer(q)) return r;
+  if (key_mode != TQ_PROD && key_mode != TQ_MSE_KEYS) return fail(TQ_EINVAL, "key mode must be TQ_PROD or TQ_MSE_KEYS");
+  if (key_mode == TQ_PROD && q->cb[TQ_PROD].bp < 1) return fail(TQ_EINVAL, "prod keys need bits >= 2 (bits=%d)", q->bits);
+  q->key_mode = key_mode;
+  return TQ_OK;
+}
+
 int64_t tq_code_words(const tq_quantizer* q, int mode, int64_t nseq, int64_t n) {
   if (check_quantizer(q) || check_mode(q, mode)) return -1;
   if (nseq < 0 || n < 0) return fail(TQ_EINVAL, "negative size");
-  const int bp = q->cb[mode].bp;
-  if (mode == TQ_PROD) return nseq * n * ((q->d + 31) / 32) * (bp + 1);
-  return nseq * ((n + 31) / 32) * bp * q->d;
+  if (mode == TQ_PROD) return nseq * n * ((q->d + 31) / 32) * (q->cb[0].bp + 1);
+  if (mode == TQ_MSE_KEYS) return nseq * n * ((q->d + 31) / 32) * q->cb[1].bp;
+  return nseq * ((n + 31) / 32) * q->cb[1].bp * q->d;
 }
 
 int tq_encode(const tq_quantizer* q, int mode, const void* x, int dtype, int64_t nseq, int64_t n, uint32_t* codes,
@@ -260,7 +275,7 @@ static int check_heads(int B, int Hq, int Hkv) {
 
 int64_t tq_scores_workspace_bytes(const tq_quantizer* q, int B, int Hq, int Hkv, int64_t n, int topk) {
   if (check_quantizer(q) || check_heads(B, Hq, Hkv)) return -1;
-  if (q->cb[TQ_PROD].bp < 1) return fail(TQ_EINVAL, "scores need a prod quantizer (bits >= 2)");
+  if (int r = check_keys(q)) return r;
   if (topk > 0) return tq::topk_ws_bytes(q, B, Hq, Hkv, n, topk);
   return tq::scores_ws_bytes(q, B, Hq, Hkv);
 }
@@ -270,15 +285,16 @@ int tq_scores(const tq_quantizer* q, const void* queries, int q_dtype, int B, in
               void* workspace, int64_t ws_bytes, void* stream) {
   if (int r = check_quantizer(q)) return r;
   if (int r = check_heads(B, Hq, Hkv)) return r;
-  if (q->cb[TQ_PROD].bp < 1) return fail(TQ_EINVAL, "scores need a prod quantizer (bits >= 2)");
+  if (int r = check_keys(q)) return r;
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return fail(TQ_EINVAL, "q_dtype must be TQ_F32 or TQ_BF16");
   if (n < 0) return fail(TQ_EINVAL, "negative n");
   if (topk < 0 || topk > 32) return fail(TQ_EINVAL, "topk must be in [0, 32]");
   if (topk > 0 && n < topk) return fail(TQ_EINVAL, "topk (%d) larger than n (%lld)", topk, static_cast<long long>(n));
   if (n == 0) return TQ_OK;
-  if (!queries || !codes || !norms || !gammas || !out || (topk > 0 && !out_idx))
+  if (!tq::key_qjl(q)) gammas = nullptr;   // MSE-only keys carry no gamma
+  if (!queries || !codes || !norms || (tq::key_qjl(q) && !gammas) || !out || (topk > 0 && !out_idx))
     return fail(TQ_EINVAL, "NULL array argument");
-  if (!aligned(queries, 16) || !aligned(codes, 16) || !aligned(norms, 16) || !aligned(gammas, 16) ||
+  if (!aligned(queries, 16) || !aligned(codes, 16) || !aligned(norms, 16) || (gammas && !aligned(gammas, 16)) ||
       !aligned(out, 16) || (out_idx && !aligned(out_idx, 16)))
     return fail(TQ_EINVAL, "device pointers must be 16-byte aligned");
   if (q->d > 256) return fail(TQ_EUNSUPPORTED, "scores support d <= 256 (d=%d)", q->d);
@@ -302,7 +318,7 @@ int tq_query_prep(const tq_quantizer* q, const void* queries, int q_dtype, int B
                   int64_t ws_bytes, void* stream) {
   if (int r = check_quantizer(q)) return r;
   if (int r = check_heads(B, Hq, Hkv)) return r;
-  if (q->cb[TQ_PROD].bp < 1) return fail(TQ_EINVAL, "scores need a prod quantizer (bits >= 2)");
+  if (int r = check_keys(q)) return r;
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return fail(TQ_EINVAL, "q_dtype must be TQ_F32 or TQ_BF16");
   if (!queries) return fail(TQ_EINVAL, "NULL queries");
   if (!aligned(queries, 16)) return fail(TQ_EINVAL, "device pointers must be 16-byte aligned");
@@ -323,11 +339,12 @@ int tq_scores_from_prep(const tq_quantizer* q, int B, int Hq, int Hkv, const uin
                         void* stream) {
   if (int r = check_quantizer(q)) return r;
   if (int r = check_heads(B, Hq, Hkv)) return r;
-  if (q->cb[TQ_PROD].bp < 1) return fail(TQ_EINVAL, "scores need a prod quantizer (bits >= 2)");
+  if (int r = check_keys(q)) return r;
   if (n < 0) return fail(TQ_EINVAL, "negative n");
   if (n == 0) return TQ_OK;
-  if (!codes || !norms || !gammas || !logits) return fail(TQ_EINVAL, "NULL array argument");
-  if (!aligned(codes, 16) || !aligned(norms, 16) || !aligned(gammas, 16) || !aligned(logits, 16))
+  if (!tq::key_qjl(q)) gammas = nullptr;   // MSE-only keys carry no gamma
+  if (!codes || !norms || (tq::key_qjl(q) && !gammas) || !logits) return fail(TQ_EINVAL, "NULL array argument");
+  if (!aligned(codes, 16) || !aligned(norms, 16) || (gammas && !aligned(gammas, 16)) || !aligned(logits, 16))
     return fail(TQ_EINVAL, "device pointers must be 16-byte aligned");
   if (q->d > 256) return fail(TQ_EUNSUPPORTED, "scores support d <= 256 (d=%d)", q->d);
   const int64_t need = tq::scores_ws_bytes(q, B, Hq, Hkv);
@@ -359,12 +376,14 @@ int tq_attend_decode(const tq_quantizer* kq, const tq_quantizer* vq, const void*
   if (int r = check_quantizer(vq)) return r;
   if (int r = check_heads(B, Hq, Hkv)) return r;
   if (kq->d != vq->d) return fail(TQ_EINVAL, "key and value quantizers differ in d");
-  if (kq->cb[TQ_PROD].bp < 1) return fail(TQ_EINVAL, "keys need a prod quantizer (bits >= 2)");
+  if (int r = check_keys(kq)) return r;
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return fail(TQ_EINVAL, "q_dtype must be TQ_F32 or TQ_BF16");
   if (n_comp < 0 || n_tail < 0) return fail(TQ_EINVAL, "negative size");
   if (n_comp + n_tail < 1) return fail(TQ_EINVAL, "empty cache (n_comp + n_tail == 0)");
   if (!queries || !out) return fail(TQ_EINVAL, "NULL queries or output");
-  if (n_comp > 0 && (!kcodes || !knorms || !kgammas || !vcodes || !vnorms)) return fail(TQ_EINVAL, "NULL cache array");
+  if (!tq::key_qjl(kq)) kgammas = nullptr;   // MSE-only keys carry no gamma
+  if (n_comp > 0 && (!kcodes || !knorms || (tq::key_qjl(kq) && !kgammas) || !vcodes || !vnorms))
+    return fail(TQ_EINVAL, "NULL cache array");
   if (n_tail > 0 && (!k_tail || !v_tail)) return fail(TQ_EINVAL, "NULL tail array");
   const void* ptrs[] = {queries, out, kcodes, knorms, kgammas, vcodes, vnorms, k_tail, v_tail};
   for (const void* p : ptrs)

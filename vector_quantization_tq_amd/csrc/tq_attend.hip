@@ -97,15 +97,16 @@ __device__ __forceinline__ void dma_tok(float* dst, const float* src, int64_t t0
   __builtin_amdgcn_global_load_lds(src + t, as_lds(dst), 4, 0, 0);
 }
 
-template <int BPK, int BPV, int NSLOT>
+// QJL: prod keys (QJL plane + gammas); without it MSE-only keys.
+template <int BPK, int BPV, int NSLOT, bool QJL>
 __device__ __forceinline__ void attend_chunk_body(
     const uint32_t* __restrict__ kcodes, const float* __restrict__ knorms, const float* __restrict__ kgammas,
     const uint32_t* __restrict__ vcodes, const float* __restrict__ vnorms, int64_t n, int64_t chunk, int G, int RT,
     float scale_log2, const uint8_t* __restrict__ wsA, const float* __restrict__ wsC, const Codebook& vcb,
     float* __restrict__ part) {
   constexpr int d = 128;
-  constexpr int TK = (1 << (BPK - 1)) + 1;   // key MFMA terms (Walsh + QJL)
-  constexpr int WK = BPK + 1;                // key words per 32-coordinate group
+  constexpr int TK = (1 << (BPK - 1)) + (QJL ? 1 : 0);   // key MFMA terms (Walsh + QJL)
+  constexpr int WK = BPK + (QJL ? 1 : 0);                // key words per 32-coordinate group
   constexpr int WPK = 4 * WK;                // key words per token
   constexpr int NV = 1 << (BPV - 1);         // value Walsh terms
   constexpr int KW = kStep * WPK;            // key words of a step
@@ -126,7 +127,7 @@ __device__ __forceinline__ void attend_chunk_body(
 
   const uint32_t* kb = kcodes + static_cast<int64_t>(grp) * n * WPK;
   const float* knb = knorms + static_cast<int64_t>(grp) * n;
-  const float* kgb = kgammas + static_cast<int64_t>(grp) * n;
+  const float* kgb = QJL ? kgammas + static_cast<int64_t>(grp) * n : nullptr;
   const int64_t nbk = (n + 31) >> 5;
   const uint32_t* vb = vcodes + static_cast<int64_t>(grp) * nbk * BPV * d;
   const float* vnb = vnorms + static_cast<int64_t>(grp) * n;
@@ -142,7 +143,7 @@ __device__ __forceinline__ void attend_chunk_body(
     float* nz = reinterpret_cast<float*>(sl + KW + VW);
     if (wave < 2) {
       dma_tok(nz + 64 * wave, knb, t0 + 64 * wave, n, lane);
-      dma_tok(nz + kStep + 64 * wave, kgb, t0 + 64 * wave, n, lane);
+      if constexpr (QJL) dma_tok(nz + kStep + 64 * wave, kgb, t0 + 64 * wave, n, lane);
     } else {
       dma_tok(nz + 2 * kStep + 64 * (wave - 2), vnb, t0 + 64 * (wave - 2), n, lane);
     }
@@ -172,7 +173,7 @@ __device__ __forceinline__ void attend_chunk_body(
 
   // DMA instructions this wave issues per step (the same for every step)
   constexpr int KI = KW / 256, VI = VW / 256;
-  const int per_step = (KI + 3 - wave) / 4 + (VI + 3 - wave) / 4 + (wave < 2 ? 2 : 1);
+  const int per_step = (KI + 3 - wave) / 4 + (VI + 3 - wave) / 4 + (wave < 2 ? (QJL ? 2 : 1) : 1);
   // softmax tokens of this lane: tA and tB = tA + 4, whose value-MFMA A bytes
   // are adjacent (K and K + 1 in the same fp4 slot), so each limb of the pair
   // is one 16-bit LDS write.  token = 32(K/32) + 4(K%8) + (K%32)/8.
@@ -215,14 +216,18 @@ __device__ __forceinline__ void attend_chunk_body(
       for (int p = 0; p < WK; ++p) w[p] = sl[(tt * 4 + g) * WK + p];
       v4f aM = {0.f, 0.f, 0.f, 0.f}, aQ = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < TK - 1; ++t) aM = mfma_fp8_fp4(AK[t], bits_to_fp4(walsh_word<BPK>(w, t)), aM);
-      aQ = mfma_fp8_fp4(AK[TK - 1], bits_to_fp4(w[BPK]), aQ);
+      for (int t = 0; t < (1 << (BPK - 1)); ++t) aM = mfma_fp8_fp4(AK[t], bits_to_fp4(walsh_word<BPK>(w, t)), aM);
+      if constexpr (QJL) aQ = mfma_fp8_fp4(AK[TK - 1], bits_to_fp4(w[BPK]), aQ);
       pin(aM);
-      pin(aQ);
       const float mse = fmaf(aM[0], cs[2], fmaf(aM[1], cs[3], fmaf(aM[2], cs[4], fmaf(aM[3], cs[5], cs[0]))));
-      const float qjl = fmaf(aQ[0], cs[6], fmaf(aQ[1], cs[7], fmaf(aQ[2], cs[8], fmaf(aQ[3], cs[9], cs[1]))));
+      float logit = kns[tt] * mse;
+      if constexpr (QJL) {
+        pin(aQ);
+        const float qjl = fmaf(aQ[0], cs[6], fmaf(aQ[1], cs[7], fmaf(aQ[2], cs[8], fmaf(aQ[3], cs[9], cs[1]))));
+        logit = fmaf(kns[tt], mse, kns[kStep + tt] * qjl);
+      }
       float s = -INFINITY;
-      if (t0 + tt < c1) s = fmaf(kns[tt], mse, kns[kStep + tt] * qjl) * scale_log2;
+      if (t0 + tt < c1) s = logit * scale_log2;
       sc[qi][tt] = s;
     }
     __syncthreads();
@@ -322,13 +327,13 @@ __device__ __forceinline__ void attend_chunk_body(
   }
 }
 
-template <int BPK, int BPV>
+template <int BPK, int BPV, bool QJL>
 __global__ void __launch_bounds__(256) attend_chunk_kernel(
     const uint32_t* __restrict__ kcodes, const float* __restrict__ knorms, const float* __restrict__ kgammas,
     const uint32_t* __restrict__ vcodes, const float* __restrict__ vnorms, int64_t n, int64_t chunk, int G, int RT,
     float scale_log2, const uint8_t* __restrict__ wsA, const float* __restrict__ wsC, Codebook vcb,
     float* __restrict__ part) {
-  attend_chunk_body<BPK, BPV, 3>(kcodes, knorms, kgammas, vcodes, vnorms, n, chunk, G, RT, scale_log2, wsA, wsC, vcb,
+  attend_chunk_body<BPK, BPV, 3, QJL>(kcodes, knorms, kgammas, vcodes, vnorms, n, chunk, G, RT, scale_log2, wsA, wsC, vcb,
                                  part);
 }
 
@@ -492,19 +497,22 @@ hipError_t launch_attend(const tq_quantizer* kq, const tq_quantizer* vq, const v
   if (nch > 0) {
     e = launch_query_prep_ws(kq, queries, q_dtype, B, Hq, Hkv, ws, st);
     if (e != hipSuccess) return e;
-    const int T = kq->cb[0].nterms + 1;
+    const int T = key_terms(kq);
     const uint8_t* wsA = static_cast<const uint8_t*>(ws);
     const float* wsC = reinterpret_cast<const float*>(wsA + groups * T * 2048);
     const int64_t ch = attend_chunk_len(n_comp, groups);
     dim3 grid(static_cast<unsigned>(nch), static_cast<unsigned>(groups));
-    const int bpk = kq->cb[0].bp, bpv = vq->cb[1].bp;
-#define TQ_AT(K, V)                                                                                              \
-  if (bpk == K && bpv == V) {                                                                                    \
-    hipLaunchKernelGGL((attend_chunk_kernel<K, V>), grid, dim3(256), 0, st, kcodes, knorms, kgammas, vcodes, vnorms, \
-                       n_comp, ch, G, RT, sl, wsA, wsC, vq->cb[1], part);                                       \
+    const int bpk = key_codebook(kq).bp, bpv = vq->cb[1].bp;
+    const bool qjl = key_qjl(kq);
+#define TQ_AT(K, V, QV)                                                                                       \
+  if (bpk == K && bpv == V && qjl == QV) {                                                                    \
+    hipLaunchKernelGGL((attend_chunk_kernel<K, V, QV>), grid, dim3(256), 0, st, kcodes, knorms, kgammas, vcodes, \
+                       vnorms, n_comp, ch, G, RT, sl, wsA, wsC, vq->cb[1], part);                            \
   } else
-    TQ_AT(1, 1) TQ_AT(1, 2) TQ_AT(1, 3) TQ_AT(1, 4) TQ_AT(2, 1) TQ_AT(2, 2) TQ_AT(2, 3) TQ_AT(2, 4)
-    TQ_AT(3, 1) TQ_AT(3, 2) TQ_AT(3, 3) TQ_AT(3, 4) { return hipErrorNotSupported; }
+#define TQ_AT4(K, QV) TQ_AT(K, 1, QV) TQ_AT(K, 2, QV) TQ_AT(K, 3, QV) TQ_AT(K, 4, QV)
+    TQ_AT4(1, true) TQ_AT4(2, true) TQ_AT4(3, true)
+    TQ_AT4(1, false) TQ_AT4(2, false) TQ_AT4(3, false) TQ_AT4(4, false) { return hipErrorNotSupported; }
+#undef TQ_AT4
 #undef TQ_AT
     e = hipGetLastError();
     if (e != hipSuccess) return e;

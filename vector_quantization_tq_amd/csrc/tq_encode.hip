@@ -173,10 +173,10 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(const void* __restrict
 
   // ---- bit packing ----
   const int bp = cb.bp;
-  if (mode == 0) {
-    // prod: words [vec][g][bp+1]
+  if (mode != 1) {
+    // keys: words [vec][g][W], W = bp + 1 with the QJL plane, bp without
     const int G = (d + 31) >> 5;
-    const int W = bp + 1;
+    const int W = bp + (mode == 0 ? 1 : 0);
     for (int task = tid; task < kTileRows * G; task += kThreads) {
       const int row = task / G, g = task - row * G;
       if (row >= rows) continue;
@@ -187,7 +187,7 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(const void* __restrict
         if (32 * g + i >= DP) break;
         const uint32_t iv = ib[i];
         for (int p = 0; p < bp; ++p) w[p] |= ((iv >> p) & 1u) << i;
-        w[bp] |= static_cast<uint32_t>(sb[i]) << i;
+        if (mode == 0) w[bp] |= static_cast<uint32_t>(sb[i]) << i;
       }
       uint32_t* out = codes + ((base + row) * G + g) * W;
       for (int p = 0; p < W; ++p) out[p] = w[p];
@@ -284,13 +284,18 @@ __device__ __forceinline__ float pick_centroid(const float (&cen)[1 << BP], cons
 }
 
 // LK: how a tile is loaded: 0 element by element (any d, either dtype),
-// 1 bf16 and 2 fp32 in 16-byte chunks fetched one tile ahead.  BP: index bits.
-template <int KS, int LK, bool PROD, int BP>
+// 1 bf16 and 2 fp32 in 16-byte chunks fetched one tile ahead.  BP: index
+// bits.  MODE: 0 keys with the QJL sketch (token-major words + rho, gamma),
+// 1 values (coordinate-major 32-token words), 2 MSE-only keys (token-major
+// words, no QJL plane).
+template <int KS, int LK, int MODE, int BP>
 __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restrict__ x, int dtype, int64_t nseq,
                                                              int64_t n, int d, const float* __restrict__ pi,
                                                              const float* __restrict__ sp, Codebook cb,
                                                              uint32_t* __restrict__ codes, float* __restrict__ norms,
                                                              float* __restrict__ gammas) {
+  constexpr bool PROD = MODE != 1;       // token-major words, C[vector][coordinate]
+  constexpr bool QJL = MODE == 0;        // residual, QJL plane and gamma
   constexpr int KP = 32 * KS;            // padded contraction length
   constexpr int LDH = KP + 8;            // LDS row stride in halves (16-byte rows, conflict-free reads)
   constexpr bool XLO = LK != 1;          // fp32 keys need x_lo (bf16 keys are exact in fp16)
@@ -298,8 +303,8 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
   constexpr int EPT = KP / 4;            // elements per loader thread (scalar path)
   __shared__ __attribute__((aligned(16))) _Float16 xh[kEncRows * LDH];
   __shared__ __attribute__((aligned(16))) _Float16 xl[XLO ? kEncRows * LDH : 8];
-  __shared__ __attribute__((aligned(16))) _Float16 rh[PROD ? kEncRows * LDH : 8];
-  __shared__ __attribute__((aligned(16))) _Float16 rl[PROD ? kEncRows * LDH : 8];
+  __shared__ __attribute__((aligned(16))) _Float16 rh[QJL ? kEncRows * LDH : 8];
+  __shared__ __attribute__((aligned(16))) _Float16 rl[QJL ? kEncRows * LDH : 8];
   __shared__ float scl2[2][kEncRows];    // 2^-(row scale + 8) / n, by tile parity
   __shared__ float nrm2[2][kEncRows];    // n, by tile parity
   __shared__ float part2[4][kEncRows];
@@ -310,7 +315,7 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
   constexpr int bp = BP;
   constexpr int NT = (1 << BP) - 1;      // thresholds
   const int G = (d + 31) >> 5;
-  const int W = bp + 1;                  // prod words per group
+  const int W = bp + (QJL ? 1 : 0);      // token-major words per group
   const int WPK = G * W;
   const int64_t tps = (n + kEncRows - 1) / kEncRows;   // tiles per sequence
   const int64_t total = nseq * tps;
@@ -318,7 +323,7 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
 
   // stationary operands: lane (r16, q) holds row 32w + 16ct + r16, columns
   // 32s + 8q .. +7 of Pi (and S'), split into hi + lo
-  v8h bPh[2][KS], bPl[2][KS], bSh[2][PROD ? KS : 1], bSl[2][PROD ? KS : 1];
+  v8h bPh[2][KS], bPl[2][KS], bSh[2][QJL ? KS : 1], bSl[2][QJL ? KS : 1];
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
     const int j = 32 * w + 16 * ct + r16;
@@ -332,7 +337,7 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
         const _Float16 ph = static_cast<_Float16>(vp);
         bPh[ct][s2][e] = ph;
         bPl[ct][s2][e] = static_cast<_Float16>(vp - static_cast<float>(ph));
-        if constexpr (PROD) {
+        if constexpr (QJL) {
           const float vs = in ? sp[static_cast<int64_t>(j) * d + k] * kPiScale : 0.f;
           const _Float16 sh = static_cast<_Float16>(vs);
           bSh[ct][s2][e] = sh;
@@ -343,7 +348,7 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
   for (int e = tid; e < kEncRows * LDH; e += 256) {
     xh[e] = static_cast<_Float16>(0.f);
     if constexpr (XLO) xl[e] = static_cast<_Float16>(0.f);
-    if constexpr (PROD) {
+    if constexpr (QJL) {
       rh[e] = static_cast<_Float16>(0.f);
       rl[e] = static_cast<_Float16>(0.f);
     }
@@ -567,16 +572,18 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
               const int c = 32 * w + 16 * ct + r16;
               const float a = acc[h2][ct][i];
               classify(a * sc, pos[ct], jb[ct]);
-              // rho * 2^14 = y 2^14 - c[idx] 2^14 in one rounding
-              float cabs;
-              if constexpr (BP > 1) cabs = pick_centroid<BP - 1>(cenS, jb[ct]);
-              else cabs = cenS[0];
-              const float rs = c < d ? fmaf(a, scS, pos[ct] ? -cabs : cabs) : 0.f;
-              r2 = fmaf(rs, rs, r2);
-              if (c < KP) {
-                const _Float16 hh = static_cast<_Float16>(rs);
-                rh[(vbase + i) * LDH + c] = hh;
-                rl[(vbase + i) * LDH + c] = static_cast<_Float16>(rs - static_cast<float>(hh));
+              if constexpr (QJL) {
+                // rho * 2^14 = y 2^14 - c[idx] 2^14 in one rounding
+                float cabs;
+                if constexpr (BP > 1) cabs = pick_centroid<BP - 1>(cenS, jb[ct]);
+                else cabs = cenS[0];
+                const float rs = c < d ? fmaf(a, scS, pos[ct] ? -cabs : cabs) : 0.f;
+                r2 = fmaf(rs, rs, r2);
+                if (c < KP) {
+                  const _Float16 hh = static_cast<_Float16>(rs);
+                  rh[(vbase + i) * LDH + c] = hh;
+                  rl[(vbase + i) * LDH + c] = static_cast<_Float16>(rs - static_cast<float>(hh));
+                }
               }
             }
             if (w < G) {
@@ -594,32 +601,36 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
               }
             }
             // partial ||rho||^2 (x 2^28) over this wave's 32 coordinates
-            r2 = sum16(r2);
-            if (r16 == 0) part2[w][vbase + i] = r2;
+            if constexpr (QJL) {
+              r2 = sum16(r2);
+              if (r16 == 0) part2[w][vbase + i] = r2;
+            }
           }
         }
       }
-      __syncthreads();
+      __syncthreads();   // rho complete; every wave done with the x tile
 
       // ---- QJL: z = S' rho (scaled), bit = [z >= 0] (all ones for a zero vector) ----
+      if constexpr (QJL) {
 #pragma unroll 1
-      for (int h = 0; h < 2; ++h) {
-        v4f acc[2][2];
-        zero_acc(acc);
-        contract(rh, bSh, h, false, acc);
-        contract(rl, bSh, h, false, acc);
-        contract(rh, bSl, h, false, acc);
-        pin_acc(acc);
-        if (w < G) {
+        for (int h = 0; h < 2; ++h) {
+          v4f acc[2][2];
+          zero_acc(acc);
+          contract(rh, bSh, h, false, acc);
+          contract(rl, bSh, h, false, acc);
+          contract(rh, bSl, h, false, acc);
+          pin_acc(acc);
+          if (w < G) {
 #pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            const int vbase = 32 * h + 16 * h2 + 4 * q;
+            for (int h2 = 0; h2 < 2; ++h2) {
+              const int vbase = 32 * h + 16 * h2 + 4 * q;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const bool zero = !(nrm[vbase + i] > 0.f);
-              const uint64_t m0 = __ballot((32 * w + r16 < d) && (acc[h2][0][i] >= 0.f || zero));
-              const uint64_t m1 = __ballot((32 * w + 16 + r16 < d) && (acc[h2][1][i] >= 0.f || zero));
-              if (r16 == 0) ost[buf][(vbase + i) * WPK + w * W + bp] = halves(m0, m1);
+              for (int i = 0; i < 4; ++i) {
+                const bool zero = !(nrm[vbase + i] > 0.f);
+                const uint64_t m0 = __ballot((32 * w + r16 < d) && (acc[h2][0][i] >= 0.f || zero));
+                const uint64_t m1 = __ballot((32 * w + 16 + r16 < d) && (acc[h2][1][i] >= 0.f || zero));
+                if (r16 == 0) ost[buf][(vbase + i) * WPK + w * W + bp] = halves(m0, m1);
+              }
             }
           }
         }
@@ -627,8 +638,9 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
       if (tid < rows) {
         const float nv = nrm[tid];
         norms[seq * n + v0 + tid] = nv;
-        gammas[seq * n + v0 + tid] =
-            nv * sqrtf(part2[0][tid] + part2[1][tid] + part2[2][tid] + part2[3][tid]) * (1.f / kRhoScale);
+        if constexpr (QJL)
+          gammas[seq * n + v0 + tid] =
+              nv * sqrtf(part2[0][tid] + part2[1][tid] + part2[2][tid] + part2[3][tid]) * (1.f / kRhoScale);
       }
     } else {
       // lane holds coordinate 32w + 16ct + 4q + i, token 32h + 16h2 + r16;
@@ -692,9 +704,9 @@ __global__ void __launch_bounds__(256) decode_kernel(const uint32_t* __restrict_
     float val = 0.f;
     if (t < n) {
       uint32_t idx = 0;
-      if (mode == 0) {
+      if (mode != 1) {
         const int G = (d + 31) >> 5;
-        const uint32_t* w = codes + ((seq * n + t) * G + (j >> 5)) * (bp + 1);
+        const uint32_t* w = codes + ((seq * n + t) * G + (j >> 5)) * (bp + (mode == 0 ? 1 : 0));
         for (int p = 0; p < bp; ++p) idx |= ((w[p] >> (j & 31)) & 1u) << p;
       } else {
         const int64_t nb = (n + 31) >> 5;
@@ -738,7 +750,7 @@ hipError_t launch_encode_nt(const tq_quantizer* q, int mode, const void* x, int 
   const size_t lds = sizeof(float) * (kTileRows * (DP + 1) + kTileRows + kMaxLevels) + 2 * kTileRows * DP;
   dim3 grid(static_cast<unsigned>((n + kTileRows - 1) / kTileRows), static_cast<unsigned>(nseq));
   hipLaunchKernelGGL((encode_kernel<NT>), grid, dim3(kThreads), lds, st, x, dtype, n, q->d, mode, q->d_pi, q->d_sp,
-                     q->cb[mode], codes, norms, gammas);
+                     q->cb[mode == 0 ? 0 : 1], codes, norms, gammas);
   return hipGetLastError();
 }
 
@@ -760,22 +772,22 @@ static int encode_tile_blocks() {
   return blocks;
 }
 
-template <int LK, bool PROD>
+template <int LK, int MODE>
 hipError_t launch_encode_tile_m(const tq_quantizer* q, const void* x, int dtype, int64_t nseq, int64_t n,
                                 uint32_t* codes, float* norms, float* gammas, hipStream_t st) {
   const int64_t tiles = nseq * ((n + kEncRows - 1) / kEncRows);
   const dim3 grid(static_cast<unsigned>(std::min<int64_t>(tiles, encode_tile_blocks())));
-  const Codebook& cb = q->cb[PROD ? 0 : 1];
+  const Codebook& cb = q->cb[MODE == 0 ? 0 : 1];
 #define TQ_ENC(BPV)                                                                                                 \
   case BPV:                                                                                                         \
-    hipLaunchKernelGGL((encode_tile_kernel<4, LK, PROD, BPV>), grid, dim3(256), 0, st, x, dtype, nseq, n, q->d,     \
+    hipLaunchKernelGGL((encode_tile_kernel<4, LK, MODE, BPV>), grid, dim3(256), 0, st, x, dtype, nseq, n, q->d,     \
                        q->d_pi, q->d_sp, cb, codes, norms, gammas);                                               \
     break;
   switch (cb.bp) {
     TQ_ENC(1) TQ_ENC(2) TQ_ENC(3)
     case 4:
-      if constexpr (!PROD) {
-        hipLaunchKernelGGL((encode_tile_kernel<4, LK, PROD, 4>), grid, dim3(256), 0, st, x, dtype, nseq, n, q->d,
+      if constexpr (MODE != 0) {
+        hipLaunchKernelGGL((encode_tile_kernel<4, LK, MODE, 4>), grid, dim3(256), 0, st, x, dtype, nseq, n, q->d,
                            q->d_pi, q->d_sp, cb, codes, norms, gammas);
         break;
       }
@@ -789,8 +801,9 @@ hipError_t launch_encode_tile_m(const tq_quantizer* q, const void* x, int dtype,
 template <int LK>
 hipError_t launch_encode_tile_lk(const tq_quantizer* q, int mode, const void* x, int dtype, int64_t nseq, int64_t n,
                                  uint32_t* codes, float* norms, float* gammas, hipStream_t st) {
-  return mode == 0 ? launch_encode_tile_m<LK, true>(q, x, dtype, nseq, n, codes, norms, gammas, st)
-                   : launch_encode_tile_m<LK, false>(q, x, dtype, nseq, n, codes, norms, gammas, st);
+  if (mode == 0) return launch_encode_tile_m<LK, 0>(q, x, dtype, nseq, n, codes, norms, gammas, st);
+  if (mode == 1) return launch_encode_tile_m<LK, 1>(q, x, dtype, nseq, n, codes, norms, gammas, st);
+  return launch_encode_tile_m<LK, 2>(q, x, dtype, nseq, n, codes, norms, gammas, st);
 }
 
 hipError_t launch_encode_tile(const tq_quantizer* q, int mode, const void* x, int dtype, int64_t nseq, int64_t n,
@@ -822,7 +835,7 @@ hipError_t launch_decode(const tq_quantizer* q, int mode, const uint32_t* codes,
   const size_t lds = sizeof(float) * 8 * (q->d + (mode == 0 ? q->m : 0));
   dim3 grid(static_cast<unsigned>((n + 7) / 8), static_cast<unsigned>(nseq));
   hipLaunchKernelGGL(decode_kernel, grid, dim3(256), lds, st, codes, norms, gammas, n, q->d, q->m, mode, q->d_pi, q->d_s,
-                     q->cb[mode], out);
+                     q->cb[mode == 0 ? 0 : 1], out);
   return hipGetLastError();
 }
 

@@ -37,9 +37,17 @@ struct tq_quantizer {
   int d = 0, bits = 0, m = 0, device = 0;
   uint64_t seed = 0;
   std::vector<double> pi, s;          // host float64 copies (row major)
-  tq::Codebook cb[2];                 // [TQ_PROD], [TQ_MSE]
+  tq::Codebook cb[2];                 // [TQ_PROD] b-1 bits, [TQ_MSE] b bits (values and MSE-only keys)
   float* d_pi = nullptr;              // [d][d]   y = Pi x
   float* d_s = nullptr;               // [m][d]   QJL matrix
   float* d_sp = nullptr;              // [m][d]   S' = S Pi^T (acts on rotated residuals)
   float* d_qt = nullptr;              // [d][d+m] column k of Pi then of S (query transform, k-major)
+  int key_mode = 0;                   // key layout the scoring calls read: TQ_PROD (0) or TQ_MSE_KEYS (2)
 };
+
+namespace tq {
+// codebook and term count of the keys the scoring calls read
+inline bool key_qjl(const tq_quantizer* q) { return q->key_mode != 2; }
+inline const Codebook& key_codebook(const tq_quantizer* q) { return q->cb[key_qjl(q) ? 0 : 1]; }
+inline int key_terms(const tq_quantizer* q) { return key_codebook(q).nterms + (key_qjl(q) ? 1 : 0); }
+}  // namespace tq

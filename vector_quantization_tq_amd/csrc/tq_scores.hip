@@ -33,10 +33,12 @@ namespace tq {
 // Writes the fp8 A operands [group*RT + rt][term][chunk][lane][32 bytes] and
 // per-query constants [group*RT + rt][qi][16 floats]:
 //   {cM, cQ, sM0..3, sQ0..3}: logit = n (sum_k sM_k C_M,k + cM) + gamma (sum_k sQ_k C_Q,k + cQ)
+// The terms are the Walsh terms of the key codebook, then (prod keys) the
+// QJL term; MSE-only keys have no QJL term.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) query_prep_kernel(const void* __restrict__ queries, int q_dtype, int Hq, int Hkv,
                                                          int G, int RT, int d, int m, const float* __restrict__ qt,
-                                                         Codebook cb, int C, uint8_t* __restrict__ wsA,
+                                                         Codebook cb, int qjl, int C, uint8_t* __restrict__ wsA,
                                                          float* __restrict__ wsC) {
   extern __shared__ float sm[];
   float* qv = sm;           // [d]
@@ -49,7 +51,7 @@ __global__ void __launch_bounds__(256) query_prep_kernel(const void* __restrict_
   const int b = grp / Hkv, kvh = grp - b * Hkv;
   const int qg = rt * 4 + qi;                 // query index inside the KV group
   const bool valid = qg < G;
-  const int T = cb.nterms + 1;
+  const int T = cb.nterms + (qjl ? 1 : 0);   // Walsh terms (+ the QJL term)
 
   if (valid) {
     const int64_t qoff = (static_cast<int64_t>(b) * Hq + kvh * G + qg) * d;
@@ -156,7 +158,7 @@ __global__ void __launch_bounds__(256) query_prep_kernel(const void* __restrict_
   for (int idx = tid; idx < T * C * 128; idx += blockDim.x) {
     const int t = idx / (C * 128), c = (idx >> 7) - t * C, ge = idx & 127;
     const int g = ge >> 5, e = ge & 31;
-    const bool is_q = t == T - 1;
+    const bool is_q = qjl && t == T - 1;
     const int k = a_elem_to_k(g, e);
     const int coord = c * 128 + 32 * (k >> 5) + k_to_bit(k);
     float x = 0.f;
@@ -177,7 +179,7 @@ __global__ void __launch_bounds__(256) query_prep_kernel(const void* __restrict_
     float val = 0.f;
     if (valid) {
       if (tid == 0) val = -cb.coef_sum * sum_h;
-      else if (tid == 1) val = -0.5f * alpha2 * sum_s;
+      else if (tid == 1) val = qjl ? -0.5f * alpha2 * sum_s : 0.f;
       else if (tid < 6) val = ldexpf(1.f, -E_m - 4 * (tid - 2));
       else if (tid < 10) val = ldexpf(1.f, -E_q - 4 * (tid - 6));
     }
@@ -210,21 +212,21 @@ constexpr int kTargetWaves = TQ_SCORES_WAVES;   // resident waves aimed at (256 
 constexpr int kRing = TQ_SCORES_RING;
 constexpr int kBatchKeys = 64;
 
-template <int WPK>
+template <int WPK, bool QJL>
 struct DmaPlan {
   // bytes per lane per load; the 12-byte form places lanes 16 bytes apart in LDS, so it is not used
   static constexpr int SZ = (WPK % 4 == 0) ? 16 : 4;
   static constexpr int WPL = SZ / 4;                                            // words per lane per load
   static constexpr int NC = WPK / WPL;                                          // loads for the packed words
-  static constexpr int L = NC + 2;                                              // + norms + gammas
+  static constexpr int L = NC + (QJL ? 2 : 1);                                  // + norms (+ gammas)
 };
 
 // issue the loads of one batch (keys k0 .. k0+63 of a sequence of n keys) into an LDS slot
-template <int WPK>
+template <int WPK, bool QJL>
 __device__ __forceinline__ void issue_batch(uint32_t* slot, const uint32_t* __restrict__ cbase,
                                             const float* __restrict__ nb, const float* __restrict__ gb, int64_t k0,
                                             int64_t n, int lane) {
-  using P = DmaPlan<WPK>;
+  using P = DmaPlan<WPK, QJL>;
   const int64_t limit = (n - k0) * WPK;        // valid words from this batch's start (> 0)
 #pragma unroll
   for (int i = 0; i < P::NC; ++i) {
@@ -242,21 +244,23 @@ __device__ __forceinline__ void issue_batch(uint32_t* slot, const uint32_t* __re
   if (kk >= n) kk = n - 1;
   float* ng = reinterpret_cast<float*>(slot + kBatchKeys * WPK);
   __builtin_amdgcn_global_load_lds(nb + kk, as_lds(ng), 4, 0, 0);
-  __builtin_amdgcn_global_load_lds(gb + kk, as_lds(ng + kBatchKeys), 4, 0, 0);
+  if constexpr (QJL) __builtin_amdgcn_global_load_lds(gb + kk, as_lds(ng + kBatchKeys), 4, 0, 0);
 }
 
-template <int BP, int GW>
+// QJL: prod keys (BP index planes + the QJL plane, gamma per key); without
+// it MSE-only keys (BP index planes, norms only).
+template <int BP, int GW, bool QJL>
 __global__ void __launch_bounds__(256) scores_kernel(const uint32_t* __restrict__ codes, const float* __restrict__ norms,
                                                      const float* __restrict__ gammas, int64_t n, int Hq, int Hkv,
                                                      int G, int RT, const uint8_t* __restrict__ wsA,
                                                      const float* __restrict__ wsC, float* __restrict__ out) {
-  constexpr int T = (1 << (BP - 1)) + 1;
-  constexpr int W = BP + 1;
+  constexpr int T = (1 << (BP - 1)) + (QJL ? 1 : 0);
+  constexpr int W = BP + (QJL ? 1 : 0);
   constexpr int C = (GW + 3) / 4;
   constexpr int WPK = GW * W;                                   // packed words per key
   constexpr int SLOTW = kBatchKeys * WPK + 2 * kBatchKeys;      // words per ring slot
   constexpr int WAVEW = kRing * SLOTW + 4 * kBatchKeys;         // + logit staging
-  using P = DmaPlan<WPK>;
+  using P = DmaPlan<WPK, QJL>;
   constexpr int L = P::L;
   __shared__ __attribute__((aligned(16))) uint32_t lds[4 * WAVEW];
 
@@ -271,7 +275,7 @@ __global__ void __launch_bounds__(256) scores_kernel(const uint32_t* __restrict_
 
   const uint32_t* cbase = codes + static_cast<int64_t>(grp) * n * WPK;
   const float* nb = norms + static_cast<int64_t>(grp) * n;
-  const float* gb = gammas + static_cast<int64_t>(grp) * n;
+  const float* gb = QJL ? gammas + static_cast<int64_t>(grp) * n : nullptr;
   const int64_t nbatch = (n + kBatchKeys - 1) / kBatchKeys;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * 4;
   const int64_t first = static_cast<int64_t>(blockIdx.x) * 4 + wave;
@@ -281,7 +285,7 @@ __global__ void __launch_bounds__(256) scores_kernel(const uint32_t* __restrict_
   // prologue: fill the ring
 #pragma unroll
   for (int s2 = 0; s2 < kRing; ++s2)
-    if (s2 < nbw) issue_batch<WPK>(ring + s2 * SLOTW, cbase, nb, gb, (first + s2 * stride) * kBatchKeys, n, lane);
+    if (s2 < nbw) issue_batch<WPK, QJL>(ring + s2 * SLOTW, cbase, nb, gb, (first + s2 * stride) * kBatchKeys, n, lane);
 
   // query-side operands (L2 resident)
   v8i A[T][C];
@@ -327,14 +331,19 @@ __global__ void __launch_bounds__(256) scores_kernel(const uint32_t* __restrict_
           for (int p = 0; p < W; ++p) w[p] = slot[(kk * GW + gg) * W + p];
         }
 #pragma unroll
-        for (int t = 0; t < T - 1; ++t) accM = mfma_fp8_fp4(A[t][c], bits_to_fp4(walsh_word<BP>(w, t)), accM);
-        accQ = mfma_fp8_fp4(A[T - 1][c], bits_to_fp4(w[BP]), accQ);
+        for (int t = 0; t < (1 << (BP - 1)); ++t)
+          accM = mfma_fp8_fp4(A[t][c], bits_to_fp4(walsh_word<BP>(w, t)), accM);
+        if constexpr (QJL) accQ = mfma_fp8_fp4(A[T - 1][c], bits_to_fp4(w[BP]), accQ);
       }
       pin(accM);
-      pin(accQ);
       const float mse = fmaf(accM[0], cs[2], fmaf(accM[1], cs[3], fmaf(accM[2], cs[4], fmaf(accM[3], cs[5], cs[0]))));
-      const float qjl = fmaf(accQ[0], cs[6], fmaf(accQ[1], cs[7], fmaf(accQ[2], cs[8], fmaf(accQ[3], cs[9], cs[1]))));
-      lout[qi * kBatchKeys + kk] = fmaf(lng[kk], mse, lng[kBatchKeys + kk] * qjl);
+      if constexpr (QJL) {
+        pin(accQ);
+        const float qjl = fmaf(accQ[0], cs[6], fmaf(accQ[1], cs[7], fmaf(accQ[2], cs[8], fmaf(accQ[3], cs[9], cs[1]))));
+        lout[qi * kBatchKeys + kk] = fmaf(lng[kk], mse, lng[kBatchKeys + kk] * qjl);
+      } else {
+        lout[qi * kBatchKeys + kk] = lng[kk] * mse;
+      }
     }
     __builtin_amdgcn_wave_barrier();
     {
@@ -357,14 +366,14 @@ __global__ void __launch_bounds__(256) scores_kernel(const uint32_t* __restrict_
     wait_lgkm0();
     __builtin_amdgcn_wave_barrier();
     if (i + kRing < nbw)
-      issue_batch<WPK>(slot, cbase, nb, gb, (first + static_cast<int64_t>(i + kRing) * stride) * kBatchKeys, n, lane);
+      issue_batch<WPK, QJL>(slot, cbase, nb, gb, (first + static_cast<int64_t>(i + kRing) * stride) * kBatchKeys, n, lane);
   }
 }
 
 int64_t scores_ws_bytes(const tq_quantizer* q, int B, int Hq, int Hkv) {
   const int G = Hq / Hkv;
   const int RT = (G + 3) / 4;
-  const int T = q->cb[0].nterms + 1;
+  const int T = key_terms(q);
   const int C = (q->d + 127) / 128;
   const int64_t groups = static_cast<int64_t>(B) * Hkv * RT;
   return groups * T * C * 2048 + groups * 4 * 16 * 4;
@@ -378,7 +387,7 @@ hipError_t launch_query_prep(const tq_quantizer* q, const void* queries, int q_d
   const size_t lds = sizeof(float) * (2 * q->d + q->m + 4 * (q->d + q->m));
   dim3 grid(static_cast<unsigned>(static_cast<int64_t>(B) * Hkv * RT * 4));
   hipLaunchKernelGGL(query_prep_kernel, grid, dim3(256), lds, st, queries, q_dtype, Hq, Hkv, G, RT, q->d, q->m, q->d_qt,
-                     q->cb[0], C, wsA, wsC);
+                     key_codebook(q), key_qjl(q) ? 1 : 0, C, wsA, wsC);
   return hipGetLastError();
 }
 
@@ -386,7 +395,7 @@ hipError_t launch_query_prep_ws(const tq_quantizer* q, const void* queries, int 
                                 void* ws, hipStream_t st) {
   const int G = Hq / Hkv;
   const int RT = (G + 3) / 4;
-  const int T = q->cb[0].nterms + 1;
+  const int T = key_terms(q);
   const int C = (q->d + 127) / 128;
   const int64_t groups = static_cast<int64_t>(B) * Hkv * RT;
   uint8_t* wsA = static_cast<uint8_t*>(ws);
@@ -398,7 +407,7 @@ hipError_t launch_scores_scan(const tq_quantizer* q, int B, int Hq, int Hkv, con
                               const float* gammas, int64_t n, float* out, const void* ws, hipStream_t st) {
   const int G = Hq / Hkv;
   const int RT = (G + 3) / 4;
-  const int T = q->cb[0].nterms + 1;
+  const int T = key_terms(q);
   const int C = (q->d + 127) / 128;
   const int64_t groups = static_cast<int64_t>(B) * Hkv * RT;
   const uint8_t* wsA = static_cast<const uint8_t*>(ws);
@@ -409,15 +418,18 @@ hipError_t launch_scores_scan(const tq_quantizer* q, int B, int Hq, int Hkv, con
   if (bx > need) bx = need;
   if (bx < 1) bx = 1;
   dim3 grid(static_cast<unsigned>(bx), static_cast<unsigned>(groups));
-  const int bp = q->cb[0].bp;
+  const int bp = key_codebook(q).bp;
+  const bool qjl = key_qjl(q);
   const int gw = (q->d + 31) / 32;
-#define TQ_SC(BPV, GWV)                                                                                          \
-  if (bp == BPV && gw == GWV) {                                                                                  \
-    hipLaunchKernelGGL((scores_kernel<BPV, GWV>), grid, dim3(256), 0, st, codes, norms, gammas, n, Hq, Hkv, G, RT, \
-                       wsA, wsC, out);                                                                           \
-    return hipGetLastError();                                                                                    \
+#define TQ_SC(BPV, GWV, QV)                                                                                       \
+  if (bp == BPV && gw == GWV && qjl == QV) {                                                                      \
+    hipLaunchKernelGGL((scores_kernel<BPV, GWV, QV>), grid, dim3(256), 0, st, codes, norms, gammas, n, Hq, Hkv, G, \
+                       RT, wsA, wsC, out);                                                                        \
+    return hipGetLastError();                                                                                     \
   }
-#define TQ_SC_ALL(GWV) TQ_SC(1, GWV) TQ_SC(2, GWV) TQ_SC(3, GWV)
+#define TQ_SC_ALL(GWV)                                                                                  \
+  TQ_SC(1, GWV, true) TQ_SC(2, GWV, true) TQ_SC(3, GWV, true) TQ_SC(1, GWV, false) TQ_SC(2, GWV, false) \
+  TQ_SC(3, GWV, false) TQ_SC(4, GWV, false)
   TQ_SC_ALL(1) TQ_SC_ALL(2) TQ_SC_ALL(3) TQ_SC_ALL(4) TQ_SC_ALL(5) TQ_SC_ALL(6) TQ_SC_ALL(7) TQ_SC_ALL(8)
 #undef TQ_SC_ALL
 #undef TQ_SC

@@ -131,7 +131,8 @@ int64_t topk_ws_bytes(const tq_quantizer* q, int B, int Hq, int Hkv, int64_t n, 
   return topk_prep_bytes(q, B, Hq, Hkv) + p.rg_count * p.slices * 16 * topk * 8 + 256;
 }
 
-template <int BP, int GW, int KK>
+// QJL: prod keys (with the QJL plane and gammas); without it MSE-only keys.
+template <int BP, int GW, int KK, bool QJL>
 __global__ void __launch_bounds__(256) topk_scan_kernel(const uint32_t* __restrict__ codes,
                                                         const float* __restrict__ norms,
                                                         const float* __restrict__ gammas, int64_t n, int RT,
@@ -139,8 +140,8 @@ __global__ void __launch_bounds__(256) topk_scan_kernel(const uint32_t* __restri
                                                         int64_t slice_keys, int topk, const uint8_t* __restrict__ wsA,
                                                         const float* __restrict__ wsC, float* __restrict__ cand_s,
                                                         int* __restrict__ cand_i) {
-  constexpr int T = (1 << (BP - 1)) + 1;
-  constexpr int W = BP + 1;
+  constexpr int T = (1 << (BP - 1)) + (QJL ? 1 : 0);
+  constexpr int W = BP + (QJL ? 1 : 0);
   constexpr int C = (GW + 3) / 4;
   constexpr int WPK = GW * W;                      // packed words per key
   constexpr int BW = kTopBlockKeys * WPK;          // words of a batch
@@ -187,14 +188,15 @@ __global__ void __launch_bounds__(256) topk_scan_kernel(const uint32_t* __restri
 
   const uint32_t* cbase = codes + seq * n * WPK;
   const float* nb = norms + seq * n;
-  const float* gb = gammas + seq * n;
+  const float* gb = QJL ? gammas + seq * n : nullptr;
   const int64_t k_begin = slice * slice_keys;
   const int64_t k_end = min(n, k_begin + slice_keys);
   const int nbat = static_cast<int>((k_end - k_begin + kTopBlockKeys - 1) / kTopBlockKeys);
 
   // batch bi of the slice goes HBM -> LDS by dword DMA (no registers, no
   // alignment assumptions); past the slice end the last valid word is re-read
-  const int wave_dma = (WPK + 3 - wave) / 4 + (wave >= 2 ? 1 : 0);   // DMA instructions per batch
+  // DMA instructions per batch: words round-robin, norms by wave 2, gammas by wave 3
+  const int wave_dma = (WPK + 3 - wave) / 4 + ((wave == 2 || (QJL && wave == 3)) ? 1 : 0);
   auto issue = [&](int bi, int slot) {
     const int64_t k0 = k_begin + static_cast<int64_t>(bi) * kTopBlockKeys;
     const int valid = static_cast<int>(min(k_end, k0 + kTopBlockKeys) - k0);
@@ -205,7 +207,7 @@ __global__ void __launch_bounds__(256) topk_scan_kernel(const uint32_t* __restri
       if (off >= valid * WPK) off = valid * WPK - 1;
       __builtin_amdgcn_global_load_lds(src + off, as_lds(dst + i * 64), 4, 0, 0);
     }
-    if (wave >= 2) {
+    if (wave == 2 || (QJL && wave == 3)) {
       const float* arr = wave == 2 ? nb : gb;
       int64_t t = k0 + lane;
       if (t >= k0 + valid) t = k0 + valid - 1;
@@ -250,14 +252,18 @@ __global__ void __launch_bounds__(256) topk_scan_kernel(const uint32_t* __restri
             for (int p = 0; p < W; ++p) w[p] = kw[(kk * GW + gg) * W + p];
           }
 #pragma unroll
-          for (int t = 0; t < T - 1; ++t) aM = mfma_fp8_fp4(A[t][c], bits_to_fp4(walsh_word<BP>(w, t)), aM);
-          aQ = mfma_fp8_fp4(A[T - 1][c], bits_to_fp4(w[BP]), aQ);
+          for (int t = 0; t < (1 << (BP - 1)); ++t)
+            aM = mfma_fp8_fp4(A[t][c], bits_to_fp4(walsh_word<BP>(w, t)), aM);
+          if constexpr (QJL) aQ = mfma_fp8_fp4(A[T - 1][c], bits_to_fp4(w[BP]), aQ);
         }
         pin(aM);
-        pin(aQ);
         const float mse = fmaf(aM[0], cs[2], fmaf(aM[1], cs[3], fmaf(aM[2], cs[4], fmaf(aM[3], cs[5], cs[0]))));
-        const float qjl = fmaf(aQ[0], cs[6], fmaf(aQ[1], cs[7], fmaf(aQ[2], cs[8], fmaf(aQ[3], cs[9], cs[1]))));
-        const float s = fmaf(kn[kk], mse, kn[kTopBlockKeys + kk] * qjl);
+        float s = kn[kk] * mse;
+        if constexpr (QJL) {
+          pin(aQ);
+          const float qjl = fmaf(aQ[0], cs[6], fmaf(aQ[1], cs[7], fmaf(aQ[2], cs[8], fmaf(aQ[3], cs[9], cs[1]))));
+          s = fmaf(kn[kk], mse, kn[kTopBlockKeys + kk] * qjl);
+        }
         const int key = static_cast<int>(k0) + kk;
         const bool ins = kk < nk && s >= tau && ranks_before(s, key, ls[KK - 1], li[KK - 1]);
         // wave-uniform gate: the insertion (selects over the whole list) only
@@ -311,7 +317,7 @@ hipError_t launch_topk(const tq_quantizer* q, const void* queries, int q_dtype, 
                        int64_t* out_idx, void* ws, hipStream_t st) {
   if (topk < 1 || topk > 32 || n >= 0x7fffffff) return hipErrorNotSupported;
   const TopkPlan p = topk_plan(B, Hq, Hkv, n);
-  const int T = q->cb[0].nterms + 1;
+  const int T = key_terms(q);
   const int Cc = (q->d + 127) / 128;
   const int64_t row_tiles = static_cast<int64_t>(B) * Hkv * p.RT;
   // whole rounds of 8 slices so that each XCD's workgroups share slices
@@ -323,23 +329,26 @@ hipError_t launch_topk(const tq_quantizer* q, const void* queries, int q_dtype, 
   const float* wsC = reinterpret_cast<const float*>(wsA + row_tiles * T * Cc * 2048);
   float* cs = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + topk_prep_bytes(q, B, Hq, Hkv));
   int* ci = reinterpret_cast<int*>(cs + p.rg_count * p.slices * 16 * topk);
-  const int bp = q->cb[0].bp;
+  const int bp = key_codebook(q).bp;
+  const bool qjl = key_qjl(q);
   const int gw = (q->d + 31) / 32;
   const bool big = topk > 16;
   bool launched = false;
-#define TQ_TK(BPV, GWV)                                                                                            \
-  if (!launched && bp == BPV && gw == GWV) {                                                                       \
-    if (big)                                                                                                       \
-      hipLaunchKernelGGL((topk_scan_kernel<BPV, GWV, 32>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,  \
-                         codes, norms, gammas, n, p.RT, p.rg_per_seq, p.rg_count, p.slices, p.slice_keys, topk, wsA, \
-                         wsC, cs, ci);                                                                             \
-    else                                                                                                           \
-      hipLaunchKernelGGL((topk_scan_kernel<BPV, GWV, 16>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,  \
-                         codes, norms, gammas, n, p.RT, p.rg_per_seq, p.rg_count, p.slices, p.slice_keys, topk, wsA, \
-                         wsC, cs, ci);                                                                             \
-    launched = true;                                                                                               \
+#define TQ_TK(BPV, GWV, QV)                                                                                          \
+  if (!launched && bp == BPV && gw == GWV && qjl == QV) {                                                            \
+    if (big)                                                                                                         \
+      hipLaunchKernelGGL((topk_scan_kernel<BPV, GWV, 32, QV>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, \
+                         codes, norms, gammas, n, p.RT, p.rg_per_seq, p.rg_count, p.slices, p.slice_keys, topk, wsA,   \
+                         wsC, cs, ci);                                                                               \
+    else                                                                                                             \
+      hipLaunchKernelGGL((topk_scan_kernel<BPV, GWV, 16, QV>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, \
+                         codes, norms, gammas, n, p.RT, p.rg_per_seq, p.rg_count, p.slices, p.slice_keys, topk, wsA,   \
+                         wsC, cs, ci);                                                                               \
+    launched = true;                                                                                                 \
   }
-#define TQ_TK_ALL(GWV) TQ_TK(1, GWV) TQ_TK(2, GWV) TQ_TK(3, GWV)
+#define TQ_TK_ALL(GWV)                                                                                  \
+  TQ_TK(1, GWV, true) TQ_TK(2, GWV, true) TQ_TK(3, GWV, true) TQ_TK(1, GWV, false) TQ_TK(2, GWV, false) \
+  TQ_TK(3, GWV, false) TQ_TK(4, GWV, false)
   TQ_TK_ALL(1) TQ_TK_ALL(2) TQ_TK_ALL(3) TQ_TK_ALL(4) TQ_TK_ALL(5) TQ_TK_ALL(6) TQ_TK_ALL(7) TQ_TK_ALL(8)
 #undef TQ_TK_ALL
 #undef TQ_TK

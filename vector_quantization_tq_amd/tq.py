@@ -16,14 +16,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtq.so")
 
 TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EHIP, TQ_ENOMEM, TQ_EWORKSPACE = 0, -1, -2, -3, -4, -5
-TQ_PROD, TQ_MSE = 0, 1
+TQ_PROD, TQ_MSE, TQ_MSE_KEYS = 0, 1, 2
 TQ_F32, TQ_BF16 = 0, 1
 
 EXPORTS = [
     "tq_version", "tq_last_error", "tq_host_normals", "tq_host_rotation", "tq_host_qjl_matrix", "tq_host_codebook",
-    "tq_make_quantizer", "tq_free_quantizer", "tq_quantizer_info", "tq_code_words", "tq_encode", "tq_decode",
-    "tq_scores_workspace_bytes", "tq_query_prep", "tq_scores_from_prep", "tq_scores", "tq_attend_workspace_bytes",
-    "tq_attend_decode",
+    "tq_make_quantizer", "tq_free_quantizer", "tq_quantizer_info", "tq_set_key_mode", "tq_code_words", "tq_encode",
+    "tq_decode", "tq_scores_workspace_bytes", "tq_query_prep", "tq_scores_from_prep", "tq_scores",
+    "tq_attend_workspace_bytes", "tq_attend_decode",
 ]
 
 
@@ -56,6 +56,7 @@ def lib() -> ctypes.CDLL:
         "tq_make_quantizer": (c_p, [c_i, c_i, c_u64]),
         "tq_free_quantizer": (None, [c_p]),
         "tq_quantizer_info": (c_i, [c_p, ctypes.POINTER(c_i), ctypes.POINTER(c_i), ctypes.POINTER(c_i)]),
+        "tq_set_key_mode": (c_i, [c_p, c_i]),
         "tq_code_words": (c_i64, [c_p, c_i, c_i64, c_i64]),
         "tq_encode": (c_i, [c_p, c_i, c_p, c_i, c_i64, c_i64, c_p, c_p, c_p, c_p]),
         "tq_decode": (c_i, [c_p, c_i, c_p, c_p, c_p, c_i64, c_i64, c_p, c_p]),
@@ -156,6 +157,12 @@ class Quantizer:
         dd, bb, mm = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
         _check(L.tq_quantizer_info(self._h, ctypes.byref(dd), ctypes.byref(bb), ctypes.byref(mm)))
         self.d, self.bits, self.m, self.seed = dd.value, bb.value, mm.value, seed
+        self.key_mode = TQ_PROD
+
+    def set_key_mode(self, key_mode: int):
+        """TQ_PROD or TQ_MSE_KEYS: the key encoding the scoring calls read."""
+        _check(lib().tq_set_key_mode(self._h, key_mode))
+        self.key_mode = key_mode
 
     @property
     def handle(self):
