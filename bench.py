@@ -58,7 +58,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gqa", choices=["gqa", "long", "decode", "search"])
-    ap.add_argument("--bits", type=int, default=None, help="bits for the decode/search workloads (default 3 / 4)")
+    ap.add_argument("--bits", type=int, default=None,
+                    help="key bits (default: gqa 3, long 4, decode 3, search 4)")
+    ap.add_argument("--key-mode", default="prod", choices=["prod", "mse"],
+                    help="gqa/long: prod keys (b-1 MSE bits + QJL) or MSE-only keys (all b bits to the index)")
+    ap.add_argument("--value-bits", type=int, default=None, help="gqa/long: value bits (default: the key bits)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a 256 MiB device copy 3 times (the known-size kernel for counter scaling)")
@@ -210,14 +214,20 @@ def run_gqa(args, torch, dev, tq, wl_fn, name, bits, n_tail=0):
     v = v_all[:, :n_comp].contiguous()
     k_tail = k_all[:, n_comp:].contiguous().view(B, Hkv, n_tail, d) if n_tail else None
     v_tail = v_all[:, n_comp:].contiguous().view(B, Hkv, n_tail, d) if n_tail else None
+    mse_keys = args.key_mode == "mse"
+    kmode = tq.TQ_MSE_KEYS if mse_keys else tq.TQ_PROD
+    vbits = args.value_bits or bits
     qz = tq.Quantizer(d, bits, 0)
+    if mse_keys:
+        qz.set_key_mode(tq.TQ_MSE_KEYS)
+    qv = qz if vbits == bits else tq.Quantizer(d, vbits, 0)
     nseq = B * Hkv
     copies = []
     for _ in range(2):
-        ck = torch.empty(qz.code_words(tq.TQ_PROD, nseq, n_comp), dtype=torch.int32, device=dev)
+        ck = torch.empty(qz.code_words(kmode, nseq, n_comp), dtype=torch.int32, device=dev)
         kn = torch.empty(nseq * n_comp, dtype=torch.float32, device=dev)
-        kg = torch.empty(nseq * n_comp, dtype=torch.float32, device=dev)
-        cv = torch.empty(qz.code_words(tq.TQ_MSE, nseq, n_comp), dtype=torch.int32, device=dev)
+        kg = None if mse_keys else torch.empty(nseq * n_comp, dtype=torch.float32, device=dev)
+        cv = torch.empty(qv.code_words(tq.TQ_MSE, nseq, n_comp), dtype=torch.int32, device=dev)
         vn = torch.empty(nseq * n_comp, dtype=torch.float32, device=dev)
         copies.append((ck, kn, kg, cv, vn))
     logits = torch.empty((B, Hq, n_comp), dtype=torch.float32, device=dev)
@@ -225,18 +235,18 @@ def run_gqa(args, torch, dev, tq, wl_fn, name, bits, n_tail=0):
     ws_s = torch.empty(tq.scores_workspace_bytes(qz, B, Hq, Hkv, n_comp), dtype=torch.uint8, device=dev)
     attend_ok = True
     try:
-        ws_a = torch.empty(max(tq.attend_workspace_bytes(qz, qz, B, Hq, Hkv, n_comp, n_tail), 256), dtype=torch.uint8,
+        ws_a = torch.empty(max(tq.attend_workspace_bytes(qz, qv, B, Hq, Hkv, n_comp, n_tail), 256), dtype=torch.uint8,
                            device=dev)
     except Exception:
         attend_ok = False
     # fill both copies once
     for c in copies:
-        tq.tq_encode(qz, tq.TQ_PROD, k, out=(c[0], c[1], c[2]))
-        tq.tq_encode(qz, tq.TQ_MSE, v, out=(c[3], c[4], None))
+        tq.tq_encode(qz, kmode, k, out=(c[0], c[1], c[2]))
+        tq.tq_encode(qv, tq.TQ_MSE, v, out=(c[3], c[4], None))
     if attend_ok:
         try:
             c = copies[0]
-            tq.tq_attend_decode(qz, qz, q, c[0], c[1], c[2], c[3], c[4], Hkv, n_comp, k_tail, v_tail, 0.0, out=out,
+            tq.tq_attend_decode(qz, qv, q, c[0], c[1], c[2], c[3], c[4], Hkv, n_comp, k_tail, v_tail, 0.0, out=out,
                                 workspace=ws_a)
         except tq.TQError:
             attend_ok = False
@@ -248,16 +258,16 @@ def run_gqa(args, torch, dev, tq, wl_fn, name, bits, n_tail=0):
         w = copies[i % 2]          # written now
         r = copies[(i + 1) % 2]    # written one step ago
         e0 = timer.mark()
-        tq.tq_encode(qz, tq.TQ_PROD, k, out=(w[0], w[1], w[2]))
+        tq.tq_encode(qz, kmode, k, out=(w[0], w[1], w[2]))
         e1 = timer.mark()
-        tq.tq_encode(qz, tq.TQ_MSE, v, out=(w[3], w[4], None))
+        tq.tq_encode(qv, tq.TQ_MSE, v, out=(w[3], w[4], None))
         e2 = timer.mark()
         tq.tq_query_prep(qz, q, Hkv, workspace=ws_s)
         e3 = timer.mark()
         tq.tq_scores_from_prep(qz, B, Hq, Hkv, r[0], r[1], r[2], n_comp, ws_s, out=logits)
         e4 = timer.mark()
         if attend_ok:
-            tq.tq_attend_decode(qz, qz, q, r[0], r[1], r[2], r[3], r[4], Hkv, n_comp, k_tail, v_tail, 0.0, out=out,
+            tq.tq_attend_decode(qz, qv, q, r[0], r[1], r[2], r[3], r[4], Hkv, n_comp, k_tail, v_tail, 0.0, out=out,
                                 workspace=ws_a)
         e5 = timer.mark()
         if timed:
@@ -279,14 +289,15 @@ def run_gqa(args, torch, dev, tq, wl_fn, name, bits, n_tail=0):
     timer.collect()
 
     nkeys = nseq * n_comp
-    rec_k = 4 * ((d + 31) // 32) * bits + 8          # packed key bytes per key (codes + norm + gamma)
-    rec_v = (bits * d) // 8 + 4                       # packed value bytes per token (codes + norm)
+    # packed key bytes per key: codes + norm (+ gamma for prod keys)
+    rec_k = 4 * ((d + 31) // 32) * bits + (4 if mse_keys else 8)
+    rec_v = (vbits * d) // 8 + 4                      # packed value bytes per token (codes + norm)
     G = Hq // Hkv
     scores_ms = timer.avg_ms("scores")
     scores_alg = nkeys * (rec_k + 4 * G)              # read packed keys, write fp32 logits
     packed_gbs = nkeys * rec_k / (scores_ms * 1e-3) / 1e9
     enc_ms = timer.avg_ms("encode_keys")
-    enc_flop = nkeys * 4.0 * d * d                    # Pi x and S' rho per key
+    enc_flop = nkeys * (2.0 if mse_keys else 4.0) * d * d   # Pi x (and S' rho for prod keys) per key
     res = {
         "metric": METRIC,
         "value": round(packed_gbs, 1),
@@ -301,7 +312,8 @@ def run_gqa(args, torch, dev, tq, wl_fn, name, bits, n_tail=0):
         "dtype": "u8",
         "data": "synthetic",
         "config": {"workload": name, "batch": B, "kv_heads": Hkv, "q_heads": Hq, "tokens": N, "tail_bf16": n_tail,
-                   "d": d, "bits_keys": bits, "bits_values": bits, "key_mode": "prod (b-1 MSE + 1 QJL)",
+                   "d": d, "bits_keys": bits, "bits_values": vbits,
+                   "key_mode": "mse-only (b MSE bits)" if mse_keys else "prod (b-1 MSE + 1 QJL)",
                    "value_mode": "mse"},
         "packed_pct_of_hbm_peak": round(100 * packed_gbs / HBM_PEAK_GBS, 1),
         "encode_keys_per_s": round(nkeys / (enc_ms * 1e-3), 0),
@@ -313,21 +325,22 @@ def run_gqa(args, torch, dev, tq, wl_fn, name, bits, n_tail=0):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(scores_alg / (scores_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic() if name.startswith("gqa") else None,
+            "traffic": measured_traffic() if name.startswith("gqa") and not mse_keys else None,
             "algorithmic_bytes_per_launch": scores_alg,
             "bytes_per_key": rec_k + 4 * G,
         },
         "roofline_encode": {
-            "kernel": "encode_tile_kernel (tq_encode, prod)",
+            "kernel": "encode_tile_kernel (tq_encode, %s)" % ("mse keys" if mse_keys else "prod"),
             "bound": "mfma",
             "achieved": round(enc_flop / (enc_ms * 1e-3) / 1e12, 2),
             "peak": FP16_MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(enc_flop / (enc_ms * 1e-3) / 1e12 / FP16_MFMA_PEAK_TFLOPS, 4),
-            "flop_per_key": 4 * d * d,
-            "note": "algorithmic 4d^2 flop per key; the fp16 MFMA runs hi/lo split operands, 2 products per "
-                    "rotation term (bf16 keys) and 3 per QJL term, i.e. 2.5x the algorithmic flop",
-            "issued_frac": round(2.5 * enc_flop / (enc_ms * 1e-3) / 1e12 / FP16_MFMA_PEAK_TFLOPS, 4),
+            "flop_per_key": (2 if mse_keys else 4) * d * d,
+            "note": "algorithmic flop per key (4d^2 prod, 2d^2 mse keys); the fp16 MFMA runs hi/lo split operands, "
+                    "2 products per rotation term (bf16 keys) and 3 per QJL term",
+            "issued_frac": round((2.0 if mse_keys else 2.5) * enc_flop / (enc_ms * 1e-3) / 1e12
+                                 / FP16_MFMA_PEAK_TFLOPS, 4),
         },
     }
     if attend_ok:
@@ -489,12 +502,14 @@ def main():
     if args.copy_calibration:
         copy_calibration(torch, dev)
     if args.workload == "gqa":
-        res, wl = run_gqa(args, torch, dev, tq, W.gqa_layer, "gqa-decode-layer b8 kv8 q32 n32768 d128 3-bit", 3)
-        if not args.no_cpu_baseline:
+        bits = args.bits or 3
+        res, wl = run_gqa(args, torch, dev, tq, W.gqa_layer, f"gqa-decode-layer b8 kv8 q32 n32768 d128 {bits}-bit", bits)
+        if not args.no_cpu_baseline and args.key_mode == "prod" and bits == 3 and not args.value_bits:
             res["cpu_baseline"] = cpu_baseline_gqa(wl, args.steps)
     elif args.workload == "long":
-        res, wl = run_gqa(args, torch, dev, tq, W.long_context, "long-context b1 kv8 q32 n131072 tail256 d128 4-bit", 4,
-                          n_tail=256)
+        bits = args.bits or 4
+        res, wl = run_gqa(args, torch, dev, tq, W.long_context,
+                          f"long-context b1 kv8 q32 n131072 tail256 d128 {bits}-bit", bits, n_tail=256)
     elif args.workload == "decode":
         res = run_decode(args, torch, dev, tq, W)
     else:

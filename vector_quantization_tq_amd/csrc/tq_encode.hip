@@ -310,7 +310,9 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
   __shared__ float part2[4][kEncRows];
   __shared__ uint32_t ost[2][1024];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  static_assert(KS == 4, "four waves own 32 coordinates each");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
   const int r16 = lane & 15, q = lane >> 4;
   constexpr int bp = BP;
   constexpr int NT = (1 << BP) - 1;      // thresholds
@@ -359,12 +361,30 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
   constexpr int esz = LK == 1 ? 2 : 4;
   const int CH = d * esz / 16;           // 16-byte chunks per row (vector paths)
   uint4 pre[PREN];
-  auto tile_of = [&](int64_t t, int64_t& seq, int64_t& v0, int& rows) {
-    seq = t / tps;
-    v0 = (t - seq * tps) * kEncRows;
+  // tile t = seq * tps + r; the loop steps t by the grid size, so the next
+  // tile's (seq, r) comes from the current one without a division in the
+  // common cases
+  struct TileAt { int64_t seq, r; };
+  auto advance = [&](TileAt a) {
+    a.r += gridDim.x;
+    if (a.r >= tps) {
+      if (a.r < 2 * tps) {
+        a.r -= tps;
+        ++a.seq;
+      } else {
+        const int64_t k = a.r / tps;
+        a.seq += k;
+        a.r -= k * tps;
+      }
+    }
+    return a;
+  };
+  auto tile_of = [&](TileAt a, int64_t& seq, int64_t& v0, int& rows) {
+    seq = a.seq;
+    v0 = a.r * kEncRows;
     rows = static_cast<int>(min(static_cast<int64_t>(kEncRows), n - v0));
   };
-  auto fetch = [&](int64_t t) {
+  auto fetch = [&](TileAt t) {
     if constexpr (LK != 0) {
       int64_t seq, v0;
       int rows;
@@ -374,12 +394,13 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
 #pragma unroll
       for (int j = 0; j < PREN; ++j) {
         const int c = part + 4 * j;
+        pre[j] = make_uint4(0u, 0u, 0u, 0u);   // rows past n and chunks past d read as 0
         if (lrow < rows && c < CH) pre[j] = src[c];
       }
     }
   };
   // element e of this thread's share of the row (column col(e)), as float
-  auto commit = [&](int64_t t, float* scl, float* nrm) {
+  auto commit = [&](TileAt t, float* scl, float* nrm) {
     int64_t seq, v0;
     int rows;
     tile_of(t, seq, v0, rows);
@@ -393,8 +414,8 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
         const uint32_t u[4] = {pre[j].x, pre[j].y, pre[j].z, pre[j].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          v[8 * j + 2 * e] = (lrow < rows && c < CH) ? __uint_as_float(u[e] << 16) : 0.f;
-          v[8 * j + 2 * e + 1] = (lrow < rows && c < CH) ? __uint_as_float(u[e] & 0xFFFF0000u) : 0.f;
+          v[8 * j + 2 * e] = __uint_as_float(u[e] << 16);
+          v[8 * j + 2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
           cols[8 * j + 2 * e] = 8 * c + 2 * e;
           cols[8 * j + 2 * e + 1] = 8 * c + 2 * e + 1;
         }
@@ -407,7 +428,7 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
         const uint32_t u[4] = {pre[j].x, pre[j].y, pre[j].z, pre[j].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          v[4 * j + e] = (lrow < rows && c < CH) ? __uint_as_float(u[e]) : 0.f;
+          v[4 * j + e] = __uint_as_float(u[e]);
           cols[4 * j + e] = 4 * c + e;
         }
       }
@@ -465,7 +486,7 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
       scl[lrow] = nv > 0.f ? ldexpf(1.f / nv, -(sig + 8)) : 0.f;
     }
   };
-  auto store = [&](int64_t t, int buf) {
+  auto store = [&](TileAt t, int buf) {
     int64_t seq, v0;
     int rows;
     tile_of(t, seq, v0, rows);
@@ -529,24 +550,29 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
   };
   // row sum over the 16 lanes of a row of the C layout (one DPP row)
   auto sum16 = [&](float v) { return row_sum16(v); };
+  // lanes whose coordinate exists (token-major layouts): 32w + 16ct + r16 < d
+  const uint64_t okm0 = __ballot(32 * w + r16 < d), okm1 = __ballot(32 * w + 16 + r16 < d);
 
   int64_t t = blockIdx.x;
-  if (t < total) fetch(t);
+  TileAt cur = {static_cast<int64_t>(blockIdx.x) / tps, static_cast<int64_t>(blockIdx.x) % tps}, prev = cur;
+  if (t < total) fetch(cur);
   __syncthreads();   // zero fill done before the first commit
   int it = 0;
   for (; t < total; t += gridDim.x, ++it) {
     const int buf = it & 1;
     float* scl = scl2[buf];
     float* nrm = nrm2[buf];
-    commit(t, scl, nrm);
-    const int64_t tn = t + gridDim.x;
-    if (tn < total) fetch(tn);   // in flight while this tile is encoded
+    commit(cur, scl, nrm);
+    const TileAt nxt = advance(cur);
+    if (t + gridDim.x < total) fetch(nxt);   // in flight while this tile is encoded
     __syncthreads();
-    if (it > 0) store(t - gridDim.x, buf ^ 1);
+    if (it > 0) store(prev, buf ^ 1);
 
     int64_t seq, v0;
     int rows;
-    tile_of(t, seq, v0, rows);
+    tile_of(cur, seq, v0, rows);
+    prev = cur;
+    cur = nxt;
 
     if constexpr (PROD) {
 #pragma unroll 1
@@ -565,45 +591,46 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
           for (int i = 0; i < 4; ++i) {
             const float sc = scl[vbase + i];
             const float scS = sc * kRhoScale;
-            bool pos[2], jb[2][BP > 1 ? BP - 1 : 1];
+            // lane masks of the sign and the magnitude bits, taken as soon as
+            // each is decided (no per-lane booleans kept alive)
+            uint64_t ms[2], mj[2][BP > 1 ? BP - 1 : 1];
             float r2 = 0.f;
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct) {
               const int c = 32 * w + 16 * ct + r16;
               const float a = acc[h2][ct][i];
-              classify(a * sc, pos[ct], jb[ct]);
+              bool pos, jb[BP > 1 ? BP - 1 : 1];
+              classify(a * sc, pos, jb);
+              ms[ct] = __ballot(pos);
+#pragma unroll
+              for (int p = 0; p + 1 < BP; ++p) mj[ct][p] = __ballot(jb[p]);
               if constexpr (QJL) {
                 // rho * 2^14 = y 2^14 - c[idx] 2^14 in one rounding
                 float cabs;
-                if constexpr (BP > 1) cabs = pick_centroid<BP - 1>(cenS, jb[ct]);
+                if constexpr (BP > 1) cabs = pick_centroid<BP - 1>(cenS, jb);
                 else cabs = cenS[0];
-                const float rs = c < d ? fmaf(a, scS, pos[ct] ? -cabs : cabs) : 0.f;
+                const float rs = c < d ? fmaf(a, scS, pos ? -cabs : cabs) : 0.f;
                 r2 = fmaf(rs, rs, r2);
-                if (c < KP) {
-                  const _Float16 hh = static_cast<_Float16>(rs);
-                  rh[(vbase + i) * LDH + c] = hh;
-                  rl[(vbase + i) * LDH + c] = static_cast<_Float16>(rs - static_cast<float>(hh));
-                }
+                const _Float16 hh = static_cast<_Float16>(rs);   // c < KP: four waves of 32
+                rh[(vbase + i) * LDH + c] = hh;
+                rl[(vbase + i) * LDH + c] = static_cast<_Float16>(rs - static_cast<float>(hh));
               }
             }
-            if (w < G) {
-              const bool ok0 = 32 * w + r16 < d, ok1 = 32 * w + 16 + r16 < d;
-              {
-                const uint64_t m0 = __ballot(pos[0] && ok0);
-                const uint64_t m1 = __ballot(pos[1] && ok1);
-                if (r16 == 0) ost[buf][(vbase + i) * WPK + w * W + BP - 1] = halves(m0, m1);
-              }
+            // plane words: the sign plane is [y > 0], the low planes are
+            // [bit of j == sign] (complemented for y <= 0)
+            uint32_t wd[BP];
+            const uint64_t s0 = ms[0] & okm0, s1 = ms[1] & okm1;
+            wd[BP - 1] = halves(s0, s1);
 #pragma unroll
-              for (int p = 0; p + 1 < BP; ++p) {
-                const uint64_t m0 = __ballot((jb[0][p] == pos[0]) && ok0);
-                const uint64_t m1 = __ballot((jb[1][p] == pos[1]) && ok1);
-                if (r16 == 0) ost[buf][(vbase + i) * WPK + w * W + p] = halves(m0, m1);
-              }
-            }
+            for (int p = 0; p + 1 < BP; ++p) wd[p] = halves(~(mj[0][p] ^ s0) & okm0, ~(mj[1][p] ^ s1) & okm1);
             // partial ||rho||^2 (x 2^28) over this wave's 32 coordinates
-            if constexpr (QJL) {
-              r2 = sum16(r2);
-              if (r16 == 0) part2[w][vbase + i] = r2;
+            if constexpr (QJL) r2 = sum16(r2);
+            if (r16 == 0) {
+              if (w < G) {
+#pragma unroll
+                for (int p = 0; p < BP; ++p) ost[buf][(vbase + i) * WPK + w * W + p] = wd[p];
+              }
+              if constexpr (QJL) part2[w][vbase + i] = r2;
             }
           }
         }
@@ -621,16 +648,23 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
           contract(rh, bSl, h, false, acc);
           pin_acc(acc);
           if (w < G) {
+            uint32_t wd[2][4];
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
               const int vbase = 32 * h + 16 * h2 + 4 * q;
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
-                const bool zero = !(nrm[vbase + i] > 0.f);
-                const uint64_t m0 = __ballot((32 * w + r16 < d) && (acc[h2][0][i] >= 0.f || zero));
-                const uint64_t m1 = __ballot((32 * w + 16 + r16 < d) && (acc[h2][1][i] >= 0.f || zero));
-                if (r16 == 0) ost[buf][(vbase + i) * WPK + w * W + bp] = halves(m0, m1);
+                const uint64_t zm = __ballot(!(nrm[vbase + i] > 0.f));   // zero vectors: all bits 1
+                const uint64_t m0 = (__ballot(acc[h2][0][i] >= 0.f) | zm) & okm0;
+                const uint64_t m1 = (__ballot(acc[h2][1][i] >= 0.f) | zm) & okm1;
+                wd[h2][i] = halves(m0, m1);
               }
+            }
+            if (r16 == 0) {
+#pragma unroll
+              for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ost[buf][(32 * h + 16 * h2 + 4 * q + i) * WPK + w * W + bp] = wd[h2][i];
             }
           }
         }
@@ -655,7 +689,7 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
         pin_acc(acc);
         // lane holds coordinate 32w + 16ct + 4q + i, token 32h + 16h2 + r16
         const float sc0 = scl[32 * h + r16], sc1 = scl[32 * h + 16 + r16];
-        const bool tok0 = 32 * h + r16 < rows, tok1 = 32 * h + 16 + r16 < rows;
+        const uint64_t tm0 = __ballot(32 * h + r16 < rows), tm1 = __ballot(32 * h + 16 + r16 < rows);
         if (w < G) {
 #pragma unroll
           for (int ct = 0; ct < 2; ++ct)
@@ -665,12 +699,12 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
               bool p0, p1, j0[BP > 1 ? BP - 1 : 1], j1[BP > 1 ? BP - 1 : 1];
               classify(acc[0][ct][i] * sc0, p0, j0);
               classify(acc[1][ct][i] * sc1, p1, j1);
+              // sign plane [y > 0]; low planes [bit of j == sign]; padding tokens 0
+              const uint64_t s0 = __ballot(p0) & tm0, s1 = __ballot(p1) & tm1;
 #pragma unroll
               for (int p = 0; p < BP; ++p) {
-                const bool c0b = p == BP - 1 ? p0 : (j0[p < BP - 1 ? p : 0] == p0);
-                const bool c1b = p == BP - 1 ? p1 : (j1[p < BP - 1 ? p : 0] == p1);
-                const uint64_t m0 = __ballot(c0b && tok0);
-                const uint64_t m1 = __ballot(c1b && tok1);
+                const uint64_t m0 = p == BP - 1 ? s0 : ~(__ballot(j0[p < BP - 1 ? p : 0]) ^ s0) & tm0;
+                const uint64_t m1 = p == BP - 1 ? s1 : ~(__ballot(j1[p < BP - 1 ? p : 0]) ^ s1) & tm1;
                 if (r16 == 0 && c < d) ost[buf][(h * bp + p) * d + c] = halves(m0, m1);
               }
             }
@@ -681,7 +715,7 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
     }
   }
   __syncthreads();
-  if (it > 0) store(t - gridDim.x, (it - 1) & 1);
+  if (it > 0) store(prev, (it - 1) & 1);
 }
 
 // Decode: one workgroup per 8 vectors; plain fp32 FMAs (not on the hot path).
