@@ -163,7 +163,10 @@ __device__ __forceinline__ void attend_chunk_body(
   }
 
   // running softmax state of query `wave` (softmax phase), uniform over that wave
-  float m_run = -INFINITY, l_run = 0.f, w_run = 0.f;
+  // m_run: running max logit; wmax: largest weight p n so far (relative to
+  // m_run), which sets the limb exponent e_run; the sums of p and of the
+  // quantised weights stay per lane and are reduced once at the end
+  float m_run = -INFINITY, wmax = 0.f, l_lane = 0.f, w_lane = 0.f;
   int e_run = 0;
   // value accumulators: [Walsh term][column tile of this wave]; rows 4q+limb, column 16ct+j
   v4f acc[NV][2];
@@ -207,6 +210,7 @@ __device__ __forceinline__ void attend_chunk_body(
     if (t0 + P * kStep < c1) issue(t0 + P * kStep, buf == 0 ? NSLOT - 1 : buf - 1);
     const uint32_t* sl = stage[buf];
     const float* kns = reinterpret_cast<const float*>(sl + KW + VW);
+    const int live = static_cast<int>(min(static_cast<int64_t>(kStep), c1 - t0));   // tokens of the step in the chunk
     // ---------------- K phase: logits of tokens t0 + 32*wave .. +31 ----------------
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -227,7 +231,7 @@ __device__ __forceinline__ void attend_chunk_body(
         logit = fmaf(kns[tt], mse, kns[kStep + tt] * qjl);
       }
       float s = -INFINITY;
-      if (t0 + tt < c1) s = logit * scale_log2;
+      if (tt < live) s = logit * scale_log2;
       sc[qi][tt] = s;
     }
     __syncthreads();
@@ -235,20 +239,24 @@ __device__ __forceinline__ void attend_chunk_body(
     {
       const int q = wave;
       const float sa = sc[q][tA], sb = sc[q][tB];
-      const float mx = wave_max(fmaxf(sa, sb));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = exp2f(m_run - m_new);   // 0 on the first step
-      const float pa = exp2f(sa - m_new), pb = exp2f(sb - m_new);
+      // the max is reduced over the wave only when some logit exceeds it
+      float m_new = m_run;
+      if (__ballot(sa > m_run || sb > m_run) != 0ull) m_new = fmaxf(m_run, wave_max(fmaxf(sa, sb)));
+      const float alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first step
+      const float pa = __builtin_amdgcn_exp2f(sa - m_new), pb = __builtin_amdgcn_exp2f(sb - m_new);
       const float* vns = kns + 2 * kStep;
-      const float na = (t0 + tA < c1) ? vns[tA] : 0.f;
-      const float nb2 = (t0 + tB < c1) ? vns[tB] : 0.f;
+      const float na = tA < live ? vns[tA] : 0.f;
+      const float nb2 = tB < live ? vns[tB] : 0.f;
       const float wa = pa * na, wb = pb * nb2;
-      const float ps = wave_sum(pa + pb);
-      const float wm = wave_max(fmaxf(wa, wb));
-      l_run = fmaf(l_run, alpha, ps);
+      l_lane = fmaf(l_lane, alpha, pa + pb);
       m_run = m_new;
-      // the A values are w / (fp4 slot value >= 0.5): 2 * max lands in [8, 16)
-      const int e_new = wm > 0.f ? 3 - ilogbf(2.f * wm) : e_run;
+      // the limb exponent follows the running max weight, so the accumulator
+      // rescale alpha 2^(e_new - e_run) stays bounded (about 2 at most) and is
+      // exactly 1 in steps that set no new maximum
+      wmax *= alpha;
+      if (__ballot(wa > wmax || wb > wmax) != 0ull) wmax = fmaxf(wmax, wave_max(fmaxf(wa, wb)));
+      // the A values are w / (fp4 slot value >= 0.5): 2 * wmax lands in [8, 16)
+      const int e_new = wmax > 0.f ? 3 - ilogb_pos(2.f * wmax) : e_run;
       if (lane == 0) {
         qst[q][0] = ldexpf(alpha, e_new - e_run);   // accumulator rescale for this query
         qst[q][1] = static_cast<float>(e_new);
@@ -260,13 +268,15 @@ __device__ __forceinline__ void attend_chunk_body(
       float qa, qb;
       const uint32_t la = fixed_limbs4(ldexpf(wa * a_inv, e_new), qa);
       const uint32_t lb = fixed_limbs4(ldexpf(wb * a_inv, e_new), qb);
-      const float wq_sum = ldexpf(qa + qb, -e_new) * a_slot;
-      uint8_t* avb = reinterpret_cast<uint8_t*>(av) + 4 * q * 32 + a_off;
-#pragma unroll
-      for (int lb2 = 0; lb2 < 4; ++lb2)
-        *reinterpret_cast<uint16_t*>(avb + lb2 * 32) =
-            static_cast<uint16_t>(((la >> (8 * lb2)) & 0xFFu) | (((lb >> (8 * lb2)) & 0xFFu) << 8));
-      w_run = fmaf(w_run, alpha, wave_sum(wq_sum));
+      w_lane = fmaf(w_lane, alpha, ldexpf(qa + qb, -e_new) * a_slot);
+      // limb k of tokens tA and tB are adjacent bytes: one 16-bit write per limb
+      const uint32_t p01 = __builtin_amdgcn_perm(lb, la, 0x05010400u);   // la0 lb0 la1 lb1
+      const uint32_t p23 = __builtin_amdgcn_perm(lb, la, 0x07030602u);   // la2 lb2 la3 lb3
+      uint16_t* avh = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(av) + 4 * q * 32 + a_off);
+      avh[0] = static_cast<uint16_t>(p01);
+      avh[16] = static_cast<uint16_t>(p01 >> 16);
+      avh[32] = static_cast<uint16_t>(p23);
+      avh[48] = static_cast<uint16_t>(p23 >> 16);
     }
     __syncthreads();
     // ---------------- V phase: wave owns coordinates 32*wave .. +31 ----------------
@@ -274,10 +284,12 @@ __device__ __forceinline__ void attend_chunk_body(
       const v8i A = *reinterpret_cast<const v8i*>(av + lane * 8);
       const float rs = qst[qi][0];
       e_acc = static_cast<int>(qst[qi][1]);
+      if (__ballot(rs != 1.f) != 0ull) {
 #pragma unroll
-      for (int t = 0; t < NV; ++t) {
-        acc[t][0] *= rs;
-        acc[t][1] *= rs;
+        for (int t = 0; t < NV; ++t) {
+          acc[t][0] *= rs;
+          acc[t][1] *= rs;
+        }
       }
       // lane group g reads the 32-token block g of the step; blocks past the
       // end hold re-read words, which meet zero weights
@@ -302,10 +314,13 @@ __device__ __forceinline__ void attend_chunk_body(
   // value part: sum_t w_t c[idx] = sum_S coef_S (2 sum_t w_t b_S - sum_t w_t);
   // the softmax state of query q lives in wave q: publish it
   __syncthreads();
-  if (lane == 0) {
-    qst[wave][2] = w_run;
-    qst[wave][3] = l_run;
-    qst[wave][0] = m_run;
+  {
+    const float w_run = wave_sum(w_lane), l_run = wave_sum(l_lane);
+    if (lane == 0) {
+      qst[wave][2] = w_run;
+      qst[wave][3] = l_run;
+      qst[wave][0] = m_run;
+    }
   }
   __syncthreads();
   const float wq = qst[qi][2];

@@ -104,6 +104,10 @@ __device__ __forceinline__ lds_ptr_t* as_lds(const void* p) {
   return reinterpret_cast<lds_ptr_t*>(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)));
 }
 
+// floor(log2 x) for finite x > 0 (normal or subnormal), from the exponent
+// field the hardware extracts (x = m 2^e with m in [0.5, 1))
+__device__ __forceinline__ int ilogb_pos(float x) { return __builtin_amdgcn_frexp_expf(x) - 1; }
+
 // value of a set bit at element slot s = (K % 32) / 8
 __host__ __device__ __forceinline__ float fp4_slot_value(int s) { return s == 0 ? 0.5f : (s == 1 ? 1.f : 2.f); }
 

@@ -454,7 +454,7 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
     mx = fmaxf(mx, __shfl_xor(mx, 1));
     mx = fmaxf(mx, __shfl_xor(mx, 2));
     // power-of-two row scale putting the largest element in [2^14, 2^15)
-    const int sig = mx > 0.f ? 14 - ilogbf(mx) : 0;
+    const int sig = mx > 0.f ? 14 - ilogb_pos(mx) : 0;
     _Float16* hr = xh + lrow * LDH;
     _Float16* lr = xl + lrow * LDH;
     if constexpr (LK == 1) {
