@@ -131,3 +131,31 @@ def test_attend_asymmetric_bits(kbits, vbits):
     k, v, q = _gqa_inputs(1, 4, 16, 2000, 128, seed=kbits * 10 + vbits)
     w = _run_case(k, v, q, 1, 4, 16, 1900, 100, kbits, vbits=vbits)
     print("worst relative error", w)
+
+
+def test_attend_steep_logit_drop_within_chunk():
+    """Regression: within each chunk the first 128-token step scores 122.5
+    log2 units above the second (a weight ratio of 2^-122.5, still a normal
+    float).  The accumulator rescale between the two steps must stay finite;
+    the output is the oracle's attention to within the usual tolerance.  All
+    keys share one direction u (fp32, so every key gets the same code and
+    logit_t = n_t * L for the unit key's logit L, measured first).  Shape
+    8 x 8 x 8192 gives chunks of two steps."""
+    print("case: attend steep logit drop B=8 Hkv=8 Hq=32 N=8192", flush=True)
+    B, Hkv, Hq, N, d = 8, 8, 32, 8192, 128
+    rng = np.random.default_rng(21)
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    qt = torch.from_numpy(np.broadcast_to(u, (B, Hq, d)).astype(np.float32).copy()).to(_dev()).bfloat16()
+    gk, _ = _pair(d, 3, 0)
+    cu, nu, gu = tq.tq_encode(gk, tq.TQ_PROD, torch.from_numpy(u[None, None, :].astype(np.float32)).to(_dev()))
+    L = float(tq.tq_scores(gk, qt[:1, :1].contiguous(), cu, nu, gu, 1, 1)[0, 0, 0]) / math.sqrt(d)
+    assert L > 0.5 / math.sqrt(d)                        # <u, u> = 1 up to quantisation
+    a_low = 7.0 / L                                      # scaled logit 7 nats
+    a_high = a_low + 122.5 * math.log(2.0) / L           # 122.5 log2 units higher
+    a = np.where((np.arange(N) % 256) < 128, a_high, a_low)
+    k = (a[None, :, None] * u[None, None, :]).astype(np.float32)
+    kt = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(k, (B * Hkv, N, d)))).to(_dev())
+    vt = torch.from_numpy(rng.standard_normal((B * Hkv, N, d)).astype(np.float32)).to(_dev()).bfloat16()
+    w = _run_case(kt, vt, qt, B, Hkv, Hq, N, 0, 3, groups=[(0, 0), (7, 7)])
+    print("worst relative error", w)
