@@ -55,6 +55,7 @@ MIX1 = np.uint64(0xBF58476D1CE4E5B9)
 MIX2 = np.uint64(0x94D049BB133111EB)
 TAG_ROTATION = 1   # stream that fills the Gaussian matrix G whose QR gives Pi
 TAG_QJL = 2        # stream that fills the QJL matrix S
+TAG_SIGNS = 3      # stream of the random signs of the structured (Hadamard) rotation
 
 
 def splitmix64(state: int, n: int) -> np.ndarray:
@@ -99,6 +100,36 @@ def rotation(d: int, seed: int) -> np.ndarray:
     g = normals(seed, TAG_ROTATION, d * d).reshape(d, d)
     q, r = np.linalg.qr(g)
     return q * np.sign(np.diag(r))[None, :]
+
+
+def rademacher_signs(seed: int, d: int) -> np.ndarray:
+    """d random signs: output i of stream (seed, TAG_SIGNS) gives -1 when its
+    top bit is set, +1 otherwise."""
+    z = splitmix64(stream_state(seed, TAG_SIGNS), d)
+    return np.where((z >> np.uint64(63)) == np.uint64(1), -1.0, 1.0)
+
+
+def hadamard(d: int) -> np.ndarray:
+    """Sylvester-Hadamard matrix of order d (a power of two):
+    H[i, j] = (-1)^popcount(i & j)."""
+    if d < 1 or d & (d - 1):
+        raise ValueError("Hadamard order must be a power of two")
+    i = np.arange(d)
+    bits = np.bitwise_and(i[:, None], i[None, :])
+    pop = np.zeros_like(bits)
+    while bits.any():
+        pop += bits & 1
+        bits >>= 1
+    return np.where(pop % 2 == 0, 1.0, -1.0)
+
+
+def rotation_hadamard(d: int, seed: int) -> np.ndarray:
+    """Structured rotation Pi = H D / sqrt(d), D = diag(random signs)
+    ([wiselychen] community implementation section: a Walsh-Hadamard
+    rotation in place of the dense one, bringing the rotated coordinates
+    close to Gaussian).  Reading: one randomized Hadamard transform (signs
+    on the input side, Sylvester order), for d a power of two."""
+    return hadamard(d) * rademacher_signs(seed, d)[None, :] / math.sqrt(d)
 
 
 def qjl_matrix(m: int, d: int, seed: int) -> np.ndarray:
@@ -182,14 +213,20 @@ def codebook_distortion(d: int, c: np.ndarray, t: np.ndarray) -> float:
 #    [a2a] "how to implement", step 2).
 # ---------------------------------------------------------------------------
 class Quantizer:
-    def __init__(self, d: int, bits: int, seed: int = 0, m: int | None = None):
+    def __init__(self, d: int, bits: int, seed: int = 0, m: int | None = None, rotation_kind: str = "haar"):
         if not (3 <= d <= 1024):
             raise ValueError("d out of range")
         if not (1 <= bits <= 4):
             raise ValueError("bits out of range")
         self.d, self.bits, self.seed = d, bits, seed
         self.m = d if m is None else m
-        self.pi = rotation(d, seed)
+        self.rotation_kind = rotation_kind
+        if rotation_kind == "haar":
+            self.pi = rotation(d, seed)
+        elif rotation_kind == "hadamard":
+            self.pi = rotation_hadamard(d, seed)
+        else:
+            raise ValueError("rotation_kind must be 'haar' or 'hadamard'")
         self.s = qjl_matrix(self.m, d, seed)
         # keys ("prod"): b-1 MSE bits + 1 QJL bit; values ("mse"): b MSE bits
         self.bp_prod = bits - 1
