@@ -17,6 +17,10 @@
  *             rotated once)
  *   [friday]  friday-blog, "TurboQuant 深度解析（二）": section "1. 三步壓縮的
  *             數學細節" (rotation, QJL, residual correction)
+ *   [wiselychen] ai-coding.wiselychen.com, "Google TurboQuant：KV Cache 壓縮
+ *             6x…": section "最猛的社群實作：TurboQuant+" (a Walsh-Hadamard
+ *             rotation in a community implementation; near-Gaussian rotated
+ *             coordinates)
  *
  * Conventions
  *   - Every array argument of the compute calls (tq_encode, tq_decode,
@@ -73,6 +77,9 @@ enum { TQ_PROD = 0,     /* keys: (bits-1)-bit Lloyd-Max index + 1-bit QJL sketch
 
 enum { TQ_F32 = 0, TQ_BF16 = 1 };
 
+enum { TQ_ROT_HAAR = 0,      /* dense Haar rotation: QR of a Gaussian matrix ([a2a] stage 1) */
+       TQ_ROT_HADAMARD = 1   /* structured: H D / sqrt(d) ([wiselychen] community implementation) */ };
+
 typedef struct tq_quantizer tq_quantizer;
 
 /* Layout/ABI version of this header. */
@@ -98,6 +105,13 @@ int tq_host_normals(uint64_t seed, int tag, int64_t n, double* out);
  * matrix).  3 <= d <= 1024. */
 int tq_host_rotation(int d, uint64_t seed, double* pi_out);
 
+/* Structured rotation Pi = H D / sqrt(d) (d x d, row major): H the
+ * Sylvester-Hadamard matrix, H[i][j] = (-1)^popcount(i & j); D = diag of d
+ * random signs, sign j = -1 when the top bit of output j of stream 3 is set
+ * ([wiselychen] community implementation: Walsh-Hadamard rotation; the signs
+ * and the ordering are our reading).  d a power of two in [4, 1024]. */
+int tq_host_rotation_hadamard(int d, uint64_t seed, double* pi_out);
+
 /* QJL matrix S (m x d, row major), iid N(0,1) from stream 2 ([hotdry] QJL
  * section). */
 int tq_host_qjl_matrix(int m, int d, uint64_t seed, double* s_out);
@@ -118,6 +132,12 @@ int tq_host_codebook(int d, int levels, double* centroids, double* thresholds);
  * Returns NULL on failure (see tq_last_error).
  * ------------------------------------------------------------------------ */
 tq_quantizer* tq_make_quantizer(int d, int bits, uint64_t seed);
+
+/* As tq_make_quantizer with the rotation chosen: TQ_ROT_HAAR (the default
+ * above) or TQ_ROT_HADAMARD (tq_host_rotation_hadamard; d a power of two).
+ * Every compute call works with either: the kernels take Pi as a dense
+ * matrix, so the structured rotation changes the codes, not the cost. */
+tq_quantizer* tq_make_quantizer_ex(int d, int bits, uint64_t seed, int rotation);
 void tq_free_quantizer(tq_quantizer* q);
 
 /* d, bits, m of a quantizer (any output pointer may be NULL). */

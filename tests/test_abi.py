@@ -45,6 +45,25 @@ def test_rotation_matches_oracle(d):
     assert np.max(np.abs(tq.tq_host_rotation(d, 0) - o.rotation(d, 0))) < 1e-12
 
 
+@pytest.mark.parametrize("d", [4, 64, 128, 256])
+def test_hadamard_rotation_matches_oracle(d):
+    # entries are +-1/sqrt(d) on both sides, computed the same way: exact
+    assert np.array_equal(tq.tq_host_rotation_hadamard(d, 9), o.rotation_hadamard(d, 9))
+
+
+def test_hadamard_rotation_argument_errors():
+    L = tq.lib()
+    buf = np.zeros(128 * 128)
+    p = buf.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    assert L.tq_host_rotation_hadamard(96, 0, p) == tq.TQ_EINVAL
+    assert L.tq_host_rotation_hadamard(2, 0, p) == tq.TQ_EINVAL
+    # the quantizer checks its arguments before touching a device
+    assert not L.tq_make_quantizer_ex(96, 3, 0, tq.TQ_ROT_HADAMARD)
+    assert b"power of two" in L.tq_last_error()
+    assert not L.tq_make_quantizer_ex(128, 3, 0, 7)
+    assert b"rotation" in L.tq_last_error()
+
+
 def test_qjl_matrix_matches_oracle():
     # libm and numpy may differ in the last bit of log/cos/sin
     a, b = tq.tq_host_qjl_matrix(128, 128, 3), o.qjl_matrix(128, 128, 3)

@@ -1,0 +1,131 @@
+"""GPU parity for quantizers with the structured rotation Pi = H D / sqrt(d)
+(tq_make_quantizer_ex with TQ_ROT_HADAMARD): encode (keys and values),
+decode, logits, top-k and decode attention through the C ABI against the
+oracle built with the same rotation (tolerances in tests/parity.py)."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import tq_oracle as o
+from tests import parity as P
+from vector_quantization_tq_amd import workloads as W
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from vector_quantization_tq_amd import tq  # noqa: E402
+
+_QZ = {}
+
+
+def _dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def _pair(d, bits, seed=0):
+    key = (d, bits, seed)
+    if key not in _QZ:
+        _QZ[key] = (tq.Quantizer(d, bits, seed, rotation=tq.TQ_ROT_HADAMARD),
+                    o.Quantizer(d, bits, seed, rotation_kind="hadamard"))
+    return _QZ[key]
+
+
+def _keys(rng, nseq, n, d):
+    return (rng.standard_normal((nseq, n, d)) * np.exp(rng.uniform(0, math.log(50), (nseq, 1, d)))).astype(np.float32)
+
+
+@pytest.mark.parametrize("d,bits,nseq,n,bf16", [
+    (128, 3, 2, 1000, True), (128, 4, 1, 777, False), (64, 2, 1, 300, True), (256, 3, 1, 200, False),
+    (16, 2, 2, 65, False)])
+def test_encode_prod_hadamard(d, bits, nseq, n, bf16):
+    print(f"case: hadamard prod encode d={d} bits={bits} nseq={nseq} n={n}", flush=True)
+    g, oq = _pair(d, bits)
+    xt = torch.from_numpy(_keys(np.random.default_rng(d + bits), nseq, n, d)).to(_dev())
+    if bf16:
+        xt = xt.bfloat16()
+    codes, norms, gam = tq.tq_encode(g, tq.TQ_PROD, xt)
+    torch.cuda.synchronize()
+    N = nseq * n
+    xs = xt.float().cpu().numpy().astype(np.float64).reshape(N, d)
+    _, _, st = P.check_prod_codes(oq, xs, P.to_u32(codes)[: g.code_words(tq.TQ_PROD, nseq, n)],
+                                  norms.cpu().numpy()[:N], gam.cpu().numpy()[:N])
+    print(st)
+
+
+@pytest.mark.parametrize("d,bits,n", [(128, 3, 1000), (128, 4, 4101), (32, 1, 70)])
+def test_encode_mse_and_decode_hadamard(d, bits, n):
+    print(f"case: hadamard mse encode + decode d={d} bits={bits} n={n}", flush=True)
+    g, oq = _pair(d, bits)
+    x = np.random.default_rng(n).standard_normal((n, d)).astype(np.float32)
+    xt = torch.from_numpy(x).to(_dev())
+    codes, norms, _ = tq.tq_encode(g, tq.TQ_MSE, xt)
+    dec = tq.tq_decode(g, tq.TQ_MSE, codes, norms, None, 1, n)[0].cpu().numpy()
+    idx, _ = P.check_mse_codes(oq, x.astype(np.float64), P.to_u32(codes), norms.cpu().numpy())
+    ref = o.decode_mse(oq, idx, norms.cpu().numpy().astype(np.float64))
+    err = np.abs(dec - ref).max(axis=1) / np.linalg.norm(ref, axis=1)
+    assert err.max() < 1e-5
+
+
+@pytest.mark.parametrize("d,bits,B,Hkv,Hq,n,topk", [
+    (128, 3, 2, 2, 8, 1000, 0), (128, 4, 1, 4, 16, 3000, 0), (256, 2, 1, 1, 5, 500, 0), (128, 3, 1, 1, 10, 5000, 10)])
+def test_scores_hadamard(d, bits, B, Hkv, Hq, n, topk):
+    print(f"case: hadamard scores d={d} bits={bits} B={B} Hkv={Hkv} Hq={Hq} n={n} k={topk}", flush=True)
+    rng = np.random.default_rng(d * bits + n)
+    g, oq = _pair(d, bits)
+    kt = torch.from_numpy(_keys(rng, B * Hkv, n, d)).to(_dev()).bfloat16()
+    qt = torch.from_numpy(rng.standard_normal((B, Hq, d)).astype(np.float32)).to(_dev())
+    codes, norms, gam = tq.tq_encode(g, tq.TQ_PROD, kt)
+    logits = tq.tq_scores(g, qt, codes, norms, gam, Hkv, n).cpu().numpy()
+    if topk:
+        s, i = tq.tq_scores(g, qt, codes, norms, gam, Hkv, n, topk=topk)
+        s, i = s.cpu().numpy(), i.cpu().numpy()
+    cw = P.to_u32(codes)
+    nn, gg = norms.cpu().numpy().astype(np.float64), gam.cpu().numpy().astype(np.float64)
+    qs = qt.cpu().numpy().astype(np.float64)
+    G, per = Hq // Hkv, g.code_words(tq.TQ_PROD, 1, n)
+    for b in range(B):
+        for h in range(Hkv):
+            sq, hs = b * Hkv + h, slice(h * (Hq // Hkv), (h + 1) * (Hq // Hkv))
+            idx, bits01 = o.unpack_prod(cw[sq * per:(sq + 1) * per].reshape(n, -1), bits - 1, d)
+            kn = nn[sq * n:(sq + 1) * n]
+            ref = o.scores(oq, qs[b, hs], idx, bits01, kn, gg[sq * n:(sq + 1) * n])
+            P.check_logits(logits[b, hs], ref, np.linalg.norm(qs[b, hs], axis=1), kn, d)
+            if topk:
+                P.check_topk(s[b, hs], i[b, hs], ref, np.linalg.norm(qs[b, hs], axis=1), kn, d)
+
+
+@pytest.mark.parametrize("B,Hkv,Hq,N,tail,bits", [(1, 2, 8, 1000, 0, 3), (2, 2, 8, 777, 37, 4)])
+def test_attend_hadamard(B, Hkv, Hq, N, tail, bits):
+    print(f"case: hadamard attend B={B} Hkv={Hkv} Hq={Hq} N={N} tail={tail} bits={bits}", flush=True)
+    d = 128
+    a = W._gqa_tensors(np.random.default_rng(N + bits), B, Hkv, Hq, N, d)
+
+    def bf(u16):
+        return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).to(_dev()).view(torch.bfloat16)
+
+    k, v, q = bf(a["k_bf16"]).view(B * Hkv, N, d), bf(a["v_bf16"]).view(B * Hkv, N, d), bf(a["q_bf16"])
+    n_comp = N - tail
+    gk, ok = _pair(d, bits, 0)
+    gv, ov = _pair(d, bits, 1)
+    kcodes, kn, kg = tq.tq_encode(gk, tq.TQ_PROD, k[:, :n_comp].contiguous())
+    vcodes, vn, _ = tq.tq_encode(gv, tq.TQ_MSE, v[:, :n_comp].contiguous())
+    kt = k[:, n_comp:].contiguous().view(B, Hkv, tail, d) if tail else None
+    vt = v[:, n_comp:].contiguous().view(B, Hkv, tail, d) if tail else None
+    out = tq.tq_attend_decode(gk, gv, q, kcodes, kn, kg, vcodes, vn, Hkv, n_comp, kt, vt).cpu().numpy()
+    G = Hq // Hkv
+    kw, vw = P.to_u32(kcodes), P.to_u32(vcodes)
+    kn, kg, vn = (t.cpu().numpy().astype(np.float64) for t in (kn, kg, vn))
+    qs = q.float().cpu().numpy().astype(np.float64)
+    kf, vf = k.float().cpu().numpy().astype(np.float64), v.float().cpu().numpy().astype(np.float64)
+    perk, perv = gk.code_words(tq.TQ_PROD, 1, n_comp), gv.code_words(tq.TQ_MSE, 1, n_comp)
+    for b in range(B):
+        for h in range(Hkv):
+            s = b * Hkv + h
+            ki, kb = o.unpack_prod(kw[s * perk:(s + 1) * perk].reshape(n_comp, -1), bits - 1, d)
+            vi = o.unpack_mse(vw[s * perv:(s + 1) * perv], n_comp, bits, d)
+            sl = slice(s * n_comp, (s + 1) * n_comp)
+            ref = o.attend(ok, ov, qs[b, h * G:(h + 1) * G], ki, kb, kn[sl], kg[sl], vi, vn[sl],
+                           kf[s, n_comp:] if tail else None, vf[s, n_comp:] if tail else None)
+            P.check_attention(out[b, h * G:(h + 1) * G], ref)

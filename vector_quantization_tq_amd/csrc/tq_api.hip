@@ -128,6 +128,13 @@ int tq_host_rotation(int d, uint64_t seed, double* pi_out) {
   return TQ_OK;
 }
 
+int tq_host_rotation_hadamard(int d, uint64_t seed, double* pi_out) {
+  if (d < 4 || d > 1024 || (d & (d - 1)) || !pi_out)
+    return fail(TQ_EINVAL, "need d a power of two in [4, 1024] and an output array");
+  tq::rotation_hadamard(d, seed, pi_out);
+  return TQ_OK;
+}
+
 int tq_host_qjl_matrix(int m, int d, uint64_t seed, double* s_out) {
   if (m < 1 || d < 1 || !s_out) return fail(TQ_EINVAL, "need m, d >= 1 and an output array");
   tq::qjl_matrix(m, d, seed, s_out);
@@ -142,18 +149,32 @@ int tq_host_codebook(int d, int levels, double* centroids, double* thresholds) {
   return TQ_OK;
 }
 
-tq_quantizer* tq_make_quantizer(int d, int bits, uint64_t seed) {
+tq_quantizer* tq_make_quantizer(int d, int bits, uint64_t seed) { return tq_make_quantizer_ex(d, bits, seed, TQ_ROT_HAAR); }
+
+tq_quantizer* tq_make_quantizer_ex(int d, int bits, uint64_t seed, int rotation) {
   if (d < 3 || d > 1024) { fail(TQ_EINVAL, "d=%d out of [3, 1024]", d); return nullptr; }
   if (bits < 1 || bits > 4) { fail(TQ_EINVAL, "bits=%d out of [1, 4]", bits); return nullptr; }
+  if (rotation != TQ_ROT_HAAR && rotation != TQ_ROT_HADAMARD) {
+    fail(TQ_EINVAL, "rotation must be TQ_ROT_HAAR or TQ_ROT_HADAMARD");
+    return nullptr;
+  }
+  if (rotation == TQ_ROT_HADAMARD && (d < 4 || (d & (d - 1)))) {
+    fail(TQ_EINVAL, "the Hadamard rotation needs d a power of two >= 4 (d=%d)", d);
+    return nullptr;
+  }
   tq_quantizer* q = new (std::nothrow) tq_quantizer();
   if (!q) { fail(TQ_ENOMEM, "host allocation failed"); return nullptr; }
   q->d = d;
   q->bits = bits;
   q->m = d;
   q->seed = seed;
+  q->rotation = rotation;
   q->pi.resize(static_cast<size_t>(d) * d);
   q->s.resize(static_cast<size_t>(q->m) * d);
-  tq::rotation(d, seed, q->pi.data());
+  if (rotation == TQ_ROT_HADAMARD)
+    tq::rotation_hadamard(d, seed, q->pi.data());
+  else
+    tq::rotation(d, seed, q->pi.data());
   tq::qjl_matrix(q->m, d, seed, q->s.data());
   if (bits >= 2 && !fill_codebook(d, bits - 1, q->cb[TQ_PROD])) { fail(TQ_EINVAL, "prod codebook failed"); delete q; return nullptr; }
   if (!fill_codebook(d, bits, q->cb[TQ_MSE])) { fail(TQ_EINVAL, "mse codebook failed"); delete q; return nullptr; }

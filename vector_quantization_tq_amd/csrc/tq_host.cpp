@@ -43,6 +43,27 @@ void normals(uint64_t seed, int tag, int64_t n, double* out) {
   }
 }
 
+// d random signs: output i of stream (seed, 3) gives -1 when its top bit is
+// set, +1 otherwise.
+void signs(uint64_t seed, int d, double* out) {
+  const uint64_t gamma = 0x9E3779B97F4A7C15ull;
+  const uint64_t state = seed ^ (static_cast<uint64_t>(3) << 56);
+  for (int i = 0; i < d; ++i) out[i] = (mix64(state + static_cast<uint64_t>(i + 1) * gamma) >> 63) ? -1.0 : 1.0;
+}
+
+// Structured rotation Pi = H D / sqrt(d) (ai-coding.wiselychen.com, "Google
+// TurboQuant：KV Cache 壓縮 6x…", community implementation section: a
+// Walsh-Hadamard rotation): H the Sylvester-Hadamard matrix,
+// H[i][j] = (-1)^popcount(i & j), D = diag(signs).  d a power of two.
+void rotation_hadamard(int d, uint64_t seed, double* pi) {
+  std::vector<double> sg(d);
+  signs(seed, d, sg.data());
+  const double inv = 1.0 / std::sqrt(static_cast<double>(d));
+  for (int i = 0; i < d; ++i)
+    for (int j = 0; j < d; ++j)
+      pi[static_cast<size_t>(i) * d + j] = ((__builtin_popcount(static_cast<unsigned>(i & j)) & 1) ? -sg[j] : sg[j]) * inv;
+}
+
 // ---------------------------------------------------------------------------
 // Householder QR of G (d x d, row major).  Returns Q with the column signs
 // chosen so that R has a positive diagonal (the unique such factor).

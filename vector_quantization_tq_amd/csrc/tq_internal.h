@@ -9,6 +9,8 @@ namespace tq {
 // host precompute (tq_host.cpp)
 void normals(uint64_t seed, int tag, int64_t n, double* out);
 void rotation(int d, uint64_t seed, double* pi);
+void signs(uint64_t seed, int d, double* out);
+void rotation_hadamard(int d, uint64_t seed, double* pi);
 void qjl_matrix(int m, int d, uint64_t seed, double* s);
 int codebook(int d, int K, double* centroids, double* thresholds);
 
@@ -34,7 +36,7 @@ struct Codebook {
 }  // namespace tq
 
 struct tq_quantizer {
-  int d = 0, bits = 0, m = 0, device = 0;
+  int d = 0, bits = 0, m = 0, device = 0, rotation = 0;   // rotation: TQ_ROT_HAAR (0) or TQ_ROT_HADAMARD (1)
   uint64_t seed = 0;
   std::vector<double> pi, s;          // host float64 copies (row major)
   tq::Codebook cb[2];                 // [TQ_PROD] b-1 bits, [TQ_MSE] b bits (values and MSE-only keys)

@@ -18,10 +18,11 @@ LIB_PATH = os.path.join(_HERE, "libtq.so")
 TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EHIP, TQ_ENOMEM, TQ_EWORKSPACE = 0, -1, -2, -3, -4, -5
 TQ_PROD, TQ_MSE, TQ_MSE_KEYS = 0, 1, 2
 TQ_F32, TQ_BF16 = 0, 1
+TQ_ROT_HAAR, TQ_ROT_HADAMARD = 0, 1
 
 EXPORTS = [
-    "tq_version", "tq_last_error", "tq_host_normals", "tq_host_rotation", "tq_host_qjl_matrix", "tq_host_codebook",
-    "tq_make_quantizer", "tq_free_quantizer", "tq_quantizer_info", "tq_set_key_mode", "tq_code_words", "tq_encode",
+    "tq_version", "tq_last_error", "tq_host_normals", "tq_host_rotation", "tq_host_rotation_hadamard",
+    "tq_host_qjl_matrix", "tq_host_codebook", "tq_make_quantizer", "tq_make_quantizer_ex", "tq_free_quantizer", "tq_quantizer_info", "tq_set_key_mode", "tq_code_words", "tq_encode",
     "tq_decode", "tq_scores_workspace_bytes", "tq_query_prep", "tq_scores_from_prep", "tq_scores",
     "tq_attend_workspace_bytes", "tq_attend_decode",
 ]
@@ -51,9 +52,11 @@ def lib() -> ctypes.CDLL:
         "tq_last_error": (ctypes.c_char_p, []),
         "tq_host_normals": (c_i, [c_u64, c_i, c_i64, dp]),
         "tq_host_rotation": (c_i, [c_i, c_u64, dp]),
+        "tq_host_rotation_hadamard": (c_i, [c_i, c_u64, dp]),
         "tq_host_qjl_matrix": (c_i, [c_i, c_i, c_u64, dp]),
         "tq_host_codebook": (c_i, [c_i, c_i, dp, dp]),
         "tq_make_quantizer": (c_p, [c_i, c_i, c_u64]),
+        "tq_make_quantizer_ex": (c_p, [c_i, c_i, c_u64, c_i]),
         "tq_free_quantizer": (None, [c_p]),
         "tq_quantizer_info": (c_i, [c_p, ctypes.POINTER(c_i), ctypes.POINTER(c_i), ctypes.POINTER(c_i)]),
         "tq_set_key_mode": (c_i, [c_p, c_i]),
@@ -97,6 +100,12 @@ def tq_host_normals(seed: int, tag: int, n: int) -> np.ndarray:
 def tq_host_rotation(d: int, seed: int) -> np.ndarray:
     out = np.empty((d, d), dtype=np.float64)
     _check(lib().tq_host_rotation(d, seed, _dptr(out)))
+    return out
+
+
+def tq_host_rotation_hadamard(d: int, seed: int) -> np.ndarray:
+    out = np.empty((d, d), dtype=np.float64)
+    _check(lib().tq_host_rotation_hadamard(d, seed, _dptr(out)))
     return out
 
 
@@ -148,15 +157,15 @@ def _need_cuda(*ts):
 class Quantizer:
     """Handle of a tq_quantizer (owns the device tables)."""
 
-    def __init__(self, d: int, bits: int, seed: int = 0):
+    def __init__(self, d: int, bits: int, seed: int = 0, rotation: int = TQ_ROT_HAAR):
         L = lib()
-        h = L.tq_make_quantizer(d, bits, seed)
+        h = L.tq_make_quantizer_ex(d, bits, seed, rotation)
         if not h:
             raise TQError(TQ_EINVAL, L.tq_last_error().decode())
         self._h = ctypes.c_void_p(h)
         dd, bb, mm = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
         _check(L.tq_quantizer_info(self._h, ctypes.byref(dd), ctypes.byref(bb), ctypes.byref(mm)))
-        self.d, self.bits, self.m, self.seed = dd.value, bb.value, mm.value, seed
+        self.d, self.bits, self.m, self.seed, self.rotation = dd.value, bb.value, mm.value, seed, rotation
         self.key_mode = TQ_PROD
 
     def set_key_mode(self, key_mode: int):
@@ -186,8 +195,8 @@ class Quantizer:
         return w
 
 
-def tq_make_quantizer(d: int, bits: int, seed: int = 0) -> Quantizer:
-    return Quantizer(d, bits, seed)
+def tq_make_quantizer(d: int, bits: int, seed: int = 0, rotation: int = TQ_ROT_HAAR) -> Quantizer:
+    return Quantizer(d, bits, seed, rotation)
 
 
 def tq_encode(qz: Quantizer, mode: int, x, out=None):
