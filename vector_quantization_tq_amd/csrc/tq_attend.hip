@@ -58,10 +58,12 @@ __device__ __forceinline__ uint32_t fixed_limbs4(float x, float& xq) {
 constexpr int kPartStride = 128 + 4;
 
 // chunk length (a multiple of the step): the largest power-of-two multiple of
-// 128 tokens, up to 4096, that still leaves about 2048 workgroups
+// 128 tokens, up to 1024, that still leaves at least 768 workgroups (three
+// resident per CU); longer chunks only lengthen the merge, shorter ones add
+// partial records and pipeline fills
 static int64_t attend_chunk_len(int64_t n_comp, int64_t groups) {
   int64_t ch = kStep;
-  while (ch < 4096 && (n_comp + 2 * ch - 1) / (2 * ch) * groups >= 2048) ch *= 2;
+  while (ch < 1024 && (n_comp + 2 * ch - 1) / (2 * ch) * groups >= 768) ch *= 2;
   return ch;
 }
 
