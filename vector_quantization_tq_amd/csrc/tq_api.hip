@@ -188,6 +188,9 @@ tq_quantizer* tq_make_quantizer_ex(int d, int bits, uint64_t seed, int rotation)
       for (int k = 0; k < d; ++k) a += q->s[static_cast<size_t>(r) * d + k] * q->pi[static_cast<size_t>(j) * d + k];
       sp32[static_cast<size_t>(r) * d + j] = static_cast<float>(a);
     }
+  std::vector<float> spt32(sp32.size());   // S' k-major for the general-d encoder
+  for (int r = 0; r < q->m; ++r)
+    for (int j = 0; j < d; ++j) spt32[static_cast<size_t>(j) * q->m + r] = sp32[static_cast<size_t>(r) * d + j];
   const int dm = d + q->m;
   std::vector<float> qt32(static_cast<size_t>(d) * dm);
   for (int k = 0; k < d; ++k) {
@@ -202,7 +205,8 @@ tq_quantizer* tq_make_quantizer_ex(int d, int bits, uint64_t seed, int rotation)
   const size_t bp = pi32.size() * sizeof(float), bs = s32.size() * sizeof(float);
   if ((e = hipMalloc(&q->d_pi, bp)) != hipSuccess || (e = hipMalloc(&q->d_s, bs)) != hipSuccess ||
       (e = hipMalloc(&q->d_sp, bs)) != hipSuccess ||
-      (e = hipMalloc(&q->d_qt, qt32.size() * sizeof(float))) != hipSuccess) {
+      (e = hipMalloc(&q->d_qt, qt32.size() * sizeof(float))) != hipSuccess ||
+      (e = hipMalloc(&q->d_spt, bs)) != hipSuccess) {
     hip_fail(e, "hipMalloc");
     tq_free_quantizer(q);
     return nullptr;
@@ -210,7 +214,8 @@ tq_quantizer* tq_make_quantizer_ex(int d, int bits, uint64_t seed, int rotation)
   if ((e = hipMemcpy(q->d_pi, pi32.data(), bp, hipMemcpyHostToDevice)) != hipSuccess ||
       (e = hipMemcpy(q->d_s, s32.data(), bs, hipMemcpyHostToDevice)) != hipSuccess ||
       (e = hipMemcpy(q->d_sp, sp32.data(), bs, hipMemcpyHostToDevice)) != hipSuccess ||
-      (e = hipMemcpy(q->d_qt, qt32.data(), qt32.size() * sizeof(float), hipMemcpyHostToDevice)) != hipSuccess) {
+      (e = hipMemcpy(q->d_qt, qt32.data(), qt32.size() * sizeof(float), hipMemcpyHostToDevice)) != hipSuccess ||
+      (e = hipMemcpy(q->d_spt, spt32.data(), bs, hipMemcpyHostToDevice)) != hipSuccess) {
     hip_fail(e, "hipMemcpy");
     tq_free_quantizer(q);
     return nullptr;
@@ -220,12 +225,13 @@ tq_quantizer* tq_make_quantizer_ex(int d, int bits, uint64_t seed, int rotation)
 
 void tq_free_quantizer(tq_quantizer* q) {
   if (!q) return;
-  if (q->d_pi || q->d_s || q->d_sp || q->d_qt) {
+  if (q->d_pi || q->d_s || q->d_sp || q->d_qt || q->d_spt) {
     DeviceGuard g(q->device);
     if (q->d_pi) (void)hipFree(q->d_pi);
     if (q->d_s) (void)hipFree(q->d_s);
     if (q->d_sp) (void)hipFree(q->d_sp);
     if (q->d_qt) (void)hipFree(q->d_qt);
+    if (q->d_spt) (void)hipFree(q->d_spt);
   }
   delete q;
 }

@@ -23,12 +23,14 @@ namespace {
 constexpr int kTileRows = 64;
 constexpr int kThreads = 256;
 
-// Y[16 rows of this wave][DP] = X[rows][0:d] * M^T, with M [rows_m][d] row
-// major (row j of M gives output column j).  X in LDS with row stride `ld`.
-// acc[ct] holds output column tile ct (16 columns) in MFMA C layout.
+// Y[16 rows of this wave][DP] = X[rows][0:d] * M^T, with M given k-major:
+// Mt[k * ldm + j] = M[j][k] (row j of M gives output column j), so that the
+// 16 lanes of a column tile read 16 consecutive floats.  X in LDS with row
+// stride `ld`.  acc[ct] holds output column tile ct (16 columns) in MFMA C
+// layout.
 template <int NT>
-__device__ __forceinline__ void gemm_rows_16(const float* xs, int ld, const float* __restrict__ M, int rows_m, int d,
-                                             v4f (&acc)[NT]) {
+__device__ __forceinline__ void gemm_rows_16(const float* xs, int ld, const float* __restrict__ Mt, int ldm, int rows_m,
+                                             int d, v4f (&acc)[NT]) {
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, kq = lane >> 4;
 #pragma unroll
@@ -39,7 +41,7 @@ __device__ __forceinline__ void gemm_rows_16(const float* xs, int ld, const floa
 #pragma unroll
     for (int ct = 0; ct < NT; ++ct) {
       const int j = ct * 16 + r;
-      const float b = (k < d && j < rows_m) ? M[static_cast<int64_t>(j) * d + k] : 0.f;
+      const float b = (k < d && j < rows_m) ? Mt[static_cast<int64_t>(k) * ldm + j] : 0.f;
       acc[ct] = mfma_f32(a, b, acc[ct]);
     }
   }
@@ -49,7 +51,8 @@ __device__ __forceinline__ void gemm_rows_16(const float* xs, int ld, const floa
 
 template <int NT>
 __global__ void __launch_bounds__(kThreads) encode_kernel(const void* __restrict__ x, int dtype, int64_t n, int d, int mode,
-                                                          const float* __restrict__ pi, const float* __restrict__ sp,
+                                                          const float* __restrict__ pit, int ldp,
+                                                          const float* __restrict__ spt,
                                                           Codebook cb, uint32_t* __restrict__ codes,
                                                           float* __restrict__ norms, float* __restrict__ gammas) {
   constexpr int DP = NT * 16;
@@ -94,7 +97,7 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(const void* __restrict
   // ---- rotation: y = Pi x / n ----
   const float* xw = xs + wave * 16 * LD;   // this wave's 16 rows
   v4f acc[NT];
-  gemm_rows_16<NT>(xw, LD, pi, d, d, acc);
+  gemm_rows_16<NT>(xw, LD, pit, ldp, d, d, acc);
 
   const int col_in = lane & 15, rq = lane >> 4;   // C layout: rows 4*rq+i, column ct*16+col_in
   float inv_n[4], rho2[4];
@@ -138,7 +141,7 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(const void* __restrict
     }
     __syncthreads();
     // ---- QJL projection z = S' rho; bit = [z >= 0] (all ones for n = 0) ----
-    gemm_rows_16<NT>(xw, LD, sp, d, d, acc);
+    gemm_rows_16<NT>(xw, LD, spt, d, d, d, acc);
 #pragma unroll
     for (int ct = 0; ct < NT; ++ct) {
       const int col = ct * 16 + col_in;
@@ -783,7 +786,9 @@ hipError_t launch_encode_nt(const tq_quantizer* q, int mode, const void* x, int 
   constexpr int DP = NT * 16;
   const size_t lds = sizeof(float) * (kTileRows * (DP + 1) + kTileRows + kMaxLevels) + 2 * kTileRows * DP;
   dim3 grid(static_cast<unsigned>((n + kTileRows - 1) / kTileRows), static_cast<unsigned>(nseq));
-  hipLaunchKernelGGL((encode_kernel<NT>), grid, dim3(kThreads), lds, st, x, dtype, n, q->d, mode, q->d_pi, q->d_sp,
+  // Pi k-major = the first d columns of the query table (row stride d + m); S' k-major
+  hipLaunchKernelGGL((encode_kernel<NT>), grid, dim3(kThreads), lds, st, x, dtype, n, q->d, mode, q->d_qt, q->d + q->m,
+                     q->d_spt,
                      q->cb[mode == 0 ? 0 : 1], codes, norms, gammas);
   return hipGetLastError();
 }

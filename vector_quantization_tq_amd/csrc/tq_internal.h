@@ -44,6 +44,7 @@ struct tq_quantizer {
   float* d_s = nullptr;               // [m][d]   QJL matrix
   float* d_sp = nullptr;              // [m][d]   S' = S Pi^T (acts on rotated residuals)
   float* d_qt = nullptr;              // [d][d+m] column k of Pi then of S (query transform, k-major)
+  float* d_spt = nullptr;             // [d][m]   S' k-major (d_spt[k * m + r] = S'[r][k]), general-d encoder
   int key_mode = 0;                   // key layout the scoring calls read: TQ_PROD (0) or TQ_MSE_KEYS (2)
 };
 
