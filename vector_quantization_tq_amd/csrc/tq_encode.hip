@@ -246,6 +246,15 @@ constexpr float kRhoScale = 16384.f;    // 2^14
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
+// rs - hh rounded once to fp16, for hh = rs rounded to fp16 (so rs - hh is
+// exact in fp32): v_fma_mixlo_f16 reads hh as an fp16 source and rs as fp32
+// (one instruction in place of a convert, a subtract and a convert)
+__device__ __forceinline__ _Float16 f16_remainder(float rs, _Float16 hh) {
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(hh), "v"(rs));
+  return __builtin_bit_cast(_Float16, static_cast<uint16_t>(r));
+}
+
 __device__ __forceinline__ v4f mfma_f16(const v8h& a, const v8h& b, const v4f& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -290,8 +299,9 @@ __device__ __forceinline__ float pick_centroid(const float (&cen)[1 << BP], cons
 // 1 bf16 and 2 fp32 in 16-byte chunks fetched one tile ahead.  BP: index
 // bits.  MODE: 0 keys with the QJL sketch (token-major words + rho, gamma),
 // 1 values (coordinate-major 32-token words), 2 MSE-only keys (token-major
-// words, no QJL plane).
-template <int KS, int LK, int MODE, int BP>
+// words, no QJL plane).  FULL: d == 32 KS, so every wave owns 32 existing
+// coordinates and the coordinate guards compile away.
+template <int KS, int LK, int MODE, int BP, bool FULL>
 __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restrict__ x, int dtype, int64_t nseq,
                                                              int64_t n, int d, const float* __restrict__ pi,
                                                              const float* __restrict__ sp, Codebook cb,
@@ -308,12 +318,13 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
   __shared__ __attribute__((aligned(16))) _Float16 xl[XLO ? kEncRows * LDH : 8];
   __shared__ __attribute__((aligned(16))) _Float16 rh[QJL ? kEncRows * LDH : 8];
   __shared__ __attribute__((aligned(16))) _Float16 rl[QJL ? kEncRows * LDH : 8];
-  __shared__ float scl2[2][kEncRows];    // 2^-(row scale + 8) / n, by tile parity
+  __shared__ __attribute__((aligned(16))) float scl2[2][kEncRows];   // 2^(6 - row scale) / n, by tile parity
   __shared__ float nrm2[2][kEncRows];    // n, by tile parity
   __shared__ float part2[4][kEncRows];
   __shared__ uint32_t ost[2][1024];
 
   static_assert(KS == 4, "four waves own 32 coordinates each");
+  if constexpr (FULL) d = 32 * KS;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
   const int r16 = lane & 15, q = lane >> 4;
@@ -486,7 +497,8 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
     if (part == 0) {
       const float nv = lrow < rows ? sqrtf(ss) : 0.f;
       nrm[lrow] = nv;
-      scl[lrow] = nv > 0.f ? ldexpf(1.f / nv, -(sig + 8)) : 0.f;
+      // y 2^14 = acc * scl: the rotation of u, times 2^14 (Pi carries 2^8, the row 2^sig)
+      scl[lrow] = nv > 0.f ? ldexpf(1.f / nv, 6 - sig) : 0.f;
     }
   };
   auto store = [&](TileAt t, int buf) {
@@ -532,7 +544,9 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
   };
   // packed word of row 4q + i of a ballot pair (low 16 bits, high 16 bits)
   auto halves = [&](uint64_t m0, uint64_t m1) {
-    return static_cast<uint32_t>((m0 >> (16 * q)) & 0xFFFFu) | (static_cast<uint32_t>((m1 >> (16 * q)) & 0xFFFFu) << 16);
+    // bytes 0-1 of m0 >> 16q, then bytes 0-1 of m1 >> 16q (one byte permute)
+    return __builtin_amdgcn_perm(static_cast<uint32_t>(m1 >> (16 * q)), static_cast<uint32_t>(m0 >> (16 * q)),
+                                 0x05040100u);
   };
   // The codebook is symmetric (the middle threshold is 0 and c[K-1-i] = -c[i]
   // exactly), so idx = #{t_k < y} is K/2 + j for y > 0 and K/2 - 1 - j
@@ -542,19 +556,21 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
   constexpr int KH = 1 << (BP - 1);      // centroids per half
   float thp[KH > 1 ? KH - 1 : 1], cenS[KH];
 #pragma unroll
-  for (int k2 = 0; k2 + 1 < KH; ++k2) thp[k2] = cb.t[KH + k2];
+  for (int k2 = 0; k2 + 1 < KH; ++k2) thp[k2] = cb.t[KH + k2] * kRhoScale;   // compared with y 2^14
 #pragma unroll
   for (int k2 = 0; k2 < KH; ++k2) cenS[k2] = cb.c[KH + k2] * kRhoScale;
-  // sign and magnitude bits of y: pos = [y > 0], jb = bits of j
-  auto classify = [&](float y, bool& pos, bool (&jb)[BP > 1 ? BP - 1 : 1]) {
-    pos = y > 0.f;
-    if constexpr (BP > 1) decide_bits<BP - 1, BP - 2>(fabsf(y), thp, jb);
+  // sign and magnitude bits of y from a (the accumulator, y 2^14 = a * scl):
+  // pos = [y > 0] = [a > 0] (the scale is positive, or 0 with a = 0), jb =
+  // bits of j from |y 2^14| against the thresholds times 2^14 (power-of-two
+  // scaling: the same decisions)
+  auto classify = [&](float a, float ys, bool& pos, bool (&jb)[BP > 1 ? BP - 1 : 1]) {
+    pos = a > 0.f;
+    if constexpr (BP > 1) decide_bits<BP - 1, BP - 2>(fabsf(ys), thp, jb);
     else jb[0] = false;
   };
-  // row sum over the 16 lanes of a row of the C layout (one DPP row)
-  auto sum16 = [&](float v) { return row_sum16(v); };
   // lanes whose coordinate exists (token-major layouts): 32w + 16ct + r16 < d
-  const uint64_t okm0 = __ballot(32 * w + r16 < d), okm1 = __ballot(32 * w + 16 + r16 < d);
+  const uint64_t okm0 = FULL ? ~0ull : __ballot(32 * w + r16 < d);
+  const uint64_t okm1 = FULL ? ~0ull : __ballot(32 * w + 16 + r16 < d);
 
   int64_t t = blockIdx.x;
   TileAt cur = {static_cast<int64_t>(blockIdx.x) / tps, static_cast<int64_t>(blockIdx.x) % tps}, prev = cur;
@@ -587,13 +603,15 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
         if constexpr (XLO) contract(xl, bPh, h, false, acc);
         pin_acc(acc);
         // lane holds vector 32h + 16h2 + 4q + i, coordinate 32w + 16ct + r16
+        float r2v[2][4];   // partial ||rho||^2 (x 2^28) of this lane's two coordinates
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           const int vbase = 32 * h + 16 * h2 + 4 * q;
+          const float4 sc4 = *reinterpret_cast<const float4*>(scl + vbase);   // one LDS read for 4 rows
+          const float scv[4] = {sc4.x, sc4.y, sc4.z, sc4.w};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float sc = scl[vbase + i];
-            const float scS = sc * kRhoScale;
+            const float scS = scv[i];
             // lane masks of the sign and the magnitude bits, taken as soon as
             // each is decided (no per-lane booleans kept alive)
             uint64_t ms[2], mj[2][BP > 1 ? BP - 1 : 1];
@@ -603,7 +621,7 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
               const int c = 32 * w + 16 * ct + r16;
               const float a = acc[h2][ct][i];
               bool pos, jb[BP > 1 ? BP - 1 : 1];
-              classify(a * sc, pos, jb);
+              classify(a, a * scS, pos, jb);
               ms[ct] = __ballot(pos);
 #pragma unroll
               for (int p = 0; p + 1 < BP; ++p) mj[ct][p] = __ballot(jb[p]);
@@ -612,11 +630,12 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
                 float cabs;
                 if constexpr (BP > 1) cabs = pick_centroid<BP - 1>(cenS, jb);
                 else cabs = cenS[0];
-                const float rs = c < d ? fmaf(a, scS, pos ? -cabs : cabs) : 0.f;
+                const float rs = (FULL || c < d) ? fmaf(a, scS, pos ? -cabs : cabs) : 0.f;
                 r2 = fmaf(rs, rs, r2);
+                // hi + lo split
                 const _Float16 hh = static_cast<_Float16>(rs);   // c < KP: four waves of 32
                 rh[(vbase + i) * LDH + c] = hh;
-                rl[(vbase + i) * LDH + c] = static_cast<_Float16>(rs - static_cast<float>(hh));
+                rl[(vbase + i) * LDH + c] = f16_remainder(rs, hh);
               }
             }
             // plane words: the sign plane is [y > 0], the low planes are
@@ -626,16 +645,32 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
             wd[BP - 1] = halves(s0, s1);
 #pragma unroll
             for (int p = 0; p + 1 < BP; ++p) wd[p] = halves(~(mj[0][p] ^ s0) & okm0, ~(mj[1][p] ^ s1) & okm1);
-            // partial ||rho||^2 (x 2^28) over this wave's 32 coordinates
-            if constexpr (QJL) r2 = sum16(r2);
-            if (r16 == 0) {
-              if (w < G) {
+            if constexpr (QJL) r2v[h2][i] = r2;
+            if (r16 == 0 && (FULL || w < G)) {
 #pragma unroll
-                for (int p = 0; p < BP; ++p) ost[buf][(vbase + i) * WPK + w * W + p] = wd[p];
-              }
-              if constexpr (QJL) part2[w][vbase + i] = r2;
+              for (int p = 0; p < BP; ++p) ost[buf][(vbase + i) * WPK + w * W + p] = wd[p];
             }
           }
+        }
+        if constexpr (QJL) {
+          // ||rho||^2 over this wave's 32 coordinates: the 8 rows' partial sums
+          // reduced over the 16 lanes of a row by a transposing butterfly (each
+          // stage halves the values a lane keeps); lane r16 ends with the row
+          // 16 b3 + 2 b2 + b0 (bits of r16) of its h2 = b3 half, summed over all
+          // 16 lanes, and lanes r16 and r16 ^ 2 hold the same sum
+          const bool b3 = (r16 & 8) != 0, b2 = (r16 & 4) != 0, b0 = (r16 & 1) != 0;
+          float a4[4], a2[2];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float lo = r2v[0][k], hi = r2v[1][k];
+            a4[k] = (b3 ? hi : lo) + dpp_f<0x128>(b3 ? lo : hi);   // partner r16 ^ 8 (row_ror:8)
+          }
+#pragma unroll
+          for (int k = 0; k < 2; ++k)
+            a2[k] = (b2 ? a4[k + 2] : a4[k]) + dpp_f<0x141>(b2 ? a4[k] : a4[k + 2]);   // partner r16 ^ 7 (row_half_mirror)
+          float t = (b0 ? a2[1] : a2[0]) + dpp_f<0xB1>(b0 ? a2[0] : a2[1]);         // partner r16 ^ 1
+          t += dpp_f<0x4E>(t);                                                        // partner r16 ^ 2
+          if ((r16 & 2) == 0) part2[w][32 * h + 16 * (b3 ? 1 : 0) + 4 * q + 2 * (b2 ? 1 : 0) + (b0 ? 1 : 0)] = t;
         }
       }
       __syncthreads();   // rho complete; every wave done with the x tile
@@ -650,7 +685,7 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
           contract(rl, bSh, h, false, acc);
           contract(rh, bSl, h, false, acc);
           pin_acc(acc);
-          if (w < G) {
+          if (FULL || w < G) {
             uint32_t wd[2][4];
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
@@ -693,15 +728,15 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
         // lane holds coordinate 32w + 16ct + 4q + i, token 32h + 16h2 + r16
         const float sc0 = scl[32 * h + r16], sc1 = scl[32 * h + 16 + r16];
         const uint64_t tm0 = __ballot(32 * h + r16 < rows), tm1 = __ballot(32 * h + 16 + r16 < rows);
-        if (w < G) {
+        if (FULL || w < G) {
 #pragma unroll
           for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int c = 32 * w + 16 * ct + 4 * q + i;
               bool p0, p1, j0[BP > 1 ? BP - 1 : 1], j1[BP > 1 ? BP - 1 : 1];
-              classify(acc[0][ct][i] * sc0, p0, j0);
-              classify(acc[1][ct][i] * sc1, p1, j1);
+              classify(acc[0][ct][i], acc[0][ct][i] * sc0, p0, j0);
+              classify(acc[1][ct][i], acc[1][ct][i] * sc1, p1, j1);
               // sign plane [y > 0]; low planes [bit of j == sign]; padding tokens 0
               const uint64_t s0 = __ballot(p0) & tm0, s1 = __ballot(p1) & tm1;
 #pragma unroll
@@ -811,7 +846,7 @@ static int encode_tile_blocks() {
   return blocks;
 }
 
-template <int LK, int MODE>
+template <int LK, int MODE, bool FULL>
 hipError_t launch_encode_tile_m(const tq_quantizer* q, const void* x, int dtype, int64_t nseq, int64_t n,
                                 uint32_t* codes, float* norms, float* gammas, hipStream_t st) {
   const int64_t tiles = nseq * ((n + kEncRows - 1) / kEncRows);
@@ -819,14 +854,14 @@ hipError_t launch_encode_tile_m(const tq_quantizer* q, const void* x, int dtype,
   const Codebook& cb = q->cb[MODE == 0 ? 0 : 1];
 #define TQ_ENC(BPV)                                                                                                 \
   case BPV:                                                                                                         \
-    hipLaunchKernelGGL((encode_tile_kernel<4, LK, MODE, BPV>), grid, dim3(256), 0, st, x, dtype, nseq, n, q->d,     \
+    hipLaunchKernelGGL((encode_tile_kernel<4, LK, MODE, BPV, FULL>), grid, dim3(256), 0, st, x, dtype, nseq, n, q->d,     \
                        q->d_pi, q->d_sp, cb, codes, norms, gammas);                                               \
     break;
   switch (cb.bp) {
     TQ_ENC(1) TQ_ENC(2) TQ_ENC(3)
     case 4:
       if constexpr (MODE != 0) {
-        hipLaunchKernelGGL((encode_tile_kernel<4, LK, MODE, 4>), grid, dim3(256), 0, st, x, dtype, nseq, n, q->d,
+        hipLaunchKernelGGL((encode_tile_kernel<4, LK, MODE, 4, FULL>), grid, dim3(256), 0, st, x, dtype, nseq, n, q->d,
                            q->d_pi, q->d_sp, cb, codes, norms, gammas);
         break;
       }
@@ -840,9 +875,16 @@ hipError_t launch_encode_tile_m(const tq_quantizer* q, const void* x, int dtype,
 template <int LK>
 hipError_t launch_encode_tile_lk(const tq_quantizer* q, int mode, const void* x, int dtype, int64_t nseq, int64_t n,
                                  uint32_t* codes, float* norms, float* gammas, hipStream_t st) {
-  if (mode == 0) return launch_encode_tile_m<LK, 0>(q, x, dtype, nseq, n, codes, norms, gammas, st);
-  if (mode == 1) return launch_encode_tile_m<LK, 1>(q, x, dtype, nseq, n, codes, norms, gammas, st);
-  return launch_encode_tile_m<LK, 2>(q, x, dtype, nseq, n, codes, norms, gammas, st);
+  // d = 128 (the usual head dimension) takes the variant without coordinate guards
+  constexpr bool F = LK != 0;
+  if (F && q->d == 128) {
+    if (mode == 0) return launch_encode_tile_m<LK, 0, F>(q, x, dtype, nseq, n, codes, norms, gammas, st);
+    if (mode == 1) return launch_encode_tile_m<LK, 1, F>(q, x, dtype, nseq, n, codes, norms, gammas, st);
+    return launch_encode_tile_m<LK, 2, F>(q, x, dtype, nseq, n, codes, norms, gammas, st);
+  }
+  if (mode == 0) return launch_encode_tile_m<LK, 0, false>(q, x, dtype, nseq, n, codes, norms, gammas, st);
+  if (mode == 1) return launch_encode_tile_m<LK, 1, false>(q, x, dtype, nseq, n, codes, norms, gammas, st);
+  return launch_encode_tile_m<LK, 2, false>(q, x, dtype, nseq, n, codes, norms, gammas, st);
 }
 
 hipError_t launch_encode_tile(const tq_quantizer* q, int mode, const void* x, int dtype, int64_t nseq, int64_t n,
