@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--key-mode", default="prod", choices=["prod", "mse"],
                     help="gqa/long: prod keys (b-1 MSE bits + QJL) or MSE-only keys (all b bits to the index)")
     ap.add_argument("--value-bits", type=int, default=None, help="gqa/long: value bits (default: the key bits)")
+    ap.add_argument("--v-threshold", type=float, default=None,
+                    help="gqa/long: sparse V (tq_attend_decode_sparse with this threshold in [0, 1))")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a 256 MiB device copy 3 times (the known-size kernel for counter scaling)")
@@ -247,7 +249,7 @@ def run_gqa(args, torch, dev, tq, wl_fn, name, bits, n_tail=0):
         try:
             c = copies[0]
             tq.tq_attend_decode(qz, qv, q, c[0], c[1], c[2], c[3], c[4], Hkv, n_comp, k_tail, v_tail, 0.0, out=out,
-                                workspace=ws_a)
+                                workspace=ws_a, v_threshold=args.v_threshold)
         except tq.TQError:
             attend_ok = False
     torch.cuda.synchronize()
@@ -268,7 +270,7 @@ def run_gqa(args, torch, dev, tq, wl_fn, name, bits, n_tail=0):
         e4 = timer.mark()
         if attend_ok:
             tq.tq_attend_decode(qz, qv, q, r[0], r[1], r[2], r[3], r[4], Hkv, n_comp, k_tail, v_tail, 0.0, out=out,
-                                workspace=ws_a)
+                                workspace=ws_a, v_threshold=args.v_threshold)
         e5 = timer.mark()
         if timed:
             timer.span("encode_keys", e0, e1)
@@ -314,7 +316,7 @@ def run_gqa(args, torch, dev, tq, wl_fn, name, bits, n_tail=0):
         "config": {"workload": name, "batch": B, "kv_heads": Hkv, "q_heads": Hq, "tokens": N, "tail_bf16": n_tail,
                    "d": d, "bits_keys": bits, "bits_values": vbits,
                    "key_mode": "mse-only (b MSE bits)" if mse_keys else "prod (b-1 MSE + 1 QJL)",
-                   "value_mode": "mse"},
+                   "value_mode": "mse" if args.v_threshold is None else f"mse, sparse V threshold {args.v_threshold}"},
         "packed_pct_of_hbm_peak": round(100 * packed_gbs / HBM_PEAK_GBS, 1),
         "encode_keys_per_s": round(nkeys / (enc_ms * 1e-3), 0),
         "kernels_ms": {k2: round(timer.avg_ms(k2), 4) for k2 in timer.acc},
@@ -504,7 +506,8 @@ def main():
     if args.workload == "gqa":
         bits = args.bits or 3
         res, wl = run_gqa(args, torch, dev, tq, W.gqa_layer, f"gqa-decode-layer b8 kv8 q32 n32768 d128 {bits}-bit", bits)
-        if not args.no_cpu_baseline and args.key_mode == "prod" and bits == 3 and not args.value_bits:
+        if (not args.no_cpu_baseline and args.key_mode == "prod" and bits == 3 and not args.value_bits
+                and args.v_threshold is None):
             res["cpu_baseline"] = cpu_baseline_gqa(wl, args.steps)
     elif args.workload == "long":
         bits = args.bits or 4

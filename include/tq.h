@@ -20,7 +20,8 @@
  *   [wiselychen] ai-coding.wiselychen.com, "Google TurboQuant：KV Cache 壓縮
  *             6x…": section "最猛的社群實作：TurboQuant+" (a Walsh-Hadamard
  *             rotation in a community implementation; near-Gaussian rotated
- *             coordinates)
+ *             coordinates; "Sparse V": the value work of low-weight tokens
+ *             skipped)
  *
  * Conventions
  *   - Every array argument of the compute calls (tq_encode, tq_decode,
@@ -229,6 +230,25 @@ int tq_attend_decode(const tq_quantizer* kq, const tq_quantizer* vq, const void*
                      const float* kgammas, const uint32_t* vcodes, const float* vnorms, int64_t n_comp,
                      const uint16_t* k_tail, const uint16_t* v_tail, int n_tail, float scale, float* out,
                      void* workspace, int64_t ws_bytes, void* stream);
+
+/* Sparse V ([wiselychen] TurboQuant+ table: the value work of low-weight
+ * tokens is skipped).  tq_attend_decode with one more argument, v_threshold in
+ * [0, 1) (TQ_EINVAL otherwise).  The weight of compressed token t is
+ * w_t = p_t * n_t (softmax weight times value norm, the size of its term in
+ * the output).  Tokens are visited in sequence order within chunks of at most
+ * 1024 tokens; a token with w_t < v_threshold * (largest w so far in its
+ * chunk, itself included) leaves the value sum, while its p_t stays in the
+ * normaliser.  A 128-token step in which no weight is left (for any query of
+ * the row tile) skips the value MFMAs.  Tail tokens are never dropped.
+ * Because the running maximum never exceeds the overall one, the dropped set
+ * lies inside D = {t : w_t < v_threshold * max_u w_u}, and each output element
+ * differs from tq_attend_decode's by at most sum_{t in D} p_t |v_t[e]| / sum_t
+ * p_t.  v_threshold = 0 gives tq_attend_decode's result bit for bit. */
+int tq_attend_decode_sparse(const tq_quantizer* kq, const tq_quantizer* vq, const void* queries, int q_dtype,
+                            int B, int Hq, int Hkv, const uint32_t* kcodes, const float* knorms,
+                            const float* kgammas, const uint32_t* vcodes, const float* vnorms, int64_t n_comp,
+                            const uint16_t* k_tail, const uint16_t* v_tail, int n_tail, float scale,
+                            float v_threshold, float* out, void* workspace, int64_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

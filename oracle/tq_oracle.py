@@ -383,6 +383,48 @@ def attend(kq: Quantizer, vq: Quantizer, q, k_idx, k_bits, k_norms, k_gammas,
     return p @ vals
 
 
+def sparse_v_dropset(kq: Quantizer, vq: Quantizer, q, k_idx, k_bits, k_norms, k_gammas, v_idx, v_norms,
+                     v_threshold, k_tail=None, v_tail=None, scale=None, margin=1.0):
+    """Sparse V ([wiselychen] TurboQuant+ table: the value work of low-weight
+    tokens is skipped).  Reading (R26): the weight of compressed token t is
+    w_t = p_t n_t, its softmax weight times its value norm (the size of its
+    term in the output), and a token may leave the value sum when w_t is
+    below v_threshold times the largest weight; its p_t stays in the
+    normaliser.  Returns (p [Hg, N + T] normalised softmax weights, D [Hg, N]
+    boolean: w_t < margin * v_threshold * max_u w_u over compressed u).  An
+    implementation that compares against a running maximum drops a subset of
+    D, since a running maximum never exceeds the overall one."""
+    q = np.asarray(q, dtype=np.float64)
+    d = q.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if k_bits is None:
+        logit = scores_mse(kq, q, k_idx, k_norms)
+    else:
+        logit = scores(kq, q, k_idx, k_bits, k_norms, k_gammas)
+    n_comp = logit.shape[1]
+    if k_tail is not None and len(k_tail):
+        logit = np.concatenate([logit, q @ np.asarray(k_tail, dtype=np.float64).T], axis=1)
+    s = scale * logit
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    w = p[:, :n_comp] * np.asarray(v_norms, dtype=np.float64)[None, :]
+    wmax = w.max(axis=1, keepdims=True) if n_comp else np.zeros((len(q), 1))
+    return p, w < margin * v_threshold * wmax
+
+
+def sparse_v_bound(kq: Quantizer, vq: Quantizer, q, k_idx, k_bits, k_norms, k_gammas, v_idx, v_norms,
+                   v_threshold, k_tail=None, v_tail=None, scale=None, margin=1.0):
+    """Largest change of each output element [Hg, d] that dropping any subset
+    of the set D of sparse_v_dropset from the value sum can cause:
+    sum_{t in D} p_t |v_t[e]| (p normalised over all tokens), by the triangle
+    inequality on out = sum_t p_t v_t."""
+    p, D = sparse_v_dropset(kq, vq, q, k_idx, k_bits, k_norms, k_gammas, v_idx, v_norms, v_threshold,
+                            k_tail, v_tail, scale, margin)
+    vals = decode_mse(vq, v_idx, v_norms)
+    n_comp = D.shape[1]
+    return (p[:, :n_comp] * D) @ np.abs(vals)
+
+
 # ---------------------------------------------------------------------------
 # 8. Top-k by score (vector search with codes, [a2a] benchmark section on
 #    GloVe-style search): order by (score descending, index ascending).

@@ -105,6 +105,12 @@ def test_quantizer_argument_errors():
     assert L.tq_scores(None, None, 0, 1, 1, 1, None, None, None, 1, 0, None, None, None, 0, None) == tq.TQ_EINVAL
     assert L.tq_attend_decode(None, None, None, 0, 1, 1, 1, None, None, None, None, None, 1, None, None, 0,
                               0.0, None, None, 0, None) == tq.TQ_EINVAL
+    assert L.tq_attend_decode_sparse(None, None, None, 0, 1, 1, 1, None, None, None, None, None, 1, None, None, 0,
+                                     0.0, 0.0, None, None, 0, None) == tq.TQ_EINVAL
+    for bad in (-1e-3, 1.0, 2.0, float("nan"), float("inf")):
+        assert L.tq_attend_decode_sparse(None, None, None, 0, 1, 1, 1, None, None, None, None, None, 1, None, None,
+                                         0, 0.0, bad, None, None, 0, None) == tq.TQ_EINVAL
+        assert b"v_threshold" in L.tq_last_error()
     assert L.tq_set_key_mode(None, tq.TQ_MSE_KEYS) == tq.TQ_EINVAL
     assert L.tq_code_words(None, 0, 1, 1) < 0
     assert L.tq_scores_workspace_bytes(None, 1, 1, 1, 1, 0) < 0

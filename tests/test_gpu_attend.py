@@ -159,3 +159,98 @@ def test_attend_steep_logit_drop_within_chunk():
     vt = torch.from_numpy(rng.standard_normal((B * Hkv, N, d)).astype(np.float32)).to(_dev()).bfloat16()
     w = _run_case(kt, vt, qt, B, Hkv, Hq, N, 0, 3, groups=[(0, 0), (7, 7)])
     print("worst relative error", w)
+
+
+def _sparse_run(k, v, q, B, Hkv, Hq, n_comp, n_tail, bits, tau, groups=None):
+    """tq_attend_decode_sparse against the oracle's dense attention: per
+    element |gpu - oracle| <= 1e-3 max(|oracle_e|, ||oracle_row||/sqrt(d)) +
+    the oracle's sparse-V bound (the largest change any allowed drop can make;
+    drop set taken with a 1% margin on the threshold for the GPU's rounding
+    of the weights).  Returns (worst excess ratio, dropped fraction of D)."""
+    d = k.shape[-1]
+    gk, ok = _pair(d, bits, 0)
+    gv, ov = _pair(d, bits, 1)
+    kcodes, kn, kg = tq.tq_encode(gk, tq.TQ_PROD, k[:, :n_comp].contiguous())
+    vcodes, vn, _ = tq.tq_encode(gv, tq.TQ_MSE, v[:, :n_comp].contiguous())
+    kt = k[:, n_comp:].contiguous().view(B, Hkv, n_tail, d) if n_tail else None
+    vt = v[:, n_comp:].contiguous().view(B, Hkv, n_tail, d) if n_tail else None
+    dense = tq.tq_attend_decode(gk, gv, q, kcodes, kn, kg, vcodes, vn, Hkv, n_comp, kt, vt).cpu().numpy()
+    out = tq.tq_attend_decode(gk, gv, q, kcodes, kn, kg, vcodes, vn, Hkv, n_comp, kt, vt,
+                              v_threshold=tau).cpu().numpy()
+    G = Hq // Hkv
+    kw, vw = P.to_u32(kcodes), P.to_u32(vcodes)
+    kn, kg, vn = (t.cpu().numpy().astype(np.float64) for t in (kn, kg, vn))
+    qs = q.float().cpu().numpy().astype(np.float64)
+    kf, vf = k.float().cpu().numpy().astype(np.float64), v.float().cpu().numpy().astype(np.float64)
+    perk, perv = gk.code_words(tq.TQ_PROD, 1, n_comp), gv.code_words(tq.TQ_MSE, 1, n_comp)
+    worst, moved = 0.0, 0.0
+    for (b, h) in (groups or [(b, h) for b in range(B) for h in range(Hkv)]):
+        s = b * Hkv + h
+        ki, kb = o.unpack_prod(kw[s * perk:(s + 1) * perk].reshape(n_comp, -1), bits - 1, d)
+        vi = o.unpack_mse(vw[s * perv:(s + 1) * perv], n_comp, bits, d)
+        sl = slice(s * n_comp, (s + 1) * n_comp)
+        qq = qs[b, h * G:(h + 1) * G]
+        tails = (kf[s, n_comp:], vf[s, n_comp:]) if n_tail else (None, None)
+        ref = o.attend(ok, ov, qq, ki, kb, kn[sl], kg[sl], vi, vn[sl], *tails)
+        bound = o.sparse_v_bound(ok, ov, qq, ki, kb, kn[sl], kg[sl], vi, vn[sl], tau, *tails, margin=1.01)
+        floor = np.linalg.norm(ref, axis=1, keepdims=True) / math.sqrt(d)
+        tol = 1e-3 * np.maximum(np.abs(ref), floor) + bound
+        err = np.abs(out[b, h * G:(h + 1) * G] - ref)
+        assert np.all(err <= tol + 1e-30), f"sparse V error beyond the bound ({np.max(err / tol):.3g})"
+        worst = max(worst, float(np.max(err / tol)))
+        moved = max(moved, float(np.max(np.abs(out[b, h * G:(h + 1) * G] - dense[b, h * G:(h + 1) * G]))))
+    return worst, moved
+
+
+@pytest.mark.parametrize("B,Hkv,Hq,N,tail,bits", [(2, 2, 8, 1000, 0, 3), (1, 2, 8, 777, 37, 4), (2, 8, 32, 4096, 0, 3)])
+def test_attend_sparse_zero_threshold_is_dense(B, Hkv, Hq, N, tail, bits):
+    """v_threshold = 0 reproduces tq_attend_decode bit for bit."""
+    print(f"case: attend sparse tau=0 B={B} Hkv={Hkv} Hq={Hq} N={N} tail={tail} bits={bits}", flush=True)
+    k, v, q = _gqa_inputs(B, Hkv, Hq, N, 128, seed=N + 5)
+    gk, _ = _pair(128, bits, 0)
+    gv, _ = _pair(128, bits, 1)
+    kc, kn, kg = tq.tq_encode(gk, tq.TQ_PROD, k[:, :N - tail].contiguous())
+    vc, vn, _ = tq.tq_encode(gv, tq.TQ_MSE, v[:, :N - tail].contiguous())
+    kt = k[:, N - tail:].contiguous().view(B, Hkv, tail, 128) if tail else None
+    vt = v[:, N - tail:].contiguous().view(B, Hkv, tail, 128) if tail else None
+    a = tq.tq_attend_decode(gk, gv, q, kc, kn, kg, vc, vn, Hkv, N - tail, kt, vt)
+    b = tq.tq_attend_decode(gk, gv, q, kc, kn, kg, vc, vn, Hkv, N - tail, kt, vt, v_threshold=0.0)
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("B,Hkv,Hq,N,tail,bits,tau,qscale", [
+    (2, 2, 8, 1000, 0, 3, 1e-4, 1.0), (1, 2, 8, 777, 37, 4, 1e-2, 1.0), (2, 8, 32, 4096, 0, 3, 0.3, 3.0),
+    (1, 4, 16, 3000, 100, 3, 1e-3, 3.0), (1, 1, 4, 129, 0, 2, 0.9, 1.0)])
+def test_attend_sparse_within_bound(B, Hkv, Hq, N, tail, bits, tau, qscale):
+    """Sparse V against the oracle's dense attention plus the drop bound;
+    qscale 3 makes the softmax peaked (logits / sqrt(d) with std about 9) so
+    that whole 128-token steps drop out and skip their value MFMAs."""
+    print(f"case: attend sparse tau={tau} B={B} Hkv={Hkv} Hq={Hq} N={N} tail={tail} bits={bits} qscale={qscale}",
+          flush=True)
+    k, v, q = _gqa_inputs(B, Hkv, Hq, N, 128, seed=N + 11)
+    q = (q.float() * qscale).bfloat16()
+    worst, moved = _sparse_run(k, v, q, B, Hkv, Hq, N - tail, tail, bits, tau, groups=[(0, 0), (B - 1, Hkv - 1)])
+    print("worst error / tolerance", worst, "largest change from dense", moved)
+
+
+def test_attend_sparse_full_size_gqa():
+    """The GQA decode layer at full size with v_threshold 1e-3."""
+    print("case: attend sparse full size gqa tau=1e-3", flush=True)
+    wl = W.gqa_layer()
+    B, Hkv, Hq, N = wl.meta["B"], wl.meta["Hkv"], wl.meta["Hq"], wl.meta["N"]
+    k = _bf16(wl.arrays["k_bf16"]).view(B * Hkv, N, 128)
+    v = _bf16(wl.arrays["v_bf16"]).view(B * Hkv, N, 128)
+    q = _bf16(wl.arrays["q_bf16"])
+    worst, moved = _sparse_run(k, v, q, B, Hkv, Hq, N, 0, wl.bits, 1e-3, groups=[(0, 0), (B - 1, Hkv - 1)])
+    print("worst error / tolerance", worst, "largest change from dense", moved)
+
+
+def test_attend_sparse_rejects_bad_threshold():
+    k, v, q = _gqa_inputs(1, 1, 4, 64, 128, seed=3)
+    gk, _ = _pair(128, 3, 0)
+    gv, _ = _pair(128, 3, 1)
+    kc, kn, kg = tq.tq_encode(gk, tq.TQ_PROD, k.contiguous())
+    vc, vn, _ = tq.tq_encode(gv, tq.TQ_MSE, v.contiguous())
+    for bad in (-0.1, 1.0, float("nan")):
+        with pytest.raises(RuntimeError):
+            tq.tq_attend_decode(gk, gv, q, kc, kn, kg, vc, vn, 1, 64, v_threshold=bad)

@@ -121,3 +121,72 @@ def test_topk_parity_helper_accepts_ties_and_rejects_wrong_keys():
     i3[1, 1] = int(np.argmin(ref[1]))      # the worst key is no top-2 key
     with pytest.raises(AssertionError):
         P.check_topk(ref[np.arange(2)[:, None], i3].astype(np.float32), i3, ref, qn, kn, 16)
+
+
+def _sparse_case(seed, tau, spread=3.0):
+    kq, vq, q, (ki, kb, kn, kg), (vi, vn), kt, vt = _setup(N=300, seed=seed)
+    q = q * spread
+    return kq, vq, q, (ki, kb, kn, kg), (vi, vn), kt, vt
+
+
+def test_sparse_v_threshold_zero_drops_nothing():
+    kq, vq, q, (ki, kb, kn, kg), (vi, vn), kt, vt = _sparse_case(5, 0.0)
+    p, D = o.sparse_v_dropset(kq, vq, q, ki, kb, kn, kg, vi, vn, 0.0, kt, vt)
+    assert not D.any()
+    assert np.allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+    assert np.max(o.sparse_v_bound(kq, vq, q, ki, kb, kn, kg, vi, vn, 0.0, kt, vt)) == 0.0
+
+
+@pytest.mark.parametrize("tau", [1e-4, 1e-2, 0.3])
+def test_sparse_v_bound_covers_every_allowed_drop(tau):
+    # Any subset S of the drop set D, removed from the value sum of the dense
+    # textbook attention (decoded matrices, scipy softmax, values of S set to
+    # 0), moves each output element by at most the oracle's bound.
+    kq, vq, q, (ki, kb, kn, kg), (vi, vn), kt, vt = _sparse_case(6, tau)
+    d = q.shape[1]
+    Kd = np.concatenate([o.decode_prod(kq, ki, kb, kn, kg), kt])
+    Vd = np.concatenate([o.decode_mse(vq, vi, vn), vt])
+    p = special.softmax(q @ Kd.T / math.sqrt(d), axis=1)
+    dense = p @ Vd
+    _, D = o.sparse_v_dropset(kq, vq, q, ki, kb, kn, kg, vi, vn, tau, kt, vt)
+    bound = o.sparse_v_bound(kq, vq, q, ki, kb, kn, kg, vi, vn, tau, kt, vt)
+    assert D.any()
+    rng = np.random.default_rng(7)
+    for trial in range(6):
+        for r in range(len(q)):
+            S = D[r] & (rng.random(D.shape[1]) < (1.0 if trial == 0 else 0.5))
+            V2 = Vd.copy()
+            V2[:len(vi)][S] = 0.0
+            out = p[r] @ V2
+            assert np.all(np.abs(out - dense[r]) <= bound[r] + 1e-12)
+    # the whole of D reaches the bound on some element only when the dropped
+    # terms share a sign there; it is never exceeded
+    assert np.all(bound >= 0)
+
+
+def test_sparse_v_running_max_drops_a_subset():
+    # The rule against the running maximum of the chunk (sequence order,
+    # 16-token steps, each step's maximum included before its tokens are
+    # judged) never drops a token outside D: the running maximum is at most
+    # the overall one.  Written here as a plain loop, independent of the
+    # oracle's set construction.
+    tau = 0.05
+    kq, vq, q, (ki, kb, kn, kg), (vi, vn), kt, vt = _sparse_case(8, tau, spread=5.0)
+    d = q.shape[1]
+    logit = o.scores(kq, q, ki, kb, kn, kg)
+    _, D = o.sparse_v_dropset(kq, vq, q, ki, kb, kn, kg, vi, vn, tau, None, None)
+    for r in range(len(q)):
+        s = logit[r] / math.sqrt(d)
+        w = np.exp(s - s.max()) * vn
+        run = 0.0
+        for t0 in range(0, len(s), 16):
+            run = max(run, w[t0:t0 + 16].max())
+            drop = w[t0:t0 + 16] < tau * run
+            assert np.all(D[r, t0:t0 + 16][drop])
+
+
+def test_sparse_v_dropset_grows_with_the_threshold():
+    kq, vq, q, (ki, kb, kn, kg), (vi, vn), kt, vt = _sparse_case(9, 0.0)
+    sets = [o.sparse_v_dropset(kq, vq, q, ki, kb, kn, kg, vi, vn, tau, kt, vt)[1] for tau in (1e-6, 1e-3, 0.1, 0.9)]
+    for a, b in zip(sets, sets[1:]):
+        assert np.all(b[a])

@@ -395,10 +395,12 @@ int64_t tq_attend_workspace_bytes(const tq_quantizer* kq, const tq_quantizer* vq
   return tq::attend_ws_bytes(kq, vq, B, Hq, Hkv, n_comp, n_tail);
 }
 
-int tq_attend_decode(const tq_quantizer* kq, const tq_quantizer* vq, const void* queries, int q_dtype, int B, int Hq,
-                     int Hkv, const uint32_t* kcodes, const float* knorms, const float* kgammas, const uint32_t* vcodes,
-                     const float* vnorms, int64_t n_comp, const uint16_t* k_tail, const uint16_t* v_tail, int n_tail,
-                     float scale, float* out, void* workspace, int64_t ws_bytes, void* stream) {
+int tq_attend_decode_sparse(const tq_quantizer* kq, const tq_quantizer* vq, const void* queries, int q_dtype, int B,
+                            int Hq, int Hkv, const uint32_t* kcodes, const float* knorms, const float* kgammas,
+                            const uint32_t* vcodes, const float* vnorms, int64_t n_comp, const uint16_t* k_tail,
+                            const uint16_t* v_tail, int n_tail, float scale, float v_threshold, float* out,
+                            void* workspace, int64_t ws_bytes, void* stream) {
+  if (!(v_threshold >= 0.f && v_threshold < 1.f)) return fail(TQ_EINVAL, "v_threshold must lie in [0, 1)");
   if (int r = check_quantizer(kq)) return r;
   if (int r = check_quantizer(vq)) return r;
   if (int r = check_heads(B, Hq, Hkv)) return r;
@@ -425,9 +427,18 @@ int tq_attend_decode(const tq_quantizer* kq, const tq_quantizer* vq, const void*
   DeviceGuard g(kq->device);
   if (!g.ok) return fail(TQ_EHIP, "cannot select the quantizer's device");
   hipError_t e = tq::launch_attend(kq, vq, queries, q_dtype, B, Hq, Hkv, kcodes, knorms, kgammas, vcodes, vnorms, n_comp,
-                                   k_tail, v_tail, n_tail, scale, out, workspace, static_cast<hipStream_t>(stream));
+                                   k_tail, v_tail, n_tail, scale, v_threshold, out, workspace,
+                                   static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) return fail(TQ_EUNSUPPORTED, "shape not supported by the attention kernels");
   return e == hipSuccess ? TQ_OK : hip_fail(e, "attend launch");
+}
+
+int tq_attend_decode(const tq_quantizer* kq, const tq_quantizer* vq, const void* queries, int q_dtype, int B, int Hq,
+                     int Hkv, const uint32_t* kcodes, const float* knorms, const float* kgammas, const uint32_t* vcodes,
+                     const float* vnorms, int64_t n_comp, const uint16_t* k_tail, const uint16_t* v_tail, int n_tail,
+                     float scale, float* out, void* workspace, int64_t ws_bytes, void* stream) {
+  return tq_attend_decode_sparse(kq, vq, queries, q_dtype, B, Hq, Hkv, kcodes, knorms, kgammas, vcodes, vnorms, n_comp,
+                                 k_tail, v_tail, n_tail, scale, 0.f, out, workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -108,7 +108,7 @@ template <int BPK, int BPV, int NSLOT, bool QJL>
 __device__ __forceinline__ void attend_chunk_body(
     const uint32_t* __restrict__ kcodes, const float* __restrict__ knorms, const float* __restrict__ kgammas,
     const uint32_t* __restrict__ vcodes, const float* __restrict__ vnorms, int64_t n, int64_t chunk, int G, int RT,
-    float scale_log2, const uint8_t* __restrict__ wsA, const float* __restrict__ wsC, const Codebook& vcb,
+    float scale_log2, float vtau, const uint8_t* __restrict__ wsA, const float* __restrict__ wsC, const Codebook& vcb,
     float* __restrict__ part) {
   constexpr int d = 128;
   constexpr int TK = (1 << (BPK - 1)) + (QJL ? 1 : 0);   // key MFMA terms (Walsh + QJL)
@@ -122,7 +122,7 @@ __device__ __forceinline__ void attend_chunk_body(
   __shared__ __attribute__((aligned(16))) uint32_t stage[NSLOT][SLOT];
   __shared__ float sc[4][kStep];             // scaled logits (base 2)
   __shared__ __attribute__((aligned(16))) uint32_t av[64 * 8];   // value A operand (fp8 limbs)
-  __shared__ float qst[4][4];                // per query: rescale factor, E
+  __shared__ float qst[4][4];                // per query: rescale factor, E, value work left in the step
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int gy = blockIdx.y;
@@ -252,7 +252,7 @@ __device__ __forceinline__ void attend_chunk_body(
       const float* vns = kns + 2 * kStep;
       const float na = tA < live ? vns[tA] : 0.f;
       const float nb2 = tB < live ? vns[tB] : 0.f;
-      const float wa = pa * na, wb = pb * nb2;
+      float wa = pa * na, wb = pb * nb2;
       l_lane = fmaf(l_lane, alpha, pa + pb);
       m_run = m_new;
       // the limb exponent follows the running max weight, so the accumulator
@@ -262,9 +262,19 @@ __device__ __forceinline__ void attend_chunk_body(
       if (__ballot(wa > wmax || wb > wmax) != 0ull) wmax = fmaxf(wmax, wave_max(fmaxf(wa, wb)));
       // the weights are quantised on the grid 2^(-12 - e): wmax 2^e lands in [8, 16)
       const int e_new = wmax > 0.f ? 3 - ilogb_pos(wmax) : e_run;
+      // sparse V: a token whose weight is below vtau times the largest weight
+      // of the chunk so far leaves the value sum (its p stays in the
+      // normaliser); a step with no weight left skips the value MFMAs
+      if (vtau > 0.f) {
+        const float thr = vtau * wmax;
+        wa = wa < thr ? 0.f : wa;
+        wb = wb < thr ? 0.f : wb;
+      }
+      const bool vwork = __ballot(wa > 0.f || wb > 0.f) != 0ull;
       if (lane == 0) {
         qst[q][0] = ldexpf(alpha, e_new - e_run);   // accumulator rescale for this query
         qst[q][1] = static_cast<float>(e_new);
+        qst[q][2] = vwork ? 1.f : 0.f;
       }
       e_run = e_new;
       // A operand of the value MFMA: rows 4q + limb, K = token slot.  The
@@ -298,8 +308,9 @@ __device__ __forceinline__ void attend_chunk_body(
       }
       // lane group g reads the 32-token block g of the step; blocks past the
       // end hold re-read words, which meet zero weights
+      const bool vwork = vtau <= 0.f || qst[0][2] != 0.f || qst[1][2] != 0.f || qst[2][2] != 0.f || qst[3][2] != 0.f;
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
+      for (int ct = 0; ct < 2 && vwork; ++ct) {
         const int col = 32 * wave + 16 * ct + j;
         uint32_t w[5] = {0u, 0u, 0u, 0u, 0u};
 #pragma unroll
@@ -351,10 +362,10 @@ template <int BPK, int BPV, bool QJL>
 __global__ void __launch_bounds__(256) attend_chunk_kernel(
     const uint32_t* __restrict__ kcodes, const float* __restrict__ knorms, const float* __restrict__ kgammas,
     const uint32_t* __restrict__ vcodes, const float* __restrict__ vnorms, int64_t n, int64_t chunk, int G, int RT,
-    float scale_log2, const uint8_t* __restrict__ wsA, const float* __restrict__ wsC, Codebook vcb,
+    float scale_log2, float vtau, const uint8_t* __restrict__ wsA, const float* __restrict__ wsC, Codebook vcb,
     float* __restrict__ part) {
-  attend_chunk_body<BPK, BPV, 3, QJL>(kcodes, knorms, kgammas, vcodes, vnorms, n, chunk, G, RT, scale_log2, wsA, wsC, vcb,
-                                 part);
+  attend_chunk_body<BPK, BPV, 3, QJL>(kcodes, knorms, kgammas, vcodes, vnorms, n, chunk, G, RT, scale_log2, vtau, wsA,
+                                      wsC, vcb, part);
 }
 
 // One workgroup (256 threads) per (batch, query head): combine the chunk
@@ -504,7 +515,8 @@ __global__ void __launch_bounds__(256) attend_merge_kernel(const void* __restric
 hipError_t launch_attend(const tq_quantizer* kq, const tq_quantizer* vq, const void* queries, int q_dtype, int B, int Hq,
                          int Hkv, const uint32_t* kcodes, const float* knorms, const float* kgammas,
                          const uint32_t* vcodes, const float* vnorms, int64_t n_comp, const uint16_t* k_tail,
-                         const uint16_t* v_tail, int n_tail, float scale, float* out, void* ws, hipStream_t st) {
+                         const uint16_t* v_tail, int n_tail, float scale, float vtau, float* out, void* ws,
+                         hipStream_t st) {
   if (kq->d != 128 || n_tail > 512) return hipErrorNotSupported;
   const int G = Hq / Hkv;
   const int RT = (G + 3) / 4;
@@ -527,7 +539,7 @@ hipError_t launch_attend(const tq_quantizer* kq, const tq_quantizer* vq, const v
 #define TQ_AT(K, V, QV)                                                                                       \
   if (bpk == K && bpv == V && qjl == QV) {                                                                    \
     hipLaunchKernelGGL((attend_chunk_kernel<K, V, QV>), grid, dim3(256), 0, st, kcodes, knorms, kgammas, vcodes, \
-                       vnorms, n_comp, ch, G, RT, sl, wsA, wsC, vq->cb[1], part);                            \
+                       vnorms, n_comp, ch, G, RT, sl, vtau, wsA, wsC, vq->cb[1], part);                      \
   } else
 #define TQ_AT4(K, QV) TQ_AT(K, 1, QV) TQ_AT(K, 2, QV) TQ_AT(K, 3, QV) TQ_AT(K, 4, QV)
     TQ_AT4(1, true) TQ_AT4(2, true) TQ_AT4(3, true)

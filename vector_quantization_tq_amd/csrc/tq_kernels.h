@@ -33,7 +33,8 @@ int64_t attend_ws_bytes(const tq_quantizer* kq, const tq_quantizer* vq, int B, i
 hipError_t launch_attend(const tq_quantizer* kq, const tq_quantizer* vq, const void* queries, int q_dtype, int B, int Hq,
                          int Hkv, const uint32_t* kcodes, const float* knorms, const float* kgammas,
                          const uint32_t* vcodes, const float* vnorms, int64_t n_comp, const uint16_t* k_tail,
-                         const uint16_t* v_tail, int n_tail, float scale, float* out, void* ws, hipStream_t st);
+                         const uint16_t* v_tail, int n_tail, float scale, float vtau, float* out, void* ws,
+                         hipStream_t st);
 
 hipError_t set_kernel_attributes();
 

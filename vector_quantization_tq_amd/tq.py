@@ -24,7 +24,7 @@ EXPORTS = [
     "tq_version", "tq_last_error", "tq_host_normals", "tq_host_rotation", "tq_host_rotation_hadamard",
     "tq_host_qjl_matrix", "tq_host_codebook", "tq_make_quantizer", "tq_make_quantizer_ex", "tq_free_quantizer", "tq_quantizer_info", "tq_set_key_mode", "tq_code_words", "tq_encode",
     "tq_decode", "tq_scores_workspace_bytes", "tq_query_prep", "tq_scores_from_prep", "tq_scores",
-    "tq_attend_workspace_bytes", "tq_attend_decode",
+    "tq_attend_workspace_bytes", "tq_attend_decode", "tq_attend_decode_sparse",
 ]
 
 
@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
         "tq_attend_workspace_bytes": (c_i64, [c_p, c_p, c_i, c_i, c_i, c_i64, c_i]),
         "tq_attend_decode": (c_i, [c_p, c_p, c_p, c_i, c_i, c_i, c_i, c_p, c_p, c_p, c_p, c_p, c_i64, c_p, c_p, c_i,
                                    c_f, c_p, c_p, c_i64, c_p]),
+        "tq_attend_decode_sparse": (c_i, [c_p, c_p, c_p, c_i, c_i, c_i, c_i, c_p, c_p, c_p, c_p, c_p, c_i64, c_p, c_p,
+                                          c_i, c_f, c_f, c_p, c_p, c_i64, c_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -290,8 +292,10 @@ def attend_workspace_bytes(kq: Quantizer, vq: Quantizer, B: int, Hq: int, Hkv: i
 
 
 def tq_attend_decode(kq: Quantizer, vq: Quantizer, q, kcodes, knorms, kgammas, vcodes, vnorms, Hkv: int,
-                     n_comp: int, k_tail=None, v_tail=None, scale: float = 0.0, out=None, workspace=None):
-    """q: [B, Hq, d]; tails: [B, Hkv, n_tail, d] bfloat16 or None.  Returns [B, Hq, d] float32."""
+                     n_comp: int, k_tail=None, v_tail=None, scale: float = 0.0, out=None, workspace=None,
+                     v_threshold=None):
+    """q: [B, Hq, d]; tails: [B, Hkv, n_tail, d] bfloat16 or None.  Returns [B, Hq, d] float32.
+    v_threshold (a float in [0, 1)) calls tq_attend_decode_sparse instead."""
     torch = _torch()
     _need_cuda(q, kcodes, knorms, kgammas, vcodes, vnorms, k_tail, v_tail)
     B, Hq, d = q.shape
@@ -304,8 +308,14 @@ def tq_attend_decode(kq: Quantizer, vq: Quantizer, q, kcodes, knorms, kgammas, v
     if workspace is None:
         workspace = torch.empty(max(attend_workspace_bytes(kq, vq, B, Hq, Hkv, n_comp, n_tail), 256),
                                 dtype=torch.uint8, device=dev)
-    _check(lib().tq_attend_decode(kq.handle, vq.handle, _ptr(q), _dtype_code(q), B, Hq, Hkv, _ptr(kcodes),
-                                  _ptr(knorms), _ptr(kgammas), _ptr(vcodes), _ptr(vnorms), n_comp, _ptr(k_tail),
-                                  _ptr(v_tail), n_tail, scale, _ptr(out), _ptr(workspace), workspace.numel(),
-                                  _stream()))
+    if v_threshold is None:
+        _check(lib().tq_attend_decode(kq.handle, vq.handle, _ptr(q), _dtype_code(q), B, Hq, Hkv, _ptr(kcodes),
+                                      _ptr(knorms), _ptr(kgammas), _ptr(vcodes), _ptr(vnorms), n_comp, _ptr(k_tail),
+                                      _ptr(v_tail), n_tail, scale, _ptr(out), _ptr(workspace), workspace.numel(),
+                                      _stream()))
+    else:
+        _check(lib().tq_attend_decode_sparse(kq.handle, vq.handle, _ptr(q), _dtype_code(q), B, Hq, Hkv,
+                                             _ptr(kcodes), _ptr(knorms), _ptr(kgammas), _ptr(vcodes), _ptr(vnorms),
+                                             n_comp, _ptr(k_tail), _ptr(v_tail), n_tail, scale, float(v_threshold),
+                                             _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
     return out
