@@ -103,8 +103,10 @@ __device__ __forceinline__ void dma_tok(float* dst, const float* src, int64_t t0
   __builtin_amdgcn_global_load_lds(src + t, as_lds(dst), 4, 0, 0);
 }
 
-// QJL: prod keys (QJL plane + gammas); without it MSE-only keys.
-template <int BPK, int BPV, int NSLOT, bool QJL>
+// QJL: prod keys (QJL plane + gammas); without it MSE-only keys.  SPARSE:
+// the sparse-V threshold vtau is applied (a separate instantiation, so that
+// the dense kernel carries none of its cost).
+template <int BPK, int BPV, int NSLOT, bool QJL, bool SPARSE>
 __device__ __forceinline__ void attend_chunk_body(
     const uint32_t* __restrict__ kcodes, const float* __restrict__ knorms, const float* __restrict__ kgammas,
     const uint32_t* __restrict__ vcodes, const float* __restrict__ vnorms, int64_t n, int64_t chunk, int G, int RT,
@@ -265,16 +267,16 @@ __device__ __forceinline__ void attend_chunk_body(
       // sparse V: a token whose weight is below vtau times the largest weight
       // of the chunk so far leaves the value sum (its p stays in the
       // normaliser); a step with no weight left skips the value MFMAs
-      if (vtau > 0.f) {
+      if constexpr (SPARSE) {
         const float thr = vtau * wmax;
         wa = wa < thr ? 0.f : wa;
         wb = wb < thr ? 0.f : wb;
+        const bool vwork = __ballot(wa > 0.f || wb > 0.f) != 0ull;
+        if (lane == 0) qst[q][2] = vwork ? 1.f : 0.f;
       }
-      const bool vwork = __ballot(wa > 0.f || wb > 0.f) != 0ull;
       if (lane == 0) {
         qst[q][0] = ldexpf(alpha, e_new - e_run);   // accumulator rescale for this query
         qst[q][1] = static_cast<float>(e_new);
-        qst[q][2] = vwork ? 1.f : 0.f;
       }
       e_run = e_new;
       // A operand of the value MFMA: rows 4q + limb, K = token slot.  The
@@ -308,7 +310,8 @@ __device__ __forceinline__ void attend_chunk_body(
       }
       // lane group g reads the 32-token block g of the step; blocks past the
       // end hold re-read words, which meet zero weights
-      const bool vwork = vtau <= 0.f || qst[0][2] != 0.f || qst[1][2] != 0.f || qst[2][2] != 0.f || qst[3][2] != 0.f;
+      bool vwork = true;
+      if constexpr (SPARSE) vwork = qst[0][2] != 0.f || qst[1][2] != 0.f || qst[2][2] != 0.f || qst[3][2] != 0.f;
 #pragma unroll
       for (int ct = 0; ct < 2 && vwork; ++ct) {
         const int col = 32 * wave + 16 * ct + j;
@@ -358,14 +361,14 @@ __device__ __forceinline__ void attend_chunk_body(
   }
 }
 
-template <int BPK, int BPV, bool QJL>
+template <int BPK, int BPV, bool QJL, bool SPARSE>
 __global__ void __launch_bounds__(256) attend_chunk_kernel(
     const uint32_t* __restrict__ kcodes, const float* __restrict__ knorms, const float* __restrict__ kgammas,
     const uint32_t* __restrict__ vcodes, const float* __restrict__ vnorms, int64_t n, int64_t chunk, int G, int RT,
     float scale_log2, float vtau, const uint8_t* __restrict__ wsA, const float* __restrict__ wsC, Codebook vcb,
     float* __restrict__ part) {
-  attend_chunk_body<BPK, BPV, 3, QJL>(kcodes, knorms, kgammas, vcodes, vnorms, n, chunk, G, RT, scale_log2, vtau, wsA,
-                                      wsC, vcb, part);
+  attend_chunk_body<BPK, BPV, 3, QJL, SPARSE>(kcodes, knorms, kgammas, vcodes, vnorms, n, chunk, G, RT, scale_log2, vtau,
+                                              wsA, wsC, vcb, part);
 }
 
 // One workgroup (256 threads) per (batch, query head): combine the chunk
@@ -538,8 +541,12 @@ hipError_t launch_attend(const tq_quantizer* kq, const tq_quantizer* vq, const v
     const bool qjl = key_qjl(kq);
 #define TQ_AT(K, V, QV)                                                                                       \
   if (bpk == K && bpv == V && qjl == QV) {                                                                    \
-    hipLaunchKernelGGL((attend_chunk_kernel<K, V, QV>), grid, dim3(256), 0, st, kcodes, knorms, kgammas, vcodes, \
-                       vnorms, n_comp, ch, G, RT, sl, vtau, wsA, wsC, vq->cb[1], part);                      \
+    if (vtau > 0.f)                                                                                           \
+      hipLaunchKernelGGL((attend_chunk_kernel<K, V, QV, true>), grid, dim3(256), 0, st, kcodes, knorms, kgammas,  \
+                         vcodes, vnorms, n_comp, ch, G, RT, sl, vtau, wsA, wsC, vq->cb[1], part);             \
+    else                                                                                                      \
+      hipLaunchKernelGGL((attend_chunk_kernel<K, V, QV, false>), grid, dim3(256), 0, st, kcodes, knorms, kgammas, \
+                         vcodes, vnorms, n_comp, ch, G, RT, sl, 0.f, wsA, wsC, vq->cb[1], part);              \
   } else
 #define TQ_AT4(K, QV) TQ_AT(K, 1, QV) TQ_AT(K, 2, QV) TQ_AT(K, 3, QV) TQ_AT(K, 4, QV)
     TQ_AT4(1, true) TQ_AT4(2, true) TQ_AT4(3, true)
