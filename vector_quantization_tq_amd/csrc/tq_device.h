@@ -68,6 +68,13 @@ __device__ __forceinline__ float row_max16(float v) {
   v = fmaxf(v, dpp_f<0x128>(v));
   return v;
 }
+__device__ __forceinline__ float row_min16(float v) {
+  v = fminf(v, dpp_f<0xB1>(v));
+  v = fminf(v, dpp_f<0x4E>(v));
+  v = fminf(v, dpp_f<0x124>(v));
+  v = fminf(v, dpp_f<0x128>(v));
+  return v;
+}
 __device__ __forceinline__ float lane_f(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }

@@ -132,14 +132,14 @@ int64_t topk_ws_bytes(const tq_quantizer* q, int B, int Hq, int Hkv, int64_t n, 
 }
 
 // QJL: prod keys (with the QJL plane and gammas); without it MSE-only keys.
+// Three workgroups per CU where the query operands leave room (the
+// compiler would otherwise take a few more registers and drop to two).
 template <int BP, int GW, int KK, bool QJL>
-__global__ void __launch_bounds__(256) topk_scan_kernel(const uint32_t* __restrict__ codes,
-                                                        const float* __restrict__ norms,
-                                                        const float* __restrict__ gammas, int64_t n, int RT,
-                                                        int64_t rg_per_seq, int64_t rg_count, int64_t slices,
-                                                        int64_t slice_keys, int topk, const uint8_t* __restrict__ wsA,
-                                                        const float* __restrict__ wsC, float* __restrict__ cand_s,
-                                                        int* __restrict__ cand_i) {
+__global__ void __launch_bounds__(256, (KK <= 16 && ((1 << (BP - 1)) + QJL) * ((GW + 3) / 4) <= 10) ? 3 : 1)
+    topk_scan_kernel(const uint32_t* __restrict__ codes, const float* __restrict__ norms,
+                     const float* __restrict__ gammas, int64_t n, int RT, int64_t rg_per_seq, int64_t rg_count,
+                     int64_t slices, int64_t slice_keys, int topk, const uint8_t* __restrict__ wsA,
+                     const float* __restrict__ wsC, float* __restrict__ cand_s, int* __restrict__ cand_i) {
   constexpr int T = (1 << (BP - 1)) + (QJL ? 1 : 0);
   constexpr int W = BP + (QJL ? 1 : 0);
   constexpr int C = (GW + 3) / 4;
@@ -234,7 +234,13 @@ __global__ void __launch_bounds__(256) topk_scan_kernel(const uint32_t* __restri
 #pragma unroll
       for (int k = 1; k < KK; ++k)
         if (k == topk - 1) kth = ls[k];
-      const float tau = row_max16(kth);
+      // A second bound: each of the 16 lanes holds j + 1 scores at least its
+      // entry j, so the smallest entry j over the lanes is at most the query's
+      // k-th best when 16 (j + 1) >= k.  With j = (k - 1) / 16 this takes the
+      // lanes' best scores, which rank near the query's top k (the first
+      // bound, a single lane's k-th best, ranks near its 16 k-th).
+      const float topj = (KK > 16 && topk > 16) ? ls[1] : ls[0];
+      const float tau = fmaxf(row_max16(kth), row_min16(topj));
       const uint32_t* kw = buf[slot];
       const float* kn = reinterpret_cast<const float*>(kw + BW);
       const int64_t k0 = k_begin + static_cast<int64_t>(bi) * kTopBlockKeys;
