@@ -29,7 +29,10 @@ namespace {
 constexpr int kTopBlockKeys = 64;
 
 // (s, i) ranks before (t, j): higher score, ties to the lower index
-__device__ __forceinline__ bool ranks_before(float s, int i, float t, int j) { return s > t || (s == t && i < j); }
+// (bitwise, so that no operand is evaluated under a branch)
+__device__ __forceinline__ bool ranks_before(float s, int i, float t, int j) {
+  return static_cast<bool>(static_cast<int>(s > t) | (static_cast<int>(s == t) & static_cast<int>(i < j)));
+}
 
 // insert into a list sorted by ranks_before; the last entry falls off
 template <int KK>
