@@ -88,6 +88,7 @@ def _topk_case(d, bits, B, Hkv, Hq, n, topk, keys=None, seed=0, bf16=False):
     (64, 2, 1, 1, 9, 5000, 32),       # the 32-entry lists
     (64, 2, 1, 1, 9, 5000, 17),
     (48, 4, 1, 1, 3, 64, 16),
+    (128, 3, 1, 2, 8, 3000, 13),      # the 16-entry lists above the 12-entry ones
     (16, 2, 1, 1, 5, 12, 12),         # k == n
 ])
 def test_topk_shapes(d, bits, B, Hkv, Hq, n, topk):

@@ -354,19 +354,23 @@ hipError_t launch_topk(const tq_quantizer* q, const void* queries, int q_dtype, 
   const int bp = key_codebook(q).bp;
   const bool qjl = key_qjl(q);
   const int gw = (q->d + 31) / 32;
-  const bool big = topk > 16;
+  // per-lane list length: the shortest of 12, 16, 32 that holds k entries
+  // (the insertion cost grows with it)
+  const int kk = topk <= 12 ? 12 : (topk <= 16 ? 16 : 32);
   bool launched = false;
-#define TQ_TK(BPV, GWV, QV)                                                                                          \
-  if (!launched && bp == BPV && gw == GWV && qjl == QV) {                                                            \
-    if (big)                                                                                                         \
-      hipLaunchKernelGGL((topk_scan_kernel<BPV, GWV, 32, QV>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, \
-                         codes, norms, gammas, n, p.RT, p.rg_per_seq, p.rg_count, p.slices, p.slice_keys, topk, wsA,   \
-                         wsC, cs, ci);                                                                               \
-    else                                                                                                             \
-      hipLaunchKernelGGL((topk_scan_kernel<BPV, GWV, 16, QV>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, \
-                         codes, norms, gammas, n, p.RT, p.rg_per_seq, p.rg_count, p.slices, p.slice_keys, topk, wsA,   \
-                         wsC, cs, ci);                                                                               \
-    launched = true;                                                                                                 \
+#define TQ_TK_L(BPV, GWV, KKV, QV)                                                                              \
+  hipLaunchKernelGGL((topk_scan_kernel<BPV, GWV, KKV, QV>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, \
+                     codes, norms, gammas, n, p.RT, p.rg_per_seq, p.rg_count, p.slices, p.slice_keys, topk, wsA, wsC,   \
+                     cs, ci)
+#define TQ_TK(BPV, GWV, QV)                                           \
+  if (!launched && bp == BPV && gw == GWV && qjl == QV) {             \
+    if (kk == 32)                                                     \
+      TQ_TK_L(BPV, GWV, 32, QV);                                      \
+    else if (kk == 16)                                                \
+      TQ_TK_L(BPV, GWV, 16, QV);                                      \
+    else                                                              \
+      TQ_TK_L(BPV, GWV, 12, QV);                                      \
+    launched = true;                                                  \
   }
 #define TQ_TK_ALL(GWV)                                                                                  \
   TQ_TK(1, GWV, true) TQ_TK(2, GWV, true) TQ_TK(3, GWV, true) TQ_TK(1, GWV, false) TQ_TK(2, GWV, false) \
@@ -374,15 +378,19 @@ hipError_t launch_topk(const tq_quantizer* q, const void* queries, int q_dtype, 
   TQ_TK_ALL(1) TQ_TK_ALL(2) TQ_TK_ALL(3) TQ_TK_ALL(4) TQ_TK_ALL(5) TQ_TK_ALL(6) TQ_TK_ALL(7) TQ_TK_ALL(8)
 #undef TQ_TK_ALL
 #undef TQ_TK
+#undef TQ_TK_L
   if (!launched) return hipErrorNotSupported;
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 mgrid(static_cast<unsigned>(static_cast<int64_t>(B) * Hq));
-  if (big)
+  if (kk == 32)
     hipLaunchKernelGGL((topk_merge_kernel<32>), mgrid, dim3(64), 0, st, cs, ci, p.slices, Hq, Hkv, p.rg_per_seq, topk,
                        out, out_idx);
-  else
+  else if (kk == 16)
     hipLaunchKernelGGL((topk_merge_kernel<16>), mgrid, dim3(64), 0, st, cs, ci, p.slices, Hq, Hkv, p.rg_per_seq, topk,
+                       out, out_idx);
+  else
+    hipLaunchKernelGGL((topk_merge_kernel<12>), mgrid, dim3(64), 0, st, cs, ci, p.slices, Hq, Hkv, p.rg_per_seq, topk,
                        out, out_idx);
   return hipGetLastError();
 }
