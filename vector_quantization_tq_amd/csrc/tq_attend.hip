@@ -63,11 +63,14 @@ constexpr int kPartStride = 128 + 4;
 
 // chunk length (a multiple of the step): the largest power-of-two multiple of
 // 128 tokens, up to 1024, that still leaves at least 768 workgroups (three
-// resident per CU); longer chunks only lengthen the merge, shorter ones add
-// partial records and pipeline fills
+// resident per CU); shorter ones add partial records and pipeline fills
 static int64_t attend_chunk_len(int64_t n_comp, int64_t groups) {
   int64_t ch = kStep;
   while (ch < 1024 && (n_comp + 2 * ch - 1) / (2 * ch) * groups >= 768) ch *= 2;
+  // and no more than 64 partial records per query where 2048-token chunks
+  // allow it: the merge reads them with one workgroup per query, and for few
+  // long sequences it, not the chunk kernel, is the longer part
+  if (ch == 1024 && (n_comp + ch - 1) / ch > 64) ch = 2048;
   return ch;
 }
 
