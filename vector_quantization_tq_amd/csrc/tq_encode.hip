@@ -28,25 +28,44 @@ constexpr int kThreads = 256;
 // 16 lanes of a column tile read 16 consecutive floats.  X in LDS with row
 // stride `ld`.  acc[ct] holds output column tile ct (16 columns) in MFMA C
 // layout.
-template <int NT>
-__device__ __forceinline__ void gemm_rows_16(const float* xs, int ld, const float* __restrict__ Mt, int ldm, int rows_m,
-                                             int d, v4f (&acc)[NT]) {
+// acc[rt][j] = rows 16 rt .. 16 rt + 15 of xs (64 rows, row stride ld) times
+// column tile ct = w + 4 j of the k-major matrix Mt (column j of the product
+// = row j of the matrix), for the column tiles ct < NT that wave w owns.  The
+// 16x16x4 fp32 MFMA: lane (r, kq) holds A[row r][k0 + kq] and B[k0 + kq][col
+// r]; each matrix load feeds the four row tiles, and no two waves load the
+// same matrix elements.
+template <int NT, int NTW>
+__device__ __forceinline__ void gemm_tile64(const float* xs, int ld, const float* __restrict__ Mt, int ldm, int rows_m,
+                                           int d, int w, v4f (&acc)[4][NTW]) {
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, kq = lane >> 4;
 #pragma unroll
-  for (int ct = 0; ct < NT; ++ct) acc[ct] = (v4f){0.f, 0.f, 0.f, 0.f};
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) acc[rt][j] = (v4f){0.f, 0.f, 0.f, 0.f};
   for (int k0 = 0; k0 < d; k0 += 4) {
     const int k = k0 + kq;
-    const float a = k < d ? xs[r * ld + k] : 0.f;
+    const bool kin = k < d;
+    float b[NTW];
 #pragma unroll
-    for (int ct = 0; ct < NT; ++ct) {
-      const int j = ct * 16 + r;
-      const float b = (k < d && j < rows_m) ? Mt[static_cast<int64_t>(k) * ldm + j] : 0.f;
-      acc[ct] = mfma_f32(a, b, acc[ct]);
+    for (int j = 0; j < NTW; ++j) {
+      const int col = (w + 4 * j) * 16 + r;
+      b[j] = (kin && w + 4 * j < NT && col < rows_m) ? Mt[static_cast<int64_t>(k) * ldm + col] : 0.f;
     }
+    float a[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) a[rt] = kin ? xs[(16 * rt + r) * ld + k] : 0.f;
+#pragma unroll
+    for (int j = 0; j < NTW; ++j)
+      if (w + 4 * j < NT) {
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) acc[rt][j] = mfma_f32(a[rt], b[j], acc[rt][j]);
+      }
   }
 #pragma unroll
-  for (int ct = 0; ct < NT; ++ct) pin(acc[ct]);
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) pin(acc[rt][j]);
 }
 
 template <int NT>
@@ -57,15 +76,17 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(const void* __restrict
                                                           float* __restrict__ norms, float* __restrict__ gammas) {
   constexpr int DP = NT * 16;
   constexpr int LD = DP + 1;
+  constexpr int NTW = (NT + 3) / 4;   // column tiles per wave
   extern __shared__ float smem[];
   float* xs = smem;                                               // [64][LD] floats: x, then rho
   float* nrm = xs + kTileRows * LD;                               // [64]
   float* cen = nrm + kTileRows;                                   // [16]
   uint8_t* idxb = reinterpret_cast<uint8_t*>(cen + kMaxLevels);   // [64][DP]
   uint8_t* sgnb = idxb + kTileRows * DP;                          // [64][DP]
+  __shared__ float part2[4][kTileRows];                           // per wave: partial ||rho||^2 of each row
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int64_t seq = blockIdx.y;
   const int64_t v0 = static_cast<int64_t>(blockIdx.x) * kTileRows;
   const int rows = static_cast<int>(n - v0 < kTileRows ? n - v0 : kTileRows);
@@ -94,83 +115,87 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(const void* __restrict
   }
   __syncthreads();
 
-  // ---- rotation: y = Pi x / n ----
-  const float* xw = xs + wave * 16 * LD;   // this wave's 16 rows
-  v4f acc[NT];
-  gemm_rows_16<NT>(xw, LD, pit, ldp, d, d, acc);
+  // ---- rotation: y = Pi x / n; wave w takes column tiles w, w + 4, ... of all 64 rows ----
+  v4f acc[4][NTW];
+  gemm_tile64<NT, NTW>(xs, LD, pit, ldp, d, d, wave, acc);
 
-  const int col_in = lane & 15, rq = lane >> 4;   // C layout: rows 4*rq+i, column ct*16+col_in
-  float inv_n[4], rho2[4];
+  const int col_in = lane & 15, rq = lane >> 4;   // C layout: rows 16 rt + 4 rq + i, column 16 ct + col_in
+  float inv_n[4][4], rho2[4][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float nv = nrm[wave * 16 + 4 * rq + i];
-    inv_n[i] = nv > 0.f ? 1.f / nv : 0.f;
-    rho2[i] = 0.f;
-  }
-  // bucketize, residual; write rho back over this wave's rows of x
-#pragma unroll
-  for (int ct = 0; ct < NT; ++ct) {
-    const int col = ct * 16 + col_in;
+  for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = wave * 16 + 4 * rq + i;
-      const float y = acc[ct][i] * inv_n[i];
-      int idx = 0;
-      for (int k = 0; k < cb.levels - 1; ++k) idx += (cb.t[k] < y) ? 1 : 0;
-      const float rho = col < d ? y - cen[idx] : 0.f;
-      if (col < d) rho2[i] = fmaf(rho, rho, rho2[i]);
-      idxb[row * DP + col] = col < d ? static_cast<uint8_t>(idx) : 0;
-      acc[ct][i] = rho;
+      const float nv = nrm[16 * rt + 4 * rq + i];
+      inv_n[rt][i] = nv > 0.f ? 1.f / nv : 0.f;
+      rho2[rt][i] = 0.f;
+    }
+  // bucketize, residual (rho stays in acc until every wave has read x)
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) {
+    const int col = (wave + 4 * j) * 16 + col_in;
+    if (wave + 4 * j < NT) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * rt + 4 * rq + i;
+          const float y = acc[rt][j][i] * inv_n[rt][i];
+          int idx = 0;
+          for (int k = 0; k < cb.levels - 1; ++k) idx += (cb.t[k] < y) ? 1 : 0;
+          const float rho = col < d ? y - cen[idx] : 0.f;
+          rho2[rt][i] = fmaf(rho, rho, rho2[rt][i]);
+          idxb[row * DP + col] = col < d ? static_cast<uint8_t>(idx) : 0;
+          acc[rt][j][i] = rho;
+        }
     }
   }
   __syncthreads();   // all waves finished reading x before rho overwrites it
 #pragma unroll
-  for (int ct = 0; ct < NT; ++ct)
+  for (int j = 0; j < NTW; ++j)
+    if (wave + 4 * j < NT) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xs[(wave * 16 + 4 * rq + i) * LD + ct * 16 + col_in] = acc[ct][i];
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xs[(16 * rt + 4 * rq + i) * LD + (wave + 4 * j) * 16 + col_in] = acc[rt][j][i];
+    }
 
   if (mode == 0) {
+    // this wave's part of ||rho||^2 per row (a sum over its 16 column lanes)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float s = rho2[i];
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      s += __shfl_xor(s, 4);
-      s += __shfl_xor(s, 8);
-      rho2[i] = s;
-    }
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float sum = rho2[rt][i];
+        sum += __shfl_xor(sum, 1);
+        sum += __shfl_xor(sum, 2);
+        sum += __shfl_xor(sum, 4);
+        sum += __shfl_xor(sum, 8);
+        if (col_in == 0) part2[wave][16 * rt + 4 * rq + i] = sum;
+      }
     __syncthreads();
     // ---- QJL projection z = S' rho; bit = [z >= 0] (all ones for n = 0) ----
-    gemm_rows_16<NT>(xw, LD, spt, d, d, d, acc);
+    gemm_tile64<NT, NTW>(xs, LD, spt, d, d, d, wave, acc);
 #pragma unroll
-    for (int ct = 0; ct < NT; ++ct) {
-      const int col = ct * 16 + col_in;
+    for (int j = 0; j < NTW; ++j) {
+      const int col = (wave + 4 * j) * 16 + col_in;
+      if (wave + 4 * j < NT) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = wave * 16 + 4 * rq + i;
-        const bool bit = (acc[ct][i] >= 0.f) || (inv_n[i] == 0.f);
-        sgnb[row * DP + col] = (col < d && bit) ? 1 : 0;
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = 16 * rt + 4 * rq + i;
+            const bool bit = (acc[rt][j][i] >= 0.f) || (inv_n[rt][i] == 0.f);
+            sgnb[row * DP + col] = (col < d && bit) ? 1 : 0;
+          }
       }
     }
-    if (col_in == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = wave * 16 + 4 * rq + i;
-        if (row < rows) {
-          const float nv = nrm[row];
-          norms[base + row] = nv;
-          gammas[base + row] = nv * sqrtf(rho2[i]);
-        }
-      }
+    if (tid < rows) {
+      const float nv = nrm[tid];
+      norms[base + tid] = nv;
+      gammas[base + tid] = nv * sqrtf((part2[0][tid] + part2[1][tid]) + (part2[2][tid] + part2[3][tid]));
     }
   } else {
-    if (col_in == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = wave * 16 + 4 * rq + i;
-        if (row < rows) norms[base + row] = nrm[row];
-      }
-    }
+    if (tid < rows) norms[base + tid] = nrm[tid];
   }
   __syncthreads();
 
