@@ -43,24 +43,29 @@ __device__ __forceinline__ void gemm_tile64(const float* xs, int ld, const float
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
     for (int j = 0; j < NTW; ++j) acc[rt][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+  // Loads at clamped (always valid) addresses and no branches around the
+  // loads or the MFMAs.  Only A is zeroed past k = d (a select on the LDS
+  // value); B is not masked: a product column past d (or a column tile past
+  // NT) holds values that nothing reads.
+  int colc[NTW];
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) colc[j] = min((w + 4 * j) * 16 + r, rows_m - 1);
   for (int k0 = 0; k0 < d; k0 += 4) {
     const int k = k0 + kq;
     const bool kin = k < d;
-    float b[NTW];
+    const int kc = min(k, d - 1);
+    float b[NTW], a[4];
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-      const int col = (w + 4 * j) * 16 + r;
-      b[j] = (kin && w + 4 * j < NT && col < rows_m) ? Mt[static_cast<int64_t>(k) * ldm + col] : 0.f;
+    for (int j = 0; j < NTW; ++j) b[j] = Mt[static_cast<int64_t>(kc) * ldm + colc[j]];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const float v = xs[(16 * rt + r) * ld + kc];
+      a[rt] = kin ? v : 0.f;
     }
-    float a[4];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) a[rt] = kin ? xs[(16 * rt + r) * ld + k] : 0.f;
 #pragma unroll
     for (int j = 0; j < NTW; ++j)
-      if (w + 4 * j < NT) {
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) acc[rt][j] = mfma_f32(a[rt], b[j], acc[rt][j]);
-      }
+      for (int rt = 0; rt < 4; ++rt) acc[rt][j] = mfma_f32(a[rt], b[j], acc[rt][j]);
   }
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
@@ -93,12 +98,37 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(const void* __restrict
   const int64_t base = seq * n + v0;   // first vector of the tile
 
   if (tid < kMaxLevels) cen[tid] = tid < cb.levels ? cb.c[tid] : 0.f;
-  // ---- load the tile (coalesced), zero rows past n and columns past d ----
-  for (int e = tid; e < kTileRows * DP; e += kThreads) {
-    const int row = e / DP, col = e - row * DP;
-    float v = 0.f;
-    if (row < rows && col < d) v = load_elem(x, dtype, (base + row) * d + col);
-    xs[row * LD + col] = v;
+  // ---- load the tile, zero rows past n and columns past d ----
+  if (dtype == 0 && (d & 3) == 0) {   // fp32 rows of whole 16-byte chunks
+    // four threads per row, 16-byte chunks c = part, part + 4, ...: every
+    // load of a thread is issued before the first store
+    constexpr int CPT = (DP / 4 + 3) / 4;   // chunks per thread
+    const int row = tid >> 2, part = tid & 3, cpr = d >> 2;
+    const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(x) + (base + row) * d);
+    float4 v[CPT];
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int c = part + 4 * u;
+      v[u] = (row < rows && c < cpr) ? src[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int c = part + 4 * u;
+      if (4 * c < DP) {
+        float* dst = xs + row * LD + 4 * c;
+        dst[0] = v[u].x;
+        dst[1] = v[u].y;
+        dst[2] = v[u].z;
+        dst[3] = v[u].w;
+      }
+    }
+  } else {
+    for (int e = tid; e < kTileRows * DP; e += kThreads) {
+      const int row = e / DP, col = e - row * DP;
+      float v = 0.f;
+      if (row < rows && col < d) v = load_elem(x, dtype, (base + row) * d + col);
+      xs[row * LD + col] = v;
+    }
   }
   __syncthreads();
   // ---- norms: 4 threads per row ----
