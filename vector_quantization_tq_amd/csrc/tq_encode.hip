@@ -159,6 +159,7 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(const void* __restrict
       inv_n[rt][i] = nv > 0.f ? 1.f / nv : 0.f;
       rho2[rt][i] = 0.f;
     }
+  const int kh = cb.levels >> 1;   // centroids per half of the codebook
   // bucketize, residual (rho stays in acc until every wave has read x)
 #pragma unroll
   for (int j = 0; j < NTW; ++j) {
@@ -170,8 +171,15 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(const void* __restrict
         for (int i = 0; i < 4; ++i) {
           const int row = 16 * rt + 4 * rq + i;
           const float y = acc[rt][j][i] * inv_n[rt][i];
-          int idx = 0;
-          for (int k = 0; k < cb.levels - 1; ++k) idx += (cb.t[k] < y) ? 1 : 0;
+          // idx = #{t_k < y} on the symmetric codebook (middle threshold 0,
+          // t[K/2 + k] = -t[K/2 - 2 - k]): K/2 + j for y > 0, K/2 - 1 - j
+          // otherwise, j = #{positive thresholds below |y|}
+          const float ay = fabsf(y);
+          int jm = 0;
+#pragma unroll
+          for (int k = 0; k + 1 < kMaxLevels / 2; ++k)
+            if (k + 1 < kh) jm += (cb.t[kh + k] < ay) ? 1 : 0;
+          const int idx = y > 0.f ? kh + jm : kh - 1 - jm;
           const float rho = col < d ? y - cen[idx] : 0.f;
           rho2[rt][i] = fmaf(rho, rho, rho2[rt][i]);
           idxb[row * DP + col] = col < d ? static_cast<uint8_t>(idx) : 0;
