@@ -800,13 +800,19 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
               bool p0, p1, j0[BP > 1 ? BP - 1 : 1], j1[BP > 1 ? BP - 1 : 1];
               classify(acc[0][ct][i], acc[0][ct][i] * sc0, p0, j0);
               classify(acc[1][ct][i], acc[1][ct][i] * sc1, p1, j1);
-              // sign plane [y > 0]; low planes [bit of j == sign]; padding tokens 0
+              // sign plane [y > 0]; low planes [bit of j == sign]; padding tokens 0.
+              // Every ballot is taken before the one branch that writes the words.
               const uint64_t s0 = __ballot(p0) & tm0, s1 = __ballot(p1) & tm1;
+              uint32_t wd[BP];
 #pragma unroll
               for (int p = 0; p < BP; ++p) {
                 const uint64_t m0 = p == BP - 1 ? s0 : ~(__ballot(j0[p < BP - 1 ? p : 0]) ^ s0) & tm0;
                 const uint64_t m1 = p == BP - 1 ? s1 : ~(__ballot(j1[p < BP - 1 ? p : 0]) ^ s1) & tm1;
-                if (r16 == 0 && c < d) ost[buf][(h * bp + p) * d + c] = halves(m0, m1);
+                wd[p] = halves(m0, m1);
+              }
+              if (r16 == 0 && (FULL || c < d)) {
+#pragma unroll
+                for (int p = 0; p < BP; ++p) ost[buf][(h * bp + p) * d + c] = wd[p];
               }
             }
         }
