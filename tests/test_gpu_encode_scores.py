@@ -56,7 +56,8 @@ def test_encode_tiny_workload():
 @pytest.mark.parametrize("d,bits,nseq,n,bf16", [
     (128, 2, 3, 1000, True), (128, 4, 2, 777, True), (128, 3, 1, 64, False), (128, 3, 2, 1, False),
     (200, 2, 1, 3000, False), (200, 4, 1, 1500, False), (16, 3, 2, 100, False), (48, 2, 1, 65, False),
-    (3, 2, 1, 10, False), (256, 3, 1, 130, True)])
+    (3, 2, 1, 10, False), (256, 3, 1, 130, True),
+    (201, 3, 2, 333, False)])   # d > 128 and not a multiple of 4: the element-wise tile load
 def test_encode_prod_shapes(d, bits, nseq, n, bf16):
     print(f"case: prod d={d} bits={bits} nseq={nseq} n={n} bf16={bf16}", flush=True)
     rng = np.random.default_rng(d * 100 + bits)
@@ -68,7 +69,7 @@ def test_encode_prod_shapes(d, bits, nseq, n, bf16):
 
 @pytest.mark.parametrize("d,bits,nseq,n,bf16", [
     (128, 3, 4, 1000, True), (128, 4, 2, 4101, True), (16, 1, 1, 33, False), (128, 2, 3, 64, False),
-    (200, 4, 1, 70, False)])
+    (200, 4, 1, 70, False), (130, 2, 1, 200, False)])
 def test_encode_mse_shapes(d, bits, nseq, n, bf16):
     print(f"case: mse d={d} bits={bits} nseq={nseq} n={n} bf16={bf16}", flush=True)
     rng = np.random.default_rng(d + bits)
