@@ -352,7 +352,7 @@ __global__ void __launch_bounds__(256) scores_kernel(const uint32_t* __restrict_
       const int64_t key = k0 + 4 * (lane & 15);
       if (srow) {
         if (vec_store && key + 4 <= n) {
-          __builtin_nontemporal_store(v, reinterpret_cast<f4*>(srow + key));
+          *reinterpret_cast<f4*>(srow + key) = v;   // write-back: the next consumer reads it from cache
         } else {
           if (key + 0 < n) srow[key + 0] = v.x;
           if (key + 1 < n) srow[key + 1] = v.y;
