@@ -211,6 +211,10 @@ __global__ void __launch_bounds__(256) query_prep_kernel(const void* __restrict_
 constexpr int kTargetWaves = TQ_SCORES_WAVES;   // resident waves aimed at (256 CUs x 4 SIMDs x 4)
 constexpr int kRing = TQ_SCORES_RING;
 constexpr int kBatchKeys = 64;
+// cache policy of the staging copies: non-temporal (nt).  Every packed key is
+// read once per call; marking the stream non-temporal keeps it from
+// displacing other lines and measured 5% faster (30.4 -> 28.9 us back to back)
+constexpr int kNt = 2;
 
 template <int WPK, bool QJL>
 struct DmaPlan {
@@ -235,16 +239,16 @@ __device__ __forceinline__ void issue_batch(uint32_t* slot, const uint32_t* __re
     const uint32_t* src = cbase + k0 * WPK + off;
     lds_ptr_t* dst = as_lds(slot + i * 64 * P::WPL);
     if constexpr (P::SZ == 16) {
-      __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src, dst, 16, 0, kNt);
     } else {
-      __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(src, dst, 4, 0, kNt);
     }
   }
   int64_t kk = k0 + lane;
   if (kk >= n) kk = n - 1;
   float* ng = reinterpret_cast<float*>(slot + kBatchKeys * WPK);
-  __builtin_amdgcn_global_load_lds(nb + kk, as_lds(ng), 4, 0, 0);
-  if constexpr (QJL) __builtin_amdgcn_global_load_lds(gb + kk, as_lds(ng + kBatchKeys), 4, 0, 0);
+  __builtin_amdgcn_global_load_lds(nb + kk, as_lds(ng), 4, 0, kNt);
+  if constexpr (QJL) __builtin_amdgcn_global_load_lds(gb + kk, as_lds(ng + kBatchKeys), 4, 0, kNt);
 }
 
 // QJL: prod keys (BP index planes + the QJL plane, gamma per key); without
