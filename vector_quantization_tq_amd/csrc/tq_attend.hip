@@ -66,7 +66,8 @@ constexpr int kPartStride = 128 + 4;
 
 // chunk length (a multiple of the step): the largest power-of-two multiple of
 // 128 tokens, up to 1024, that still leaves at least 768 workgroups (three
-// resident per CU); shorter ones add partial records and pipeline fills
+// resident per CU, or three quarters of the slots where four fit); shorter
+// ones add partial records and pipeline fills
 static int64_t attend_chunk_len(int64_t n_comp, int64_t groups) {
   int64_t ch = kStep;
   while (ch < 1024 && (n_comp + 2 * ch - 1) / (2 * ch) * groups >= 768) ch *= 2;
@@ -367,13 +368,28 @@ __device__ __forceinline__ void attend_chunk_body(
   }
 }
 
+// Residency.  With a 2-step staging ring and at most 128 VGPRs four
+// workgroups share a CU (4 waves per SIMD) instead of three with a 3-step
+// ring: the extra waves hide each other's ALU phases better than the deeper
+// ring hides memory latency (GQA layer, 3-bit: 78 -> 72 us).  That register
+// budget holds the query terms and the value accumulators without spilling
+// where the key's MSE bits and the value bits are at most 3 each and the key
+// and value bits sum to at most 6; the other kernels, and the sparse-V ones,
+// keep the 3-step ring.
 template <int BPK, int BPV, bool QJL, bool SPARSE>
-__global__ void __launch_bounds__(256) attend_chunk_kernel(
+struct AttendResidency {
+  static constexpr bool kFour = !SPARSE && BPK <= 3 && BPV <= 3 && BPK + (QJL ? 1 : 0) + BPV <= 6;
+  static constexpr int kSlots = kFour ? 2 : 3;
+  static constexpr int kBlocksPerCu = kFour ? 4 : 1;
+};
+
+template <int BPK, int BPV, bool QJL, bool SPARSE>
+__global__ void __launch_bounds__(256, (AttendResidency<BPK, BPV, QJL, SPARSE>::kBlocksPerCu)) attend_chunk_kernel(
     const uint32_t* __restrict__ kcodes, const float* __restrict__ knorms, const float* __restrict__ kgammas,
     const uint32_t* __restrict__ vcodes, const float* __restrict__ vnorms, int64_t n, int64_t chunk, int G, int RT,
     float scale_log2, float vtau, const uint8_t* __restrict__ wsA, const float* __restrict__ wsC, Codebook vcb,
     float* __restrict__ part) {
-  attend_chunk_body<BPK, BPV, 3, QJL, SPARSE>(kcodes, knorms, kgammas, vcodes, vnorms, n, chunk, G, RT, scale_log2, vtau,
+  attend_chunk_body<BPK, BPV, AttendResidency<BPK, BPV, QJL, SPARSE>::kSlots, QJL, SPARSE>(kcodes, knorms, kgammas, vcodes, vnorms, n, chunk, G, RT, scale_log2, vtau,
                                               wsA, wsC, vcb, part);
 }
 
