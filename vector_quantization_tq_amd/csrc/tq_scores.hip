@@ -36,6 +36,7 @@ namespace tq {
 // The terms are the Walsh terms of the key codebook, then (prod keys) the
 // QJL term; MSE-only keys have no QJL term.
 // ---------------------------------------------------------------------------
+template <bool QBF16, bool ONE>
 __global__ void __launch_bounds__(256) query_prep_kernel(const void* __restrict__ queries, int q_dtype, int Hq, int Hkv,
                                                          int G, int RT, int d, int m, const float* __restrict__ qt,
                                                          Codebook cb, int qjl, int C, uint8_t* __restrict__ wsA,
@@ -53,11 +54,6 @@ __global__ void __launch_bounds__(256) query_prep_kernel(const void* __restrict_
   const bool valid = qg < G;
   const int T = cb.nterms + (qjl ? 1 : 0);   // Walsh terms (+ the QJL term)
 
-  if (valid) {
-    const int64_t qoff = (static_cast<int64_t>(b) * Hq + kvh * G + qg) * d;
-    for (int j = tid; j < d; j += blockDim.x) qv[j] = load_elem(queries, q_dtype, qoff + j);
-  }
-  __syncthreads();
   // [Pi q, S q] from the k-major table: wave w takes the contraction slice
   // k in [w KQ, (w+1) KQ), lane the 4 consecutive outputs 4 lane + 256 r;
   // the loads of a slice are independent 16-byte reads (indices clamped, no
@@ -65,10 +61,54 @@ __global__ void __launch_bounds__(256) query_prep_kernel(const void* __restrict_
   float lmax_h = 0.f, lmax_s = 0.f, lsum_h = 0.f, lsum_s = 0.f;
   const int dm = d + m;
   float* pw = sq + m;   // [4][dm] partial sums
+  const int wave = tid >> 6, lane = tid & 63;
+  const int KQ = (d + 3) / 4;
+  const int k0 = min(d, wave * KQ), k1 = min(d, k0 + KQ);
+  // ONE (d <= 128, d + m <= 256 and a multiple of 4, checked by the host):
+  // a wave's whole slice is one batch of 32 loads per lane, issued right
+  // after the query element so that both are in flight together.  The query
+  // load has no branch (row and index clamped) and its value is stored
+  // unconditionally, so it stays ahead of the table loads and the wait for it
+  // leaves them outstanding (vector loads retire in issue order).
+  float qe;
   {
-    const int wave = tid >> 6, lane = tid & 63;
-    const int KQ = (d + 3) / 4;
-    const int k0 = min(d, wave * KQ), k1 = min(d, k0 + KQ);
+    const int64_t qi0 = (static_cast<int64_t>(b) * Hq + kvh * G + (valid ? qg : 0)) * d + min(tid, d - 1);
+    if constexpr (QBF16) qe = bf16_to_f32(static_cast<const uint16_t*>(queries)[qi0]);
+    else qe = static_cast<const float*>(queries)[qi0];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  float4 v1[32];
+  if constexpr (ONE) {
+    const int oc = min(4 * lane, dm - 4);
+#pragma unroll
+    for (int u = 0; u < 32; ++u)
+      v1[u] = *reinterpret_cast<const float4*>(qt + static_cast<int64_t>(min(k0 + u, k1 - 1)) * dm + oc);
+  }
+  __shared__ float qstage[256];   // element tid of the query (clamped duplicates past d)
+  qstage[tid] = qe;
+  if constexpr (!ONE) {
+    if (valid) {
+      if (tid < d) qv[tid] = qe;
+      for (int j = tid + blockDim.x; j < d; j += blockDim.x)
+        qv[j] = load_elem(queries, q_dtype, (static_cast<int64_t>(b) * Hq + kvh * G + qg) * d + j);
+    }
+  }
+  __syncthreads();
+  if constexpr (ONE) {
+    const int o = 4 * lane;
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      const float qk = (valid && k0 + u < k1) ? qstage[min(k0 + u, k1 - 1)] : 0.f;
+      a[0] = fmaf(v1[u].x, qk, a[0]);
+      a[1] = fmaf(v1[u].y, qk, a[1]);
+      a[2] = fmaf(v1[u].z, qk, a[2]);
+      a[3] = fmaf(v1[u].w, qk, a[3]);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (o + e < dm) pw[wave * dm + o + e] = a[e];
+  } else {
     for (int ob = 0; ob < dm; ob += 256) {
       const int o = ob + 4 * lane;
       float a[4] = {0.f, 0.f, 0.f, 0.f};
@@ -390,8 +430,17 @@ hipError_t launch_query_prep(const tq_quantizer* q, const void* queries, int q_d
   const int C = (q->d + 127) / 128;
   const size_t lds = sizeof(float) * (2 * q->d + q->m + 4 * (q->d + q->m));
   dim3 grid(static_cast<unsigned>(static_cast<int64_t>(B) * Hkv * RT * 4));
-  hipLaunchKernelGGL(query_prep_kernel, grid, dim3(256), lds, st, queries, q_dtype, Hq, Hkv, G, RT, q->d, q->m, q->d_qt,
-                     key_codebook(q), key_qjl(q) ? 1 : 0, C, wsA, wsC);
+  const int dm = q->d + q->m;
+  const bool one = dm % 4 == 0 && dm <= 256 && q->d <= 128;
+#define TQ_QP(BF, ONE)                                                                                              \
+  hipLaunchKernelGGL((query_prep_kernel<BF, ONE>), grid, dim3(256), lds, st, queries, q_dtype, Hq, Hkv, G, RT, q->d, \
+                     q->m, q->d_qt, key_codebook(q), key_qjl(q) ? 1 : 0, C, wsA, wsC)
+  if (q_dtype == 1) {
+    if (one) TQ_QP(true, true); else TQ_QP(true, false);
+  } else {
+    if (one) TQ_QP(false, true); else TQ_QP(false, false);
+  }
+#undef TQ_QP
   return hipGetLastError();
 }
 
