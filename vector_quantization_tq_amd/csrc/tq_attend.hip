@@ -96,18 +96,24 @@ int64_t attend_ws_bytes(const tq_quantizer* kq, const tq_quantizer*, int B, int 
 // Copy `words` 32-bit words (a multiple of 4) from src to LDS dst by 16-byte
 // DMA loads (global -> LDS, no registers), spread over the 4 waves; words at
 // or past `limit` (a multiple of 4, > 0) re-read the last valid 16 bytes.
+// `wave` is wave-uniform; offsets are 32-bit bytes from the uniform source,
+// so each copy addresses as scalar base + vector offset.
 __device__ __forceinline__ void dma16(uint32_t* dst, const uint32_t* src, int words, int limit, int wave, int lane) {
+  const char* s8 = reinterpret_cast<const char*>(src);
   for (int i = wave; i * 256 < words; i += 4) {
-    int off = i * 256 + lane * 4;
-    if (off + 4 > limit) off = limit - 4;
-    __builtin_amdgcn_global_load_lds(src + off, as_lds(dst + i * 256), 16, 0, kNtPolicy);
+    uint32_t off = static_cast<uint32_t>(i * 256) + 4u * static_cast<uint32_t>(lane);
+    if (off + 4u > static_cast<uint32_t>(limit)) off = static_cast<uint32_t>(limit) - 4u;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(s8 + 4u * off), as_lds(dst + i * 256), 16, 0,
+                                     kNtPolicy);
   }
 }
 // 64 floats of a per-token array, one per lane, index clamped to [0, n-1]
+// (t0 >= 0, n >= 1)
 __device__ __forceinline__ void dma_tok(float* dst, const float* src, int64_t t0, int64_t n, int lane) {
-  int64_t t = t0 + lane;
-  if (t >= n) t = n - 1;
-  __builtin_amdgcn_global_load_lds(src + t, as_lds(dst), 4, 0, kNtPolicy);
+  const int64_t tb = min(t0, n - 1);                                    // uniform
+  const uint32_t l = static_cast<uint32_t>(min(static_cast<int64_t>(lane), n - 1 - tb));
+  const char* s8 = reinterpret_cast<const char*>(src + tb);
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const float*>(s8 + 4u * l), as_lds(dst), 4, 0, kNtPolicy);
 }
 
 // QJL: prod keys (QJL plane + gammas); without it MSE-only keys.  SPARSE:
@@ -133,7 +139,7 @@ __device__ __forceinline__ void attend_chunk_body(
   __shared__ __attribute__((aligned(16))) uint32_t av[64 * 8];   // value A operand (fp8 limbs)
   __shared__ float qst[4][4];                // per query: rescale factor, E, value work left in the step
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int gy = blockIdx.y;
   const int grp = gy / RT;
   const int64_t c0 = static_cast<int64_t>(blockIdx.x) * chunk;

@@ -271,12 +271,16 @@ __device__ __forceinline__ void issue_batch(uint32_t* slot, const uint32_t* __re
                                             const float* __restrict__ nb, const float* __restrict__ gb, int64_t k0,
                                             int64_t n, int lane) {
   using P = DmaPlan<WPK, QJL>;
-  const int64_t limit = (n - k0) * WPK;        // valid words from this batch's start (> 0)
+  // valid words from this batch's start (> 0), at most the batch's own; the
+  // offsets are 32-bit bytes from the batch's uniform start, so each copy
+  // addresses as scalar base + vector offset
+  const uint32_t limit = static_cast<uint32_t>(min((n - k0) * WPK, static_cast<int64_t>(kBatchKeys * WPK)));
+  const char* base = reinterpret_cast<const char*>(cbase + k0 * WPK);
 #pragma unroll
   for (int i = 0; i < P::NC; ++i) {
-    int64_t off = static_cast<int64_t>(i) * 64 * P::WPL + lane * P::WPL;
+    uint32_t off = static_cast<uint32_t>(i * 64 * P::WPL) + static_cast<uint32_t>(lane * P::WPL);
     if (off + P::WPL > limit) off = limit - P::WPL;   // past the end: re-read the last valid words
-    const uint32_t* src = cbase + k0 * WPK + off;
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(base + 4u * off);
     lds_ptr_t* dst = as_lds(slot + i * 64 * P::WPL);
     if constexpr (P::SZ == 16) {
       __builtin_amdgcn_global_load_lds(src, dst, 16, 0, kNt);
@@ -284,11 +288,14 @@ __device__ __forceinline__ void issue_batch(uint32_t* slot, const uint32_t* __re
       __builtin_amdgcn_global_load_lds(src, dst, 4, 0, kNt);
     }
   }
-  int64_t kk = k0 + lane;
-  if (kk >= n) kk = n - 1;
+  // key k0 + lane, clamped to n - 1 (k0 < n)
+  const uint32_t kb = 4u * static_cast<uint32_t>(min(static_cast<int64_t>(lane), n - 1 - k0));
   float* ng = reinterpret_cast<float*>(slot + kBatchKeys * WPK);
-  __builtin_amdgcn_global_load_lds(nb + kk, as_lds(ng), 4, 0, kNt);
-  if constexpr (QJL) __builtin_amdgcn_global_load_lds(gb + kk, as_lds(ng + kBatchKeys), 4, 0, kNt);
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const float*>(reinterpret_cast<const char*>(nb + k0) + kb), as_lds(ng),
+                                   4, 0, kNt);
+  if constexpr (QJL)
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const float*>(reinterpret_cast<const char*>(gb + k0) + kb),
+                                     as_lds(ng + kBatchKeys), 4, 0, kNt);
 }
 
 // QJL: prod keys (BP index planes + the QJL plane, gamma per key); without
@@ -308,7 +315,7 @@ __global__ void __launch_bounds__(256) scores_kernel(const uint32_t* __restrict_
   constexpr int L = P::L;
   __shared__ __attribute__((aligned(16))) uint32_t lds[4 * WAVEW];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint32_t* ring = lds + wave * WAVEW;
   float* lout = reinterpret_cast<float*>(ring + kRing * SLOTW);
 

@@ -165,7 +165,7 @@ __global__ void __launch_bounds__(256, (KK <= 16 && ((1 << (BP - 1)) + QJL) * ((
   constexpr int NS = 3;                            // batches b, b+1, b+2 staged at once
   __shared__ __attribute__((aligned(16))) uint32_t buf[NS][BUFW];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // workgroup -> (row group, slice); consecutive workgroups go round-robin over
   // the 8 XCDs, so XCD x takes slices x, x+8, ... with all row groups of each
   const int64_t L = blockIdx.x;
@@ -217,17 +217,19 @@ __global__ void __launch_bounds__(256, (KK <= 16 && ((1 << (BP - 1)) + QJL) * ((
     const int64_t k0 = k_begin + static_cast<int64_t>(bi) * kTopBlockKeys;
     const int valid = static_cast<int>(min(k_end, k0 + kTopBlockKeys) - k0);
     uint32_t* dst = buf[slot];
-    const uint32_t* src = cbase + k0 * WPK;
+    // 32-bit byte offsets from the batch's uniform start: scalar base + vector offset
+    const char* src = reinterpret_cast<const char*>(cbase + k0 * WPK);
+    const uint32_t vw = static_cast<uint32_t>(valid * WPK);
     for (int i = wave; i < WPK; i += 4) {
-      int off = i * 64 + lane;
-      if (off >= valid * WPK) off = valid * WPK - 1;
-      __builtin_amdgcn_global_load_lds(src + off, as_lds(dst + i * 64), 4, 0, 0);
+      uint32_t off = static_cast<uint32_t>(i * 64 + lane);
+      if (off >= vw) off = vw - 1;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(src + 4u * off), as_lds(dst + i * 64), 4, 0, 0);
     }
     if (wave == 2 || (QJL && wave == 3)) {
-      const float* arr = wave == 2 ? nb : gb;
-      int64_t t = k0 + lane;
-      if (t >= k0 + valid) t = k0 + valid - 1;
-      __builtin_amdgcn_global_load_lds(arr + t, as_lds(dst + BW + (wave - 2) * kTopBlockKeys), 4, 0, 0);
+      const char* arr = reinterpret_cast<const char*>((wave == 2 ? nb : gb) + k0);
+      const uint32_t t = 4u * static_cast<uint32_t>(min(lane, valid - 1));
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const float*>(arr + t),
+                                       as_lds(dst + BW + (wave - 2) * kTopBlockKeys), 4, 0, 0);
     }
   };
 
