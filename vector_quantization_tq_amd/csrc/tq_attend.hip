@@ -64,31 +64,79 @@ __device__ __forceinline__ uint32_t fixed_limbs4(float x, float s, float& xq) {
 // partial record of one (group row tile, chunk, query): acc[128] then m, l
 constexpr int kPartStride = 128 + 4;
 
+// Residency of the chunk kernel (workgroups per CU it is built for; 0: the
+// compiler's choice with a 3-step staging ring, 2 or 3 per CU by its VGPRs
+// and LDS).  With a 2-step ring and at most 128 VGPRs four workgroups share
+// a CU (4 waves per SIMD): the extra waves hide each other's ALU phases
+// better than the deeper ring hides memory latency (GQA layer, 3-bit: 78 ->
+// 72 us).  That budget holds the query terms and the value accumulators
+// without spilling where the key's MSE bits and the value bits are at most 3
+// each and the key and value bits sum to at most 6.  4-bit prod keys with
+// 4-bit values need 190 VGPRs and 58 KB of LDS with the 3-step ring (two per
+// CU); with the 2-step ring they fit 168 VGPRs, three per CU.  The sparse-V
+// kernels keep the compiler's choice.
+constexpr int attend_blocks_per_cu(int bpk, int bpv, bool qjl, bool sparse) {
+  return sparse ? 0
+         : (bpk <= 3 && bpv <= 3 && bpk + (qjl ? 1 : 0) + bpv <= 6) ? 4
+         : (qjl && bpk == 3 && bpv == 4) ? 3
+                                         : 0;
+}
+
+static int64_t device_cus() {
+  static int64_t cus = [] {
+    int dev = 0, c = 256;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        c < 1)
+      c = 256;
+    return static_cast<int64_t>(c);
+  }();
+  return cus;
+}
+
 // chunk length (a multiple of the step): the largest power-of-two multiple of
 // 128 tokens, up to 1024, that still leaves at least 768 workgroups (three
 // resident per CU, or three quarters of the slots where four fit); shorter
-// ones add partial records and pipeline fills
-static int64_t attend_chunk_len(int64_t n_comp, int64_t groups) {
+// ones add partial records and pipeline fills.  `bpc` is the dense kernel's
+// residency (attend_blocks_per_cu): the chunking never depends on whether
+// sparse V is on, so the workspace size does not either.
+static int64_t attend_chunk_len(int64_t n_comp, int64_t groups, int bpc) {
   int64_t ch = kStep;
   while (ch < 1024 && (n_comp + 2 * ch - 1) / (2 * ch) * groups >= 768) ch *= 2;
-  // and no more than 64 partial records per query where 2048-token chunks
-  // allow it: the merge reads them with one workgroup per query, and for few
-  // long sequences it, not the chunk kernel, is the longer part
-  if (ch == 1024 && (n_comp + ch - 1) / ch > 64) ch = 2048;
+  // few long sequences: no more than 64 partial records per query (the merge
+  // reads them with one workgroup per query, and there it, not the chunk
+  // kernel, is the longer part) ...
+  if (ch == 1024 && (n_comp + ch - 1) / ch > 64) {
+    ch = 2048;
+    // ... unless 2048-token chunks fill less than one round of the resident
+    // workgroups: then the shortest multiple of the step whose chunks fill at
+    // most one round, with at most 96 records per query (4-bit long context,
+    // 8 groups of 130816 tokens at three per CU: 93 chunks of 1408 tokens,
+    // 60.1 -> 56.2 us)
+    const int64_t slots = bpc * device_cus();
+    if (bpc > 0 && (n_comp + ch - 1) / ch * groups < slots) {
+      const int64_t per = min(static_cast<int64_t>(96), max(static_cast<int64_t>(1), slots / groups));
+      const int64_t c = ((n_comp + per - 1) / per + kStep - 1) / kStep * kStep;
+      ch = min(static_cast<int64_t>(2048), max(static_cast<int64_t>(1024), c));
+    }
+  }
   return ch;
 }
 
-static int64_t attend_chunks(int64_t n_comp, int64_t groups) {
+static int attend_bpc(const tq_quantizer* kq, const tq_quantizer* vq) {
+  return attend_blocks_per_cu(key_codebook(kq).bp, vq->cb[1].bp, key_qjl(kq), false);
+}
+
+static int64_t attend_chunks(int64_t n_comp, int64_t groups, int bpc) {
   if (n_comp <= 0) return 0;
-  const int64_t ch = attend_chunk_len(n_comp, groups);
+  const int64_t ch = attend_chunk_len(n_comp, groups, bpc);
   return (n_comp + ch - 1) / ch;
 }
 
-int64_t attend_ws_bytes(const tq_quantizer* kq, const tq_quantizer*, int B, int Hq, int Hkv, int64_t n_comp, int) {
+int64_t attend_ws_bytes(const tq_quantizer* kq, const tq_quantizer* vq, int B, int Hq, int Hkv, int64_t n_comp, int) {
   const int G = Hq / Hkv;
   const int RT = (G + 3) / 4;
   const int64_t groups = static_cast<int64_t>(B) * Hkv * RT;
-  const int64_t nch = attend_chunks(n_comp, groups);
+  const int64_t nch = attend_chunks(n_comp, groups, attend_bpc(kq, vq));
   const int64_t prep = (scores_ws_bytes(kq, B, Hq, Hkv) + 255) / 256 * 256;
   return prep + groups * nch * 4 * kPartStride * 4 + 256;
 }
@@ -374,19 +422,11 @@ __device__ __forceinline__ void attend_chunk_body(
   }
 }
 
-// Residency.  With a 2-step staging ring and at most 128 VGPRs four
-// workgroups share a CU (4 waves per SIMD) instead of three with a 3-step
-// ring: the extra waves hide each other's ALU phases better than the deeper
-// ring hides memory latency (GQA layer, 3-bit: 78 -> 72 us).  That register
-// budget holds the query terms and the value accumulators without spilling
-// where the key's MSE bits and the value bits are at most 3 each and the key
-// and value bits sum to at most 6; the other kernels, and the sparse-V ones,
-// keep the 3-step ring.
 template <int BPK, int BPV, bool QJL, bool SPARSE>
 struct AttendResidency {
-  static constexpr bool kFour = !SPARSE && BPK <= 3 && BPV <= 3 && BPK + (QJL ? 1 : 0) + BPV <= 6;
-  static constexpr int kSlots = kFour ? 2 : 3;
-  static constexpr int kBlocksPerCu = kFour ? 4 : 1;
+  static constexpr int kBlocks = attend_blocks_per_cu(BPK, BPV, QJL, SPARSE);
+  static constexpr int kSlots = kBlocks > 0 ? 2 : 3;
+  static constexpr int kBlocksPerCu = kBlocks > 0 ? kBlocks : 1;
 };
 
 template <int BPK, int BPV, bool QJL, bool SPARSE>
@@ -552,7 +592,8 @@ hipError_t launch_attend(const tq_quantizer* kq, const tq_quantizer* vq, const v
   const int G = Hq / Hkv;
   const int RT = (G + 3) / 4;
   const int64_t groups = static_cast<int64_t>(B) * Hkv * RT;
-  const int64_t nch = attend_chunks(n_comp, groups);
+  const int bpc = attend_bpc(kq, vq);
+  const int64_t nch = attend_chunks(n_comp, groups, bpc);
   const int64_t prep = (scores_ws_bytes(kq, B, Hq, Hkv) + 255) / 256 * 256;
   float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + prep);
   const float sl = scale * kLog2e;
@@ -563,7 +604,7 @@ hipError_t launch_attend(const tq_quantizer* kq, const tq_quantizer* vq, const v
     const int T = key_terms(kq);
     const uint8_t* wsA = static_cast<const uint8_t*>(ws);
     const float* wsC = reinterpret_cast<const float*>(wsA + groups * T * 2048);
-    const int64_t ch = attend_chunk_len(n_comp, groups);
+    const int64_t ch = attend_chunk_len(n_comp, groups, bpc);
     dim3 grid(static_cast<unsigned>(nch), static_cast<unsigned>(groups));
     const int bpk = key_codebook(kq).bp, bpv = vq->cb[1].bp;
     const bool qjl = key_qjl(kq);
