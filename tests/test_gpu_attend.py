@@ -123,6 +123,19 @@ def test_attend_full_size_sampled(name):
     print("worst relative error", w)
 
 
+def test_attend_one_round_chunks_ten_groups():
+    """4-bit keys and values over 131072 tokens with 10 KV heads: the chunk
+    kernel runs three workgroups per CU, 2048-token chunks would leave 640 of
+    the 768 resident slots, and the chunking fills one round instead (at most
+    76 chunks per group: 74 chunks of 1792 tokens).  The oracle checks two
+    groups."""
+    print("case: attend one-round chunks B=1 Hkv=10 Hq=40 N=131072 bits=4", flush=True)
+    B, Hkv, Hq, N = 1, 10, 40, 131072
+    k, v, q = _gqa_inputs(B, Hkv, Hq, N, 128, seed=77)
+    w = _run_case(k, v, q, B, Hkv, Hq, N, 0, 4, groups=[(0, 0), (0, 9)])
+    print("worst relative error", w)
+
+
 @pytest.mark.parametrize("kbits,vbits", [(4, 2), (2, 4), (3, 1), (4, 3)])
 def test_attend_asymmetric_bits(kbits, vbits):
     """Keys and values at different bit widths (each quantizer owns its own
