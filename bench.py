@@ -492,8 +492,8 @@ def run_search(args, torch, dev, tq, W):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU sharding is "
-              "described in DESIGN.md, not implemented.", file=sys.stderr)
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); sharding the path over several GPUs "
+              "is not implemented.", file=sys.stderr)
         sys.exit(2)
     import torch
 
