@@ -3,12 +3,16 @@
     python -m vector_quantization_tq_amd.prof_summary stats KERNEL_STATS_CSV
     python -m vector_quantization_tq_amd.prof_summary traffic --fetch FETCH_CSV --write WRITE_CSV \\
         --kernel scores_kernel --copy neg_kernel --copy-bytes 268435456 --sources FILE ...
+    python -m vector_quantization_tq_amd.prof_summary counters --kernel attend_chunk_kernel COUNTER_CSV ...
 
 `stats` prints one line per kernel (calls, average / min / max duration).
 `traffic` turns the FETCH_SIZE and WRITE_SIZE counters (KiB per dispatch,
 each from its own rocprofv3 --pmc run) of one kernel into bytes per launch,
 each scaled by what the same counter reads for a copy kernel of known size,
-and prints them with the sha256 of the kernel's sources.
+and prints them with the sha256 of the kernel's sources.  `counters` prints
+the mean per dispatch of every counter in the given runs for one kernel,
+per wave (divided by SQ_WAVES), and the shares of the wave cycles spent
+issuing (SQ_ACTIVE_INST_*) and waiting (SQ_WAIT_*).
 """
 from __future__ import annotations
 
@@ -88,7 +92,30 @@ def main(argv=None):
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--sources", nargs="+", required=True)
     t.add_argument("--root", default=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    c = sub.add_parser("counters")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("csv", nargs="+")
     a = ap.parse_args(argv)
+    if a.cmd == "counters":
+        means, name = {}, None
+        for path in a.csv:
+            with open(path, newline="") as f:
+                counters = sorted({r["Counter_Name"] for r in csv.DictReader(f)})
+            for ctr in counters:
+                k, (v, n) = pick(counter_means(path, ctr), a.kernel)
+                means[ctr], name = (v, n), k
+        waves = means.get("SQ_WAVES", (1.0, 1))[0]
+        print(f"kernel: {short_name(name)}")
+        print(f"{'counter':30s} {'per dispatch':>16} {'per wave':>12} {'dispatches':>10}")
+        for ctr in sorted(means):
+            v, n = means[ctr]
+            print(f"{ctr:30s} {v:16.0f} {v / waves:12.1f} {n:10d}")
+        if "SQ_WAVE_CYCLES" in means:
+            wc = means["SQ_WAVE_CYCLES"][0]
+            for ctr in sorted(means):
+                if ctr.startswith(("SQ_ACTIVE_INST", "SQ_WAIT")):
+                    print(f"share of wave cycles, {ctr}: {means[ctr][0] / wc:.3f}")
+        return 0
     if a.cmd == "stats":
         rows = kernel_stats(a.csv)
         print(f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}  kernel")
