@@ -317,8 +317,10 @@ __device__ __forceinline__ void attend_chunk_body(
       const float alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first step
       const float pa = __builtin_amdgcn_exp2f(sa - m_new), pb = __builtin_amdgcn_exp2f(sb - m_new);
       const float* vns = kns + 2 * kStep;
-      const float na = tA < live ? vns[tA] : 0.f;
-      const float nb2 = tB < live ? vns[tB] : 0.f;
+      // past the chunk's end p is exactly 0 (logit -inf) and the staged norm a
+      // finite re-read, so the weight is 0 without a mask
+      const float na = vns[tA];
+      const float nb2 = vns[tB];
       float wa = pa * na, wb = pb * nb2;
       l_lane = fmaf(l_lane, alpha, pa + pb);
       m_run = m_new;
