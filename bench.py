@@ -311,7 +311,7 @@ def run_gqa(args, torch, dev, tq, wl_fn, name, bits, n_tail=0):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u8",
+        "dtype": "fp8xfp4 MFMA, f32 accumulate",
         "data": "synthetic",
         "config": {"workload": name, "batch": B, "kv_heads": Hkv, "q_heads": Hq, "tokens": N, "tail_bf16": n_tail,
                    "d": d, "bits_keys": bits, "bits_values": vbits,
@@ -374,7 +374,7 @@ def _timed_loop(args, torch, step):
 def _common(args, ms_step, config, value, unit, metric=METRIC):
     return {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-            "dtype": "u8", "data": "synthetic", "config": config}
+            "dtype": "fp8xfp4 MFMA, f32 accumulate", "data": "synthetic", "config": config}
 
 
 def run_decode(args, torch, dev, tq, W):
@@ -475,7 +475,6 @@ def run_search(args, torch, dev, tq, W):
     res = _common(args, el * 1e3 / args.steps,
                   {"workload": f"vector-search 1000000 x 200 fp32, 1000 queries, top-10, {bits}-bit"},
                   round(nq / (tk * 1e-3), 1), "queries/s", metric="top-10 queries/s from packed codes, 1 MI355X")
-    res["dtype"] = "fp8 x fp4 MFMA, f32 accumulate"
     res["scan_gb_per_s"] = round(n * rec_k / (tk * 1e-3) / 1e9, 1)
     res["encode_keys_per_s"] = round(n / (enc * 1e-3), 0)
     res["recall_at_10_vs_exact_fp32"] = round(recall, 4)

@@ -31,6 +31,15 @@ def to_u32(t):
     return t.detach().cpu().numpy().view(np.uint32)
 
 
+def _threshold_distance(qz, x, n_o, t, where):
+    """Distance of the oracle's rotated coordinate y = Pi x / ||x|| to the
+    nearest decision threshold, at the coordinates selected by `where`."""
+    rows = np.any(where, axis=1) & (n_o > 0)
+    y = np.zeros(x.shape)
+    y[rows] = (x[rows] / n_o[rows, None]) @ qz.pi.T
+    return np.min(np.abs(y[where][:, None] - t[None, :]), axis=-1)
+
+
 def check_prod_codes(qz, x, codes, norms, gammas):
     """qz: oracle Quantizer; x float64 [N, d]; GPU outputs as numpy.  Returns
     (idx_gpu, bits_gpu, stats)."""
@@ -39,13 +48,10 @@ def check_prod_codes(qz, x, codes, norms, gammas):
     N = x.shape[0]
     idx_g, bits_g = o.unpack_prod(codes.reshape(N, -1), bp, d)
     idx_o, bits_o, n_o, g_o = o.encode_prod(qz, x)
-    nz = n_o > 0
-    y = np.zeros_like(x)
-    y[nz] = (x[nz] / n_o[nz, None]) @ qz.pi.T
-    dist = np.min(np.abs(y[..., None] - t), axis=-1)
     bad_idx = idx_g != idx_o
     assert np.all(np.abs(idx_g - idx_o)[bad_idx] == 1), "index differs by more than one level"
-    assert np.all(dist[bad_idx] < BAND), f"index flips outside the band: {np.sum(dist[bad_idx] >= BAND)}"
+    dist = _threshold_distance(qz, x, n_o, t, bad_idx)
+    assert np.all(dist < BAND), f"index flips outside the band: {np.sum(dist >= BAND)}"
     # cascade rule: recompute sketch and gamma from the GPU's indices where they differ
     rows = np.any(bad_idx, axis=1)
     bits_ref = bits_o.copy()
@@ -75,13 +81,10 @@ def check_mse_codes(qz, x, codes, norms):
     N = x.shape[0]
     idx_g = o.unpack_mse(codes, N, bp, d)
     idx_o, n_o = o.encode_mse(qz, x)
-    nz = n_o > 0
-    y = np.zeros_like(x)
-    y[nz] = (x[nz] / n_o[nz, None]) @ qz.pi.T
-    dist = np.min(np.abs(y[..., None] - t), axis=-1)
     bad = idx_g != idx_o
     assert np.all(np.abs(idx_g - idx_o)[bad] == 1)
-    assert np.all(dist[bad] < BAND), f"index flips outside the band: {np.sum(dist[bad] >= BAND)}"
+    dist = _threshold_distance(qz, x, n_o, t, bad)
+    assert np.all(dist < BAND), f"index flips outside the band: {np.sum(dist >= BAND)}"
     assert bad.sum() <= MAX_FLIP_FRAC * N * d + 0.5
     assert np.allclose(norms, n_o, rtol=1e-5, atol=1e-30)
     # padding tokens of the last block must be zero bits
@@ -102,13 +105,10 @@ def check_mse_key_codes(qz, x, codes, norms):
     words = codes.reshape(N, G, bp)
     idx_g = o.unpack_mse_keys(words.reshape(N, -1), bp, d)
     idx_o, n_o = o.encode_mse(qz, x)
-    nz = n_o > 0
-    y = np.zeros_like(x)
-    y[nz] = (x[nz] / n_o[nz, None]) @ qz.pi.T
-    dist = np.min(np.abs(y[..., None] - t), axis=-1)
     bad = idx_g != idx_o
     assert np.all(np.abs(idx_g - idx_o)[bad] == 1)
-    assert np.all(dist[bad] < BAND), f"index flips outside the band: {np.sum(dist[bad] >= BAND)}"
+    dist = _threshold_distance(qz, x, n_o, t, bad)
+    assert np.all(dist < BAND), f"index flips outside the band: {np.sum(dist >= BAND)}"
     assert bad.sum() <= MAX_FLIP_FRAC * N * d + 0.5
     assert np.allclose(norms, n_o, rtol=1e-5, atol=1e-30)
     if d % 32:

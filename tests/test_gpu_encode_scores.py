@@ -176,8 +176,8 @@ def test_scores_shapes(d, bits, B, Hkv, Hq, n, bf16):
 @pytest.mark.parametrize("bits", [2, 3, 4])
 def test_decode_layer_full_size_sampled(bits):
     """Single-layer decode workload at full size (32 heads x 8192 keys):
-    every key is encoded on the GPU; 1/64 of the keys are checked against
-    the oracle, and all 32 x 8192 logits are checked on identical codes."""
+    every key is encoded on the GPU and checked against the oracle (head by
+    head), and all 32 x 8192 logits are checked on identical codes."""
     print(f"case: decode layer full size bits={bits}", flush=True)
     wl = W.decode_layer(bits)
     g, oq = _pair(128, bits)
@@ -189,11 +189,52 @@ def test_decode_layer_full_size_sampled(bits):
     nn = norms.cpu().numpy().astype(np.float64)
     gg = gam.cpu().numpy().astype(np.float64)
     kv = wl.arrays["k"].reshape(-1, 128).astype(np.float64)
-    sample = np.arange(0, 32 * 8192, 64)
-    P.check_prod_codes(oq, kv[sample], cw[sample].reshape(-1), nn[sample], gg[sample])
     qv = wl.arrays["q"].astype(np.float64)
     for h in range(32):
         sl = slice(h * 8192, (h + 1) * 8192)
+        P.check_prod_codes(oq, kv[sl], cw[sl].reshape(-1), nn[sl], gg[sl])
         idx, bits01 = o.unpack_prod(cw[sl].reshape(-1).reshape(8192, -1), bits - 1, 128)
         ref = o.scores(oq, qv[h:h + 1], idx, bits01, nn[sl], gg[sl])
         P.check_logits(logits[h:h + 1], ref, np.linalg.norm(qv[h:h + 1], axis=1), nn[sl], 128)
+
+
+def test_binding_rejects_mis_sized_buffers():
+    """The C ABI takes no buffer lengths, so the binding checks every tensor
+    it forwards (shape, dtype, element count) and raises before any launch."""
+    print("case: binding argument checks", flush=True)
+    g, _ = _pair(128, 3)
+    dev = _dev()
+    x = torch.randn(2, 100, 128, device=dev)
+    codes, norms, gam = tq.tq_encode(g, tq.TQ_PROD, x)
+    q = torch.randn(1, 4, 128, device=dev)
+    with pytest.raises(ValueError):                       # 4-D input
+        tq.tq_encode(g, tq.TQ_PROD, x[None])
+    with pytest.raises(ValueError):                       # codes too short
+        tq.tq_encode(g, tq.TQ_PROD, x, out=(codes[:10], norms, gam))
+    with pytest.raises(ValueError):                       # norms too short
+        tq.tq_encode(g, tq.TQ_PROD, x, out=(codes, norms[:199], gam))
+    with pytest.raises(TypeError):                        # wrong dtype
+        tq.tq_encode(g, tq.TQ_PROD, x, out=(codes, norms.double(), gam))
+    with pytest.raises(ValueError):                       # query d differs from the quantizer's
+        tq.tq_scores(g, torch.randn(1, 4, 64, device=dev), codes, norms, gam, 2, 100)
+    with pytest.raises(ValueError):                       # more keys than the codes hold
+        tq.tq_scores(g, q, codes, norms, gam, 1, 201)
+    with pytest.raises(ValueError):                       # output too small
+        tq.tq_scores(g, q, codes, norms, gam, 1, 200, out=torch.empty(4, 100, device=dev))
+    with pytest.raises(ValueError):                       # workspace too small
+        tq.tq_scores(g, q, codes, norms, gam, 1, 200, workspace=torch.empty(16, dtype=torch.uint8, device=dev))
+    with pytest.raises(ValueError):                       # decode output too small
+        tq.tq_decode(g, tq.TQ_PROD, codes, norms, gam, 2, 100, out=torch.empty(2, 99, 128, device=dev))
+    gv = tq.Quantizer(128, 3, 1)
+    vc, vn, _ = tq.tq_encode(gv, tq.TQ_MSE, x)
+    qa = torch.randn(2, 4, 128, device=dev)
+    with pytest.raises(ValueError):                       # tail of the wrong shape
+        tq.tq_attend_decode(g, gv, qa, codes, norms, gam, vc, vn, 1, 100,
+                            torch.zeros(2, 1, 5, 128, device=dev, dtype=torch.bfloat16),
+                            torch.zeros(2, 1, 6, 128, device=dev, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):                       # value codes too short
+        tq.tq_attend_decode(g, gv, qa, codes, norms, gam, vc[:50], vn, 1, 100)
+    # the correct call still runs
+    out = tq.tq_attend_decode(g, gv, qa, codes, norms, gam, vc, vn, 1, 100)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()

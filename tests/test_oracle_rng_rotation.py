@@ -12,9 +12,13 @@ import pytest
 from oracle import tq_oracle as o
 
 
-def test_splitmix64_published_first_output(golden):
-    want = int(golden["books"]["splitmix64_seed0"]["values"][0], 16)
-    assert int(o.splitmix64(0, 1)[0]) == want
+def test_splitmix64_published_outputs(golden):
+    """SplittableRandom(0)'s first three outputs and Rosetta Code's five for
+    seed 1234567 (tests/golden/textbook_values.json)."""
+    want0 = [int(v, 16) for v in golden["books"]["splitmix64_seed0"]["values"]]
+    assert [int(v) for v in o.splitmix64(0, 3)] == want0
+    want1 = [int(v) for v in golden["books"]["splitmix64_seed1234567"]["values"]]
+    assert [int(v) for v in o.splitmix64(1234567, 5)] == want1
 
 
 def test_splitmix64_counter_based():

@@ -2,25 +2,29 @@
 
     python -m vector_quantization_tq_amd.build
 
-Runs hipcc once over all sources: host C++ (precompute), the C ABI and the
-kernels.  Always recompiles.
+Compiles every source to an object with hipcc (in parallel, objects under
+_build/ next to this file), then links them into libtq.so.  Always
+recompiles.
 """
 from __future__ import annotations
 
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
+OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtq.so")
 SOURCES = ["tq_host.cpp", "tq_api.hip", "tq_encode.hip", "tq_scores.hip", "tq_attend.hip", "tq_topk.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
+NOISE = ("is not a recognized feature for this target", "ignoring feature")
 
 
 def hipcc_flags():
-    return ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
+    return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
             # keep the compiler from forming packed fp32 ops (v_pk_*_f32)
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             # matrix-core accumulators in ordinary VGPRs: the kernels scale and
@@ -29,22 +33,31 @@ def hipcc_flags():
             "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
 
 
-def build(verbose: bool = False) -> str:
-    srcs = []
-    for s in SOURCES:
-        p = os.path.join(CSRC, s)
-        srcs += (["-x", "hip", p] if s.endswith(".hip") else ["-x", "c++", p])
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC] + hipcc_flags() + srcs + ["-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l and "ignoring feature" not in l)
+    err = "\n".join(l for l in (r.stderr or "").splitlines() if not any(n in l for n in NOISE))
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    jobs = []
+    for s in SOURCES:
+        src = os.path.join(CSRC, s)
+        obj = os.path.join(OBJ, os.path.splitext(s)[0] + ".o")
+        lang = "hip" if s.endswith(".hip") else "c++"
+        jobs.append((obj, [HIPCC] + hipcc_flags() + ["-c", "-x", lang, src, "-o", obj]))
+    workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(workers) as ex:
+        for f in [ex.submit(_run, cmd, verbose) for _, cmd in jobs]:
+            f.result()
+    tmp = LIB + ".tmp"
+    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}"] + [o for o, _ in jobs] + ["-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

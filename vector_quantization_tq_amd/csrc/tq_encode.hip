@@ -7,10 +7,19 @@
 // coordinate, rho = y - c[idx], gamma = n ||rho||, QJL bits = sign(S' rho)
 // with S' = S Pi^T (so S' rho = S r / n for the residual r = x - x_hat).
 //
-// Both products by a d x d matrix run on the fp32 MFMA (16x16x4): the code
-// decisions are taken on fp32-accurate values.  One workgroup encodes a tile
-// of 64 vectors; each of its 4 waves owns 16 vectors (rows) and all output
-// columns, so a wave only ever reads back its own rows from LDS.
+// Both products by a d x d matrix (Pi x and S' rho) are taken to fp32
+// accuracy, so the code decisions are taken on fp32-accurate values:
+//  * d <= 128 (encode_tile_kernel): the fp16 16x16x32 MFMA on split
+//    operands.  A float is written as hi + lo, two fp16 numbers (22
+//    significant bits), and the matrix core accumulates the products at fp32
+//    accuracy: x (Pi_hi + Pi_lo) for the rotation (bf16 keys are exact in
+//    fp16 after a power-of-two row scale; fp32 keys add x_lo Pi_hi) and
+//    rho_hi S'_hi + rho_lo S'_hi + rho_hi S'_lo for the QJL projection.
+//    Wave w keeps its 32 rows of Pi and S' (hi and lo) in registers as the
+//    stationary operand; workgroups are persistent over 64-vector tiles.
+//  * d > 128 (encode_kernel): the fp32 MFMA (16x16x4), one workgroup per
+//    tile of 64 vectors; each wave takes a quarter of the 16-column tiles
+//    for all 64 rows.
 #include <algorithm>
 
 #include "tq_device.h"

@@ -151,9 +151,51 @@ def _dtype_code(t):
 
 
 def _need_cuda(*ts):
+    dev = None
     for t in ts:
-        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+        if t is None:
+            continue
+        if not t.is_cuda or not t.is_contiguous():
             raise ValueError("tensors must be contiguous device tensors")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"tensors on different devices ({dev} and {t.device})")
+
+
+def _need_buf(t, name: str, numel: int, dtypes):
+    """The C ABI takes no buffer lengths: a tensor forwarded to it must hold
+    at least `numel` elements of one of `dtypes`, or the kernels would read or
+    write past its end."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}; expected {' or '.join(str(x) for x in dtypes)}")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements; {numel} needed")
+
+
+def _codes_dtypes():
+    torch = _torch()
+    return (torch.int32, torch.uint32) if hasattr(torch, "uint32") else (torch.int32,)
+
+
+def _check_queries(qz, q, name="queries"):
+    torch = _torch()
+    if q.dim() != 3:
+        raise ValueError(f"{name} must be [B, Hq, d], got shape {tuple(q.shape)}")
+    if q.shape[2] != qz.d:
+        raise ValueError(f"{name} have d = {q.shape[2]}, the quantizer d = {qz.d}")
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"{name} must be float32 or bfloat16")
+
+
+def _check_key_cache(qz, codes, norms, gammas, nseq: int, n: int, prefix=""):
+    torch = _torch()
+    _need_buf(codes, prefix + "codes", qz.code_words(qz.key_mode, nseq, n), _codes_dtypes())
+    _need_buf(norms, prefix + "norms", nseq * n, (torch.float32,))
+    if qz.key_mode == TQ_PROD:
+        _need_buf(gammas, prefix + "gammas", nseq * n, (torch.float32,))
 
 
 class Quantizer:
@@ -208,8 +250,10 @@ def tq_encode(qz: Quantizer, mode: int, x, out=None):
     _need_cuda(x)
     if x.dim() == 2:
         nseq, n = 1, x.shape[0]
-    else:
+    elif x.dim() == 3:
         nseq, n = x.shape[0], x.shape[1]
+    else:
+        raise ValueError(f"x must be [n, d] or [nseq, n, d], got shape {tuple(x.shape)}")
     if x.shape[-1] != qz.d:
         raise ValueError("last dimension must be d")
     dev = x.device
@@ -219,6 +263,11 @@ def tq_encode(qz: Quantizer, mode: int, x, out=None):
         gammas = torch.empty(max(nseq * n, 4), dtype=torch.float32, device=dev) if mode == TQ_PROD else None
     else:
         codes, norms, gammas = out
+        _need_cuda(x, codes, norms, gammas)
+        _need_buf(codes, "codes", qz.code_words(mode, nseq, n), _codes_dtypes())
+        _need_buf(norms, "norms", nseq * n, (torch.float32,))
+        if mode == TQ_PROD:
+            _need_buf(gammas, "gammas", nseq * n, (torch.float32,))
     _check(lib().tq_encode(qz.handle, mode, _ptr(x), _dtype_code(x), nseq, n, _ptr(codes), _ptr(norms),
                            _ptr(gammas), _stream()))
     return codes, norms, gammas
@@ -226,9 +275,14 @@ def tq_encode(qz: Quantizer, mode: int, x, out=None):
 
 def tq_decode(qz: Quantizer, mode: int, codes, norms, gammas, nseq: int, n: int, out=None):
     torch = _torch()
-    _need_cuda(codes, norms, gammas)
+    _need_cuda(codes, norms, gammas, out)
+    _need_buf(codes, "codes", qz.code_words(mode, nseq, n), _codes_dtypes())
+    _need_buf(norms, "norms", nseq * n, (torch.float32,))
+    if mode == TQ_PROD:
+        _need_buf(gammas, "gammas", nseq * n, (torch.float32,))
     if out is None:
         out = torch.empty((nseq, n, qz.d), dtype=torch.float32, device=codes.device)
+    _need_buf(out, "out", nseq * n * qz.d, (torch.float32,))
     _check(lib().tq_decode(qz.handle, mode, _ptr(codes), _ptr(norms), _ptr(gammas), nseq, n, _ptr(out), _stream()))
     return out
 
@@ -245,16 +299,24 @@ def tq_scores(qz: Quantizer, q, codes, norms, gammas, Hkv: int, n: int, topk: in
     """q: [B, Hq, d] device tensor (float32/bfloat16).  topk == 0 -> logits
     [B, Hq, n]; topk > 0 -> (scores [B, Hq, topk], int64 indices)."""
     torch = _torch()
-    _need_cuda(q, codes, norms, gammas)
+    _need_cuda(q, codes, norms, gammas, out, out_idx, workspace)
+    _check_queries(qz, q)
     B, Hq = q.shape[0], q.shape[1]
+    if Hkv < 1 or Hq % Hkv:
+        raise ValueError(f"Hq ({Hq}) must be a multiple of Hkv ({Hkv})")
+    _check_key_cache(qz, codes, norms, gammas, B * Hkv, n)
     dev = q.device
     if out is None:
         out = torch.empty((B, Hq, topk if topk else n), dtype=torch.float32, device=dev)
+    _need_buf(out, "out", B * Hq * (topk if topk else n), (torch.float32,))
     if topk and out_idx is None:
         out_idx = torch.empty((B, Hq, topk), dtype=torch.int64, device=dev)
+    if topk:
+        _need_buf(out_idx, "out_idx", B * Hq * topk, (torch.int64,))
     if workspace is None:
         workspace = torch.empty(max(scores_workspace_bytes(qz, B, Hq, Hkv, n, topk), 256), dtype=torch.uint8,
                                 device=dev)
+    _need_buf(workspace, "workspace", scores_workspace_bytes(qz, B, Hq, Hkv, n, topk), (torch.uint8,))
     _check(lib().tq_scores(qz.handle, _ptr(q), _dtype_code(q), B, Hq, Hkv, _ptr(codes), _ptr(norms), _ptr(gammas), n,
                            topk, _ptr(out), _ptr(out_idx) if topk else None, _ptr(workspace), workspace.numel(),
                            _stream()))
@@ -264,11 +326,13 @@ def tq_scores(qz: Quantizer, q, codes, norms, gammas, Hkv: int, n: int, topk: in
 def tq_query_prep(qz: Quantizer, q, Hkv: int, workspace=None):
     """Rotate/project the queries [B, Hq, d] once; returns the workspace."""
     torch = _torch()
-    _need_cuda(q)
+    _need_cuda(q, workspace)
+    _check_queries(qz, q)
     B, Hq = q.shape[0], q.shape[1]
     if workspace is None:
         workspace = torch.empty(max(scores_workspace_bytes(qz, B, Hq, Hkv, 1, 0), 256), dtype=torch.uint8,
                                 device=q.device)
+    _need_buf(workspace, "workspace", scores_workspace_bytes(qz, B, Hq, Hkv, 1, 0), (torch.uint8,))
     _check(lib().tq_query_prep(qz.handle, _ptr(q), _dtype_code(q), B, Hq, Hkv, _ptr(workspace), workspace.numel(),
                                _stream()))
     return workspace
@@ -276,9 +340,14 @@ def tq_query_prep(qz: Quantizer, q, Hkv: int, workspace=None):
 
 def tq_scores_from_prep(qz: Quantizer, B: int, Hq: int, Hkv: int, codes, norms, gammas, n: int, workspace, out=None):
     torch = _torch()
-    _need_cuda(codes, norms, gammas, workspace)
+    _need_cuda(codes, norms, gammas, workspace, out)
+    if Hkv < 1 or Hq % Hkv:
+        raise ValueError(f"Hq ({Hq}) must be a multiple of Hkv ({Hkv})")
+    _check_key_cache(qz, codes, norms, gammas, B * Hkv, n)
+    _need_buf(workspace, "workspace", scores_workspace_bytes(qz, B, Hq, Hkv, n, 0), (torch.uint8,))
     if out is None:
         out = torch.empty((B, Hq, n), dtype=torch.float32, device=codes.device)
+    _need_buf(out, "out", B * Hq * n, (torch.float32,))
     _check(lib().tq_scores_from_prep(qz.handle, B, Hq, Hkv, _ptr(codes), _ptr(norms), _ptr(gammas), n, _ptr(out),
                                      _ptr(workspace), workspace.numel(), _stream()))
     return out
@@ -297,17 +366,34 @@ def tq_attend_decode(kq: Quantizer, vq: Quantizer, q, kcodes, knorms, kgammas, v
     """q: [B, Hq, d]; tails: [B, Hkv, n_tail, d] bfloat16 or None.  Returns [B, Hq, d] float32.
     v_threshold (a float in [0, 1)) calls tq_attend_decode_sparse instead."""
     torch = _torch()
-    _need_cuda(q, kcodes, knorms, kgammas, vcodes, vnorms, k_tail, v_tail)
+    _need_cuda(q, kcodes, knorms, kgammas, vcodes, vnorms, k_tail, v_tail, out, workspace)
+    _check_queries(kq, q)
     B, Hq, d = q.shape
+    if Hkv < 1 or Hq % Hkv:
+        raise ValueError(f"Hq ({Hq}) must be a multiple of Hkv ({Hkv})")
+    if vq.d != kq.d:
+        raise ValueError("key and value quantizers differ in d")
+    if (k_tail is None) != (v_tail is None):
+        raise ValueError("give both tails or neither")
     n_tail = 0 if k_tail is None else k_tail.shape[2]
-    if k_tail is not None and (k_tail.dtype != torch.bfloat16 or v_tail.dtype != torch.bfloat16):
-        raise TypeError("tails must be bfloat16")
+    if k_tail is not None:
+        if k_tail.dtype != torch.bfloat16 or v_tail.dtype != torch.bfloat16:
+            raise TypeError("tails must be bfloat16")
+        for name, t in (("k_tail", k_tail), ("v_tail", v_tail)):
+            if tuple(t.shape) != (B, Hkv, n_tail, d):
+                raise ValueError(f"{name} must be [B, Hkv, n_tail, d] = {(B, Hkv, n_tail, d)}, got {tuple(t.shape)}")
+    if n_comp > 0:
+        _check_key_cache(kq, kcodes, knorms, kgammas, B * Hkv, n_comp, "k")
+        _need_buf(vcodes, "vcodes", vq.code_words(TQ_MSE, B * Hkv, n_comp), _codes_dtypes())
+        _need_buf(vnorms, "vnorms", B * Hkv * n_comp, (torch.float32,))
     dev = q.device
     if out is None:
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    _need_buf(out, "out", B * Hq * d, (torch.float32,))
     if workspace is None:
         workspace = torch.empty(max(attend_workspace_bytes(kq, vq, B, Hq, Hkv, n_comp, n_tail), 256),
                                 dtype=torch.uint8, device=dev)
+    _need_buf(workspace, "workspace", attend_workspace_bytes(kq, vq, B, Hq, Hkv, n_comp, n_tail), (torch.uint8,))
     if v_threshold is None:
         _check(lib().tq_attend_decode(kq.handle, vq.handle, _ptr(q), _dtype_code(q), B, Hq, Hkv, _ptr(kcodes),
                                       _ptr(knorms), _ptr(kgammas), _ptr(vcodes), _ptr(vnorms), n_comp, _ptr(k_tail),
