@@ -250,6 +250,26 @@ int tq_attend_decode_sparse(const tq_quantizer* kq, const tq_quantizer* vq, cons
                             const uint16_t* k_tail, const uint16_t* v_tail, int n_tail, float scale,
                             float v_threshold, float* out, void* workspace, int64_t ws_bytes, void* stream);
 
+/* Allocation-free decode attention, for callers that cannot allocate device
+ * memory: code under HIP graph capture, serving loops and harnesses that
+ * forbid hipMalloc.  Same arguments and result as tq_attend_decode without
+ * the workspace: the call uses a scratch array of TQ_NOALLOC_SCRATCH_BYTES
+ * that the library holds on each device until the process ends (its address
+ * is taken when the first quantizer is made on that device), and it calls no
+ * allocating routine.  Shapes whose tq_attend_workspace_bytes(...) exceeds
+ * TQ_NOALLOC_SCRATCH_BYTES are rejected with TQ_EWORKSPACE (16 MiB covers,
+ * e.g., 8 x 8 KV heads x 32 query heads over 32768 tokens, which needs about
+ * 4.7 MB).  Every call on a device shares that device's scratch: calls that
+ * overlap on one device (two streams, two threads) race and give undefined
+ * results; calls ordered on one stream are safe.  Nothing in the scratch
+ * needs to start at zero: each call writes every byte it reads. */
+#define TQ_NOALLOC_SCRATCH_BYTES (16ll << 20)
+int tq_attend_decode_noalloc(const tq_quantizer* kq, const tq_quantizer* vq, const void* queries, int q_dtype,
+                             int B, int Hq, int Hkv, const uint32_t* kcodes, const float* knorms,
+                             const float* kgammas, const uint32_t* vcodes, const float* vnorms, int64_t n_comp,
+                             const uint16_t* k_tail, const uint16_t* v_tail, int n_tail, float scale, float* out,
+                             void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -108,6 +109,34 @@ int check_keys(const tq_quantizer* q) {
   return TQ_OK;
 }
 
+// Library-owned workspace of tq_attend_decode_noalloc: one copy per device,
+// held until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: its device address comes from
+// hipGetSymbolAddress, taken once per device (with that device current) when
+// a quantizer is made there, and only that address is ever passed on.
+static __device__ __align__(256) uint8_t scratch[TQ_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// with device `dev` current
+int scratch_setup(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(TQ_EUNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev]) return TQ_OK;
+  void* p = nullptr;
+  hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+  g_scratch[dev] = p;
+  return TQ_OK;
+}
+
+void* scratch_of(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return g_scratch[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -202,6 +231,9 @@ tq_quantizer* tq_make_quantizer_ex(int d, int bits, uint64_t seed, int rotation)
   // raise the dynamic-LDS limit of the large encode tiles; if the runtime
   // refuses, launches that need more than the default report the error
   if (tq::set_kernel_attributes() != hipSuccess) (void)hipGetLastError();
+  // device address of the allocation-free entry point's scratch array on this
+  // device (a failure here is retried, and reported, by that entry point)
+  if (scratch_setup(q->device) != TQ_OK) (void)hipGetLastError();
   const size_t bp = pi32.size() * sizeof(float), bs = s32.size() * sizeof(float);
   if ((e = hipMalloc(&q->d_pi, bp)) != hipSuccess || (e = hipMalloc(&q->d_s, bs)) != hipSuccess ||
       (e = hipMalloc(&q->d_sp, bs)) != hipSuccess ||
@@ -395,11 +427,16 @@ int64_t tq_attend_workspace_bytes(const tq_quantizer* kq, const tq_quantizer* vq
   return tq::attend_ws_bytes(kq, vq, B, Hq, Hkv, n_comp, n_tail);
 }
 
-int tq_attend_decode_sparse(const tq_quantizer* kq, const tq_quantizer* vq, const void* queries, int q_dtype, int B,
-                            int Hq, int Hkv, const uint32_t* kcodes, const float* knorms, const float* kgammas,
-                            const uint32_t* vcodes, const float* vnorms, int64_t n_comp, const uint16_t* k_tail,
-                            const uint16_t* v_tail, int n_tail, float scale, float v_threshold, float* out,
-                            void* workspace, int64_t ws_bytes, void* stream) {
+}  // extern "C"
+
+// Argument checks and launch of decode attention.  With `noalloc` the
+// workspace is the device's scratch array (workspace/ws_bytes unused): the
+// call then allocates nothing and rejects shapes whose workspace exceeds it.
+static int attend_checked(const tq_quantizer* kq, const tq_quantizer* vq, const void* queries, int q_dtype, int B,
+                          int Hq, int Hkv, const uint32_t* kcodes, const float* knorms, const float* kgammas,
+                          const uint32_t* vcodes, const float* vnorms, int64_t n_comp, const uint16_t* k_tail,
+                          const uint16_t* v_tail, int n_tail, float scale, float v_threshold, float* out,
+                          void* workspace, int64_t ws_bytes, bool noalloc, void* stream) {
   if (!(v_threshold >= 0.f && v_threshold < 1.f)) return fail(TQ_EINVAL, "v_threshold must lie in [0, 1)");
   if (int r = check_quantizer(kq)) return r;
   if (int r = check_quantizer(vq)) return r;
@@ -420,12 +457,26 @@ int tq_attend_decode_sparse(const tq_quantizer* kq, const tq_quantizer* vq, cons
   if (kq->d != 128) return fail(TQ_EUNSUPPORTED, "attend supports d = 128 (d=%d)", kq->d);
   const int64_t need = tq_attend_workspace_bytes(kq, vq, B, Hq, Hkv, n_comp, n_tail);
   if (need < 0) return TQ_EINVAL;
-  if (!workspace || ws_bytes < need)
-    return fail(TQ_EWORKSPACE, "workspace of %lld bytes needed", static_cast<long long>(need));
-  if (!aligned(workspace, 256)) return fail(TQ_EINVAL, "workspace must be 256-byte aligned");
+  if (noalloc) {
+    if (need > static_cast<int64_t>(TQ_NOALLOC_SCRATCH_BYTES))
+      return fail(TQ_EWORKSPACE, "this shape needs %lld bytes of workspace, more than the %lld-byte scratch of the "
+                  "allocation-free call; use tq_attend_decode with a caller workspace",
+                  static_cast<long long>(need), static_cast<long long>(TQ_NOALLOC_SCRATCH_BYTES));
+  } else {
+    if (!workspace || ws_bytes < need)
+      return fail(TQ_EWORKSPACE, "workspace of %lld bytes needed", static_cast<long long>(need));
+    if (!aligned(workspace, 256)) return fail(TQ_EINVAL, "workspace must be 256-byte aligned");
+  }
   if (!(scale > 0.f)) scale = 1.f / std::sqrt(static_cast<float>(kq->d));
   DeviceGuard g(kq->device);
   if (!g.ok) return fail(TQ_EHIP, "cannot select the quantizer's device");
+  if (noalloc) {
+    workspace = scratch_of(kq->device);
+    if (!workspace) {
+      if (int r = scratch_setup(kq->device)) return r;
+      workspace = scratch_of(kq->device);
+    }
+  }
   hipError_t e = tq::launch_attend(kq, vq, queries, q_dtype, B, Hq, Hkv, kcodes, knorms, kgammas, vcodes, vnorms, n_comp,
                                    k_tail, v_tail, n_tail, scale, v_threshold, out, workspace,
                                    static_cast<hipStream_t>(stream));
@@ -433,12 +484,31 @@ int tq_attend_decode_sparse(const tq_quantizer* kq, const tq_quantizer* vq, cons
   return e == hipSuccess ? TQ_OK : hip_fail(e, "attend launch");
 }
 
+extern "C" {
+
+int tq_attend_decode_sparse(const tq_quantizer* kq, const tq_quantizer* vq, const void* queries, int q_dtype, int B,
+                            int Hq, int Hkv, const uint32_t* kcodes, const float* knorms, const float* kgammas,
+                            const uint32_t* vcodes, const float* vnorms, int64_t n_comp, const uint16_t* k_tail,
+                            const uint16_t* v_tail, int n_tail, float scale, float v_threshold, float* out,
+                            void* workspace, int64_t ws_bytes, void* stream) {
+  return attend_checked(kq, vq, queries, q_dtype, B, Hq, Hkv, kcodes, knorms, kgammas, vcodes, vnorms, n_comp, k_tail,
+                        v_tail, n_tail, scale, v_threshold, out, workspace, ws_bytes, false, stream);
+}
+
 int tq_attend_decode(const tq_quantizer* kq, const tq_quantizer* vq, const void* queries, int q_dtype, int B, int Hq,
                      int Hkv, const uint32_t* kcodes, const float* knorms, const float* kgammas, const uint32_t* vcodes,
                      const float* vnorms, int64_t n_comp, const uint16_t* k_tail, const uint16_t* v_tail, int n_tail,
                      float scale, float* out, void* workspace, int64_t ws_bytes, void* stream) {
-  return tq_attend_decode_sparse(kq, vq, queries, q_dtype, B, Hq, Hkv, kcodes, knorms, kgammas, vcodes, vnorms, n_comp,
-                                 k_tail, v_tail, n_tail, scale, 0.f, out, workspace, ws_bytes, stream);
+  return attend_checked(kq, vq, queries, q_dtype, B, Hq, Hkv, kcodes, knorms, kgammas, vcodes, vnorms, n_comp, k_tail,
+                        v_tail, n_tail, scale, 0.f, out, workspace, ws_bytes, false, stream);
+}
+
+int tq_attend_decode_noalloc(const tq_quantizer* kq, const tq_quantizer* vq, const void* queries, int q_dtype, int B,
+                             int Hq, int Hkv, const uint32_t* kcodes, const float* knorms, const float* kgammas,
+                             const uint32_t* vcodes, const float* vnorms, int64_t n_comp, const uint16_t* k_tail,
+                             const uint16_t* v_tail, int n_tail, float scale, float* out, void* stream) {
+  return attend_checked(kq, vq, queries, q_dtype, B, Hq, Hkv, kcodes, knorms, kgammas, vcodes, vnorms, n_comp, k_tail,
+                        v_tail, n_tail, scale, 0.f, out, nullptr, 0, true, stream);
 }
 
 }  // extern "C"

@@ -24,8 +24,11 @@ EXPORTS = [
     "tq_version", "tq_last_error", "tq_host_normals", "tq_host_rotation", "tq_host_rotation_hadamard",
     "tq_host_qjl_matrix", "tq_host_codebook", "tq_make_quantizer", "tq_make_quantizer_ex", "tq_free_quantizer", "tq_quantizer_info", "tq_set_key_mode", "tq_code_words", "tq_encode",
     "tq_decode", "tq_scores_workspace_bytes", "tq_query_prep", "tq_scores_from_prep", "tq_scores",
-    "tq_attend_workspace_bytes", "tq_attend_decode", "tq_attend_decode_sparse",
+    "tq_attend_workspace_bytes", "tq_attend_decode", "tq_attend_decode_sparse", "tq_attend_decode_noalloc",
 ]
+
+# size of the library's per-device scratch array used by tq_attend_decode_noalloc (include/tq.h)
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class TQError(RuntimeError):
@@ -72,6 +75,8 @@ def lib() -> ctypes.CDLL:
                                    c_f, c_p, c_p, c_i64, c_p]),
         "tq_attend_decode_sparse": (c_i, [c_p, c_p, c_p, c_i, c_i, c_i, c_i, c_p, c_p, c_p, c_p, c_p, c_i64, c_p, c_p,
                                           c_i, c_f, c_f, c_p, c_p, c_i64, c_p]),
+        "tq_attend_decode_noalloc": (c_i, [c_p, c_p, c_p, c_i, c_i, c_i, c_i, c_p, c_p, c_p, c_p, c_p, c_i64, c_p, c_p,
+                                           c_i, c_f, c_p, c_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -360,13 +365,10 @@ def attend_workspace_bytes(kq: Quantizer, vq: Quantizer, B: int, Hq: int, Hkv: i
     return w
 
 
-def tq_attend_decode(kq: Quantizer, vq: Quantizer, q, kcodes, knorms, kgammas, vcodes, vnorms, Hkv: int,
-                     n_comp: int, k_tail=None, v_tail=None, scale: float = 0.0, out=None, workspace=None,
-                     v_threshold=None):
-    """q: [B, Hq, d]; tails: [B, Hkv, n_tail, d] bfloat16 or None.  Returns [B, Hq, d] float32.
-    v_threshold (a float in [0, 1)) calls tq_attend_decode_sparse instead."""
+def _check_attend(kq, vq, q, kcodes, knorms, kgammas, vcodes, vnorms, Hkv, n_comp, k_tail, v_tail, out):
+    """Checks every tensor an attention call forwards; returns (B, Hq, d, n_tail, out)."""
     torch = _torch()
-    _need_cuda(q, kcodes, knorms, kgammas, vcodes, vnorms, k_tail, v_tail, out, workspace)
+    _need_cuda(q, kcodes, knorms, kgammas, vcodes, vnorms, k_tail, v_tail, out)
     _check_queries(kq, q)
     B, Hq, d = q.shape
     if Hkv < 1 or Hq % Hkv:
@@ -386,10 +388,22 @@ def tq_attend_decode(kq: Quantizer, vq: Quantizer, q, kcodes, knorms, kgammas, v
         _check_key_cache(kq, kcodes, knorms, kgammas, B * Hkv, n_comp, "k")
         _need_buf(vcodes, "vcodes", vq.code_words(TQ_MSE, B * Hkv, n_comp), _codes_dtypes())
         _need_buf(vnorms, "vnorms", B * Hkv * n_comp, (torch.float32,))
-    dev = q.device
     if out is None:
-        out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
     _need_buf(out, "out", B * Hq * d, (torch.float32,))
+    return B, Hq, d, n_tail, out
+
+
+def tq_attend_decode(kq: Quantizer, vq: Quantizer, q, kcodes, knorms, kgammas, vcodes, vnorms, Hkv: int,
+                     n_comp: int, k_tail=None, v_tail=None, scale: float = 0.0, out=None, workspace=None,
+                     v_threshold=None):
+    """q: [B, Hq, d]; tails: [B, Hkv, n_tail, d] bfloat16 or None.  Returns [B, Hq, d] float32.
+    v_threshold (a float in [0, 1)) calls tq_attend_decode_sparse instead."""
+    torch = _torch()
+    B, Hq, d, n_tail, out = _check_attend(kq, vq, q, kcodes, knorms, kgammas, vcodes, vnorms, Hkv, n_comp, k_tail,
+                                          v_tail, out)
+    _need_cuda(q, workspace)
+    dev = q.device
     if workspace is None:
         workspace = torch.empty(max(attend_workspace_bytes(kq, vq, B, Hq, Hkv, n_comp, n_tail), 256),
                                 dtype=torch.uint8, device=dev)
@@ -404,4 +418,19 @@ def tq_attend_decode(kq: Quantizer, vq: Quantizer, q, kcodes, knorms, kgammas, v
                                              _ptr(kcodes), _ptr(knorms), _ptr(kgammas), _ptr(vcodes), _ptr(vnorms),
                                              n_comp, _ptr(k_tail), _ptr(v_tail), n_tail, scale, float(v_threshold),
                                              _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
+    return out
+
+
+def tq_attend_decode_noalloc(kq: Quantizer, vq: Quantizer, q, kcodes, knorms, kgammas, vcodes, vnorms, Hkv: int,
+                             n_comp: int, k_tail=None, v_tail=None, scale: float = 0.0, out=None):
+    """tq_attend_decode without a workspace: the library's per-device scratch
+    array (NOALLOC_SCRATCH_BYTES) serves instead and the library allocates
+    nothing; shapes that need a larger workspace raise TQError.  Calls that
+    overlap on one device race on that scratch.  Pass `out` to allocate
+    nothing on the Python side either."""
+    B, Hq, d, n_tail, out = _check_attend(kq, vq, q, kcodes, knorms, kgammas, vcodes, vnorms, Hkv, n_comp, k_tail,
+                                          v_tail, out)
+    _check(lib().tq_attend_decode_noalloc(kq.handle, vq.handle, _ptr(q), _dtype_code(q), B, Hq, Hkv, _ptr(kcodes),
+                                          _ptr(knorms), _ptr(kgammas), _ptr(vcodes), _ptr(vnorms), n_comp,
+                                          _ptr(k_tail), _ptr(v_tail), n_tail, scale, _ptr(out), _stream()))
     return out
