@@ -68,6 +68,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a 256 MiB device copy 3 times (the known-size kernel for counter scaling)")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="gqa: also time a plain streaming kernel that moves the logits scan's bytes (same buffers, "
+                         "same read/write mix, no arithmetic) right after the scan in every step")
     return ap.parse_args()
 
 
@@ -241,10 +244,29 @@ def run_gqa(args, torch, dev, tq, wl_fn, name, bits, n_tail=0):
                            device=dev)
     except Exception:
         attend_ok = False
+    stream_mix = None
+    if args.ceiling:
+        import ctypes
+        if not (d == 128 and bits == 3 and not mse_keys and n_comp % 64 == 0):
+            raise SystemExit("--ceiling: the streaming kernel mirrors 3-bit prod keys at d = 128, n a multiple of 64")
+        slib = ctypes.CDLL(os.path.join(ROOT, "vector_quantization_tq_amd", "libtq_stream.so"))
+        slib.tq_stream_scan_mix.restype = ctypes.c_int
+        slib.tq_stream_scan_mix.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                            ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+        mix_out = torch.empty((nseq, n_comp, 4), dtype=torch.float32, device=dev)
+
+        def stream_mix(c):
+            rc = slib.tq_stream_scan_mix(ctypes.c_void_p(c[0].data_ptr()), ctypes.c_void_p(c[1].data_ptr()),
+                                         ctypes.c_void_p(c[2].data_ptr()), n_comp, nseq,
+                                         ctypes.c_void_p(mix_out.data_ptr()),
+                                         ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"tq_stream_scan_mix failed ({rc})")
     # fill both copies once
     for c in copies:
         tq.tq_encode(qz, kmode, k, out=(c[0], c[1], c[2]))
         tq.tq_encode(qv, tq.TQ_MSE, v, out=(c[3], c[4], None))
+    mix_src = [(c[0].clone(), c[1].clone(), c[2].clone()) for c in copies] if stream_mix is not None else None
     if attend_ok:
         try:
             c = copies[0]
@@ -272,6 +294,13 @@ def run_gqa(args, torch, dev, tq, wl_fn, name, bits, n_tail=0):
             tq.tq_attend_decode(qz, qv, q, r[0], r[1], r[2], r[3], r[4], Hkv, n_comp, k_tail, v_tail, 0.0, out=out,
                                 workspace=ws_a, v_threshold=args.v_threshold)
         e5 = timer.mark()
+        if stream_mix is not None:
+            # its own code copies, alternating like the scan's: each is read
+            # every other step, with more than 1 GB of other traffic between
+            stream_mix(mix_src[i % 2])
+            e6 = timer.mark()
+            if timed:
+                timer.span("stream_ceiling", e5, e6)
         if timed:
             timer.span("encode_keys", e0, e1)
             timer.span("encode_values", e1, e2)
@@ -320,6 +349,7 @@ def run_gqa(args, torch, dev, tq, wl_fn, name, bits, n_tail=0):
         "packed_pct_of_hbm_peak": round(100 * packed_gbs / HBM_PEAK_GBS, 1),
         "encode_keys_per_s": round(nkeys / (enc_ms * 1e-3), 0),
         "kernels_ms": {k2: round(timer.avg_ms(k2), 4) for k2 in timer.acc},
+        "tq_scores_call_gb_per_s": round(nkeys * rec_k / ((scores_ms + timer.avg_ms("query_prep")) * 1e-3) / 1e9, 1),
         "roofline": {
             "kernel": "scores_kernel (tq_scores_from_prep)",
             "bound": "hbm",
@@ -345,6 +375,15 @@ def run_gqa(args, torch, dev, tq, wl_fn, name, bits, n_tail=0):
                                  / FP16_MFMA_PEAK_TFLOPS, 4),
         },
     }
+    if "stream_ceiling" in timer.acc:
+        cm = timer.avg_ms("stream_ceiling")
+        res["stream_ceiling"] = {
+            "kernel": "stream_scan_mix (libtq_stream.so): the scan's reads and writes, no arithmetic",
+            "ms": round(cm, 4),
+            "gb_per_s": round(scores_alg / (cm * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(scores_alg / (cm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "scan_time_over_ceiling": round(scores_ms / cm, 3),
+        }
     if attend_ok:
         at_ms = timer.avg_ms("attend")
         at_bytes = nkeys * (rec_k + rec_v) + (nseq * n_tail * d * 2 * 2)

@@ -18,6 +18,9 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtq.so")
 SOURCES = ["tq_host.cpp", "tq_api.hip", "tq_encode.hip", "tq_scores.hip", "tq_attend.hip", "tq_topk.hip"]
+# the benchmark's streaming-ceiling kernel, in a library of its own
+STREAM_LIB = os.path.join(HERE, "libtq_stream.so")
+STREAM_SOURCES = ["tq_stream.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 NOISE = ("is not a recognized feature for this target", "ignoring feature")
@@ -47,18 +50,20 @@ def _run(cmd, verbose):
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
     jobs = []
-    for s in SOURCES:
+    for s in SOURCES + STREAM_SOURCES:
         src = os.path.join(CSRC, s)
         obj = os.path.join(OBJ, os.path.splitext(s)[0] + ".o")
         lang = "hip" if s.endswith(".hip") else "c++"
-        jobs.append((obj, [HIPCC] + hipcc_flags() + ["-c", "-x", lang, src, "-o", obj]))
+        jobs.append((s, obj, [HIPCC] + hipcc_flags() + ["-c", "-x", lang, src, "-o", obj]))
     workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
     with ThreadPoolExecutor(workers) as ex:
-        for f in [ex.submit(_run, cmd, verbose) for _, cmd in jobs]:
+        for f in [ex.submit(_run, cmd, verbose) for _, _, cmd in jobs]:
             f.result()
-    tmp = LIB + ".tmp"
-    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}"] + [o for o, _ in jobs] + ["-o", tmp], verbose)
-    os.replace(tmp, LIB)
+    for lib, srcs in ((LIB, SOURCES), (STREAM_LIB, STREAM_SOURCES)):
+        tmp = lib + ".tmp"
+        objs = [o for s, o, _ in jobs if s in srcs]
+        _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}"] + objs + ["-o", tmp], verbose)
+        os.replace(tmp, lib)
     return LIB
 
 
