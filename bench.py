@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--value-bits", type=int, default=None, help="gqa/long: value bits (default: the key bits)")
     ap.add_argument("--v-threshold", type=float, default=None,
                     help="gqa/long: sparse V (tq_attend_decode_sparse with this threshold in [0, 1))")
+    ap.add_argument("--rotation", default="haar", choices=["haar", "hadamard"],
+                    help="gqa/long: dense Haar rotation (QR of a Gaussian) or the structured H D / sqrt(d)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a 256 MiB device copy 3 times (the known-size kernel for counter scaling)")
@@ -222,10 +224,11 @@ def run_gqa(args, torch, dev, tq, wl_fn, name, bits, n_tail=0):
     mse_keys = args.key_mode == "mse"
     kmode = tq.TQ_MSE_KEYS if mse_keys else tq.TQ_PROD
     vbits = args.value_bits or bits
-    qz = tq.Quantizer(d, bits, 0)
+    rot = tq.TQ_ROT_HADAMARD if args.rotation == "hadamard" else tq.TQ_ROT_HAAR
+    qz = tq.Quantizer(d, bits, 0, rot)
     if mse_keys:
         qz.set_key_mode(tq.TQ_MSE_KEYS)
-    qv = qz if vbits == bits else tq.Quantizer(d, vbits, 0)
+    qv = qz if vbits == bits else tq.Quantizer(d, vbits, 0, rot)
     nseq = B * Hkv
     copies = []
     for _ in range(2):
@@ -345,6 +348,7 @@ def run_gqa(args, torch, dev, tq, wl_fn, name, bits, n_tail=0):
         "config": {"workload": name, "batch": B, "kv_heads": Hkv, "q_heads": Hq, "tokens": N, "tail_bf16": n_tail,
                    "d": d, "bits_keys": bits, "bits_values": vbits,
                    "key_mode": "mse-only (b MSE bits)" if mse_keys else "prod (b-1 MSE + 1 QJL)",
+                   "rotation": args.rotation,
                    "value_mode": "mse" if args.v_threshold is None else f"mse, sparse V threshold {args.v_threshold}"},
         "packed_pct_of_hbm_peak": round(100 * packed_gbs / HBM_PEAK_GBS, 1),
         "encode_keys_per_s": round(nkeys / (enc_ms * 1e-3), 0),
@@ -545,7 +549,7 @@ def main():
         bits = args.bits or 3
         res, wl = run_gqa(args, torch, dev, tq, W.gqa_layer, f"gqa-decode-layer b8 kv8 q32 n32768 d128 {bits}-bit", bits)
         if (not args.no_cpu_baseline and args.key_mode == "prod" and bits == 3 and not args.value_bits
-                and args.v_threshold is None):
+                and args.v_threshold is None and args.rotation == "haar"):
             res["cpu_baseline"] = cpu_baseline_gqa(wl, args.steps)
     elif args.workload == "long":
         bits = args.bits or 4

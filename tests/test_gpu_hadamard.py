@@ -129,3 +129,34 @@ def test_attend_hadamard(B, Hkv, Hq, N, tail, bits):
             ref = o.attend(ok, ov, qs[b, h * G:(h + 1) * G], ki, kb, kn[sl], kg[sl], vi, vn[sl],
                            kf[s, n_comp:] if tail else None, vf[s, n_comp:] if tail else None)
             P.check_attention(out[b, h * G:(h + 1) * G], ref)
+
+
+@pytest.mark.parametrize("mode", ["prod", "mse", "mse_keys"])
+def test_encode_hadamard_gqa_layer_multi_tile(mode):
+    """Keys (prod and MSE-only) and values of 8 (batch, KV head) sequences of
+    the GQA decode layer (bf16, 32768 tokens each) under the Hadamard rotation:
+    the d = 128 encoder with the exact +-1 rotation operand, many tiles per
+    persistent workgroup; every code of every sequence is checked."""
+    print(f"case: hadamard GQA-layer encode {mode} 8 x 32768", flush=True)
+    rng = np.random.default_rng(33)
+    a = W._gqa_tensors(rng, 1, 8, 32, 32768, 128)
+    key = "v_bf16" if mode == "mse" else "k_bf16"
+    xt = torch.from_numpy(np.ascontiguousarray(a[key]).view(np.int16)).to(_dev()).view(torch.bfloat16).view(8, 32768, 128)
+    xs = a[key[0]].reshape(8, 32768, 128).astype(np.float64)
+    g, oq = _pair(128, 3)
+    m = {"prod": tq.TQ_PROD, "mse": tq.TQ_MSE, "mse_keys": tq.TQ_MSE_KEYS}[mode]
+    codes, norms, gam = tq.tq_encode(g, m, xt)
+    torch.cuda.synchronize()
+    cw = P.to_u32(codes)
+    per = g.code_words(m, 1, 32768)
+    nn = norms.cpu().numpy()
+    gg = gam.cpu().numpy() if gam is not None else None
+    for s in range(8):
+        sl = slice(s * 32768, (s + 1) * 32768)
+        c = cw[s * per:(s + 1) * per]
+        if mode == "prod":
+            P.check_prod_codes(oq, xs[s], c, nn[sl], gg[sl])
+        elif mode == "mse":
+            P.check_mse_codes(oq, xs[s], c, nn[sl])
+        else:
+            P.check_mse_key_codes(oq, xs[s], c, nn[sl])

@@ -372,8 +372,12 @@ __device__ __forceinline__ float pick_centroid(const float (&cen)[1 << BP], cons
 // bits.  MODE: 0 keys with the QJL sketch (token-major words + rho, gamma),
 // 1 values (coordinate-major 32-token words), 2 MSE-only keys (token-major
 // words, no QJL plane).  FULL: d == 32 KS, so every wave owns 32 existing
-// coordinates and the coordinate guards compile away.
-template <int KS, int LK, int MODE, int BP, bool FULL>
+// coordinates and the coordinate guards compile away.  HAD: Pi = H D / sqrt(d)
+// (the structured rotation): sqrt(d) Pi has entries +-1, so the rotation's
+// stationary operand is +-2^8 exactly in fp16 and needs no lo part -- one
+// product per rotation term instead of two (bf16 input), with 1/sqrt(d)
+// moved into the fp32 row scale.
+template <int KS, int LK, int MODE, int BP, bool FULL, bool HAD = false>
 __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restrict__ x, int dtype, int64_t nseq,
                                                              int64_t n, int d, const float* __restrict__ pi,
                                                              const float* __restrict__ sp, Codebook cb,
@@ -409,9 +413,11 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
   const int64_t total = nseq * tps;
   const int64_t nb = (n + 31) >> 5;                      // mse blocks per sequence
 
+  static_assert(!HAD || FULL, "the +-1 rotation operand is built for d = 32 KS");
   // stationary operands: lane (r16, q) holds row 32w + 16ct + r16, columns
-  // 32s + 8q .. +7 of Pi (and S'), split into hi + lo
-  v8h bPh[2][KS], bPl[2][KS], bSh[2][QJL ? KS : 1], bSl[2][QJL ? KS : 1];
+  // 32s + 8q .. +7 of Pi (and S'), split into hi + lo (HAD: sqrt(d) Pi 2^8 =
+  // +-2^8, exact, no lo part)
+  v8h bPh[2][KS], bPl[2][HAD ? 1 : KS], bSh[2][QJL ? KS : 1], bSl[2][QJL ? KS : 1];
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
     const int j = 32 * w + 16 * ct + r16;
@@ -421,10 +427,15 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
       for (int e = 0; e < 8; ++e) {
         const int k = 32 * s2 + 8 * q + e;
         const bool in = j < d && k < d;
-        const float vp = in ? pi[static_cast<int64_t>(j) * d + k] * kPiScale : 0.f;
-        const _Float16 ph = static_cast<_Float16>(vp);
-        bPh[ct][s2][e] = ph;
-        bPl[ct][s2][e] = static_cast<_Float16>(vp - static_cast<float>(ph));
+        if constexpr (HAD) {
+          const float pv = in ? pi[static_cast<int64_t>(j) * d + k] : 0.f;
+          bPh[ct][s2][e] = static_cast<_Float16>(pv > 0.f ? kPiScale : pv < 0.f ? -kPiScale : 0.f);
+        } else {
+          const float vp = in ? pi[static_cast<int64_t>(j) * d + k] * kPiScale : 0.f;
+          const _Float16 ph = static_cast<_Float16>(vp);
+          bPh[ct][s2][e] = ph;
+          bPl[ct][s2][e] = static_cast<_Float16>(vp - static_cast<float>(ph));
+        }
         if constexpr (QJL) {
           const float vs = in ? sp[static_cast<int64_t>(j) * d + k] * kPiScale : 0.f;
           const _Float16 sh = static_cast<_Float16>(vs);
@@ -569,8 +580,12 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
     if (part == 0) {
       const float nv = lrow < rows ? sqrtf(ss) : 0.f;
       nrm[lrow] = nv;
-      // y 2^14 = acc * scl: the rotation of u, times 2^14 (Pi carries 2^8, the row 2^sig)
-      scl[lrow] = nv > 0.f ? ldexpf(1.f / nv, 6 - sig) : 0.f;
+      // y 2^14 = acc * scl: the rotation of u, times 2^14 (Pi carries 2^8, the row 2^sig;
+      // HAD: the operand is sqrt(d) Pi 2^8, so the scale also divides by sqrt(d))
+      if constexpr (HAD)
+        scl[lrow] = nv > 0.f ? ldexpf(1.f / (nv * sqrtf(static_cast<float>(32 * KS))), 6 - sig) : 0.f;
+      else
+        scl[lrow] = nv > 0.f ? ldexpf(1.f / nv, 6 - sig) : 0.f;
     }
   };
   auto store = [&](TileAt t, int buf) {
@@ -671,7 +686,7 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
         v4f acc[2][2];
         zero_acc(acc);
         contract(xh, bPh, h, false, acc);
-        contract(xh, bPl, h, false, acc);
+        if constexpr (!HAD) contract(xh, bPl, h, false, acc);
         if constexpr (XLO) contract(xl, bPh, h, false, acc);
         pin_acc(acc);
         // lane holds vector 32h + 16h2 + 4q + i, coordinate 32w + 16ct + r16
@@ -794,7 +809,7 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
         v4f acc[2][2];
         zero_acc(acc);
         contract(xh, bPh, h, true, acc);
-        contract(xh, bPl, h, true, acc);
+        if constexpr (!HAD) contract(xh, bPl, h, true, acc);
         if constexpr (XLO) contract(xl, bPh, h, true, acc);
         pin_acc(acc);
         // lane holds coordinate 32w + 16ct + 4q + i, token 32h + 16h2 + r16
@@ -913,34 +928,56 @@ size_t encode_lds_bytes(int d) {
   return sizeof(float) * (kTileRows * (DP + 1) + kTileRows + kMaxLevels) + 2 * kTileRows * DP;
 }
 
-static int encode_tile_blocks() {
-  static int blocks = [] {
-    int dev = 0, cus = 256;
+static int device_cu_count() {
+  static int cus = [] {
+    int dev = 0, c = 256;
     if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-      cus = 256;
-    return 2 * cus;   // two resident workgroups per CU (LDS and registers)
+        hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c < 1)
+      c = 256;
+    return c;
+  }();
+  return cus;
+}
+
+// Persistent grid of the tile encoder: as many workgroups as fit on the chip
+// at once for this instantiation (its registers and LDS decide: two per CU
+// for prod keys, three or four for values and MSE-only keys), so that every
+// resident slot loops over tiles.
+template <int LK, int MODE, int BPV, bool FULL, bool HAD>
+int encode_tile_grid() {
+  static const int blocks = [] {
+    int per = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per, reinterpret_cast<const void*>(&encode_tile_kernel<4, LK, MODE, BPV, FULL, HAD>), 256, 0) !=
+            hipSuccess ||
+        per < 1) {
+      (void)hipGetLastError();
+      per = 2;
+    }
+    return std::min(per, 4) * device_cu_count();
   }();
   return blocks;
 }
 
-template <int LK, int MODE, bool FULL>
+template <int LK, int MODE, bool FULL, bool HAD = false>
 hipError_t launch_encode_tile_m(const tq_quantizer* q, const void* x, int dtype, int64_t nseq, int64_t n,
                                 uint32_t* codes, float* norms, float* gammas, hipStream_t st) {
   const int64_t tiles = nseq * ((n + kEncRows - 1) / kEncRows);
-  const dim3 grid(static_cast<unsigned>(std::min<int64_t>(tiles, encode_tile_blocks())));
   const Codebook& cb = q->cb[MODE == 0 ? 0 : 1];
 #define TQ_ENC(BPV)                                                                                                 \
-  case BPV:                                                                                                         \
-    hipLaunchKernelGGL((encode_tile_kernel<4, LK, MODE, BPV, FULL>), grid, dim3(256), 0, st, x, dtype, nseq, n, q->d,     \
-                       q->d_pi, q->d_sp, cb, codes, norms, gammas);                                               \
-    break;
+  case BPV: {                                                                                                       \
+    const dim3 grid(static_cast<unsigned>(std::min<int64_t>(tiles, encode_tile_grid<LK, MODE, BPV, FULL, HAD>())));   \
+    hipLaunchKernelGGL((encode_tile_kernel<4, LK, MODE, BPV, FULL, HAD>), grid, dim3(256), 0, st, x, dtype, nseq, n,    \
+                       q->d, q->d_pi, q->d_sp, cb, codes, norms, gammas);                                         \
+    break;                                                                                                          \
+  }
   switch (cb.bp) {
     TQ_ENC(1) TQ_ENC(2) TQ_ENC(3)
     case 4:
       if constexpr (MODE != 0) {
-        hipLaunchKernelGGL((encode_tile_kernel<4, LK, MODE, 4, FULL>), grid, dim3(256), 0, st, x, dtype, nseq, n, q->d,
-                           q->d_pi, q->d_sp, cb, codes, norms, gammas);
+        const dim3 grid(static_cast<unsigned>(std::min<int64_t>(tiles, encode_tile_grid<LK, MODE, 4, FULL, HAD>())));
+        hipLaunchKernelGGL((encode_tile_kernel<4, LK, MODE, 4, FULL, HAD>), grid, dim3(256), 0, st, x, dtype, nseq, n,
+                           q->d, q->d_pi, q->d_sp, cb, codes, norms, gammas);
         break;
       }
       return hipErrorNotSupported;
@@ -955,6 +992,13 @@ hipError_t launch_encode_tile_lk(const tq_quantizer* q, int mode, const void* x,
                                  uint32_t* codes, float* norms, float* gammas, hipStream_t st) {
   // d = 128 (the usual head dimension) takes the variant without coordinate guards
   constexpr bool F = LK != 0;
+  if constexpr (F) {
+    if (q->d == 128 && q->rotation == 1) {   // TQ_ROT_HADAMARD: the exact +-1 rotation operand
+      if (mode == 0) return launch_encode_tile_m<LK, 0, true, true>(q, x, dtype, nseq, n, codes, norms, gammas, st);
+      if (mode == 1) return launch_encode_tile_m<LK, 1, true, true>(q, x, dtype, nseq, n, codes, norms, gammas, st);
+      return launch_encode_tile_m<LK, 2, true, true>(q, x, dtype, nseq, n, codes, norms, gammas, st);
+    }
+  }
   if (F && q->d == 128) {
     if (mode == 0) return launch_encode_tile_m<LK, 0, F>(q, x, dtype, nseq, n, codes, norms, gammas, st);
     if (mode == 1) return launch_encode_tile_m<LK, 1, F>(q, x, dtype, nseq, n, codes, norms, gammas, st);
