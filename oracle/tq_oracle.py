@@ -425,6 +425,68 @@ def sparse_v_bound(kq: Quantizer, vq: Quantizer, q, k_idx, k_bits, k_norms, k_ga
     return (p[:, :n_comp] * D) @ np.abs(vals)
 
 
+def attend_segments(segments, q, k_tail=None, v_tail=None, scale=None):
+    """Decode attention over a cache kept in several compressed segments
+    (temporal decay, [wiselychen] TurboQuant+ table: older tokens are kept at
+    a lower precision).  Reading (R28): each segment holds its own key and
+    value quantizers and codes; the logits of all compressed tokens (each
+    segment's keys scored with its own quantizer) and of the exact tail share
+    one softmax, and the output sums every token's decoded value.
+
+    segments: list of (kq, vq, k_idx, k_bits or None, k_norms, k_gammas, v_idx,
+    v_norms); q [Hg, d]; tails [T, d].  Returns out [Hg, d]."""
+    q = np.asarray(q, dtype=np.float64)
+    d = q.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    logits, vals = [], []
+    for (kq, vq, k_idx, k_bits, k_norms, k_gammas, v_idx, v_norms) in segments:
+        if len(k_idx) == 0:
+            continue
+        if k_bits is None:
+            logits.append(scores_mse(kq, q, k_idx, k_norms))
+        else:
+            logits.append(scores(kq, q, k_idx, k_bits, k_norms, k_gammas))
+        vals.append(decode_mse(vq, v_idx, v_norms))
+    if k_tail is not None and len(k_tail):
+        logits.append(q @ np.asarray(k_tail, dtype=np.float64).T)
+        vals.append(np.asarray(v_tail, dtype=np.float64))
+    logit = np.concatenate(logits, axis=1)
+    s = scale * logit
+    s = s - s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    p /= p.sum(axis=1, keepdims=True)
+    return p @ np.concatenate(vals, axis=0)
+
+
+def requantize(q_from: Quantizer, q_to: Quantizer, mode: str, idx, bits01, norms, gammas):
+    """A token moving to an older, lower-precision segment (R28): its
+    reconstruction at the old width -- x~ (MSE part plus the QJL term) for
+    prod keys, x^ for values and MSE-only keys -- is encoded again with the new
+    quantizer.  mode: "prod", "mse" (values) or "mse_keys".  Returns what
+    encode_prod / encode_mse return for the new quantizer."""
+    if mode == "prod":
+        x = decode_prod(q_from, idx, bits01, norms, gammas)
+        return encode_prod(q_to, x)
+    x = decode_mse(q_from, idx, norms)
+    return encode_mse(q_to, x)
+
+
+def kv_width_config(width: float):
+    """Fractional cache widths (R27, [hotdry] engineering configuration:
+    "3.5-bit = 3-bit MSE + 1-bit QJL", 2.5-bit the more aggressive setting;
+    [friday] comparison table: lowest width 2.5 bits): the width is the mean
+    over the cached key and value coordinates.  Keys are coded with b_k - 1
+    index bits plus one QJL bit, values with b_v index bits, and
+    (b_k + b_v) / 2 = width with b_k = b_v + 1 for a half-integer width.
+    Returns (key bits b_k, value bits b_v)."""
+    w2 = round(2 * width)
+    if abs(2 * width - w2) > 1e-9 or not 3 <= w2 <= 8:
+        raise ValueError("width must be a multiple of 0.5 in [1.5, 4]")
+    if w2 % 2 == 0:
+        return w2 // 2, w2 // 2
+    return (w2 + 1) // 2, (w2 - 1) // 2
+
+
 # ---------------------------------------------------------------------------
 # 8. Top-k by score (vector search with codes, [a2a] benchmark section on
 #    GloVe-style search): order by (score descending, index ascending).
