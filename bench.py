@@ -57,12 +57,16 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="gqa", choices=["gqa", "long", "decode", "search"])
+    ap.add_argument("--workload", default="gqa", choices=["gqa", "long", "decode", "search", "decay"])
     ap.add_argument("--bits", type=int, default=None,
                     help="key bits (default: gqa 3, long 4, decode 3, search 4)")
     ap.add_argument("--key-mode", default="prod", choices=["prod", "mse"],
                     help="gqa/long: prod keys (b-1 MSE bits + QJL) or MSE-only keys (all b bits to the index)")
     ap.add_argument("--value-bits", type=int, default=None, help="gqa/long: value bits (default: the key bits)")
+    ap.add_argument("--kv-width", type=float, default=None,
+                    help="gqa/long: mean cache width in bits per key and value coordinate, a multiple of 0.5 "
+                         "(3.5 = 4-bit prod keys, i.e. 3-bit index + 1 QJL bit, with 3-bit values); sets --bits and "
+                         "--value-bits")
     ap.add_argument("--v-threshold", type=float, default=None,
                     help="gqa/long: sparse V (tq_attend_decode_sparse with this threshold in [0, 1))")
     ap.add_argument("--rotation", default="haar", choices=["haar", "hadamard"],
@@ -349,6 +353,7 @@ def run_gqa(args, torch, dev, tq, wl_fn, name, bits, n_tail=0):
                    "d": d, "bits_keys": bits, "bits_values": vbits,
                    "key_mode": "mse-only (b MSE bits)" if mse_keys else "prod (b-1 MSE + 1 QJL)",
                    "rotation": args.rotation,
+                   "kv_width_bits": (bits + vbits) / 2,
                    "value_mode": "mse" if args.v_threshold is None else f"mse, sparse V threshold {args.v_threshold}"},
         "packed_pct_of_hbm_peak": round(100 * packed_gbs / HBM_PEAK_GBS, 1),
         "encode_keys_per_s": round(nkeys / (enc_ms * 1e-3), 0),
@@ -531,12 +536,114 @@ def run_search(args, torch, dev, tq, W):
     return res
 
 
+def run_decay(args, torch, dev, tq, W):
+    """Temporal decay on the long-context layer: the older two thirds of the
+    130816 compressed tokens (87168, a multiple of 128) are kept at 2-bit
+    keys and values, the newer 43648 at 4 bits, the last 256 in bf16.  A step
+    encodes both segments, scores them (one scan per segment) and runs decode
+    attention over the segmented cache with one softmax; beside it, the
+    re-quantization of 8 x 4096 tokens from 4 to 2 bits (keys and values) is
+    timed, the work of moving an aged block to the older segment."""
+    wl = W.long_context()
+    B, Hkv, Hq, N, tail, d = 1, 8, 32, 131072, 256, 128
+    nseq = B * Hkv
+    n_comp = N - tail
+    n_old = (2 * n_comp // 3) // 128 * 128
+    n_new = n_comp - n_old
+    b_old, b_new = 2, 4
+    k_all = bf16_tensor(torch, wl.arrays["k_bf16"], dev).view(nseq, N, d)
+    v_all = bf16_tensor(torch, wl.arrays["v_bf16"], dev).view(nseq, N, d)
+    q = bf16_tensor(torch, wl.arrays["q_bf16"], dev)
+    parts = {"old": (k_all[:, :n_old].contiguous(), v_all[:, :n_old].contiguous(), n_old, tq.Quantizer(d, b_old, 0)),
+             "new": (k_all[:, n_old:n_comp].contiguous(), v_all[:, n_old:n_comp].contiguous(), n_new,
+                     tq.Quantizer(d, b_new, 0))}
+    k_tail = k_all[:, n_comp:].contiguous().view(B, Hkv, tail, d)
+    v_tail = v_all[:, n_comp:].contiguous().view(B, Hkv, tail, d)
+    copies = []
+    for _ in range(2):
+        c = {}
+        for name, (k, v, n, qz) in parts.items():
+            c[name] = tq.tq_encode(qz, tq.TQ_PROD, k) + tq.tq_encode(qz, tq.TQ_MSE, v)[:2]
+        copies.append(c)
+    logits = {name: torch.empty((B, Hq, n), dtype=torch.float32, device=dev) for name, (_, _, n, _) in parts.items()}
+    ws = {name: torch.empty(tq.scores_workspace_bytes(qz, B, Hq, Hkv, n), dtype=torch.uint8, device=dev)
+          for name, (_, _, n, qz) in parts.items()}
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+
+    def segments(c):
+        return [tq.Segment(parts[nm][3], parts[nm][3], *c[nm][:3], *c[nm][3:5], parts[nm][2]) for nm in ("old", "new")]
+
+    ws_a = torch.empty(tq.attend_segments_workspace_bytes(segments(copies[0]), B, Hq, Hkv, tail), dtype=torch.uint8,
+                       device=dev)
+    # an aged block: 8 x 4096 tokens of the new segment re-encoded at 2 bits
+    na = 4096
+    q_old, q_new = parts["old"][3], parts["new"][3]
+    age_in = [tq.tq_encode(q_new, tq.TQ_PROD, parts["new"][0][:, :na].contiguous()),
+              tq.tq_encode(q_new, tq.TQ_MSE, parts["new"][1][:, :na].contiguous())]
+    age_out = [(torch.empty(q_old.code_words(tq.TQ_PROD, nseq, na), dtype=torch.int32, device=dev),
+                torch.empty(nseq * na, device=dev), torch.empty(nseq * na, device=dev)),
+               (torch.empty(q_old.code_words(tq.TQ_MSE, nseq, na), dtype=torch.int32, device=dev),
+                torch.empty(nseq * na, device=dev), None)]
+    age_ws = torch.empty(nseq * na * d, dtype=torch.float32, device=dev)
+    timer = Timer(torch)
+
+    def step(i, timed):
+        w, r = copies[i % 2], copies[(i + 1) % 2]
+        e = [timer.mark()]
+        for name, (k, v, n, qz) in parts.items():
+            tq.tq_encode(qz, tq.TQ_PROD, k, out=w[name][:3])
+            tq.tq_encode(qz, tq.TQ_MSE, v, out=(w[name][3], w[name][4], None))
+        e.append(timer.mark())
+        for name, (k, v, n, qz) in parts.items():
+            tq.tq_query_prep(qz, q, Hkv, workspace=ws[name])
+            tq.tq_scores_from_prep(qz, B, Hq, Hkv, *r[name][:3], n, ws[name], out=logits[name])
+        e.append(timer.mark())
+        tq.tq_attend_decode_segments(segments(r), q, Hkv, k_tail, v_tail, out=out, workspace=ws_a)
+        e.append(timer.mark())
+        tq.tq_requantize(q_new, q_old, tq.TQ_PROD, *age_in[0], nseq, na, out=age_out[0], workspace=age_ws)
+        tq.tq_requantize(q_new, q_old, tq.TQ_MSE, age_in[1][0], age_in[1][1], None, nseq, na, out=age_out[1],
+                         workspace=age_ws)
+        e.append(timer.mark())
+        if timed:
+            for nm, a, b in zip(("encode", "scores", "attend", "requantize"), e[:-1], e[1:]):
+                timer.span(nm, a, b)
+
+    el = _timed_loop(args, torch, step)
+    timer.collect()
+    rk = {b: 4 * 4 * b + 8 for b in (b_old, b_new)}        # prod key record bytes, d = 128
+    rv = {b: (b * d) // 8 + 4 for b in (b_old, b_new)}     # value record bytes
+    packed = nseq * (n_old * (rk[b_old] + rv[b_old]) + n_new * (rk[b_new] + rv[b_new]))
+    uniform = nseq * n_comp * (rk[b_new] + rv[b_new])
+    at = timer.avg_ms("attend")
+    at_bytes = packed + nseq * tail * d * 2 * 2
+    res = _common(args, el * 1e3 / args.steps,
+                  {"workload": f"long-context decay b1 kv8 q32 n131072: {n_old} tokens at {b_old}-bit, {n_new} at "
+                               f"{b_new}-bit, 256 bf16 tail"},
+                  round(at_bytes / (at * 1e-3) / 1e9, 1), "GB/s",
+                  metric="decode attention over a decayed cache, GB/s of packed K+V")
+    res["kernels_ms"] = {k2: round(timer.avg_ms(k2), 4) for k2 in timer.acc}
+    res["packed_bytes"] = packed
+    res["packed_bytes_uniform_4bit"] = uniform
+    res["memory_saving_vs_uniform"] = round(1 - packed / uniform, 4)
+    res["requantize_tokens_per_s"] = round(2 * nseq * na / (timer.avg_ms("requantize") * 1e-3), 0)
+    res["roofline"] = {"kernel": "tq_attend_decode_segments (all its launches)", "bound": "hbm",
+                       "achieved": round(at_bytes / (at * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": round(at_bytes / (at * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                       "algorithmic_bytes_per_launch": at_bytes}
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); sharding the path over several GPUs "
               "is not implemented.", file=sys.stderr)
         sys.exit(2)
+    if args.kv_width is not None:
+        w2 = round(2 * args.kv_width)
+        if abs(2 * args.kv_width - w2) > 1e-9 or not 3 <= w2 <= 8:
+            raise SystemExit("--kv-width must be a multiple of 0.5 in [1.5, 4]")
+        args.bits, args.value_bits = (w2 + 1) // 2, w2 // 2
     import torch
 
     from vector_quantization_tq_amd import tq
@@ -557,6 +664,8 @@ def main():
                           f"long-context b1 kv8 q32 n131072 tail256 d128 {bits}-bit", bits, n_tail=256)
     elif args.workload == "decode":
         res = run_decode(args, torch, dev, tq, W)
+    elif args.workload == "decay":
+        res = run_decay(args, torch, dev, tq, W)
     else:
         res = run_search(args, torch, dev, tq, W)
     print(json.dumps(res), flush=True)

@@ -250,6 +250,56 @@ int tq_attend_decode_sparse(const tq_quantizer* kq, const tq_quantizer* vq, cons
                             const uint16_t* k_tail, const uint16_t* v_tail, int n_tail, float scale,
                             float v_threshold, float* out, void* workspace, int64_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Temporal decay ([wiselychen] TurboQuant+ table: older tokens are kept at
+ * a lower precision, a further 30-34% of memory at long context).  Reading:
+ * the compressed cache is kept in age segments, each encoded with its own
+ * quantizers (e.g. the newest tokens at 4 bits, older ones at 2); decode
+ * attention runs one softmax over every segment and the exact tail; a token
+ * moves to an older segment by tq_requantize.
+ * ------------------------------------------------------------------------ */
+#define TQ_MAX_SEGMENTS 16
+
+/* One segment of a compressed cache: [B*Hkv] sequences of n tokens encoded
+ * with kq (in its key mode; kgammas may be NULL for TQ_MSE_KEYS) and, for the
+ * values, vq (TQ_MSE).  The value quantizers of all segments of one call must
+ * share d, seed and rotation (hence Pi, whatever their widths): the value
+ * sums of all segments are rotated back once.  Key quantizers are free. */
+typedef struct tq_segment {
+  const tq_quantizer* kq;
+  const tq_quantizer* vq;
+  const uint32_t* kcodes;
+  const float* knorms;
+  const float* kgammas;
+  const uint32_t* vcodes;
+  const float* vnorms;
+  int64_t n;
+} tq_segment;
+
+/* Decode attention over nseg (1..TQ_MAX_SEGMENTS) segments plus the optional
+ * bf16 tail: logits of every segment's tokens (by its own key quantizer) and
+ * of the tail share one softmax; out = sum_i p_i v_i with each value decoded
+ * by its segment's quantizer.  With one segment this is tq_attend_decode.
+ * The order of the segments does not change the result beyond rounding.
+ * queries [B][Hq][d], tails [B][Hkv][n_tail][d] bf16, out [B][Hq][d] float,
+ * scale <= 0 selects 1/sqrt(d); d = 128.  workspace: at least
+ * tq_attend_segments_workspace_bytes(...) bytes, 256-byte aligned. */
+int64_t tq_attend_segments_workspace_bytes(const tq_segment* segs, int nseg, int B, int Hq, int Hkv, int n_tail);
+int tq_attend_decode_segments(const tq_segment* segs, int nseg, const void* queries, int q_dtype, int B, int Hq,
+                              int Hkv, const uint16_t* k_tail, const uint16_t* v_tail, int n_tail, float scale,
+                              float* out, void* workspace, int64_t ws_bytes, void* stream);
+
+/* Re-encode tokens at another width (a token ageing into an older segment):
+ * decode the codes of `from` (x~ with the QJL term for TQ_PROD; x^ for TQ_MSE
+ * and TQ_MSE_KEYS) and encode the result with `to` in the same mode.  The two
+ * quantizers must have the same d.  codes_in/norms_in/gammas_in: the encoding
+ * of [nseq][n] vectors by `from`; the outputs take `to`'s layout and sizes
+ * (tq_code_words(to, mode, nseq, n) words).  workspace: nseq * n * d floats
+ * (the decoded vectors), 16-byte aligned.  Asynchronous on `stream`. */
+int tq_requantize(const tq_quantizer* from, const tq_quantizer* to, int mode, const uint32_t* codes_in,
+                  const float* norms_in, const float* gammas_in, int64_t nseq, int64_t n, uint32_t* codes_out,
+                  float* norms_out, float* gammas_out, void* workspace, int64_t ws_bytes, void* stream);
+
 /* Allocation-free decode attention, for callers that cannot allocate device
  * memory: code under HIP graph capture, serving loops and harnesses that
  * forbid hipMalloc.  Same arguments and result as tq_attend_decode without

@@ -53,14 +53,17 @@ def _scan_batches_per_wave(groups, n):
     return -(-nbatch // (4 * bx))
 
 
-def _run_layer(wl, n_tail):
+def _run_layer(wl, n_tail, bits=None, vbits=None):
     """Encode, score and attend a GQA-shaped workload the way the benchmark
-    does; return every GPU output and the float inputs as numpy arrays."""
+    does (keys at `bits`, values at `vbits`, both the workload's by default);
+    return every GPU output and the float inputs as numpy arrays."""
     B, Hkv, Hq, N, d = wl.meta["B"], wl.meta["Hkv"], wl.meta["Hq"], wl.meta["N"], wl.d
-    bits = wl.bits
+    bits = bits or wl.bits
+    vbits = vbits or bits
     n_comp = N - n_tail
     nseq = B * Hkv
     qz = tq.Quantizer(d, bits, 0)
+    qv = qz if vbits == bits else tq.Quantizer(d, vbits, 0)
     k_all = _bf16(wl.arrays["k_bf16"]).view(nseq, N, d)
     v_all = _bf16(wl.arrays["v_bf16"]).view(nseq, N, d)
     q = _bf16(wl.arrays["q_bf16"])
@@ -69,11 +72,11 @@ def _run_layer(wl, n_tail):
     kt = k_all[:, n_comp:].contiguous().view(B, Hkv, n_tail, d) if n_tail else None
     vt = v_all[:, n_comp:].contiguous().view(B, Hkv, n_tail, d) if n_tail else None
     kc, kn, kg = tq.tq_encode(qz, tq.TQ_PROD, k)
-    vc, vn, _ = tq.tq_encode(qz, tq.TQ_MSE, v)
+    vc, vn, _ = tq.tq_encode(qv, tq.TQ_MSE, v)
     ws = tq.tq_query_prep(qz, q, Hkv)
     logits = tq.tq_scores_from_prep(qz, B, Hq, Hkv, kc, kn, kg, n_comp, ws)
     logits_call = tq.tq_scores(qz, q, kc, kn, kg, Hkv, n_comp)
-    out = tq.tq_attend_decode(qz, qz, q, kc, kn, kg, vc, vn, Hkv, n_comp, kt, vt)
+    out = tq.tq_attend_decode(qz, qv, q, kc, kn, kg, vc, vn, Hkv, n_comp, kt, vt)
     torch.cuda.synchronize()
     assert torch.equal(logits, logits_call), "tq_scores and query prep + scan differ"
     del logits_call, k, v, k_all, v_all
@@ -84,7 +87,7 @@ def _run_layer(wl, n_tail):
         "vw": P.to_u32(vc).reshape(nseq, -1), "vn": vn.cpu().numpy().reshape(nseq, n_comp),
         "logits": logits.cpu().numpy(), "out": out.cpu().numpy(),
         "k": wl.arrays["k"].reshape(nseq, N, d), "v": wl.arrays["v"].reshape(nseq, N, d),
-        "q": wl.arrays["q"], "oq": o.Quantizer(d, bits, 0),
+        "q": wl.arrays["q"], "oq": o.Quantizer(d, bits, 0), "ov": o.Quantizer(d, vbits, 0), "vbits": vbits,
     }
 
 
@@ -118,7 +121,7 @@ def _check_value_codes(r, seqs):
     flips = 0
     for s in seqs:
         x = r["v"][s, :r["n_comp"]].astype(np.float64)
-        _, st = P.check_mse_codes(r["oq"], x, r["vw"][s], r["vn"][s])
+        _, st = P.check_mse_codes(r["ov"], x, r["vw"][s], r["vn"][s])
         flips += st["index_flips"]
     return flips
 
@@ -147,10 +150,10 @@ def _check_attention(r):
         for h in range(r["Hkv"]):
             s = b * r["Hkv"] + h
             ki, kb = o.unpack_prod(r["kw"][s], bits - 1, d)
-            vi = o.unpack_mse(r["vw"][s], n, bits, d)
+            vi = o.unpack_mse(r["vw"][s], n, r["vbits"], d)
             tail_k = r["k"][s, n:].astype(np.float64) if r["n_tail"] else None
             tail_v = r["v"][s, n:].astype(np.float64) if r["n_tail"] else None
-            ref = o.attend(r["oq"], r["oq"], r["q"][b, h * G:(h + 1) * G].astype(np.float64), ki, kb,
+            ref = o.attend(r["oq"], r["ov"], r["q"][b, h * G:(h + 1) * G].astype(np.float64), ki, kb,
                            r["kn"][s].astype(np.float64), r["kg"][s].astype(np.float64), vi,
                            r["vn"][s].astype(np.float64), tail_k, tail_v)
             worst = max(worst, P.check_attention(r["out"][b, h * G:(h + 1) * G], ref))
@@ -193,6 +196,22 @@ def test_long_logits_every_group(long_ctx):
 
 def test_long_attention_every_group(long_ctx):
     print("worst relative attention error", _check_attention(long_ctx))
+
+
+@pytest.mark.parametrize("width", [3.5, 2.5])
+def test_gqa_fractional_width_every_group(width):
+    """The GQA layer at a fractional cache width (the mean over key and value
+    coordinates): 3.5 bits = 4-bit prod keys (3-bit index + QJL) with 3-bit
+    values, 2.5 bits = 3-bit keys with 2-bit values.  Every logit and every
+    group's attention output checked; key and value codes of 8 sequences
+    (every 8th, so every batch) checked."""
+    bits, vbits = o.kv_width_config(width)
+    print(f"case: full-size GQA layer at {width} bits (keys {bits}, values {vbits})", flush=True)
+    r = _run_layer(W.gqa_layer(), 0, bits, vbits)
+    print("key code flips:", _check_key_codes(r, range(0, 64, 8)))
+    print("value code flips:", _check_value_codes(r, range(0, 64, 8)))
+    print("worst relative logit error", _check_logits(r))
+    print("worst relative attention error", _check_attention(r))
 
 
 @pytest.mark.parametrize("B,Hkv,Hq,n,bits", [(4, 8, 32, 32767, 3), (1, 4, 24, 100003, 4), (2, 2, 2, 262143, 2)])

@@ -503,6 +503,97 @@ int tq_attend_decode(const tq_quantizer* kq, const tq_quantizer* vq, const void*
                         v_tail, n_tail, scale, 0.f, out, workspace, ws_bytes, false, stream);
 }
 
+int64_t tq_attend_segments_workspace_bytes(const tq_segment* segs, int nseg, int B, int Hq, int Hkv, int n_tail) {
+  if (!segs || nseg < 1 || nseg > TQ_MAX_SEGMENTS) return fail(TQ_EINVAL, "need 1 <= nseg <= %d segments", TQ_MAX_SEGMENTS);
+  if (check_heads(B, Hq, Hkv)) return -1;
+  if (n_tail < 0) return fail(TQ_EINVAL, "negative n_tail");
+  tq::AttendSegment sg[TQ_MAX_SEGMENTS];
+  for (int i = 0; i < nseg; ++i) {
+    if (!segs[i].kq || !segs[i].vq) return fail(TQ_EINVAL, "segment %d: NULL quantizer", i);
+    if (segs[i].n < 0) return fail(TQ_EINVAL, "segment %d: negative n", i);
+    sg[i] = {segs[i].kq, segs[i].vq, nullptr, nullptr, nullptr, nullptr, nullptr, segs[i].n};
+  }
+  return tq::attend_segments_ws_bytes(sg, nseg, B, Hq, Hkv);
+}
+
+int tq_attend_decode_segments(const tq_segment* segs, int nseg, const void* queries, int q_dtype, int B, int Hq,
+                              int Hkv, const uint16_t* k_tail, const uint16_t* v_tail, int n_tail, float scale,
+                              float* out, void* workspace, int64_t ws_bytes, void* stream) {
+  if (!segs || nseg < 1 || nseg > TQ_MAX_SEGMENTS) return fail(TQ_EINVAL, "need 1 <= nseg <= %d segments", TQ_MAX_SEGMENTS);
+  if (int r = check_heads(B, Hq, Hkv)) return r;
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return fail(TQ_EINVAL, "q_dtype must be TQ_F32 or TQ_BF16");
+  if (n_tail < 0) return fail(TQ_EINVAL, "negative n_tail");
+  if (!queries || !out) return fail(TQ_EINVAL, "NULL queries or output");
+  if (n_tail > 0 && (!k_tail || !v_tail)) return fail(TQ_EINVAL, "NULL tail array");
+  const tq_quantizer* v0 = segs[0].vq;
+  int64_t total = n_tail;
+  tq::AttendSegment sg[TQ_MAX_SEGMENTS];
+  for (int i = 0; i < nseg; ++i) {
+    const tq_segment& g = segs[i];
+    if (!g.kq || !g.vq) return fail(TQ_EINVAL, "segment %d: NULL quantizer", i);
+    if (g.n < 0) return fail(TQ_EINVAL, "segment %d: negative n", i);
+    if (int r = check_keys(g.kq)) return r;
+    if (g.kq->d != v0->d || g.vq->d != v0->d) return fail(TQ_EINVAL, "segment %d: quantizers differ in d", i);
+    // the merge rotates the summed values back with one Pi^T
+    if (g.vq->seed != v0->seed || g.vq->rotation != v0->rotation)
+      return fail(TQ_EINVAL, "segment %d: value quantizers must share seed and rotation (one Pi)", i);
+    const float* kg = tq::key_qjl(g.kq) ? g.kgammas : nullptr;   // MSE-only keys carry no gamma
+    if (g.n > 0 && (!g.kcodes || !g.knorms || (tq::key_qjl(g.kq) && !kg) || !g.vcodes || !g.vnorms))
+      return fail(TQ_EINVAL, "segment %d: NULL cache array", i);
+    const void* ptrs[] = {g.kcodes, g.knorms, kg, g.vcodes, g.vnorms};
+    for (const void* p : ptrs)
+      if (p && !aligned(p, 16)) return fail(TQ_EINVAL, "device pointers must be 16-byte aligned");
+    sg[i] = {g.kq, g.vq, g.kcodes, g.knorms, kg, g.vcodes, g.vnorms, g.n};
+    total += g.n;
+  }
+  if (total < 1) return fail(TQ_EINVAL, "empty cache");
+  const void* ptrs[] = {queries, out, k_tail, v_tail};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, 16)) return fail(TQ_EINVAL, "device pointers must be 16-byte aligned");
+  if (v0->d != 128) return fail(TQ_EUNSUPPORTED, "attend supports d = 128 (d=%d)", v0->d);
+  const int64_t need = tq::attend_segments_ws_bytes(sg, nseg, B, Hq, Hkv);
+  if (!workspace || ws_bytes < need)
+    return fail(TQ_EWORKSPACE, "workspace of %lld bytes needed", static_cast<long long>(need));
+  if (!aligned(workspace, 256)) return fail(TQ_EINVAL, "workspace must be 256-byte aligned");
+  if (!(scale > 0.f)) scale = 1.f / std::sqrt(static_cast<float>(v0->d));
+  DeviceGuard dg(v0->device);
+  if (!dg.ok) return fail(TQ_EHIP, "cannot select the quantizer's device");
+  hipError_t e = tq::launch_attend_segments(sg, nseg, queries, q_dtype, B, Hq, Hkv, k_tail, v_tail, n_tail, scale, 0.f,
+                                            out, workspace, static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return fail(TQ_EUNSUPPORTED, "shape not supported by the attention kernels");
+  return e == hipSuccess ? TQ_OK : hip_fail(e, "attend launch");
+}
+
+int tq_requantize(const tq_quantizer* from, const tq_quantizer* to, int mode, const uint32_t* codes_in,
+                  const float* norms_in, const float* gammas_in, int64_t nseq, int64_t n, uint32_t* codes_out,
+                  float* norms_out, float* gammas_out, void* workspace, int64_t ws_bytes, void* stream) {
+  if (int r = check_quantizer(from)) return r;
+  if (int r = check_quantizer(to)) return r;
+  if (int r = check_mode(from, mode)) return r;
+  if (int r = check_mode(to, mode)) return r;
+  if (from->d != to->d) return fail(TQ_EINVAL, "quantizers differ in d");
+  if (nseq < 0 || n < 0) return fail(TQ_EINVAL, "negative size");
+  if (nseq * n == 0) return TQ_OK;
+  if (!codes_in || !norms_in || !codes_out || !norms_out || (mode == TQ_PROD && (!gammas_in || !gammas_out)))
+    return fail(TQ_EINVAL, "NULL array argument");
+  const void* ptrs[] = {codes_in, norms_in, gammas_in, codes_out, norms_out, gammas_out, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, 16)) return fail(TQ_EINVAL, "device pointers must be 16-byte aligned");
+  if (to->d > 256) return fail(TQ_EUNSUPPORTED, "encode supports d <= 256 (d=%d)", to->d);
+  if (nseq > 65535) return fail(TQ_EUNSUPPORTED, "nseq > 65535");
+  const int64_t need = nseq * n * from->d * static_cast<int64_t>(sizeof(float));
+  if (!workspace || ws_bytes < need)
+    return fail(TQ_EWORKSPACE, "workspace of %lld bytes needed", static_cast<long long>(need));
+  DeviceGuard g(to->device);
+  if (!g.ok) return fail(TQ_EHIP, "cannot select the quantizer's device");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float* x = static_cast<float*>(workspace);
+  hipError_t e = tq::launch_decode(from, mode, codes_in, norms_in, gammas_in, nseq, n, x, st);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  e = tq::launch_encode(to, mode, x, TQ_F32, nseq, n, codes_out, norms_out, gammas_out, st);
+  return e == hipSuccess ? TQ_OK : hip_fail(e, "encode launch");
+}
+
 int tq_attend_decode_noalloc(const tq_quantizer* kq, const tq_quantizer* vq, const void* queries, int q_dtype, int B,
                              int Hq, int Hkv, const uint32_t* kcodes, const float* knorms, const float* kgammas,
                              const uint32_t* vcodes, const float* vnorms, int64_t n_comp, const uint16_t* k_tail,

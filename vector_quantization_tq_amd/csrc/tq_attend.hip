@@ -136,13 +136,29 @@ static int64_t attend_chunks(int64_t n_comp, int64_t groups, int bpc) {
   return (n_comp + ch - 1) / ch;
 }
 
-int64_t attend_ws_bytes(const tq_quantizer* kq, const tq_quantizer* vq, int B, int Hq, int Hkv, int64_t n_comp, int) {
+// Workspace of a cache in segments: the query operands of each segment (its
+// key quantizer's, 256-byte aligned, only for segments with tokens), then the
+// partial records of all segments' chunks.  For one segment this is the
+// layout of tq_attend_decode.
+int64_t attend_segments_ws_bytes(const AttendSegment* segs, int nseg, int B, int Hq, int Hkv) {
   const int G = Hq / Hkv;
   const int RT = (G + 3) / 4;
   const int64_t groups = static_cast<int64_t>(B) * Hkv * RT;
-  const int64_t nch = attend_chunks(n_comp, groups, attend_bpc(kq, vq));
-  const int64_t prep = (scores_ws_bytes(kq, B, Hq, Hkv) + 255) / 256 * 256;
-  return prep + groups * nch * 4 * kPartStride * 4 + 256;
+  int64_t prep = 0, nrec = 0;
+  for (int i = 0; i < nseg; ++i) {
+    const int64_t nch = attend_chunks(segs[i].n, groups, attend_bpc(segs[i].kq, segs[i].vq));
+    if (nch == 0) continue;
+    prep += (scores_ws_bytes(segs[i].kq, B, Hq, Hkv) + 255) / 256 * 256;
+    nrec += nch;
+  }
+  if (nrec == 0)   // only a tail: keep the single-segment size rule
+    prep = (scores_ws_bytes(segs[0].kq, B, Hq, Hkv) + 255) / 256 * 256;
+  return prep + groups * nrec * 4 * kPartStride * 4 + 256;
+}
+
+int64_t attend_ws_bytes(const tq_quantizer* kq, const tq_quantizer* vq, int B, int Hq, int Hkv, int64_t n_comp, int) {
+  const AttendSegment seg = {kq, vq, nullptr, nullptr, nullptr, nullptr, nullptr, n_comp};
+  return attend_segments_ws_bytes(&seg, 1, B, Hq, Hkv);
 }
 
 // Copy `words` 32-bit words (a multiple of 4) from src to LDS dst by 16-byte
@@ -176,7 +192,7 @@ __device__ __forceinline__ void attend_chunk_body(
     const uint32_t* __restrict__ kcodes, const float* __restrict__ knorms, const float* __restrict__ kgammas,
     const uint32_t* __restrict__ vcodes, const float* __restrict__ vnorms, int64_t n, int64_t chunk, int G, int RT,
     float scale_log2, float vtau, const uint8_t* __restrict__ wsA, const float* __restrict__ wsC, const Codebook& vcb,
-    float* __restrict__ part) {
+    float* __restrict__ part, int64_t nrec, int64_t rec0) {
   constexpr int d = 128;
   constexpr int TK = (1 << (BPK - 1)) + (QJL ? 1 : 0);   // key MFMA terms (Walsh + QJL)
   constexpr int WK = BPK + (QJL ? 1 : 0);                // key words per 32-coordinate group
@@ -410,7 +426,9 @@ __device__ __forceinline__ void attend_chunk_body(
   }
   __syncthreads();
   const float wq = qst[qi][2];
-  float* pbase = part + ((static_cast<int64_t>(gy) * gridDim.x + blockIdx.x) * 4) * kPartStride;
+  // record rec0 + chunk of the nrec records of this row tile (a cache kept in
+  // several segments writes each segment's chunks to its own range)
+  float* pbase = part + ((static_cast<int64_t>(gy) * nrec + rec0 + blockIdx.x) * 4) * kPartStride;
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
     float v = 0.f;
@@ -440,9 +458,9 @@ __global__ void __launch_bounds__(256, (AttendResidency<BPK, BPV, QJL, SPARSE>::
     const uint32_t* __restrict__ kcodes, const float* __restrict__ knorms, const float* __restrict__ kgammas,
     const uint32_t* __restrict__ vcodes, const float* __restrict__ vnorms, int64_t n, int64_t chunk, int G, int RT,
     float scale_log2, float vtau, const uint8_t* __restrict__ wsA, const float* __restrict__ wsC, Codebook vcb,
-    float* __restrict__ part) {
+    float* __restrict__ part, int64_t nrec, int64_t rec0) {
   attend_chunk_body<BPK, BPV, AttendResidency<BPK, BPV, QJL, SPARSE>::kSlots, QJL, SPARSE>(kcodes, knorms, kgammas, vcodes, vnorms, n, chunk, G, RT, scale_log2, vtau,
-                                              wsA, wsC, vcb, part);
+                                              wsA, wsC, vcb, part, nrec, rec0);
 }
 
 // One workgroup (256 threads) per (batch, query head): combine the chunk
@@ -589,51 +607,81 @@ __global__ void __launch_bounds__(256) attend_merge_kernel(const void* __restric
   }
 }
 
+static hipError_t launch_chunks(const AttendSegment& sg, int64_t groups, int G, int RT, float sl, float vtau,
+                                const uint8_t* wsA, const float* wsC, float* part, int64_t nrec, int64_t rec0,
+                                int64_t nch, hipStream_t st) {
+  const int bpc = attend_bpc(sg.kq, sg.vq);
+  const int64_t ch = attend_chunk_len(sg.n, groups, bpc);
+  dim3 grid(static_cast<unsigned>(nch), static_cast<unsigned>(groups));
+  const int bpk = key_codebook(sg.kq).bp, bpv = sg.vq->cb[1].bp;
+  const bool qjl = key_qjl(sg.kq);
+#define TQ_AT(K, V, QV)                                                                                       \
+  if (bpk == K && bpv == V && qjl == QV) {                                                                    \
+    if (vtau > 0.f)                                                                                           \
+      hipLaunchKernelGGL((attend_chunk_kernel<K, V, QV, true>), grid, dim3(256), 0, st, sg.kcodes, sg.knorms,  \
+                         sg.kgammas, sg.vcodes, sg.vnorms, sg.n, ch, G, RT, sl, vtau, wsA, wsC, sg.vq->cb[1],  \
+                         part, nrec, rec0);                                                                   \
+    else                                                                                                      \
+      hipLaunchKernelGGL((attend_chunk_kernel<K, V, QV, false>), grid, dim3(256), 0, st, sg.kcodes, sg.knorms, \
+                         sg.kgammas, sg.vcodes, sg.vnorms, sg.n, ch, G, RT, sl, 0.f, wsA, wsC, sg.vq->cb[1],   \
+                         part, nrec, rec0);                                                                   \
+  } else
+#define TQ_AT4(K, QV) TQ_AT(K, 1, QV) TQ_AT(K, 2, QV) TQ_AT(K, 3, QV) TQ_AT(K, 4, QV)
+  TQ_AT4(1, true) TQ_AT4(2, true) TQ_AT4(3, true)
+  TQ_AT4(1, false) TQ_AT4(2, false) TQ_AT4(3, false) TQ_AT4(4, false) { return hipErrorNotSupported; }
+#undef TQ_AT4
+#undef TQ_AT
+  return hipGetLastError();
+}
+
+hipError_t launch_attend_segments(const AttendSegment* segs, int nseg, const void* queries, int q_dtype, int B, int Hq,
+                                  int Hkv, const uint16_t* k_tail, const uint16_t* v_tail, int n_tail, float scale,
+                                  float vtau, float* out, void* ws, hipStream_t st) {
+  if (nseg < 1 || n_tail > 512) return hipErrorNotSupported;
+  for (int i = 0; i < nseg; ++i)
+    if (segs[i].kq->d != 128 || segs[i].vq->d != 128) return hipErrorNotSupported;
+  const int G = Hq / Hkv;
+  const int RT = (G + 3) / 4;
+  const int64_t groups = static_cast<int64_t>(B) * Hkv * RT;
+  int64_t nrec = 0, prep = 0;
+  for (int i = 0; i < nseg; ++i) {
+    const int64_t nch = attend_chunks(segs[i].n, groups, attend_bpc(segs[i].kq, segs[i].vq));
+    if (nch == 0) continue;
+    prep += (scores_ws_bytes(segs[i].kq, B, Hq, Hkv) + 255) / 256 * 256;
+    nrec += nch;
+  }
+  if (nrec == 0) prep = (scores_ws_bytes(segs[0].kq, B, Hq, Hkv) + 255) / 256 * 256;
+  float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + prep);
+  const float sl = scale * kLog2e;
+  hipError_t e;
+  uint8_t* pw = static_cast<uint8_t*>(ws);
+  int64_t rec0 = 0;
+  for (int i = 0; i < nseg; ++i) {
+    const AttendSegment& sg = segs[i];
+    const int64_t nch = attend_chunks(sg.n, groups, attend_bpc(sg.kq, sg.vq));
+    if (nch == 0) continue;
+    e = launch_query_prep_ws(sg.kq, queries, q_dtype, B, Hq, Hkv, pw, st);
+    if (e != hipSuccess) return e;
+    const uint8_t* wsA = pw;
+    const float* wsC = reinterpret_cast<const float*>(wsA + groups * key_terms(sg.kq) * 2048);
+    e = launch_chunks(sg, groups, G, RT, sl, vtau, wsA, wsC, part, nrec, rec0, nch, st);
+    if (e != hipSuccess) return e;
+    pw += (scores_ws_bytes(sg.kq, B, Hq, Hkv) + 255) / 256 * 256;
+    rec0 += nch;
+  }
+  // every value quantizer shares Pi (checked by the caller): one rotation back
+  hipLaunchKernelGGL(attend_merge_kernel, dim3(static_cast<unsigned>(B * Hq)), dim3(256), 0, st, queries, q_dtype, Hq, Hkv,
+                     G, RT, nrec, part, k_tail, v_tail, n_tail, sl, segs[0].vq->d_pi, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_attend(const tq_quantizer* kq, const tq_quantizer* vq, const void* queries, int q_dtype, int B, int Hq,
                          int Hkv, const uint32_t* kcodes, const float* knorms, const float* kgammas,
                          const uint32_t* vcodes, const float* vnorms, int64_t n_comp, const uint16_t* k_tail,
                          const uint16_t* v_tail, int n_tail, float scale, float vtau, float* out, void* ws,
                          hipStream_t st) {
-  if (kq->d != 128 || n_tail > 512) return hipErrorNotSupported;
-  const int G = Hq / Hkv;
-  const int RT = (G + 3) / 4;
-  const int64_t groups = static_cast<int64_t>(B) * Hkv * RT;
-  const int bpc = attend_bpc(kq, vq);
-  const int64_t nch = attend_chunks(n_comp, groups, bpc);
-  const int64_t prep = (scores_ws_bytes(kq, B, Hq, Hkv) + 255) / 256 * 256;
-  float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + prep);
-  const float sl = scale * kLog2e;
-  hipError_t e;
-  if (nch > 0) {
-    e = launch_query_prep_ws(kq, queries, q_dtype, B, Hq, Hkv, ws, st);
-    if (e != hipSuccess) return e;
-    const int T = key_terms(kq);
-    const uint8_t* wsA = static_cast<const uint8_t*>(ws);
-    const float* wsC = reinterpret_cast<const float*>(wsA + groups * T * 2048);
-    const int64_t ch = attend_chunk_len(n_comp, groups, bpc);
-    dim3 grid(static_cast<unsigned>(nch), static_cast<unsigned>(groups));
-    const int bpk = key_codebook(kq).bp, bpv = vq->cb[1].bp;
-    const bool qjl = key_qjl(kq);
-#define TQ_AT(K, V, QV)                                                                                       \
-  if (bpk == K && bpv == V && qjl == QV) {                                                                    \
-    if (vtau > 0.f)                                                                                           \
-      hipLaunchKernelGGL((attend_chunk_kernel<K, V, QV, true>), grid, dim3(256), 0, st, kcodes, knorms, kgammas,  \
-                         vcodes, vnorms, n_comp, ch, G, RT, sl, vtau, wsA, wsC, vq->cb[1], part);             \
-    else                                                                                                      \
-      hipLaunchKernelGGL((attend_chunk_kernel<K, V, QV, false>), grid, dim3(256), 0, st, kcodes, knorms, kgammas, \
-                         vcodes, vnorms, n_comp, ch, G, RT, sl, 0.f, wsA, wsC, vq->cb[1], part);              \
-  } else
-#define TQ_AT4(K, QV) TQ_AT(K, 1, QV) TQ_AT(K, 2, QV) TQ_AT(K, 3, QV) TQ_AT(K, 4, QV)
-    TQ_AT4(1, true) TQ_AT4(2, true) TQ_AT4(3, true)
-    TQ_AT4(1, false) TQ_AT4(2, false) TQ_AT4(3, false) TQ_AT4(4, false) { return hipErrorNotSupported; }
-#undef TQ_AT4
-#undef TQ_AT
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(attend_merge_kernel, dim3(static_cast<unsigned>(B * Hq)), dim3(256), 0, st, queries, q_dtype, Hq, Hkv,
-                     G, RT, nch, part, k_tail, v_tail, n_tail, sl, vq->d_pi, out);
-  return hipGetLastError();
+  const AttendSegment seg = {kq, vq, kcodes, knorms, kgammas, vcodes, vnorms, n_comp};
+  return launch_attend_segments(&seg, 1, queries, q_dtype, B, Hq, Hkv, k_tail, v_tail, n_tail, scale, vtau, out, ws, st);
 }
 
 }  // namespace tq

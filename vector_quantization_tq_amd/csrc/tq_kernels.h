@@ -28,8 +28,24 @@ hipError_t launch_topk(const tq_quantizer* q, const void* queries, int q_dtype, 
                        const uint32_t* codes, const float* norms, const float* gammas, int64_t n, int topk,
                        float* out, int64_t* out_idx, void* ws, hipStream_t st);
 
+// one segment of a compressed cache (its quantizers, packed arrays, tokens per sequence)
+struct AttendSegment {
+  const tq_quantizer* kq;
+  const tq_quantizer* vq;
+  const uint32_t* kcodes;
+  const float* knorms;
+  const float* kgammas;
+  const uint32_t* vcodes;
+  const float* vnorms;
+  int64_t n;
+};
+
 int64_t attend_ws_bytes(const tq_quantizer* kq, const tq_quantizer* vq, int B, int Hq, int Hkv, int64_t n_comp,
                         int n_tail);
+int64_t attend_segments_ws_bytes(const AttendSegment* segs, int nseg, int B, int Hq, int Hkv);
+hipError_t launch_attend_segments(const AttendSegment* segs, int nseg, const void* queries, int q_dtype, int B, int Hq,
+                                  int Hkv, const uint16_t* k_tail, const uint16_t* v_tail, int n_tail, float scale,
+                                  float vtau, float* out, void* ws, hipStream_t st);
 hipError_t launch_attend(const tq_quantizer* kq, const tq_quantizer* vq, const void* queries, int q_dtype, int B, int Hq,
                          int Hkv, const uint32_t* kcodes, const float* knorms, const float* kgammas,
                          const uint32_t* vcodes, const float* vnorms, int64_t n_comp, const uint16_t* k_tail,

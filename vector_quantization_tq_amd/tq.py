@@ -25,7 +25,16 @@ EXPORTS = [
     "tq_host_qjl_matrix", "tq_host_codebook", "tq_make_quantizer", "tq_make_quantizer_ex", "tq_free_quantizer", "tq_quantizer_info", "tq_set_key_mode", "tq_code_words", "tq_encode",
     "tq_decode", "tq_scores_workspace_bytes", "tq_query_prep", "tq_scores_from_prep", "tq_scores",
     "tq_attend_workspace_bytes", "tq_attend_decode", "tq_attend_decode_sparse", "tq_attend_decode_noalloc",
+    "tq_attend_segments_workspace_bytes", "tq_attend_decode_segments", "tq_requantize",
 ]
+MAX_SEGMENTS = 16
+
+
+class _CSegment(ctypes.Structure):
+    """struct tq_segment (include/tq.h)."""
+    _fields_ = [("kq", ctypes.c_void_p), ("vq", ctypes.c_void_p), ("kcodes", ctypes.c_void_p),
+                ("knorms", ctypes.c_void_p), ("kgammas", ctypes.c_void_p), ("vcodes", ctypes.c_void_p),
+                ("vnorms", ctypes.c_void_p), ("n", ctypes.c_int64)]
 
 # size of the library's per-device scratch array used by tq_attend_decode_noalloc (include/tq.h)
 NOALLOC_SCRATCH_BYTES = 16 << 20
@@ -77,6 +86,10 @@ def lib() -> ctypes.CDLL:
                                           c_i, c_f, c_f, c_p, c_p, c_i64, c_p]),
         "tq_attend_decode_noalloc": (c_i, [c_p, c_p, c_p, c_i, c_i, c_i, c_i, c_p, c_p, c_p, c_p, c_p, c_i64, c_p, c_p,
                                            c_i, c_f, c_p, c_p]),
+        "tq_attend_segments_workspace_bytes": (c_i64, [ctypes.POINTER(_CSegment), c_i, c_i, c_i, c_i, c_i]),
+        "tq_attend_decode_segments": (c_i, [ctypes.POINTER(_CSegment), c_i, c_p, c_i, c_i, c_i, c_i, c_p, c_p, c_i, c_f,
+                                            c_p, c_p, c_i64, c_p]),
+        "tq_requantize": (c_i, [c_p, c_p, c_i, c_p, c_p, c_p, c_i64, c_i64, c_p, c_p, c_p, c_p, c_i64, c_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -434,3 +447,94 @@ def tq_attend_decode_noalloc(kq: Quantizer, vq: Quantizer, q, kcodes, knorms, kg
                                           _ptr(knorms), _ptr(kgammas), _ptr(vcodes), _ptr(vnorms), n_comp,
                                           _ptr(k_tail), _ptr(v_tail), n_tail, scale, _ptr(out), _stream()))
     return out
+
+
+class Segment:
+    """One age segment of a compressed cache: its key and value quantizers and
+    packed arrays, n tokens per (batch, KV head) sequence."""
+
+    def __init__(self, kq: Quantizer, vq: Quantizer, kcodes, knorms, kgammas, vcodes, vnorms, n: int):
+        self.kq, self.vq, self.n = kq, vq, n
+        self.kcodes, self.knorms, self.kgammas, self.vcodes, self.vnorms = kcodes, knorms, kgammas, vcodes, vnorms
+
+
+def _c_segments(segments):
+    if not 1 <= len(segments) <= MAX_SEGMENTS:
+        raise ValueError(f"1 to {MAX_SEGMENTS} segments")
+    arr = (_CSegment * len(segments))()
+    for i, g in enumerate(segments):
+        arr[i] = _CSegment(g.kq.handle.value, g.vq.handle.value, g.kcodes.data_ptr() if g.n else None,
+                           g.knorms.data_ptr() if g.n else None,
+                           g.kgammas.data_ptr() if (g.n and g.kgammas is not None) else None,
+                           g.vcodes.data_ptr() if g.n else None, g.vnorms.data_ptr() if g.n else None, g.n)
+    return arr
+
+
+def attend_segments_workspace_bytes(segments, B: int, Hq: int, Hkv: int, n_tail: int = 0) -> int:
+    w = lib().tq_attend_segments_workspace_bytes(_c_segments(segments), len(segments), B, Hq, Hkv, n_tail)
+    if w < 0:
+        _check(TQ_EINVAL)
+    return w
+
+
+def tq_attend_decode_segments(segments, q, Hkv: int, k_tail=None, v_tail=None, scale: float = 0.0, out=None,
+                              workspace=None):
+    """Decode attention over a cache kept in age segments (list of Segment,
+    e.g. older tokens at fewer bits) plus an optional bf16 tail, one softmax
+    over all of them.  q [B, Hq, d]; tails [B, Hkv, n_tail, d]."""
+    torch = _torch()
+    if not segments:
+        raise ValueError("at least one segment")
+    s0 = segments[0]
+    tensors = [q, k_tail, v_tail, out, workspace]
+    for g in segments:
+        tensors += [g.kcodes, g.knorms, g.kgammas, g.vcodes, g.vnorms]
+    _need_cuda(*tensors)
+    B, Hq, d, n_tail, out = _check_attend(s0.kq, s0.vq, q, None, None, None, None, None, Hkv, 0, k_tail, v_tail, out)
+    for i, g in enumerate(segments):
+        if g.kq.d != d or g.vq.d != d:
+            raise ValueError(f"segment {i}: quantizers differ in d")
+        if g.n > 0:
+            _check_key_cache(g.kq, g.kcodes, g.knorms, g.kgammas, B * Hkv, g.n, f"segment {i} k")
+            _need_buf(g.vcodes, f"segment {i} vcodes", g.vq.code_words(TQ_MSE, B * Hkv, g.n), _codes_dtypes())
+            _need_buf(g.vnorms, f"segment {i} vnorms", B * Hkv * g.n, (torch.float32,))
+    need = attend_segments_workspace_bytes(segments, B, Hq, Hkv, n_tail)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _need_buf(workspace, "workspace", need, (torch.uint8,))
+    _check(lib().tq_attend_decode_segments(_c_segments(segments), len(segments), _ptr(q), _dtype_code(q), B, Hq, Hkv,
+                                           _ptr(k_tail), _ptr(v_tail), n_tail, scale, _ptr(out), _ptr(workspace),
+                                           workspace.numel(), _stream()))
+    return out
+
+
+def tq_requantize(q_from: Quantizer, q_to: Quantizer, mode: int, codes, norms, gammas, nseq: int, n: int, out=None,
+                  workspace=None):
+    """Re-encode [nseq][n] vectors coded by q_from with q_to (same d, same
+    mode): decode, then encode.  Returns (codes, norms, gammas or None) in
+    q_to's layout."""
+    torch = _torch()
+    _need_cuda(codes, norms, gammas, workspace)
+    _need_buf(codes, "codes", q_from.code_words(mode, nseq, n), _codes_dtypes())
+    _need_buf(norms, "norms", nseq * n, (torch.float32,))
+    if mode == TQ_PROD:
+        _need_buf(gammas, "gammas", nseq * n, (torch.float32,))
+    if q_to.d != q_from.d:
+        raise ValueError("quantizers differ in d")
+    dev = codes.device
+    if out is None:
+        out = (torch.empty(max(q_to.code_words(mode, nseq, n), 4), dtype=torch.int32, device=dev),
+               torch.empty(max(nseq * n, 4), dtype=torch.float32, device=dev),
+               torch.empty(max(nseq * n, 4), dtype=torch.float32, device=dev) if mode == TQ_PROD else None)
+    c2, n2, g2 = out
+    _need_cuda(c2, n2, g2)
+    _need_buf(c2, "codes out", q_to.code_words(mode, nseq, n), _codes_dtypes())
+    _need_buf(n2, "norms out", nseq * n, (torch.float32,))
+    if mode == TQ_PROD:
+        _need_buf(g2, "gammas out", nseq * n, (torch.float32,))
+    if workspace is None:
+        workspace = torch.empty(max(nseq * n * q_from.d, 4), dtype=torch.float32, device=dev)
+    _need_buf(workspace, "workspace", nseq * n * q_from.d, (torch.float32,))
+    _check(lib().tq_requantize(q_from.handle, q_to.handle, mode, _ptr(codes), _ptr(norms), _ptr(gammas), nseq, n,
+                               _ptr(c2), _ptr(n2), _ptr(g2), _ptr(workspace), workspace.numel() * 4, _stream()))
+    return c2, n2, g2
