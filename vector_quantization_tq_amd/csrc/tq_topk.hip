@@ -27,6 +27,8 @@ namespace tq {
 namespace {
 
 constexpr int kTopBlockKeys = 64;
+// Candidates a lane may queue before the lists take them (see the scan loop)
+constexpr int kQueue = 8;
 
 // (s, i) ranks before (t, j): higher score, ties to the lower index
 // (bitwise, so that no operand is evaluated under a branch)
@@ -164,6 +166,8 @@ __global__ void __launch_bounds__(256, (KK <= 16 && ((1 << (BP - 1)) + QJL) * ((
   constexpr int BUFW = BW + 2 * kTopBlockKeys;     // + norms + gammas
   constexpr int NS = 3;                            // batches b, b+1, b+2 staged at once
   __shared__ __attribute__((aligned(16))) uint32_t buf[NS][BUFW];
+  // candidate queue: entry e of thread tid at cq[e][tid] (score bits, key)
+  __shared__ uint2 cq[kQueue][256];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // workgroup -> (row group, slice); consecutive workgroups go round-robin over
@@ -201,6 +205,25 @@ __global__ void __launch_bounds__(256, (KK <= 16 && ((1 << (BP - 1)) + QJL) * ((
   float ls[KK];
   int li[KK];
   list_init<KK>(ls, li);
+  // Keys that pass the pruning bounds are queued per lane in LDS and enter the
+  // sorted list in bulk, when some lane of the wave has a full queue and at
+  // the end of the slice.  The insertion runs under a wave-wide gate, so
+  // inserting every candidate as it arrives costs the whole wave an insertion
+  // whenever any of its 64 lanes has one; batched, it costs about as many
+  // insertion rounds as the fullest queue holds.  The bounds a queued key
+  // passed only rise until the lists take it, so the filter stays valid.
+  int qn = 0;
+  auto drain = [&]() {
+#pragma unroll 1
+    for (int e = 0; e < kQueue; ++e) {
+      if (__ballot(e < qn) == 0ull) break;
+      if (e < qn) {
+        const uint2 c = cq[e][tid];
+        list_insert<KK>(__uint_as_float(c.x), static_cast<int>(c.y), ls, li);
+      }
+    }
+    qn = 0;
+  };
 
   const uint32_t* cbase = codes + seq * n * WPK;
   const float* nb = norms + seq * n;
@@ -290,16 +313,18 @@ __global__ void __launch_bounds__(256, (KK <= 16 && ((1 << (BP - 1)) + QJL) * ((
         }
         const int key = static_cast<int>(k0) + kk;
         const bool ins = kk < nk && s >= tau && ranks_before(s, key, ls[KK - 1], li[KK - 1]);
-        // wave-uniform gate: the insertion (selects over the whole list) only
-        // runs when some lane of the wave has a key to insert
-        if (__ballot(ins) != 0ull) {
-          if (ins) list_insert<KK>(s, key, ls, li);
+        if (ins) {
+          cq[qn][tid] = make_uint2(__float_as_uint(s), static_cast<uint32_t>(key));
+          ++qn;
         }
+        // a queue is full: every lane's queued keys enter its list
+        if (__ballot(qn == kQueue) != 0ull) drain();
       }
     }
   }
 
   if (!active) return;   // no barrier follows
+  drain();
   const int64_t q16 = wave * 4 + qi;
   const int64_t base = ((rg * slices + slice) * 16 + q16) * topk;
   tournament<KK, 16>(ls, li, topk, jj == 0, cand_s + base, cand_i + base, nullptr);
