@@ -103,7 +103,16 @@ static int64_t device_cus() {
 // ones add partial records and pipeline fills.  `bpc` is the dense kernel's
 // residency (attend_blocks_per_cu): the chunking never depends on whether
 // sparse V is on, so the workspace size does not either.
-static int64_t attend_chunk_len(int64_t n_comp, int64_t groups, int bpc) {
+static int64_t attend_chunk_len(int64_t n_comp, int64_t groups, int bpc, bool segmented = false) {
+  // a cache in several segments: each segment's launch gets the shortest
+  // multiple of the step whose chunks fill one round of the resident
+  // workgroups, at least 128 and at most 2048 tokens (the launches run one
+  // after the other, and one merge reads every segment's records)
+  if (segmented && bpc > 0) {
+    const int64_t per = max(static_cast<int64_t>(1), bpc * device_cus() / groups);
+    const int64_t c = ((n_comp + per - 1) / per + kStep - 1) / kStep * kStep;
+    return min(static_cast<int64_t>(2048), max(static_cast<int64_t>(kStep), c));
+  }
   int64_t ch = kStep;
   while (ch < 1024 && (n_comp + 2 * ch - 1) / (2 * ch) * groups >= 768) ch *= 2;
   // few long sequences: no more than 64 partial records per query (the merge
@@ -130,10 +139,17 @@ static int attend_bpc(const tq_quantizer* kq, const tq_quantizer* vq) {
   return attend_blocks_per_cu(key_codebook(kq).bp, vq->cb[1].bp, key_qjl(kq), false);
 }
 
-static int64_t attend_chunks(int64_t n_comp, int64_t groups, int bpc) {
+static int64_t attend_chunks(int64_t n_comp, int64_t groups, int bpc, bool segmented = false) {
   if (n_comp <= 0) return 0;
-  const int64_t ch = attend_chunk_len(n_comp, groups, bpc);
+  const int64_t ch = attend_chunk_len(n_comp, groups, bpc, segmented);
   return (n_comp + ch - 1) / ch;
+}
+
+// segments with tokens in a call (the chunking of a segment depends on it)
+static int live_segments(const AttendSegment* segs, int nseg) {
+  int k = 0;
+  for (int i = 0; i < nseg; ++i) k += segs[i].n > 0 ? 1 : 0;
+  return k;
 }
 
 // Workspace of a cache in segments: the query operands of each segment (its
@@ -145,8 +161,9 @@ int64_t attend_segments_ws_bytes(const AttendSegment* segs, int nseg, int B, int
   const int RT = (G + 3) / 4;
   const int64_t groups = static_cast<int64_t>(B) * Hkv * RT;
   int64_t prep = 0, nrec = 0;
+  const bool multi = live_segments(segs, nseg) > 1;
   for (int i = 0; i < nseg; ++i) {
-    const int64_t nch = attend_chunks(segs[i].n, groups, attend_bpc(segs[i].kq, segs[i].vq));
+    const int64_t nch = attend_chunks(segs[i].n, groups, attend_bpc(segs[i].kq, segs[i].vq), multi);
     if (nch == 0) continue;
     prep += (scores_ws_bytes(segs[i].kq, B, Hq, Hkv) + 255) / 256 * 256;
     nrec += nch;
@@ -465,9 +482,17 @@ __global__ void __launch_bounds__(256, (AttendResidency<BPK, BPV, QJL, SPARSE>::
 
 // One workgroup (256 threads) per (batch, query head): combine the chunk
 // partials (max-shifted), add the exact bf16 tail, rotate back once and
-// normalise.  Sums over chunks and over tail tokens are spread over 8 slices
-// of 32 threads, each thread carrying 4 consecutive coordinates with 16-byte
-// loads; the slices meet in LDS.
+// normalise.  The kernel is a short chain of dependent steps over a few
+// hundred kilobytes, so its time is memory latency: every load that does not
+// depend on the softmax maximum -- the records' maxima and sums, the first MR
+// records of each slice, the first 256 tail key rows and the first 256 tail
+// values -- is issued at the start, and the half columns of Pi (read from L2)
+// all at once before the rotation back.  Record sums are spread over 8
+// slices of 32 threads (4 consecutive coordinates each, 16-byte loads); a
+// tail token's logit is taken by 4 threads (32 coordinates each, joined by
+// row shuffles) and its value by the 32 threads of its slice.  Longer caches
+// take further rounds of the same loops.
+constexpr int kMergeRec = 12;   // records per slice loaded at the start (96 records)
 __global__ void __launch_bounds__(256) attend_merge_kernel(const void* __restrict__ queries, int q_dtype, int Hq,
                                                            int Hkv, int G, int RT, int64_t nchunk,
                                                            const float* __restrict__ part,
@@ -476,15 +501,18 @@ __global__ void __launch_bounds__(256) attend_merge_kernel(const void* __restric
                                                            float scale_log2, const float* __restrict__ piv,
                                                            float* __restrict__ out) {
   constexpr int d = 128;
-  __shared__ float qv[d];
+  constexpr int MR = kMergeRec;
+  __shared__ __attribute__((aligned(16))) float qv[d];
   __shared__ float accs[d];
   __shared__ __attribute__((aligned(16))) float sl8[8][d];
+  __shared__ __attribute__((aligned(16))) float tl8[8][d];
   __shared__ float half2[2][d];
   __shared__ float red[8];
   __shared__ float ts[512];   // tail logits, then tail weights (n_tail <= 512)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = tid & (d - 1), hf = tid >> 7;
   const int slc = tid >> 5, u4 = 4 * (tid & 31);   // slice, first coordinate of this thread's quad
+  const int kq4 = tid & 3, kt64 = tid >> 2;          // tail logits: quarter row, token within a round of 64
   const int bh = blockIdx.x;
   const int b = bh / Hq, h = bh - b * Hq;
   const int kvh = h / G, qg = h - kvh * G;
@@ -492,126 +520,197 @@ __global__ void __launch_bounds__(256) attend_merge_kernel(const void* __restric
   const int64_t gy = (static_cast<int64_t>(b) * Hkv + kvh) * RT + rt;
   const float* pq = part + (gy * nchunk * 4 + qi) * kPartStride;   // chunk c at pq + c * 4 * kPartStride
   const int64_t cstride = 4 * kPartStride;
-  if (tid < d) qv[tid] = load_elem(queries, q_dtype, static_cast<int64_t>(bh) * d + tid);
-  __syncthreads();
-  // maxima: chunks, then the tail logits (one wave per tail token, lanes over coordinates)
-  float mloc = -INFINITY;
-  for (int64_t c = tid; c < nchunk; c += 256) mloc = fmaxf(mloc, pq[c * cstride + 128]);
   const int64_t toff = (static_cast<int64_t>(b) * Hkv + kvh) * n_tail;
-  // one thread per tail token: its 256-byte key row as 16 independent 16-byte loads
-  for (int t = tid; t < n_tail; t += 256) {
-    const uint4* kt = reinterpret_cast<const uint4*>(k_tail + (toff + t) * d);
-    uint4 kr[16];
+  const int64_t clast = nchunk > 0 ? nchunk - 1 : 0;
+  const int tlast = n_tail > 0 ? n_tail - 1 : 0;
+
+  // ---------------- loads issued together ----------------
+  const float qe = tid < d ? load_elem(queries, q_dtype, static_cast<int64_t>(bh) * d + tid) : 0.f;
+  // records' maxima and sums, one per thread (first 256 records)
+  const bool rec0 = tid < nchunk;
+  const float m0 = rec0 ? pq[static_cast<int64_t>(tid) * cstride + 128] : -INFINITY;
+  const float l0 = rec0 ? pq[static_cast<int64_t>(tid) * cstride + 129] : 0.f;
+  // the first MR records of this thread's slice (record c = slc + 8 k)
+  float mc[MR];
+  float4 pc[MR];
+  if (nchunk > 0) {
 #pragma unroll
-    for (int c = 0; c < 16; ++c) kr[c] = kt[c];
+    for (int k = 0; k < MR; ++k) {
+      const int64_t c = min(static_cast<int64_t>(slc + 8 * k), clast);
+      mc[k] = pq[c * cstride + 128];
+      pc[k] = *reinterpret_cast<const float4*>(pq + c * cstride + u4);
+    }
+  }
+  // tail keys: token 64 r + kt64, coordinates 32 kq4 .. +31 (4 rounds of 64 tokens)
+  uint4 kr[4][4];
+  // tail values: token slc + 8 k (k < 32), coordinates u4 .. u4 + 3
+  uint2 vr[32];
+  if (n_tail > 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint4* kt = reinterpret_cast<const uint4*>(k_tail + (toff + min(64 * r + kt64, tlast)) * d + 32 * kq4);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) kr[r][c] = kt[c];
+    }
+#pragma unroll
+    for (int k = 0; k < 32; ++k)
+      vr[k] = *reinterpret_cast<const uint2*>(v_tail + (toff + min(slc + 8 * k, tlast)) * d + u4);
+  }
+  if (tid < d) qv[tid] = qe;
+  __syncthreads();
+
+  // ---------------- the softmax maximum ----------------
+  float mloc = m0;
+  for (int64_t c = tid + 256; c < nchunk; c += 256) mloc = fmaxf(mloc, pq[c * cstride + 128]);
+  // logit of token 64 r + kt64 from its quarter rows (4 consecutive lanes)
+  auto tail_logit = [&](const uint4 (&row)[4]) {
     float s0 = 0.f, s1 = 0.f;
+    const float4* q4 = reinterpret_cast<const float4*>(qv + 32 * kq4);
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const uint32_t wv[4] = {kr[c].x, kr[c].y, kr[c].z, kr[c].w};
+    for (int c = 0; c < 4; ++c) {
+      const float4 qa = q4[2 * c], qb = q4[2 * c + 1];
+      const float qq[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+      const uint32_t wv[4] = {row[c].x, row[c].y, row[c].z, row[c].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        s0 = fmaf(qv[8 * c + 2 * e], __uint_as_float(wv[e] << 16), s0);
-        s1 = fmaf(qv[8 * c + 2 * e + 1], __uint_as_float(wv[e] & 0xFFFF0000u), s1);
+        s0 = fmaf(qq[2 * e], __uint_as_float(wv[e] << 16), s0);
+        s1 = fmaf(qq[2 * e + 1], __uint_as_float(wv[e] & 0xFFFF0000u), s1);
       }
     }
-    const float sl = (s0 + s1) * scale_log2;
-    ts[t] = sl;
-    mloc = fmaxf(mloc, sl);
+    float sv = s0 + s1;
+    sv += dpp_f<0xB1>(sv);   // quad_perm [1,0,3,2]
+    sv += dpp_f<0x4E>(sv);   // quad_perm [2,3,0,1]
+    return sv * scale_log2;
+  };
+  if (n_tail > 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 64 * r + kt64;
+      const float sl = tail_logit(kr[r]);
+      if (t < n_tail) {
+        if (kq4 == 0) ts[t] = sl;
+        mloc = fmaxf(mloc, sl);
+      }
+    }
+  }
+  for (int t0 = 256; t0 < n_tail; t0 += 64) {
+    const int t = t0 + kt64;
+    uint4 row[4];
+    const uint4* kt = reinterpret_cast<const uint4*>(k_tail + (toff + min(t, tlast)) * d + 32 * kq4);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) row[c] = kt[c];
+    const float sl = tail_logit(row);
+    if (t < n_tail) {
+      if (kq4 == 0) ts[t] = sl;
+      mloc = fmaxf(mloc, sl);
+    }
   }
   mloc = wave_max(mloc);
   if (lane == 0) red[wave] = mloc;
-  __syncthreads();
+  __syncthreads();   // the maxima, and every tail logit in ts[]
   const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  // denominators
-  float lsum = 0.f;
-  for (int64_t c = tid; c < nchunk; c += 256) lsum = fmaf(pq[c * cstride + 129], exp2f(pq[c * cstride + 128] - M), lsum);
+
+  // ---------------- denominators and tail weights ----------------
+  float lsum = rec0 ? l0 * exp2f(m0 - M) : 0.f;
+  for (int64_t c = tid + 256; c < nchunk; c += 256) lsum = fmaf(pq[c * cstride + 129], exp2f(pq[c * cstride + 128] - M), lsum);
   for (int t = tid; t < n_tail; t += 256) {
     const float pt = exp2f(ts[t] - M);
     ts[t] = pt;
     lsum += pt;
   }
   lsum = wave_sum(lsum);
-  __syncthreads();
   if (lane == 0) red[4 + wave] = lsum;
-  // rotated-frame accumulator of the compressed part: chunk c goes to slice
-  // c mod 8; 8 chunks of a slice are loaded before any is used
+
+  // ---------------- records: rotated-frame accumulator ----------------
   {
     float4 a = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t c0 = slc; c0 < nchunk; c0 += 64) {
-      float mc[8];
-      float4 pc[8];
+    if (nchunk > 0) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int64_t c = min(c0 + 8 * k, nchunk - 1);
-        mc[k] = pq[c * cstride + 128];
-        pc[k] = *reinterpret_cast<const float4*>(pq + c * cstride + u4);
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float wk = c0 + 8 * k < nchunk ? exp2f(mc[k] - M) : 0.f;
+      for (int k = 0; k < MR; ++k) {
+        const float wk = slc + 8 * k < nchunk ? exp2f(mc[k] - M) : 0.f;
         a.x = fmaf(pc[k].x, wk, a.x);
         a.y = fmaf(pc[k].y, wk, a.y);
         a.z = fmaf(pc[k].z, wk, a.z);
         a.w = fmaf(pc[k].w, wk, a.w);
       }
     }
+    for (int64_t c0 = slc + 8 * MR; c0 < nchunk; c0 += 64) {
+      float mm[8];
+      float4 pp[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int64_t c = min(c0 + 8 * k, clast);
+        mm[k] = pq[c * cstride + 128];
+        pp[k] = *reinterpret_cast<const float4*>(pq + c * cstride + u4);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float wk = c0 + 8 * k < nchunk ? exp2f(mm[k] - M) : 0.f;
+        a.x = fmaf(pp[k].x, wk, a.x);
+        a.y = fmaf(pp[k].y, wk, a.y);
+        a.z = fmaf(pp[k].z, wk, a.z);
+        a.w = fmaf(pp[k].w, wk, a.w);
+      }
+    }
     *reinterpret_cast<float4*>(&sl8[slc][u4]) = a;
   }
-  __syncthreads();
-  const float L = (red[4] + red[5]) + (red[6] + red[7]);
+  __syncthreads();   // tail weights in ts[], slice sums in sl8
   if (tid < d) {
     float v = 0.f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) v += sl8[k][i];
     accs[i] = v;
   }
-  __syncthreads();
-  // tail values: token t goes to slice t mod 8 (weights ts[] already in place)
+  // ---------------- tail values (original frame) ----------------
   {
     float4 a = {0.f, 0.f, 0.f, 0.f};
-    for (int t0 = slc; t0 < n_tail; t0 += 64) {
+    auto add = [&](float pt, uint2 raw) {
+      a.x = fmaf(pt, __uint_as_float(raw.x << 16), a.x);
+      a.y = fmaf(pt, __uint_as_float(raw.x & 0xFFFF0000u), a.y);
+      a.z = fmaf(pt, __uint_as_float(raw.y << 16), a.z);
+      a.w = fmaf(pt, __uint_as_float(raw.y & 0xFFFF0000u), a.w);
+    };
+    if (n_tail > 0) {
+#pragma unroll
+      for (int k = 0; k < 32; ++k) add(slc + 8 * k < n_tail ? ts[min(slc + 8 * k, tlast)] : 0.f, vr[k]);
+    }
+    for (int t0 = slc + 256; t0 < n_tail; t0 += 64) {
       uint2 raw[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k)
-        raw[k] = *reinterpret_cast<const uint2*>(v_tail + (toff + min(t0 + 8 * k, n_tail - 1)) * d + u4);
+        raw[k] = *reinterpret_cast<const uint2*>(v_tail + (toff + min(t0 + 8 * k, tlast)) * d + u4);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float pt = t0 + 8 * k < n_tail ? ts[min(t0 + 8 * k, n_tail - 1)] : 0.f;
-        a.x = fmaf(pt, __uint_as_float(raw[k].x << 16), a.x);
-        a.y = fmaf(pt, __uint_as_float(raw[k].x & 0xFFFF0000u), a.y);
-        a.z = fmaf(pt, __uint_as_float(raw[k].y << 16), a.z);
-        a.w = fmaf(pt, __uint_as_float(raw[k].y & 0xFFFF0000u), a.w);
-      }
+      for (int k = 0; k < 8; ++k) add(t0 + 8 * k < n_tail ? ts[min(t0 + 8 * k, tlast)] : 0.f, raw[k]);
     }
-    *reinterpret_cast<float4*>(&sl8[slc][u4]) = a;
+    *reinterpret_cast<float4*>(&tl8[slc][u4]) = a;
   }
-  // Pi^T acc (inner dimension split between the two halves), 16 loads in flight
+  __syncthreads();   // accs and the tail slice sums complete
+  // ---------------- Pi^T acc (inner index split between the two halves) ----------------
   {
     float o[4] = {0.f, 0.f, 0.f, 0.f};
     const int j0 = hf * (d / 2);
-    for (int jj = 0; jj < d / 2; jj += 16) {
-      float pv[16];
+    float pv[d / 2];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) pv[k] = piv[static_cast<int64_t>(j0 + jj + k) * d + i];
+    for (int k = 0; k < d / 2; ++k) pv[k] = piv[static_cast<int64_t>(j0 + k) * d + i];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) o[k & 3] = fmaf(pv[k], accs[j0 + jj + k], o[k & 3]);
-    }
+    for (int k = 0; k < d / 2; ++k) o[k & 3] = fmaf(pv[k], accs[j0 + k], o[k & 3]);
     half2[hf][i] = (o[0] + o[1]) + (o[2] + o[3]);
   }
   __syncthreads();
   if (tid < d) {
+    const float L = (red[4] + red[5]) + (red[6] + red[7]);
     float tv = 0.f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) tv += sl8[k][i];
+    for (int k = 0; k < 8; ++k) tv += tl8[k][i];
     out[static_cast<int64_t>(bh) * d + i] = (half2[0][i] + half2[1][i] + tv) / L;
   }
 }
 
 static hipError_t launch_chunks(const AttendSegment& sg, int64_t groups, int G, int RT, float sl, float vtau,
                                 const uint8_t* wsA, const float* wsC, float* part, int64_t nrec, int64_t rec0,
-                                int64_t nch, hipStream_t st) {
+                                int64_t nch, bool multi, hipStream_t st) {
   const int bpc = attend_bpc(sg.kq, sg.vq);
-  const int64_t ch = attend_chunk_len(sg.n, groups, bpc);
+  const int64_t ch = attend_chunk_len(sg.n, groups, bpc, multi);
   dim3 grid(static_cast<unsigned>(nch), static_cast<unsigned>(groups));
   const int bpk = key_codebook(sg.kq).bp, bpv = sg.vq->cb[1].bp;
   const bool qjl = key_qjl(sg.kq);
@@ -644,8 +743,9 @@ hipError_t launch_attend_segments(const AttendSegment* segs, int nseg, const voi
   const int RT = (G + 3) / 4;
   const int64_t groups = static_cast<int64_t>(B) * Hkv * RT;
   int64_t nrec = 0, prep = 0;
+  const bool multi = live_segments(segs, nseg) > 1;
   for (int i = 0; i < nseg; ++i) {
-    const int64_t nch = attend_chunks(segs[i].n, groups, attend_bpc(segs[i].kq, segs[i].vq));
+    const int64_t nch = attend_chunks(segs[i].n, groups, attend_bpc(segs[i].kq, segs[i].vq), multi);
     if (nch == 0) continue;
     prep += (scores_ws_bytes(segs[i].kq, B, Hq, Hkv) + 255) / 256 * 256;
     nrec += nch;
@@ -654,17 +754,34 @@ hipError_t launch_attend_segments(const AttendSegment* segs, int nseg, const voi
   float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + prep);
   const float sl = scale * kLog2e;
   hipError_t e;
+  // the query operands of every segment with tokens, up to kPrepSetMax per launch
+  {
+    const tq_quantizer* pq[kPrepSetMax];
+    void* pws[kPrepSetMax];
+    int np = 0;
+    uint8_t* pw = static_cast<uint8_t*>(ws);
+    for (int i = 0; i < nseg; ++i) {
+      if (attend_chunks(segs[i].n, groups, attend_bpc(segs[i].kq, segs[i].vq), multi) == 0) continue;
+      pq[np] = segs[i].kq;
+      pws[np] = pw;
+      ++np;
+      pw += (scores_ws_bytes(segs[i].kq, B, Hq, Hkv) + 255) / 256 * 256;
+      if (np == kPrepSetMax) {
+        if ((e = launch_query_prep_multi(pq, pws, np, queries, q_dtype, B, Hq, Hkv, st)) != hipSuccess) return e;
+        np = 0;
+      }
+    }
+    if (np > 0 && (e = launch_query_prep_multi(pq, pws, np, queries, q_dtype, B, Hq, Hkv, st)) != hipSuccess) return e;
+  }
   uint8_t* pw = static_cast<uint8_t*>(ws);
   int64_t rec0 = 0;
   for (int i = 0; i < nseg; ++i) {
     const AttendSegment& sg = segs[i];
-    const int64_t nch = attend_chunks(sg.n, groups, attend_bpc(sg.kq, sg.vq));
+    const int64_t nch = attend_chunks(sg.n, groups, attend_bpc(sg.kq, sg.vq), multi);
     if (nch == 0) continue;
-    e = launch_query_prep_ws(sg.kq, queries, q_dtype, B, Hq, Hkv, pw, st);
-    if (e != hipSuccess) return e;
     const uint8_t* wsA = pw;
     const float* wsC = reinterpret_cast<const float*>(wsA + groups * key_terms(sg.kq) * 2048);
-    e = launch_chunks(sg, groups, G, RT, sl, vtau, wsA, wsC, part, nrec, rec0, nch, st);
+    e = launch_chunks(sg, groups, G, RT, sl, vtau, wsA, wsC, part, nrec, rec0, nch, multi, st);
     if (e != hipSuccess) return e;
     pw += (scores_ws_bytes(sg.kq, B, Hq, Hkv) + 255) / 256 * 256;
     rec0 += nch;

@@ -15,6 +15,18 @@ hipError_t launch_decode(const tq_quantizer* q, int mode, const uint32_t* codes,
                          int64_t nseq, int64_t n, float* out, hipStream_t st);
 
 int64_t scores_ws_bytes(const tq_quantizer* q, int B, int Hq, int Hkv);
+
+// query operands of up to kPrepSetMax quantizers of one d in one launch
+constexpr int kPrepSetMax = 4;
+struct PrepSet {
+  const float* qt[kPrepSetMax];
+  Codebook cb[kPrepSetMax];
+  int qjl[kPrepSetMax];
+  uint8_t* wsA[kPrepSetMax];
+  float* wsC[kPrepSetMax];
+};
+hipError_t launch_query_prep_multi(const tq_quantizer* const* qs, void* const* ws, int nq, const void* queries,
+                                   int q_dtype, int B, int Hq, int Hkv, hipStream_t st);
 hipError_t launch_query_prep_ws(const tq_quantizer* q, const void* queries, int q_dtype, int B, int Hq, int Hkv,
                                 void* ws, hipStream_t st);
 hipError_t launch_scores_scan(const tq_quantizer* q, int B, int Hq, int Hkv, const uint32_t* codes, const float* norms,

@@ -37,10 +37,9 @@ namespace tq {
 // QJL term; MSE-only keys have no QJL term.
 // ---------------------------------------------------------------------------
 template <bool QBF16, bool ONE>
-__global__ void __launch_bounds__(256) query_prep_kernel(const void* __restrict__ queries, int q_dtype, int Hq, int Hkv,
-                                                         int G, int RT, int d, int m, const float* __restrict__ qt,
-                                                         Codebook cb, int qjl, int C, uint8_t* __restrict__ wsA,
-                                                         float* __restrict__ wsC) {
+__device__ __forceinline__ void query_prep_body(const void* __restrict__ queries, int q_dtype, int Hq, int Hkv, int G,
+                                                int RT, int d, int m, const float* __restrict__ qt, const Codebook& cb,
+                                                int qjl, int C, uint8_t* __restrict__ wsA, float* __restrict__ wsC) {
   extern __shared__ float sm[];
   float* qv = sm;           // [d]
   float* qh = qv + d;       // [d]   Pi q
@@ -225,6 +224,25 @@ __global__ void __launch_bounds__(256) query_prep_kernel(const void* __restrict_
     }
     wsC[(static_cast<int64_t>(gy) * 4 + qi) * 16 + tid] = val;
   }
+}
+
+template <bool QBF16, bool ONE>
+__global__ void __launch_bounds__(256) query_prep_kernel(const void* __restrict__ queries, int q_dtype, int Hq, int Hkv,
+                                                         int G, int RT, int d, int m, const float* __restrict__ qt,
+                                                         Codebook cb, int qjl, int C, uint8_t* __restrict__ wsA,
+                                                         float* __restrict__ wsC) {
+  query_prep_body<QBF16, ONE>(queries, q_dtype, Hq, Hkv, G, RT, d, m, qt, cb, qjl, C, wsA, wsC);
+}
+
+// The query operands of several quantizers (the segments of one cache) in
+// one launch: blockIdx.y picks the quantizer.
+template <bool QBF16, bool ONE>
+__global__ void __launch_bounds__(256) query_prep_multi_kernel(const void* __restrict__ queries, int q_dtype, int Hq,
+                                                               int Hkv, int G, int RT, int d, int m, int C,
+                                                               PrepSet set) {
+  const int k = blockIdx.y;
+  query_prep_body<QBF16, ONE>(queries, q_dtype, Hq, Hkv, G, RT, d, m, set.qt[k], set.cb[k], set.qjl[k], C, set.wsA[k],
+                              set.wsC[k]);
 }
 
 // ---------------------------------------------------------------------------
@@ -448,6 +466,39 @@ hipError_t launch_query_prep(const tq_quantizer* q, const void* queries, int q_d
     if (one) TQ_QP(false, true); else TQ_QP(false, false);
   }
 #undef TQ_QP
+  return hipGetLastError();
+}
+
+hipError_t launch_query_prep_multi(const tq_quantizer* const* qs, void* const* ws, int nq, const void* queries,
+                                   int q_dtype, int B, int Hq, int Hkv, hipStream_t st) {
+  if (nq < 1 || nq > kPrepSetMax) return hipErrorInvalidValue;
+  const tq_quantizer* q0 = qs[0];
+  const int G = Hq / Hkv;
+  const int RT = (G + 3) / 4;
+  const int C = (q0->d + 127) / 128;
+  const int64_t groups = static_cast<int64_t>(B) * Hkv * RT;
+  PrepSet set = {};
+  for (int k = 0; k < nq; ++k) {
+    if (qs[k]->d != q0->d || qs[k]->m != q0->m) return hipErrorInvalidValue;
+    set.qt[k] = qs[k]->d_qt;
+    set.cb[k] = key_codebook(qs[k]);
+    set.qjl[k] = key_qjl(qs[k]) ? 1 : 0;
+    set.wsA[k] = static_cast<uint8_t*>(ws[k]);
+    set.wsC[k] = reinterpret_cast<float*>(set.wsA[k] + groups * key_terms(qs[k]) * C * 2048);
+  }
+  const size_t lds = sizeof(float) * (2 * q0->d + q0->m + 4 * (q0->d + q0->m));
+  dim3 grid(static_cast<unsigned>(groups * 4), static_cast<unsigned>(nq));
+  const int dm = q0->d + q0->m;
+  const bool one = dm % 4 == 0 && dm <= 256 && q0->d <= 128;
+#define TQ_QPM(BF, ONE)                                                                                            \
+  hipLaunchKernelGGL((query_prep_multi_kernel<BF, ONE>), grid, dim3(256), lds, st, queries, q_dtype, Hq, Hkv, G, RT, \
+                     q0->d, q0->m, C, set)
+  if (q_dtype == 1) {
+    if (one) TQ_QPM(true, true); else TQ_QPM(true, false);
+  } else {
+    if (one) TQ_QPM(false, true); else TQ_QPM(false, false);
+  }
+#undef TQ_QPM
   return hipGetLastError();
 }
 
