@@ -72,6 +72,10 @@ def parse():
     ap.add_argument("--rotation", default="haar", choices=["haar", "hadamard"],
                     help="gqa/long: dense Haar rotation (QR of a Gaussian) or the structured H D / sqrt(d)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-baseline-all", action="store_true",
+                    help="only time the oracle (no GPU): encode keys/s and logits GB/s of packed keys on a bounded "
+                         "sample of each of the five workloads, with all host threads and with one; one JSON line "
+                         "per workload and thread count")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a 256 MiB device copy 3 times (the known-size kernel for counter scaling)")
     ap.add_argument("--ceiling", action="store_true",
@@ -633,8 +637,65 @@ def run_decay(args, torch, dev, tq, W):
     return res
 
 
+def cpu_baseline_all():
+    """The oracle on a bounded sample of every workload (inputs from the same
+    generators at reduced sizes, so the value laws are the workloads'):
+    encode throughput (keys/s) and logits throughput (packed key bytes/s and
+    query-key pairs/s), all host threads and one thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle import tq_oracle as o
+    from vector_quantization_tq_amd import workloads as W
+    cases = []
+    wl = W.tiny()
+    cases.append(("tiny 4096x128 fp32, 3-bit, 16 queries", 128, 3, wl.arrays["x"].astype(np.float64),
+                  wl.arrays["q"].astype(np.float64)))
+    wl = W.decode_layer(3, heads=1)
+    cases.append(("decode layer (1 head of 32), 8192 keys d128 3-bit, 1 query", 128, 3,
+                  wl.arrays["k"][0].astype(np.float64), wl.arrays["q"][:1].astype(np.float64)))
+    wl = W.gqa_layer(B=1, Hkv=1, Hq=4, N=16384)
+    cases.append(("GQA layer (1 of 64 groups), 16384 keys d128 3-bit, 4 queries", 128, 3,
+                  wl.arrays["k"].reshape(-1, 128).astype(np.float64), wl.arrays["q"][0].astype(np.float64)))
+    wl = W.long_context(B=1, Hkv=1, Hq=4, N=16384, tail=0)
+    cases.append(("long context (1 of 8 groups), 16384 keys d128 4-bit, 4 queries", 128, 4,
+                  wl.arrays["k"].reshape(-1, 128).astype(np.float64), wl.arrays["q"][0].astype(np.float64)))
+    wl = W.vector_search(4, n=20000, nq=1000)
+    cases.append(("vector search, 20000 of 10^6 keys d200 4-bit, 1000 queries", 200, 4,
+                  wl.arrays["x"].astype(np.float64), wl.arrays["q"].astype(np.float64)))
+    all_threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    for name, d, bits, x, q in cases:
+        oq = o.Quantizer(d, bits, 0)
+        packed = x.shape[0] * o.record_bytes("prod", d, bits)
+        for threads in (all_threads, 1):
+            with threadpool_limits(limits=threads):
+                t0 = time.perf_counter()
+                reps = 0
+                while True:
+                    idx, b01, nrm, gam = o.encode_prod(oq, x)
+                    reps += 1
+                    if time.perf_counter() - t0 > 2.0:
+                        break
+                enc = reps * x.shape[0] / (time.perf_counter() - t0)
+                t0 = time.perf_counter()
+                reps = 0
+                while True:
+                    o.scores(oq, q, idx, b01, nrm, gam)
+                    reps += 1
+                    if time.perf_counter() - t0 > 2.0:
+                        break
+                el = time.perf_counter() - t0
+            print(json.dumps({"workload": name, "threads": threads, "kind": "oracle (float64 numpy)",
+                              "encode_keys_per_s": round(enc, 1),
+                              "logits_packed_gb_per_s": round(packed * reps / el / 1e9, 4),
+                              "logits_pairs_per_s": round(q.shape[0] * x.shape[0] * reps / el, 1)}), flush=True)
+
+
 def main():
     args = parse()
+    if args.cpu_baseline_all:
+        cpu_baseline_all()
+        return
     if args.gpus != 1:
         print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); sharding the path over several GPUs "
               "is not implemented.", file=sys.stderr)
