@@ -221,7 +221,8 @@ int tq_scores(const tq_quantizer* q, const void* queries, int q_dtype, int B, in
  *   sequences of n_comp keys; vcodes/vnorms: mse encoding of the same;
  *   k_tail, v_tail: [B][Hkv][n_tail][d] bf16 (NULL if n_tail == 0);
  *   out: [B][Hq][d] float.  scale <= 0 selects 1/sqrt(d).
- *   n_comp + n_tail >= 1; kq and vq must have the same d.
+ *   n_comp + n_tail >= 1; kq and vq must have the same d, one of 64, 96,
+ *   128 or 256 (TQ_EUNSUPPORTED otherwise); n_tail <= 512.
  *   workspace: device scratch of at least tq_attend_workspace_bytes(...) */
 int64_t tq_attend_workspace_bytes(const tq_quantizer* kq, const tq_quantizer* vq, int B, int Hq, int Hkv,
                                   int64_t n_comp, int n_tail);
@@ -243,7 +244,8 @@ int tq_attend_decode(const tq_quantizer* kq, const tq_quantizer* vq, const void*
  * Because the running maximum never exceeds the overall one, the dropped set
  * lies inside D = {t : w_t < v_threshold * max_u w_u}, and each output element
  * differs from tq_attend_decode's by at most sum_{t in D} p_t |v_t[e]| / sum_t
- * p_t.  v_threshold = 0 gives tq_attend_decode's result bit for bit. */
+ * p_t.  v_threshold = 0 gives tq_attend_decode's result bit for bit.
+ * v_threshold > 0 needs d = 128 (TQ_EUNSUPPORTED otherwise). */
 int tq_attend_decode_sparse(const tq_quantizer* kq, const tq_quantizer* vq, const void* queries, int q_dtype,
                             int B, int Hq, int Hkv, const uint32_t* kcodes, const float* knorms,
                             const float* kgammas, const uint32_t* vcodes, const float* vnorms, int64_t n_comp,
@@ -282,7 +284,7 @@ typedef struct tq_segment {
  * by its segment's quantizer.  With one segment this is tq_attend_decode.
  * The order of the segments does not change the result beyond rounding.
  * queries [B][Hq][d], tails [B][Hkv][n_tail][d] bf16, out [B][Hq][d] float,
- * scale <= 0 selects 1/sqrt(d); d = 128.  workspace: at least
+ * scale <= 0 selects 1/sqrt(d); d in {64, 96, 128, 256}.  workspace: at least
  * tq_attend_segments_workspace_bytes(...) bytes, 256-byte aligned. */
 int64_t tq_attend_segments_workspace_bytes(const tq_segment* segs, int nseg, int B, int Hq, int Hkv, int n_tail);
 int tq_attend_decode_segments(const tq_segment* segs, int nseg, const void* queries, int q_dtype, int B, int Hq,

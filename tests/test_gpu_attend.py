@@ -101,6 +101,42 @@ def test_attend_shapes(B, Hkv, Hq, N, tail, bits, qf32):
     print("worst relative error", w)
 
 
+@pytest.mark.parametrize("d,B,Hkv,Hq,N,tail,bits,vbits", [
+    (64, 2, 2, 8, 1000, 0, 3, 3), (64, 1, 8, 32, 9000, 256, 4, 2), (64, 1, 1, 1, 300, 0, 2, 4),
+    (96, 1, 2, 8, 1000, 37, 3, 3), (96, 2, 4, 16, 5000, 0, 4, 4), (96, 1, 1, 6, 129, 5, 2, 1),
+    (256, 1, 2, 8, 1000, 0, 3, 3), (256, 1, 4, 16, 6000, 300, 4, 4), (256, 1, 1, 4, 200, 0, 2, 2),
+    (256, 1, 8, 32, 20000, 0, 3, 4)])
+def test_attend_head_dims(d, B, Hkv, Hq, N, tail, bits, vbits):
+    """Head dimensions 64, 96 and 256: keys in 1, 2 or 3 groups of a 128-wide
+    MFMA chunk (96 leaves one lane group on zero operands) or two chunks
+    (256); 16-coordinate value tiles spread over the waves (96: the last wave
+    has none); key rows of 6 or 9 words (not 16-byte runs) staged by 4-byte
+    copies; ragged tails up to 300 tokens (past the merge's first rounds)."""
+    print(f"case: attend d={d} B={B} Hkv={Hkv} Hq={Hq} N={N} tail={tail} K{bits} V{vbits}", flush=True)
+    k, v, q = _gqa_inputs(B, Hkv, Hq, N, d, seed=d + N + tail)
+    groups = [(b, h) for b in range(B) for h in range(Hkv)][:3]
+    w = _run_case(k, v, q, B, Hkv, Hq, N - tail, tail, bits, vbits=vbits, groups=groups)
+    print("worst relative error", w)
+
+
+def test_attend_head_dim_errors():
+    """Unsupported head dimensions and sparse V outside d = 128 are refused."""
+    print("case: attend head-dim errors", flush=True)
+    for d in (32, 192):
+        k, v, q = _gqa_inputs(1, 1, 4, 64, d, seed=d)
+        g = tq.Quantizer(d, 3, 0)
+        kc, kn, kg = tq.tq_encode(g, tq.TQ_PROD, k)
+        vc, vn, _ = tq.tq_encode(g, tq.TQ_MSE, v)
+        with pytest.raises(tq.TQError):
+            tq.tq_attend_decode(g, g, q, kc, kn, kg, vc, vn, 1, 64, None, None)
+    k, v, q = _gqa_inputs(1, 1, 4, 64, 64, seed=3)
+    g = tq.Quantizer(64, 3, 0)
+    kc, kn, kg = tq.tq_encode(g, tq.TQ_PROD, k)
+    vc, vn, _ = tq.tq_encode(g, tq.TQ_MSE, v)
+    with pytest.raises(tq.TQError):
+        tq.tq_attend_decode(g, g, q, kc, kn, kg, vc, vn, 1, 64, None, None, v_threshold=0.01)
+
+
 def test_attend_custom_scale_and_same_quantizer():
     print("case: attend custom scale", flush=True)
     k, v, q = _gqa_inputs(1, 2, 8, 600, 128, seed=11)

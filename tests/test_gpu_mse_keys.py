@@ -149,12 +149,12 @@ def _bf16(u16):
     return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).to(_dev()).view(torch.bfloat16)
 
 
-@pytest.mark.parametrize("B,Hkv,Hq,N,tail,kbits,vbits", [
-    (1, 2, 8, 1000, 0, 4, 4), (2, 2, 8, 777, 37, 3, 3), (1, 1, 6, 300, 5, 2, 4), (1, 2, 2, 129, 0, 1, 2),
-    (1, 8, 32, 4096, 256, 4, 3)])
-def test_attend_mse_keys(B, Hkv, Hq, N, tail, kbits, vbits):
-    print(f"case: mse keys attend B={B} Hkv={Hkv} Hq={Hq} N={N} tail={tail} K{kbits} V{vbits}", flush=True)
-    d = 128
+@pytest.mark.parametrize("d,B,Hkv,Hq,N,tail,kbits,vbits", [
+    (128, 1, 2, 8, 1000, 0, 4, 4), (128, 2, 2, 8, 777, 37, 3, 3), (128, 1, 1, 6, 300, 5, 2, 4),
+    (128, 1, 2, 2, 129, 0, 1, 2), (128, 1, 8, 32, 4096, 256, 4, 3), (64, 1, 2, 8, 2000, 10, 3, 2),
+    (96, 1, 2, 8, 2000, 0, 3, 3), (96, 1, 2, 4, 700, 3, 1, 4), (256, 1, 2, 8, 3000, 64, 4, 4)])
+def test_attend_mse_keys(d, B, Hkv, Hq, N, tail, kbits, vbits):
+    print(f"case: mse keys attend d={d} B={B} Hkv={Hkv} Hq={Hq} N={N} tail={tail} K{kbits} V{vbits}", flush=True)
     rng = np.random.default_rng(N + kbits)
     a = W._gqa_tensors(rng, B, Hkv, Hq, N, d)
     k = _bf16(a["k_bf16"]).view(B * Hkv, N, d)

@@ -17,7 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtq.so")
-SOURCES = ["tq_host.cpp", "tq_api.hip", "tq_encode.hip", "tq_scores.hip", "tq_attend.hip", "tq_topk.hip"]
+SOURCES = ["tq_host.cpp", "tq_api.hip", "tq_encode.hip", "tq_scores.hip", "tq_attend.hip", "tq_attend_d64.hip",
+           "tq_attend_d96.hip", "tq_attend_d256.hip", "tq_topk.hip"]
 # the benchmark's streaming-ceiling kernel, in a library of its own
 STREAM_LIB = os.path.join(HERE, "libtq_stream.so")
 STREAM_SOURCES = ["tq_stream.hip"]

@@ -454,7 +454,9 @@ static int attend_checked(const tq_quantizer* kq, const tq_quantizer* vq, const 
   const void* ptrs[] = {queries, out, kcodes, knorms, kgammas, vcodes, vnorms, k_tail, v_tail};
   for (const void* p : ptrs)
     if (p && !aligned(p, 16)) return fail(TQ_EINVAL, "device pointers must be 16-byte aligned");
-  if (kq->d != 128) return fail(TQ_EUNSUPPORTED, "attend supports d = 128 (d=%d)", kq->d);
+  if (!tq::attend_supports_d(kq->d))
+    return fail(TQ_EUNSUPPORTED, "attend supports d in {64, 96, 128, 256} (d=%d)", kq->d);
+  if (v_threshold > 0.f && kq->d != 128) return fail(TQ_EUNSUPPORTED, "sparse V (v_threshold > 0) needs d = 128");
   const int64_t need = tq_attend_workspace_bytes(kq, vq, B, Hq, Hkv, n_comp, n_tail);
   if (need < 0) return TQ_EINVAL;
   if (noalloc) {
@@ -550,7 +552,8 @@ int tq_attend_decode_segments(const tq_segment* segs, int nseg, const void* quer
   const void* ptrs[] = {queries, out, k_tail, v_tail};
   for (const void* p : ptrs)
     if (p && !aligned(p, 16)) return fail(TQ_EINVAL, "device pointers must be 16-byte aligned");
-  if (v0->d != 128) return fail(TQ_EUNSUPPORTED, "attend supports d = 128 (d=%d)", v0->d);
+  if (!tq::attend_supports_d(v0->d))
+    return fail(TQ_EUNSUPPORTED, "attend supports d in {64, 96, 128, 256} (d=%d)", v0->d);
   const int64_t need = tq::attend_segments_ws_bytes(sg, nseg, B, Hq, Hkv);
   if (!workspace || ws_bytes < need)
     return fail(TQ_EWORKSPACE, "workspace of %lld bytes needed", static_cast<long long>(need));

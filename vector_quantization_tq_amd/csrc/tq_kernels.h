@@ -55,6 +55,7 @@ struct AttendSegment {
 int64_t attend_ws_bytes(const tq_quantizer* kq, const tq_quantizer* vq, int B, int Hq, int Hkv, int64_t n_comp,
                         int n_tail);
 int64_t attend_segments_ws_bytes(const AttendSegment* segs, int nseg, int B, int Hq, int Hkv);
+bool attend_supports_d(int d);   // head dimensions the attention kernels are built for
 hipError_t launch_attend_segments(const AttendSegment* segs, int nseg, const void* queries, int q_dtype, int B, int Hq,
                                   int Hkv, const uint16_t* k_tail, const uint16_t* v_tail, int n_tail, float scale,
                                   float vtau, float* out, void* ws, hipStream_t st);
