@@ -69,6 +69,8 @@ def parse():
                          "--value-bits")
     ap.add_argument("--v-threshold", type=float, default=None,
                     help="gqa/long: sparse V (tq_attend_decode_sparse with this threshold in [0, 1))")
+    ap.add_argument("--head-dim", type=int, default=128, choices=[64, 96, 128, 256],
+                    help="gqa/long: head dimension d of the same layer shape (default 128)")
     ap.add_argument("--rotation", default="haar", choices=["haar", "hadamard"],
                     help="gqa/long: dense Haar rotation (QR of a Gaussian) or the structured H D / sqrt(d)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -370,7 +372,8 @@ def run_gqa(args, torch, dev, tq, wl_fn, name, bits, n_tail=0):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(scores_alg / (scores_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic() if name.startswith("gqa") and not mse_keys else None,
+            "traffic": (measured_traffic() if name.startswith("gqa") and not mse_keys and d == 128 and bits == 3
+                        and args.rotation == "haar" else None),
             "algorithmic_bytes_per_launch": scores_alg,
             "bytes_per_key": rec_k + 4 * G,
         },
@@ -715,14 +718,17 @@ def main():
         copy_calibration(torch, dev)
     if args.workload == "gqa":
         bits = args.bits or 3
-        res, wl = run_gqa(args, torch, dev, tq, W.gqa_layer, f"gqa-decode-layer b8 kv8 q32 n32768 d128 {bits}-bit", bits)
+        hd = args.head_dim
+        res, wl = run_gqa(args, torch, dev, tq, lambda: W.gqa_layer(d=hd),
+                          f"gqa-decode-layer b8 kv8 q32 n32768 d{hd} {bits}-bit", bits)
         if (not args.no_cpu_baseline and args.key_mode == "prod" and bits == 3 and not args.value_bits
-                and args.v_threshold is None and args.rotation == "haar"):
+                and args.v_threshold is None and args.rotation == "haar" and hd == 128):
             res["cpu_baseline"] = cpu_baseline_gqa(wl, args.steps)
     elif args.workload == "long":
         bits = args.bits or 4
-        res, wl = run_gqa(args, torch, dev, tq, W.long_context,
-                          f"long-context b1 kv8 q32 n131072 tail256 d128 {bits}-bit", bits, n_tail=256)
+        hd = args.head_dim
+        res, wl = run_gqa(args, torch, dev, tq, lambda: W.long_context(d=hd),
+                          f"long-context b1 kv8 q32 n131072 tail256 d{hd} {bits}-bit", bits, n_tail=256)
     elif args.workload == "decode":
         res = run_decode(args, torch, dev, tq, W)
     elif args.workload == "decay":

@@ -160,3 +160,39 @@ def test_encode_hadamard_gqa_layer_multi_tile(mode):
             P.check_mse_codes(oq, xs[s], c, nn[sl])
         else:
             P.check_mse_key_codes(oq, xs[s], c, nn[sl])
+
+
+@pytest.mark.parametrize("d,bits,nseq,n,bf16,mode", [
+    (128, 3, 3, 1000, True, "mse"), (128, 4, 2, 4101, False, "mse"), (128, 2, 2, 777, True, "mse_keys"),
+    (128, 1, 1, 300, True, "mse"), (64, 3, 2, 333, True, "mse"), (64, 4, 1, 129, False, "mse_keys"),
+    (32, 2, 2, 65, True, "mse"), (32, 3, 1, 100, False, "mse_keys"), (256, 3, 2, 1000, True, "mse"),
+    (256, 4, 1, 97, False, "mse"), (256, 2, 2, 33, True, "mse_keys"), (256, 1, 1, 64, False, "mse_keys"),
+    (128, 3, 1, 1, True, "mse"), (256, 3, 1, 1, True, "mse_keys")])
+def test_encode_walsh_hadamard_butterfly(d, bits, nseq, n, bf16, mode):
+    """Values and MSE-only keys under the Hadamard rotation take the
+    butterfly encoder (the fast Walsh-Hadamard transform in registers, one
+    token per lane, two lanes per token at d = 256): every code of every
+    sequence against the oracle, ragged tails (tiles of 64 tokens, 32 at
+    d = 256), bf16 and float input.  The first vector of each sequence is
+    zero (every coordinate of H D x exactly 0: the cell below the middle
+    threshold, as the oracle takes it)."""
+    print(f"case: hadamard butterfly encode {mode} d={d} bits={bits} nseq={nseq} n={n} bf16={bf16}", flush=True)
+    g, oq = _pair(d, bits)
+    x = _keys(np.random.default_rng(d * 10 + bits + n), nseq, n, d)
+    x[:, 0] = 0.0
+    xt = torch.from_numpy(x).to(_dev())
+    if bf16:
+        xt = xt.bfloat16()
+    m = tq.TQ_MSE if mode == "mse" else tq.TQ_MSE_KEYS
+    codes, norms, _ = tq.tq_encode(g, m, xt)
+    torch.cuda.synchronize()
+    xs = xt.float().cpu().numpy().astype(np.float64)
+    cw = P.to_u32(codes)
+    per = g.code_words(m, 1, n)
+    nn = norms.cpu().numpy()
+    for s in range(nseq):
+        c = cw[s * per:(s + 1) * per]
+        if mode == "mse":
+            P.check_mse_codes(oq, xs[s], c, nn[s * n:(s + 1) * n])
+        else:
+            P.check_mse_key_codes(oq, xs[s], c, nn[s * n:(s + 1) * n])

@@ -1,10 +1,14 @@
 """Build libtq.so (HIP, gfx950) in the package directory.
 
-    python -m vector_quantization_tq_amd.build
+    python -m vector_quantization_tq_amd.build [--define NAME ...] [--out DIR]
 
 Compiles every source to an object with hipcc (in parallel, objects under
 _build/ next to this file), then links them into libtq.so.  Always
-recompiles.
+recompiles.  --define adds a preprocessor macro and --out puts the libraries
+(and objects) in DIR instead: a variant for A/B measurements, loaded by
+setting TQ_LIBRARY=DIR/libtq.so (TQ_NO_WHT_ENCODE: Hadamard-rotation values
+and MSE-only keys on the dense +-1 matrix-core encoder instead of the
+Walsh-Hadamard butterflies).
 """
 from __future__ import annotations
 
@@ -48,25 +52,34 @@ def _run(cmd, verbose):
         print(err, file=sys.stderr)
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
+def build(verbose: bool = False, defines=(), out_dir: str | None = None) -> str:
+    obj_dir = os.path.join(out_dir, "_build") if out_dir else OBJ
+    lib_path = os.path.join(out_dir, "libtq.so") if out_dir else LIB
+    stream_path = os.path.join(out_dir, "libtq_stream.so") if out_dir else STREAM_LIB
+    os.makedirs(obj_dir, exist_ok=True)
+    extra = [f"-D{d}" for d in defines]
     jobs = []
     for s in SOURCES + STREAM_SOURCES:
         src = os.path.join(CSRC, s)
-        obj = os.path.join(OBJ, os.path.splitext(s)[0] + ".o")
+        obj = os.path.join(obj_dir, os.path.splitext(s)[0] + ".o")
         lang = "hip" if s.endswith(".hip") else "c++"
-        jobs.append((s, obj, [HIPCC] + hipcc_flags() + ["-c", "-x", lang, src, "-o", obj]))
+        jobs.append((s, obj, [HIPCC] + hipcc_flags() + extra + ["-c", "-x", lang, src, "-o", obj]))
     workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
     with ThreadPoolExecutor(workers) as ex:
         for f in [ex.submit(_run, cmd, verbose) for _, _, cmd in jobs]:
             f.result()
-    for lib, srcs in ((LIB, SOURCES), (STREAM_LIB, STREAM_SOURCES)):
+    for lib, srcs in ((lib_path, SOURCES), (stream_path, STREAM_SOURCES)):
         tmp = lib + ".tmp"
         objs = [o for s, o, _ in jobs if s in srcs]
         _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}"] + objs + ["-o", tmp], verbose)
         os.replace(tmp, lib)
-    return LIB
+    return lib_path
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import argparse
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--define", action="append", default=[], help="preprocessor macro (NAME or NAME=VALUE)")
+    ap.add_argument("--out", default=None, help="directory for a variant build (default: in-tree)")
+    a = ap.parse_args()
+    print(build(verbose=True, defines=a.define, out_dir=a.out))

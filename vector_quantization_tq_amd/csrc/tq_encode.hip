@@ -849,6 +849,278 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
   if (it > 0) store(prev, (it - 1) & 1);
 }
 
+// ---------------------------------------------------------------------------
+// Walsh-Hadamard encoder for the structured rotation Pi = H D / sqrt(d)
+// (TQ_ROT_HADAMARD; H the Sylvester-ordered Hadamard matrix, D the random
+// signs), values and MSE-only keys, d = 32 .. 256 a power of two.
+// [wiselychen] "Google TurboQuant：KV Cache 壓縮 6x…", TurboQuant+ section:
+// the community implementation applies the rotation as a fast Walsh-Hadamard
+// transform (O(d log d) butterflies) instead of a dense product.
+//
+// A lane holds one token's coordinates in registers (two lanes per token for
+// d = 256, which each keep 128): the sign flips of D are one xor per bf16 pair
+// on the raw bits, the log2(d) butterfly stages run in registers (the last
+// one across the lane pair for d = 256), and nothing goes through LDS.  The
+// decisions compare v = H D x directly with the thresholds times ||x|| sqrt(d)
+// (y = v / (||x|| sqrt(d))), one compare per index bit as in the tile kernel;
+// each compare is a lane mask over the wave's tokens, so for values (32-token
+// words, one bit per token) a plane word is half of a ballot, collected into
+// one lane per coordinate with writelane and stored 64 coordinates at a time.
+// MSE-only keys (token-major words) shift each decision into the lane's own
+// words.  One wave per 64 tokens (32 for d = 256), no synchronisation.
+// ---------------------------------------------------------------------------
+// Bits of j = #{positive thresholds < m} (m >= 0), NB of them, by the
+// binary search of decide_bits, each returned as the sign bit (bit 31) of
+// u[L] = threshold - m (set iff m > threshold); the next threshold is picked
+// with bitfield selects on the sign masks.
+template <int NB>
+__device__ __forceinline__ void mag_sign_bits(float m, const float (&th)[(1 << NB) - 1], uint32_t (&u)[NB]) {
+  static_assert(NB >= 1 && NB <= 3, "1 to 3 magnitude bits");
+  auto f = [](float x) { return __float_as_uint(x); };
+  auto sel = [](uint32_t mask, uint32_t a1, uint32_t a0) { return (mask & a1) | (~mask & a0); };   // v_bfi_b32
+  auto msk = [](uint32_t x) { return static_cast<uint32_t>(static_cast<int32_t>(x) >> 31); };
+  if constexpr (NB == 1) {
+    u[0] = f(th[0] - m);
+  } else if constexpr (NB == 2) {
+    u[1] = f(th[1] - m);
+    const uint32_t m1 = msk(u[1]);
+    u[0] = f(__uint_as_float(sel(m1, f(th[2]), f(th[0]))) - m);
+  } else {
+    u[2] = f(th[3] - m);
+    const uint32_t m2 = msk(u[2]);
+    u[1] = f(__uint_as_float(sel(m2, f(th[5]), f(th[1]))) - m);
+    const uint32_t m1 = msk(u[1]);
+    const uint32_t lo = sel(m2, f(th[4]), f(th[0])), hi = sel(m2, f(th[6]), f(th[2]));
+    u[0] = f(__uint_as_float(sel(m1, hi, lo)) - m);
+  }
+}
+
+// lane L of acc takes the wave-uniform word val (v_writelane_b32; the lane
+// select is an inline constant, so the word is the one scalar operand)
+template <int L>
+__device__ __forceinline__ uint32_t write_lane(uint32_t acc, uint32_t val) {
+  asm("v_writelane_b32 %0, %1, %2" : "+v"(acc) : "s"(val), "n"(L));
+  return acc;
+}
+// f(IC<I>{}) for I = B .. E-1, each I a compile-time constant
+template <int V>
+struct IC {
+  static constexpr int value = V;
+};
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(IC<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+struct WhtSigns {
+  uint32_t pm[128];   // bf16 pair k (coordinates 2k, 2k+1): bit 15 / bit 31 set where D is -1
+};
+
+template <int D, int BP, int MODE, bool BF16>
+__global__ void __launch_bounds__(256, (BP == 1 ? 2 : 3)) encode_wht_kernel(const void* __restrict__ x, int64_t nseq, int64_t n,
+                                                         WhtSigns sg, Codebook cb, uint32_t* __restrict__ codes,
+                                                         float* __restrict__ norms) {
+  static_assert(D >= 32 && D <= 256 && (D & (D - 1)) == 0, "d: a power of two from 32 to 256");
+  static_assert(MODE == 1 || MODE == 2, "values or MSE-only keys");
+  constexpr int S = D > 128 ? D / 128 : 1;   // lanes per token
+  constexpr int DL = D / S;                  // coordinates per lane
+  constexpr int TPW = 64 / S;                // tokens per wave
+  constexpr int KH = 1 << (BP - 1);          // centroids per half of the symmetric codebook
+  constexpr int NJ = BP > 1 ? BP - 1 : 1;
+  const int lane = threadIdx.x & 63;
+  const int64_t tiles = (n + TPW - 1) / TPW;   // per sequence
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wid >= nseq * tiles) return;   // the whole wave
+  const int64_t seq = wid / tiles, r = wid - seq * tiles;
+  const int64_t t0 = r * TPW;
+  const int rows = static_cast<int>(min(static_cast<int64_t>(TPW), n - t0));
+  const int tok = lane & (TPW - 1), part = lane / TPW;
+  const bool live = tok < rows;
+  const uint64_t lm = __ballot(live);
+
+  // ---- load this lane's coordinates part*DL .. +DL-1 (rows past n re-read the last one) ----
+  float v[DL];
+  {
+    const int64_t row = seq * n + t0 + min(tok, rows - 1);
+    if constexpr (BF16) {
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + row * D + part * DL);
+      uint4 raw[DL / 8];
+#pragma unroll
+      for (int j = 0; j < DL / 8; ++j) raw[j] = src[j];
+#pragma unroll
+      for (int j = 0; j < DL / 8; ++j) {
+        const uint32_t u[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int k = 4 * j + e;   // pair within the lane's slice
+          const uint32_t xm = S == 1 ? sg.pm[k] : (part ? sg.pm[DL / 2 + k] : sg.pm[k]);
+          const uint32_t w = u[e] ^ xm;
+          v[2 * k] = __uint_as_float(w << 16);
+          v[2 * k + 1] = __uint_as_float(w & 0xFFFF0000u);
+        }
+      }
+    } else {
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const float*>(x) + row * D + part * DL);
+      uint4 raw[DL / 4];
+#pragma unroll
+      for (int j = 0; j < DL / 4; ++j) raw[j] = src[j];
+#pragma unroll
+      for (int j = 0; j < DL / 4; ++j) {
+        const uint32_t u[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int c = 4 * j + e;
+          const int k = c >> 1;
+          const uint32_t pmk = S == 1 ? sg.pm[k] : (part ? sg.pm[DL / 2 + k] : sg.pm[k]);
+          const uint32_t xm = (c & 1) ? (pmk & 0x80000000u) : (pmk << 16);
+          v[c] = __uint_as_float(u[e] ^ xm);
+        }
+      }
+    }
+  }
+  // ---- v = H (D x): butterflies over pairs (i, i + h), h = 1, 2, ..., the last across the lane pair ----
+#pragma unroll
+  for (int h = 1; h < DL; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < DL; ++i)
+      if ((i & h) == 0) {
+        const float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+  if constexpr (S == 2) {
+    // coordinate c of part 0 pairs with c + 128 of part 1: part 0 keeps a + b, part 1 a - b
+    const float sgn = part ? -1.f : 1.f;
+#pragma unroll
+    for (int c = 0; c < DL; ++c) v[c] = fmaf(sgn, v[c], __shfl_xor(v[c], 32));
+  }
+  // ---- ||x||: H H^T = d I, so ||v||^2 = d ||x||^2 (taken from v, so that x
+  // need not stay live through the butterflies) ----
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < DL; ++c) ss = fmaf(v[c], v[c], ss);
+  if constexpr (S == 2) ss += __shfl_xor(ss, 32);
+  const float nv = sqrtf(ss * (1.f / static_cast<float>(D)));
+  // ---- thresholds of |y| scaled to v: y > t  <=>  v > t ||x|| sqrt(d) ----
+  const float tsc = nv * sqrtf(static_cast<float>(D));
+  float thr[KH > 1 ? KH - 1 : 1];
+#pragma unroll
+  for (int k = 0; k + 1 < KH; ++k) thr[k] = cb.t[KH + k] * tsc;
+
+  if constexpr (MODE == 1) {
+    // ---- values: plane words of 32 tokens, coordinate-major ----
+    const int64_t nb = (n + 31) >> 5;
+    // word (block, plane p, coordinate c) of the low / high half of a mask
+    const int64_t blk0 = S == 1 ? 2 * r : r;
+    const bool has1 = S == 2 || blk0 + 1 < nb;
+    uint32_t acc0[BP], acc1[BP];
+#pragma unroll
+    for (int p = 0; p < BP; ++p) acc0[p] = acc1[p] = 0u;
+    static_for<0, DL>([&](auto ci) {
+      constexpr int c = decltype(ci)::value;
+      const float a = v[c];
+      bool jb[NJ];
+      if constexpr (BP > 1) decide_bits<BP - 1, BP - 2>(fabsf(a), thr, jb);
+      else jb[0] = false;
+      // sign plane [y > 0]; low planes [bit of j == sign]; padding tokens 0
+      const uint64_t sm = __ballot(a > 0.f) & lm;
+#pragma unroll
+      for (int p = 0; p < BP; ++p) {
+        const uint64_t m = p == BP - 1 ? sm : ~(__ballot(jb[p < BP - 1 ? p : 0]) ^ sm) & lm;
+        acc0[p] = write_lane<(c & 63)>(acc0[p], static_cast<uint32_t>(m));
+        acc1[p] = write_lane<(c & 63)>(acc1[p], static_cast<uint32_t>(m >> 32));
+      }
+      if constexpr ((c & 63) == 63 || c == DL - 1) {
+        const int cb0 = c & ~63;
+        if (lane <= (c & 63)) {
+#pragma unroll
+          for (int p = 0; p < BP; ++p) {
+            const int64_t w0 = ((seq * nb + blk0) * BP + p) * D + cb0 + lane;
+            codes[w0] = acc0[p];
+            if (S == 2) codes[w0 + DL] = acc1[p];                                   // coordinate 128 + c
+            else if (has1) codes[w0 + static_cast<int64_t>(BP) * D] = acc1[p];     // block blk0 + 1
+          }
+        }
+      }
+    });
+  } else {
+    // ---- MSE-only keys: this lane's groups of 32 coordinates, token-major words ----
+    constexpr int GL = DL / 32;
+    constexpr int G = D / 32;
+    uint32_t* dst = codes + ((seq * n + t0 + tok) * G + part * GL) * BP;
+    // Each decision is the sign bit of a difference (exact: a difference of
+    // distinct floats is never zero): [y > 0] of 0 - v, [|y| > t] of t - |v|.
+    // alignbit(w, u, 31) = (w << 1) | (u >> 31) shifts it into the word, so
+    // the decisions stay vector bits (no lane masks held in scalar registers).
+    // Words are built from coordinate 32 g + 31 down, so bit c ends at c.
+#pragma unroll
+    for (int g = 0; g < GL; ++g) {
+      uint32_t ws = 0u, wj[NJ];
+#pragma unroll
+      for (int p = 0; p < NJ; ++p) wj[p] = 0u;
+#pragma unroll
+      for (int c = 31; c >= 0; --c) {
+        const float a = v[32 * g + c];
+        ws = __builtin_amdgcn_alignbit(ws, __float_as_uint(0.f - a), 31);
+        if constexpr (BP > 1) {
+          uint32_t u[NJ];
+          mag_sign_bits<BP - 1>(fabsf(a), thr, u);
+#pragma unroll
+          for (int p = 0; p < NJ; ++p) wj[p] = __builtin_amdgcn_alignbit(wj[p], u[p], 31);
+        }
+      }
+      if (live) {
+        // sign plane [y > 0]; low planes [bit of j == sign]
+        dst[g * BP + BP - 1] = ws;
+#pragma unroll
+        for (int p = 0; p + 1 < BP; ++p) dst[g * BP + p] = ~(wj[p] ^ ws);
+      }
+    }
+  }
+  if (part == 0 && live) norms[seq * n + t0 + tok] = nv;
+}
+
+template <int D, int MODE, bool BF16>
+hipError_t launch_encode_wht_d(const tq_quantizer* q, const void* x, int64_t nseq, int64_t n, uint32_t* codes,
+                               float* norms, hipStream_t st) {
+  WhtSigns sg;
+  // row 0 of Pi is D / sqrt(d) (row 0 of H is all ones)
+  for (int k = 0; k < D / 2; ++k)
+    sg.pm[k] = (q->pi[2 * k] < 0 ? 0x8000u : 0u) | (q->pi[2 * k + 1] < 0 ? 0x80000000u : 0u);
+  for (int k = D / 2; k < 128; ++k) sg.pm[k] = 0u;
+  constexpr int TPW = D > 128 ? 64 / (D / 128) : 64;
+  const int64_t waves = nseq * ((n + TPW - 1) / TPW);
+  if ((waves + 3) / 4 > 0x7FFFFFFFll) return hipErrorNotSupported;
+  const dim3 grid(static_cast<unsigned>((waves + 3) / 4));
+  const Codebook& cb = q->cb[1];
+  switch (cb.bp) {
+#define TQ_WHT(BPV)                                                                                       \
+  case BPV:                                                                                               \
+    hipLaunchKernelGGL((encode_wht_kernel<D, BPV, MODE, BF16>), grid, dim3(256), 0, st, x, nseq, n, sg, cb, \
+                       codes, norms);                                                                     \
+    break;
+    TQ_WHT(1) TQ_WHT(2) TQ_WHT(3) TQ_WHT(4)
+#undef TQ_WHT
+    default: return hipErrorNotSupported;
+  }
+  return hipGetLastError();
+}
+
+template <int MODE, bool BF16>
+hipError_t launch_encode_wht_m(const tq_quantizer* q, const void* x, int64_t nseq, int64_t n, uint32_t* codes,
+                               float* norms, hipStream_t st) {
+  switch (q->d) {
+    case 32: return launch_encode_wht_d<32, MODE, BF16>(q, x, nseq, n, codes, norms, st);
+    case 64: return launch_encode_wht_d<64, MODE, BF16>(q, x, nseq, n, codes, norms, st);
+    case 128: return launch_encode_wht_d<128, MODE, BF16>(q, x, nseq, n, codes, norms, st);
+    case 256: return launch_encode_wht_d<256, MODE, BF16>(q, x, nseq, n, codes, norms, st);
+    default: return hipErrorNotSupported;
+  }
+}
+
 // Decode: one workgroup per 8 vectors; plain fp32 FMAs (not on the hot path).
 __global__ void __launch_bounds__(256) decode_kernel(const uint32_t* __restrict__ codes, const float* __restrict__ norms,
                                                      const float* __restrict__ gammas, int64_t n, int d, int m, int mode,
@@ -1017,8 +1289,28 @@ hipError_t launch_encode_tile(const tq_quantizer* q, int mode, const void* x, in
   return launch_encode_tile_lk<2>(q, mode, x, dtype, nseq, n, codes, norms, gammas, st);
 }
 
+// The Walsh-Hadamard encoder takes the structured rotation wherever it
+// applies (values and MSE-only keys, d a power of two from 32 to 256); prod
+// keys need the dense S' contraction anyway and stay on the tile kernel.
+bool encode_uses_wht(const tq_quantizer* q, int mode) {
+#ifndef TQ_NO_WHT_ENCODE
+  return q->rotation == 1 && mode != 0 && q->d >= 32 && q->d <= 256 && (q->d & (q->d - 1)) == 0;
+#else
+  (void)q;
+  (void)mode;
+  return false;
+#endif
+}
+
 hipError_t launch_encode(const tq_quantizer* q, int mode, const void* x, int dtype, int64_t nseq, int64_t n,
                          uint32_t* codes, float* norms, float* gammas, hipStream_t st) {
+  if (encode_uses_wht(q, mode)) {
+    if (mode == 1)
+      return dtype == 1 ? launch_encode_wht_m<1, true>(q, x, nseq, n, codes, norms, st)
+                        : launch_encode_wht_m<1, false>(q, x, nseq, n, codes, norms, st);
+    return dtype == 1 ? launch_encode_wht_m<2, true>(q, x, nseq, n, codes, norms, st)
+                      : launch_encode_wht_m<2, false>(q, x, nseq, n, codes, norms, st);
+  }
   if (q->d <= 128) {
     return launch_encode_tile(q, mode, x, dtype, nseq, n, codes, norms, gammas, st);
   }

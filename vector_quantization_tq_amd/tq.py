@@ -13,7 +13,10 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libtq.so")
+# TQ_LIBRARY names another build of the same library (a variant built with
+# `python -m vector_quantization_tq_amd.build --define ... --out DIR`, for A/B
+# measurements); by default the in-tree libtq.so
+LIB_PATH = os.environ.get("TQ_LIBRARY") or os.path.join(_HERE, "libtq.so")
 
 TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EHIP, TQ_ENOMEM, TQ_EWORKSPACE = 0, -1, -2, -3, -4, -5
 TQ_PROD, TQ_MSE, TQ_MSE_KEYS = 0, 1, 2
