@@ -252,13 +252,39 @@ tq_quantizer* tq_make_quantizer_ex(int d, int bits, uint64_t seed, int rotation)
     tq_free_quantizer(q);
     return nullptr;
   }
+  if (d > 128 && d <= 256) {
+    // the eight-wave encoder's operands: Pi and S' scaled by 2^8 and split into
+    // fp16 hi + lo (rounded to nearest), rows j < d, columns k < d, zero padded
+    // to 256 x 256
+    constexpr int W = 256;
+    std::vector<_Float16> wide(static_cast<size_t>(4) * W * W, static_cast<_Float16>(0.f));
+    for (int j = 0; j < d; ++j)
+      for (int k = 0; k < d; ++k) {
+        const float vp = pi32[static_cast<size_t>(j) * d + k] * 256.f;
+        const float vs = sp32[static_cast<size_t>(j) * d + k] * 256.f;
+        const _Float16 ph = static_cast<_Float16>(vp), sh = static_cast<_Float16>(vs);
+        const size_t o = static_cast<size_t>(j) * W + k;
+        wide[o] = ph;
+        wide[static_cast<size_t>(W) * W + o] = static_cast<_Float16>(vp - static_cast<float>(ph));
+        wide[static_cast<size_t>(2) * W * W + o] = sh;
+        wide[static_cast<size_t>(3) * W * W + o] = static_cast<_Float16>(vs - static_cast<float>(sh));
+      }
+    const size_t bw = wide.size() * sizeof(_Float16);
+    if ((e = hipMalloc(&q->d_wide, bw)) != hipSuccess ||
+        (e = hipMemcpy(q->d_wide, wide.data(), bw, hipMemcpyHostToDevice)) != hipSuccess) {
+      hip_fail(e, "wide encoder tables");
+      tq_free_quantizer(q);
+      return nullptr;
+    }
+  }
   return q;
 }
 
 void tq_free_quantizer(tq_quantizer* q) {
   if (!q) return;
-  if (q->d_pi || q->d_s || q->d_sp || q->d_qt || q->d_spt) {
+  if (q->d_pi || q->d_s || q->d_sp || q->d_qt || q->d_spt || q->d_wide) {
     DeviceGuard g(q->device);
+    if (q->d_wide) (void)hipFree(q->d_wide);
     if (q->d_pi) (void)hipFree(q->d_pi);
     if (q->d_s) (void)hipFree(q->d_s);
     if (q->d_sp) (void)hipFree(q->d_sp);

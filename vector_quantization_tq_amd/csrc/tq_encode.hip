@@ -17,9 +17,15 @@
 //    rho_hi S'_hi + rho_lo S'_hi + rho_hi S'_lo for the QJL projection.
 //    Wave w keeps its 32 rows of Pi and S' (hi and lo) in registers as the
 //    stationary operand; workgroups are persistent over 64-vector tiles.
-//  * d > 128 (encode_kernel): the fp32 MFMA (16x16x4), one workgroup per
+//  * 128 < d <= 256 with rows in 16-byte runs (encode_tile_kernel<8, ...>):
+//    the same split products with eight waves, whose rows of Pi and S' (hi
+//    and lo) are read per 32-column step from the quantizer's fp16 tables in
+//    L2 instead of being held in registers.
+//  * otherwise (encode_kernel): the fp32 MFMA (16x16x4), one workgroup per
 //    tile of 64 vectors; each wave takes a quarter of the 16-column tiles
 //    for all 64 rows.
+//  * the Hadamard rotation, values and MSE-only keys (encode_wht_kernel): the
+//    fast Walsh-Hadamard transform in registers, no matrix core.
 #include <algorithm>
 
 #include "tq_device.h"
@@ -313,6 +319,7 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(const void* __restrict
 // same way.
 // ---------------------------------------------------------------------------
 constexpr int kEncRows = 64;
+constexpr int kWideK = 256;             // rows and columns of the wide kernel's fp16 tables
 constexpr float kPiScale = 256.f;       // 2^8
 constexpr float kRhoScale = 16384.f;    // 2^14
 
@@ -377,29 +384,41 @@ __device__ __forceinline__ float pick_centroid(const float (&cen)[1 << BP], cons
 // stationary operand is +-2^8 exactly in fp16 and needs no lo part -- one
 // product per rotation term instead of two (bf16 input), with 1/sqrt(d)
 // moved into the fp32 row scale.
+//
+// KS = 8 (128 < d <= 256): eight waves, wave w owning group w as above, but
+// the rows of Pi and S' (hi and lo, 256 inputs) do not fit in registers: they
+// are read per 32-input step from fp16 tables (`wt`: Pi hi, Pi lo, S' hi, S'
+// lo, each [256][256], row j = output coordinate j, zero past d), which stay
+// in L2, with the next step's operands in flight while the current one is
+// multiplied.
 template <int KS, int LK, int MODE, int BP, bool FULL, bool HAD = false>
-__global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restrict__ x, int dtype, int64_t nseq,
-                                                             int64_t n, int d, const float* __restrict__ pi,
-                                                             const float* __restrict__ sp, Codebook cb,
-                                                             uint32_t* __restrict__ codes, float* __restrict__ norms,
-                                                             float* __restrict__ gammas) {
+__global__ void __launch_bounds__(64 * KS, KS == 4 ? 2 : 1)
+    encode_tile_kernel(const void* __restrict__ x, int dtype, int64_t nseq, int64_t n, int d,
+                       const float* __restrict__ pi, const float* __restrict__ sp, const _Float16* __restrict__ wt,
+                       Codebook cb, uint32_t* __restrict__ codes, float* __restrict__ norms,
+                       float* __restrict__ gammas) {
   constexpr bool PROD = MODE != 1;       // token-major words, C[vector][coordinate]
   constexpr bool QJL = MODE == 0;        // residual, QJL plane and gamma
+  constexpr bool STREAM = KS == 8;       // Pi and S' rows from the L2-resident tables
+  constexpr int NTH = 64 * KS;           // threads: one wave per 32-coordinate group
+  constexpr int TPR = NTH / kEncRows;    // loader threads per row
   constexpr int KP = 32 * KS;            // padded contraction length
   constexpr int LDH = KP + 8;            // LDS row stride in halves (16-byte rows, conflict-free reads)
   constexpr bool XLO = LK != 1;          // fp32 keys need x_lo (bf16 keys are exact in fp16)
-  constexpr int PREN = LK == 2 ? KS * 2 : LK == 1 ? KS : 1;   // 16-byte chunks per loader thread
-  constexpr int EPT = KP / 4;            // elements per loader thread (scalar path)
+  constexpr int PREN = LK == 2 ? 8 : LK == 1 ? 4 : 1;   // 16-byte chunks per loader thread
+  constexpr int EPT = KP / TPR;          // elements per loader thread (scalar path)
+  constexpr int TAB = kWideK * kWideK;   // elements of one table (STREAM)
   __shared__ __attribute__((aligned(16))) _Float16 xh[kEncRows * LDH];
   __shared__ __attribute__((aligned(16))) _Float16 xl[XLO ? kEncRows * LDH : 8];
   __shared__ __attribute__((aligned(16))) _Float16 rh[QJL ? kEncRows * LDH : 8];
   __shared__ __attribute__((aligned(16))) _Float16 rl[QJL ? kEncRows * LDH : 8];
   __shared__ __attribute__((aligned(16))) float scl2[2][kEncRows];   // 2^(6 - row scale) / n, by tile parity
   __shared__ float nrm2[2][kEncRows];    // n, by tile parity
-  __shared__ float part2[4][kEncRows];
-  __shared__ uint32_t ost[2][1024];
+  __shared__ float part2[KS][kEncRows];
+  __shared__ uint32_t ost[2][256 * KS];
 
-  static_assert(KS == 4, "four waves own 32 coordinates each");
+  static_assert(KS == 4 || KS == 8, "four or eight waves own 32 coordinates each");
+  static_assert(!STREAM || !HAD, "the wide kernel takes the +-1 rotation as a general one");
   if constexpr (FULL) d = 32 * KS;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
@@ -416,8 +435,10 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
   static_assert(!HAD || FULL, "the +-1 rotation operand is built for d = 32 KS");
   // stationary operands: lane (r16, q) holds row 32w + 16ct + r16, columns
   // 32s + 8q .. +7 of Pi (and S'), split into hi + lo (HAD: sqrt(d) Pi 2^8 =
-  // +-2^8, exact, no lo part)
-  v8h bPh[2][KS], bPl[2][HAD ? 1 : KS], bSh[2][QJL ? KS : 1], bSl[2][QJL ? KS : 1];
+  // +-2^8, exact, no lo part); none with STREAM
+  constexpr int RS = STREAM ? 1 : KS;
+  v8h bPh[2][RS], bPl[2][HAD ? 1 : RS], bSh[2][QJL ? RS : 1], bSl[2][QJL ? RS : 1];
+  if constexpr (!STREAM) {
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
     const int j = 32 * w + 16 * ct + r16;
@@ -444,7 +465,8 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
         }
       }
   }
-  for (int e = tid; e < kEncRows * LDH; e += 256) {
+  }
+  for (int e = tid; e < kEncRows * LDH; e += NTH) {
     xh[e] = static_cast<_Float16>(0.f);
     if constexpr (XLO) xl[e] = static_cast<_Float16>(0.f);
     if constexpr (QJL) {
@@ -453,8 +475,8 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
     }
   }
 
-  // loader role: row = tid / 4, four threads per row
-  const int lrow = tid >> 2, part = tid & 3;
+  // loader role: row = tid / TPR, TPR threads per row
+  const int lrow = tid / TPR, part = tid % TPR;
   constexpr int esz = LK == 1 ? 2 : 4;
   const int CH = d * esz / 16;           // 16-byte chunks per row (vector paths)
   uint4 pre[PREN];
@@ -490,7 +512,7 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
                                                         ((seq * n + v0 + lrow) * d) * esz);
 #pragma unroll
       for (int j = 0; j < PREN; ++j) {
-        const int c = part + 4 * j;
+        const int c = part + TPR * j;
         pre[j] = make_uint4(0u, 0u, 0u, 0u);   // rows past n and chunks past d read as 0
         if (lrow < rows && c < CH) pre[j] = src[c];
       }
@@ -507,7 +529,7 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
     if constexpr (LK == 1) {
 #pragma unroll
       for (int j = 0; j < PREN; ++j) {
-        const int c = part + 4 * j;
+        const int c = part + TPR * j;
         const uint32_t u[4] = {pre[j].x, pre[j].y, pre[j].z, pre[j].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -521,7 +543,7 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
     } else if constexpr (LK == 2) {
 #pragma unroll
       for (int j = 0; j < PREN; ++j) {
-        const int c = part + 4 * j;
+        const int c = part + TPR * j;
         const uint32_t u[4] = {pre[j].x, pre[j].y, pre[j].z, pre[j].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -534,7 +556,7 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
       const int64_t off = (seq * n + v0 + lrow) * d;
 #pragma unroll
       for (int j = 0; j < EPT; ++j) {
-        const int col = part + 4 * j;
+        const int col = part + TPR * j;
         v[j] = (lrow < rows && col < d) ? load_elem(x, dtype, off + col) : 0.f;
         cols[j] = col;
       }
@@ -546,10 +568,11 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
       ss = fmaf(v[j], v[j], ss);
       mx = fmaxf(mx, fabsf(v[j]));
     }
-    ss += __shfl_xor(ss, 1);
-    ss += __shfl_xor(ss, 2);
-    mx = fmaxf(mx, __shfl_xor(mx, 1));
-    mx = fmaxf(mx, __shfl_xor(mx, 2));
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1) {
+      ss += __shfl_xor(ss, o);
+      mx = fmaxf(mx, __shfl_xor(mx, o));
+    }
     // power-of-two row scale putting the largest element in [2^14, 2^15)
     const int sig = mx > 0.f ? 14 - ilogb_pos(mx) : 0;
     _Float16* hr = xh + lrow * LDH;
@@ -558,7 +581,7 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
       // a 16-byte chunk of 8 bf16 values becomes one 16-byte row segment
 #pragma unroll
       for (int j = 0; j < PREN; ++j) {
-        const int c = part + 4 * j;
+        const int c = part + TPR * j;
         if (c < CH) {
           v8h hv;
 #pragma unroll
@@ -594,18 +617,18 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
     tile_of(t, seq, v0, rows);
     if constexpr (PROD) {
       uint32_t* dst = codes + (seq * n + v0) * WPK;
-      for (int e = tid; e < rows * WPK; e += 256) dst[e] = ost[buf][e];
+      for (int e = tid; e < rows * WPK; e += NTH) dst[e] = ost[buf][e];
     } else {
       const int nblk = (rows + 31) >> 5;
       uint32_t* dst = codes + ((seq * nb + (v0 >> 5)) * bp) * d;
-      for (int e = tid; e < nblk * bp * d; e += 256) dst[e] = ost[buf][e];
+      for (int e = tid; e < nblk * bp * d; e += NTH) dst[e] = ost[buf][e];
     }
   };
   // acc[h2][ct] (+)= rows 32h + 16h2 .. of src times this wave's columns;
   // SWAP puts the stationary operand first (C[coordinate][vector])
-  auto contract = [&](const _Float16* src, const v8h (&bm)[2][KS], int h, bool swap, v4f (&acc)[2][2]) {
+  auto contract = [&](const _Float16* src, const v8h (&bm)[2][RS], int h, bool swap, v4f (&acc)[2][2]) {
 #pragma unroll
-    for (int s2 = 0; s2 < KS; ++s2) {
+    for (int s2 = 0; s2 < RS; ++s2) {
       v8h a[2];
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
@@ -616,6 +639,89 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
         for (int ct = 0; ct < 2; ++ct)
           acc[h2][ct] = swap ? mfma_f16(bm[ct][s2], a[h2], acc[h2][ct]) : mfma_f16(a[h2], bm[ct][s2], acc[h2][ct]);
     }
+  };
+  // STREAM: acc[h2][ct] (+)= rows 32h + 16h2 .. of A0 times table T0, of A0
+  // times T1 and of A1 times T0 (each product only where the pointers are
+  // set): the B operands of step s2 are this wave's rows of the tables,
+  // loaded one step ahead
+  auto contract_stream = [&](const _Float16* A0, const _Float16* A1, const _Float16* T0, const _Float16* T1, int h,
+                             bool swap, v4f (&acc)[2][2]) {
+    // this lane's operand bytes within a table: row 32w + 16ct + r16, columns
+    // 8q .. 8q + 7 of each 32-column step (uniform table base + 32-bit offset)
+    auto ld = [&](const _Float16* T, int s2, int ct) {
+      const uint32_t off = static_cast<uint32_t>(((32 * w + 16 * ct + r16) * kWideK + 32 * s2 + 8 * q) * 2);
+      return *reinterpret_cast<const v8h*>(reinterpret_cast<const char*>(T) + off);
+    };
+    // SP 32-column steps per iteration, the next iteration's operands in
+    // flight while these are multiplied; not unrolled further (unrolled, the
+    // loop hoists every load and spills)
+    constexpr int SP = 2;   // d = 256, GQA shape: 1 step 3.73 ms, 2 steps 3.35 ms, 4 steps 4.93 ms (keys)
+    v8h b0[SP][2], b1[SP][2];
+#pragma unroll
+    for (int u = 0; u < SP; ++u)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        b0[u][ct] = ld(T0, u, ct);
+        if (T1) b1[u][ct] = ld(T1, u, ct);
+      }
+#pragma unroll 1
+    for (int s0 = 0; s0 < KS; s0 += SP) {
+      v8h n0[SP][2], n1[SP][2];
+      if (s0 + SP < KS) {
+#pragma unroll
+        for (int u = 0; u < SP; ++u)
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) {
+            n0[u][ct] = ld(T0, s0 + SP + u, ct);
+            if (T1) n1[u][ct] = ld(T1, s0 + SP + u, ct);
+          }
+      }
+#pragma unroll
+      for (int u = 0; u < SP; ++u) {
+        const int s2 = s0 + u;
+        v8h a0[2], a1[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          a0[h2] = *reinterpret_cast<const v8h*>(A0 + (32 * h + 16 * h2 + r16) * LDH + 32 * s2 + 8 * q);
+          if (A1) a1[h2] = *reinterpret_cast<const v8h*>(A1 + (32 * h + 16 * h2 + r16) * LDH + 32 * s2 + 8 * q);
+        }
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) {
+            acc[h2][ct] = swap ? mfma_f16(b0[u][ct], a0[h2], acc[h2][ct]) : mfma_f16(a0[h2], b0[u][ct], acc[h2][ct]);
+            if (T1)
+              acc[h2][ct] = swap ? mfma_f16(b1[u][ct], a0[h2], acc[h2][ct]) : mfma_f16(a0[h2], b1[u][ct], acc[h2][ct]);
+            if (A1)
+              acc[h2][ct] = swap ? mfma_f16(b0[u][ct], a1[h2], acc[h2][ct]) : mfma_f16(a1[h2], b0[u][ct], acc[h2][ct]);
+          }
+      }
+      if (s0 + SP < KS) {
+#pragma unroll
+        for (int u = 0; u < SP; ++u)
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) {
+            b0[u][ct] = n0[u][ct];
+            if (T1) b1[u][ct] = n1[u][ct];
+          }
+      }
+    }
+  };
+  // the rotation (x Pi^T, split products) of rows 32h .. 32h + 31
+  auto rotate = [&](int h, bool swap, v4f (&acc)[2][2]) {
+    if constexpr (STREAM) {
+      contract_stream(xh, XLO ? xl : nullptr, wt, wt + TAB, h, swap, acc);
+    } else {
+      contract(xh, bPh, h, swap, acc);
+      if constexpr (!HAD) contract(xh, bPl, h, swap, acc);
+      if constexpr (XLO) contract(xl, bPh, h, swap, acc);
+    }
+  };
+  auto sum_parts = [&](int r) {
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) t += part2[k][r];
+    return t;
   };
   auto zero_acc = [&](v4f (&acc)[2][2]) {
 #pragma unroll
@@ -685,9 +791,7 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
       for (int h = 0; h < 2; ++h) {
         v4f acc[2][2];
         zero_acc(acc);
-        contract(xh, bPh, h, false, acc);
-        if constexpr (!HAD) contract(xh, bPl, h, false, acc);
-        if constexpr (XLO) contract(xl, bPh, h, false, acc);
+        rotate(h, false, acc);
         pin_acc(acc);
         // lane holds vector 32h + 16h2 + 4q + i, coordinate 32w + 16ct + r16
         float r2v[2][4];   // partial ||rho||^2 (x 2^28) of this lane's two coordinates
@@ -768,9 +872,13 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
         for (int h = 0; h < 2; ++h) {
           v4f acc[2][2];
           zero_acc(acc);
-          contract(rh, bSh, h, false, acc);
-          contract(rl, bSh, h, false, acc);
-          contract(rh, bSl, h, false, acc);
+          if constexpr (STREAM) {
+            contract_stream(rh, rl, wt + 2 * TAB, wt + 3 * TAB, h, false, acc);
+          } else {
+            contract(rh, bSh, h, false, acc);
+            contract(rl, bSh, h, false, acc);
+            contract(rh, bSl, h, false, acc);
+          }
           pin_acc(acc);
           if (FULL || w < G) {
             uint32_t wd[2][4];
@@ -798,8 +906,7 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
         const float nv = nrm[tid];
         norms[seq * n + v0 + tid] = nv;
         if constexpr (QJL)
-          gammas[seq * n + v0 + tid] =
-              nv * sqrtf(part2[0][tid] + part2[1][tid] + part2[2][tid] + part2[3][tid]) * (1.f / kRhoScale);
+          gammas[seq * n + v0 + tid] = nv * sqrtf(sum_parts(tid)) * (1.f / kRhoScale);
       }
     } else {
       // lane holds coordinate 32w + 16ct + 4q + i, token 32h + 16h2 + r16;
@@ -808,9 +915,7 @@ __global__ void __launch_bounds__(256, 2) encode_tile_kernel(const void* __restr
       for (int h = 0; h < 2; ++h) {
         v4f acc[2][2];
         zero_acc(acc);
-        contract(xh, bPh, h, true, acc);
-        if constexpr (!HAD) contract(xh, bPl, h, true, acc);
-        if constexpr (XLO) contract(xl, bPh, h, true, acc);
+        rotate(h, true, acc);
         pin_acc(acc);
         // lane holds coordinate 32w + 16ct + 4q + i, token 32h + 16h2 + r16
         const float sc0 = scl[32 * h + r16], sc1 = scl[32 * h + 16 + r16];
@@ -1213,43 +1318,45 @@ static int device_cu_count() {
 
 // Persistent grid of the tile encoder: as many workgroups as fit on the chip
 // at once for this instantiation (its registers and LDS decide: two per CU
-// for prod keys, three or four for values and MSE-only keys), so that every
-// resident slot loops over tiles.
-template <int LK, int MODE, int BPV, bool FULL, bool HAD>
+// for prod keys, three or four for values and MSE-only keys; one for the
+// eight-wave kernel with prod keys), so that every resident slot loops over
+// tiles.
+template <int KS, int LK, int MODE, int BPV, bool FULL, bool HAD>
 int encode_tile_grid() {
   static const int blocks = [] {
     int per = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per, reinterpret_cast<const void*>(&encode_tile_kernel<4, LK, MODE, BPV, FULL, HAD>), 256, 0) !=
+            &per, reinterpret_cast<const void*>(&encode_tile_kernel<KS, LK, MODE, BPV, FULL, HAD>), 64 * KS, 0) !=
             hipSuccess ||
         per < 1) {
       (void)hipGetLastError();
-      per = 2;
+      per = KS == 4 ? 2 : 1;
     }
     return std::min(per, 4) * device_cu_count();
   }();
   return blocks;
 }
 
-template <int LK, int MODE, bool FULL, bool HAD = false>
+template <int KS, int LK, int MODE, bool FULL, bool HAD = false>
 hipError_t launch_encode_tile_m(const tq_quantizer* q, const void* x, int dtype, int64_t nseq, int64_t n,
                                 uint32_t* codes, float* norms, float* gammas, hipStream_t st) {
   const int64_t tiles = nseq * ((n + kEncRows - 1) / kEncRows);
   const Codebook& cb = q->cb[MODE == 0 ? 0 : 1];
-#define TQ_ENC(BPV)                                                                                                 \
-  case BPV: {                                                                                                       \
-    const dim3 grid(static_cast<unsigned>(std::min<int64_t>(tiles, encode_tile_grid<LK, MODE, BPV, FULL, HAD>())));   \
-    hipLaunchKernelGGL((encode_tile_kernel<4, LK, MODE, BPV, FULL, HAD>), grid, dim3(256), 0, st, x, dtype, nseq, n,    \
-                       q->d, q->d_pi, q->d_sp, cb, codes, norms, gammas);                                         \
-    break;                                                                                                          \
+  const _Float16* wt = reinterpret_cast<const _Float16*>(q->d_wide);
+  if (KS == 8 && !wt) return hipErrorNotSupported;
+#define TQ_ENC(BPV)                                                                                                  \
+  {                                                                                                                  \
+    const dim3 grid(static_cast<unsigned>(std::min<int64_t>(tiles, encode_tile_grid<KS, LK, MODE, BPV, FULL, HAD>()))); \
+    hipLaunchKernelGGL((encode_tile_kernel<KS, LK, MODE, BPV, FULL, HAD>), grid, dim3(64 * KS), 0, st, x, dtype, nseq, \
+                       n, q->d, q->d_pi, q->d_sp, wt, cb, codes, norms, gammas);                                     \
   }
   switch (cb.bp) {
-    TQ_ENC(1) TQ_ENC(2) TQ_ENC(3)
+    case 1: TQ_ENC(1) break;
+    case 2: TQ_ENC(2) break;
+    case 3: TQ_ENC(3) break;
     case 4:
       if constexpr (MODE != 0) {
-        const dim3 grid(static_cast<unsigned>(std::min<int64_t>(tiles, encode_tile_grid<LK, MODE, 4, FULL, HAD>())));
-        hipLaunchKernelGGL((encode_tile_kernel<4, LK, MODE, 4, FULL, HAD>), grid, dim3(256), 0, st, x, dtype, nseq, n,
-                           q->d, q->d_pi, q->d_sp, cb, codes, norms, gammas);
+        TQ_ENC(4)
         break;
       }
       return hipErrorNotSupported;
@@ -1266,19 +1373,34 @@ hipError_t launch_encode_tile_lk(const tq_quantizer* q, int mode, const void* x,
   constexpr bool F = LK != 0;
   if constexpr (F) {
     if (q->d == 128 && q->rotation == 1) {   // TQ_ROT_HADAMARD: the exact +-1 rotation operand
-      if (mode == 0) return launch_encode_tile_m<LK, 0, true, true>(q, x, dtype, nseq, n, codes, norms, gammas, st);
-      if (mode == 1) return launch_encode_tile_m<LK, 1, true, true>(q, x, dtype, nseq, n, codes, norms, gammas, st);
-      return launch_encode_tile_m<LK, 2, true, true>(q, x, dtype, nseq, n, codes, norms, gammas, st);
+      if (mode == 0) return launch_encode_tile_m<4, LK, 0, true, true>(q, x, dtype, nseq, n, codes, norms, gammas, st);
+      if (mode == 1) return launch_encode_tile_m<4, LK, 1, true, true>(q, x, dtype, nseq, n, codes, norms, gammas, st);
+      return launch_encode_tile_m<4, LK, 2, true, true>(q, x, dtype, nseq, n, codes, norms, gammas, st);
     }
   }
   if (F && q->d == 128) {
-    if (mode == 0) return launch_encode_tile_m<LK, 0, F>(q, x, dtype, nseq, n, codes, norms, gammas, st);
-    if (mode == 1) return launch_encode_tile_m<LK, 1, F>(q, x, dtype, nseq, n, codes, norms, gammas, st);
-    return launch_encode_tile_m<LK, 2, F>(q, x, dtype, nseq, n, codes, norms, gammas, st);
+    if (mode == 0) return launch_encode_tile_m<4, LK, 0, F>(q, x, dtype, nseq, n, codes, norms, gammas, st);
+    if (mode == 1) return launch_encode_tile_m<4, LK, 1, F>(q, x, dtype, nseq, n, codes, norms, gammas, st);
+    return launch_encode_tile_m<4, LK, 2, F>(q, x, dtype, nseq, n, codes, norms, gammas, st);
   }
-  if (mode == 0) return launch_encode_tile_m<LK, 0, false>(q, x, dtype, nseq, n, codes, norms, gammas, st);
-  if (mode == 1) return launch_encode_tile_m<LK, 1, false>(q, x, dtype, nseq, n, codes, norms, gammas, st);
-  return launch_encode_tile_m<LK, 2, false>(q, x, dtype, nseq, n, codes, norms, gammas, st);
+  if (mode == 0) return launch_encode_tile_m<4, LK, 0, false>(q, x, dtype, nseq, n, codes, norms, gammas, st);
+  if (mode == 1) return launch_encode_tile_m<4, LK, 1, false>(q, x, dtype, nseq, n, codes, norms, gammas, st);
+  return launch_encode_tile_m<4, LK, 2, false>(q, x, dtype, nseq, n, codes, norms, gammas, st);
+}
+
+// 128 < d <= 256 with rows in 16-byte runs: the eight-wave tile kernel
+// (operands streamed from the quantizer's fp16 tables)
+template <int LK>
+hipError_t launch_encode_wide_lk(const tq_quantizer* q, int mode, const void* x, int dtype, int64_t nseq, int64_t n,
+                                 uint32_t* codes, float* norms, float* gammas, hipStream_t st) {
+  if (q->d == 256) {
+    if (mode == 0) return launch_encode_tile_m<8, LK, 0, true>(q, x, dtype, nseq, n, codes, norms, gammas, st);
+    if (mode == 1) return launch_encode_tile_m<8, LK, 1, true>(q, x, dtype, nseq, n, codes, norms, gammas, st);
+    return launch_encode_tile_m<8, LK, 2, true>(q, x, dtype, nseq, n, codes, norms, gammas, st);
+  }
+  if (mode == 0) return launch_encode_tile_m<8, LK, 0, false>(q, x, dtype, nseq, n, codes, norms, gammas, st);
+  if (mode == 1) return launch_encode_tile_m<8, LK, 1, false>(q, x, dtype, nseq, n, codes, norms, gammas, st);
+  return launch_encode_tile_m<8, LK, 2, false>(q, x, dtype, nseq, n, codes, norms, gammas, st);
 }
 
 hipError_t launch_encode_tile(const tq_quantizer* q, int mode, const void* x, int dtype, int64_t nseq, int64_t n,
@@ -1313,6 +1435,10 @@ hipError_t launch_encode(const tq_quantizer* q, int mode, const void* x, int dty
   }
   if (q->d <= 128) {
     return launch_encode_tile(q, mode, x, dtype, nseq, n, codes, norms, gammas, st);
+  }
+  if (q->d <= kWideK && q->d_wide && (q->d * (dtype == 1 ? 2 : 4)) % 16 == 0) {
+    return dtype == 1 ? launch_encode_wide_lk<1>(q, mode, x, dtype, nseq, n, codes, norms, gammas, st)
+                      : launch_encode_wide_lk<2>(q, mode, x, dtype, nseq, n, codes, norms, gammas, st);
   }
   const int nt = (q->d + 15) / 16;
   switch (nt) {

@@ -45,6 +45,8 @@ struct tq_quantizer {
   float* d_sp = nullptr;              // [m][d]   S' = S Pi^T (acts on rotated residuals)
   float* d_qt = nullptr;              // [d][d+m] column k of Pi then of S (query transform, k-major)
   float* d_spt = nullptr;             // [d][m]   S' k-major (d_spt[k * m + r] = S'[r][k]), general-d encoder
+  uint16_t* d_wide = nullptr;         // 128 < d <= 256: fp16 [4][256][256] = Pi hi, Pi lo, S' hi, S' lo (x 2^8,
+                                      // zero past d), the eight-wave encoder's operands
   int key_mode = 0;                   // key layout the scoring calls read: TQ_PROD (0) or TQ_MSE_KEYS (2)
 };
 
