@@ -1,4 +1,5 @@
-// Decode attention over the packed cache, and top-k search over packed keys.
+// Decode attention over the packed cache: chunking, workspace, the merge
+// kernel and the launch sequence (the chunk kernel is in tq_attend_impl.h).
 //
 // Attention (decode step, one query per head): logits from the packed keys as
 // in tq_scores (a2a-mcp.org "什麼是TurboQuant？", how-to-implement: fused kernel
@@ -19,9 +20,10 @@
 //             on the f8f6f4 MFMA: tokens are the contraction dimension, the
 //             32-token value words are the fp4 B operand, c[idx] is written in
 //             the +-1 basis of the index bits (Walsh terms), each wave owns
-//             32 output coordinates.
+//             d/64 tiles of 16 output coordinates (32 coordinates at d = 128).
 // A merge kernel combines the chunks, adds the exact bf16 tail, applies
-// Pi_v^T once per query and divides by the softmax sum.
+// Pi_v^T once per query and divides by the softmax sum.  Head dimensions 64,
+// 96, 128 and 256 each have their chunk-kernel instantiations.
 #include "tq_attend_impl.h"
 
 namespace tq {
