@@ -46,9 +46,10 @@ def _make_segments(k, v, bounds, specs):
     mode, value bits) per segment.  Value quantizers share seed 1 (one Pi);
     key quantizers seed 0."""
     segs, host = [], []
+    d = k.shape[-1]
     for (a, b), (kb, km, vb) in zip(bounds, specs):
-        gk, ok = _pair(128, kb, 0, km)
-        gv, ov = _pair(128, vb, 1)
+        gk, ok = _pair(d, kb, 0, km)
+        gv, ov = _pair(d, vb, 1)
         kc, kn, kg = tq.tq_encode(gk, km, k[:, a:b].contiguous())
         vc, vn, _ = tq.tq_encode(gv, tq.TQ_MSE, v[:, a:b].contiguous())
         segs.append(tq.Segment(gk, gv, kc, kn, kg, vc, vn, b - a))
@@ -56,22 +57,22 @@ def _make_segments(k, v, bounds, specs):
         host.append((ok, ov, km, kb, vb, P.to_u32(kc), kn.cpu().numpy().astype(np.float64),
                      None if kg is None else kg.cpu().numpy().astype(np.float64), P.to_u32(vc),
                      vn.cpu().numpy().astype(np.float64), n,
-                     gk.code_words(km, 1, n) if n else 0, gv.code_words(tq.TQ_MSE, 1, n) if n else 0))
+                     gk.code_words(km, 1, n) if n else 0, gv.code_words(tq.TQ_MSE, 1, n) if n else 0, d))
     return segs, host
 
 
 def _oracle_segments(host, s):
     out = []
-    for (ok, ov, km, kb, vb, kw, kn, kg, vw, vn, n, per, perv) in host:
+    for (ok, ov, km, kb, vb, kw, kn, kg, vw, vn, n, per, perv, d) in host:
         if n == 0:
             continue
         sl = slice(s * n, (s + 1) * n)
         if km == tq.TQ_PROD:
-            ki, kbits = o.unpack_prod(kw[s * per:(s + 1) * per].reshape(n, -1), kb - 1, 128)
+            ki, kbits = o.unpack_prod(kw[s * per:(s + 1) * per].reshape(n, -1), kb - 1, d)
             kgs = kg[sl]
         else:
-            ki, kbits, kgs = o.unpack_mse_keys(kw[s * per:(s + 1) * per].reshape(n, -1), kb, 128), None, None
-        vi = o.unpack_mse(vw[s * perv:(s + 1) * perv], n, vb, 128)
+            ki, kbits, kgs = o.unpack_mse_keys(kw[s * per:(s + 1) * per].reshape(n, -1), kb, d), None, None
+        vi = o.unpack_mse(vw[s * perv:(s + 1) * perv], n, vb, d)
         out.append((ok, ov, ki, kbits, kn[sl], kgs, vi, vn[sl]))
     return out
 
@@ -122,6 +123,23 @@ def test_segments_against_oracle(B, Hkv, Hq, N, tail, bounds, specs):
     out = tq.tq_attend_decode_segments(segs, q, Hkv, kt, vt).cpu().numpy()
     w = _check_all(out, host, a["q"].astype(np.float64), a["k"].reshape(B * Hkv, N, 128).astype(np.float64),
                    a["v"].reshape(B * Hkv, N, 128).astype(np.float64), B, Hkv, Hq, tail)
+    print("worst relative error", w)
+
+
+@pytest.mark.parametrize("d", [64, 96, 256])
+def test_segments_other_head_dims(d):
+    """Two segments (2-bit and 4-bit) and a bf16 tail at head dimensions other
+    than 128: each segment's chunk-kernel launch and the merge at d."""
+    print(f"case: segments d={d} B=1 Hkv=4 Hq=16 N=6000 tail=40", flush=True)
+    B, Hkv, Hq, N, tail = 1, 4, 16, 6000, 40
+    a = W._gqa_tensors(np.random.default_rng(d), B, Hkv, Hq, N, d)
+    k, v, q = _bf16(a["k_bf16"]).view(B * Hkv, N, d), _bf16(a["v_bf16"]).view(B * Hkv, N, d), _bf16(a["q_bf16"])
+    segs, host = _make_segments(k, v, [(0, 3960), (3960, N - tail)], [(2, tq.TQ_PROD, 2), (4, tq.TQ_PROD, 4)])
+    kt = k[:, N - tail:].contiguous().view(B, Hkv, tail, d)
+    vt = v[:, N - tail:].contiguous().view(B, Hkv, tail, d)
+    out = tq.tq_attend_decode_segments(segs, q, Hkv, kt, vt).cpu().numpy()
+    w = _check_all(out, host, a["q"].astype(np.float64), a["k"].reshape(B * Hkv, N, d).astype(np.float64),
+                   a["v"].reshape(B * Hkv, N, d).astype(np.float64), B, Hkv, Hq, tail)
     print("worst relative error", w)
 
 

@@ -30,26 +30,26 @@ def _bf16(u16):
     return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).to(_dev()).view(torch.bfloat16)
 
 
-def _case(B, Hkv, Hq, N, tail, bits, seed):
+def _case(B, Hkv, Hq, N, tail, bits, seed, d=128):
     rng = np.random.default_rng(seed)
-    a = W._gqa_tensors(rng, B, Hkv, Hq, N, 128)
-    k = _bf16(a["k_bf16"]).view(B * Hkv, N, 128)
-    v = _bf16(a["v_bf16"]).view(B * Hkv, N, 128)
+    a = W._gqa_tensors(rng, B, Hkv, Hq, N, d)
+    k = _bf16(a["k_bf16"]).view(B * Hkv, N, d)
+    v = _bf16(a["v_bf16"]).view(B * Hkv, N, d)
     q = _bf16(a["q_bf16"])
     n_comp = N - tail
-    kq = tq.Quantizer(128, bits, 0)
-    vq = tq.Quantizer(128, bits, 1)
+    kq = tq.Quantizer(d, bits, 0)
+    vq = tq.Quantizer(d, bits, 1)
     kc, kn, kg = tq.tq_encode(kq, tq.TQ_PROD, k[:, :n_comp].contiguous())
     vc, vn, _ = tq.tq_encode(vq, tq.TQ_MSE, v[:, :n_comp].contiguous())
-    kt = k[:, n_comp:].contiguous().view(B, Hkv, tail, 128) if tail else None
-    vt = v[:, n_comp:].contiguous().view(B, Hkv, tail, 128) if tail else None
+    kt = k[:, n_comp:].contiguous().view(B, Hkv, tail, d) if tail else None
+    vt = v[:, n_comp:].contiguous().view(B, Hkv, tail, d) if tail else None
     return dict(B=B, Hkv=Hkv, Hq=Hq, n_comp=n_comp, tail=tail, bits=bits, kq=kq, vq=vq, q=q, kc=kc, kn=kn, kg=kg,
-                vc=vc, vn=vn, kt=kt, vt=vt, k=k, v=v)
+                vc=vc, vn=vn, kt=kt, vt=vt, k=k, v=v, d=d)
 
 
 def _oracle_check(c, out, groups):
-    bits, n_comp, G = c["bits"], c["n_comp"], c["Hq"] // c["Hkv"]
-    ok, ov = o.Quantizer(128, bits, 0), o.Quantizer(128, bits, 1)
+    bits, n_comp, G, d = c["bits"], c["n_comp"], c["Hq"] // c["Hkv"], c["d"]
+    ok, ov = o.Quantizer(d, bits, 0), o.Quantizer(d, bits, 1)
     kw, vw = P.to_u32(c["kc"]), P.to_u32(c["vc"])
     kn, kg, vn = (t.cpu().numpy().astype(np.float64) for t in (c["kn"], c["kg"], c["vn"]))
     qs = c["q"].float().cpu().numpy().astype(np.float64)
@@ -57,8 +57,8 @@ def _oracle_check(c, out, groups):
     perk, perv = c["kq"].code_words(tq.TQ_PROD, 1, n_comp), c["vq"].code_words(tq.TQ_MSE, 1, n_comp)
     for (b, h) in groups:
         s = b * c["Hkv"] + h
-        ki, kb = o.unpack_prod(kw[s * perk:(s + 1) * perk].reshape(n_comp, -1), bits - 1, 128)
-        vi = o.unpack_mse(vw[s * perv:(s + 1) * perv], n_comp, bits, 128)
+        ki, kb = o.unpack_prod(kw[s * perk:(s + 1) * perk].reshape(n_comp, -1), bits - 1, d)
+        vi = o.unpack_mse(vw[s * perv:(s + 1) * perv], n_comp, bits, d)
         sl = slice(s * n_comp, (s + 1) * n_comp)
         tails = (kf[s, n_comp:], vf[s, n_comp:]) if c["tail"] else (None, None)
         ref = o.attend(ok, ov, qs[b, h * G:(h + 1) * G], ki, kb, kn[sl], kg[sl], vi, vn[sl], *tails)
@@ -91,6 +91,11 @@ def test_noalloc_matches_attend_decode_twice_then_smaller():
     ref2, out2 = _pair_of_calls(small)
     assert torch.equal(ref2, out2), float((ref2 - out2).abs().max())
     _oracle_check(small, out2.cpu().numpy(), [(0, 0), (0, 1)])
+    print("case: noalloc call 3 (head dimension 256) B=1 Hkv=4 Hq=16 N=3000 tail=20 3-bit", flush=True)
+    wide = _case(1, 4, 16, 3000, 20, 3, seed=103, d=256)
+    ref3, out3 = _pair_of_calls(wide)
+    assert torch.equal(ref3, out3), float((ref3 - out3).abs().max())
+    _oracle_check(wide, out3.cpu().numpy(), [(0, 0), (0, 3)])
 
 
 def test_noalloc_refuses_shapes_beyond_its_scratch():
