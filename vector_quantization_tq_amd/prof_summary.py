@@ -24,8 +24,38 @@ import re
 import sys
 
 
+def _demangle_nested(s: str) -> str:
+    """Nested name and integer / bool template arguments of an Itanium-mangled
+    kernel name.  rocprofv3 leaves a name mangled when its demangler stops on a
+    parameter type (``DF16_``, _Float16); the parameter list is dropped here."""
+    i, parts = 3, []
+    while i < len(s) and s[i].isdigit():
+        j = i
+        while s[j].isdigit():
+            j += 1
+        n = int(s[i:j])
+        ident = s[j:j + n]
+        i = j + n
+        parts.append("anon" if ident.startswith("_GLOBAL__N") else ident)
+    name = "::".join(parts)
+    if i < len(s) and s[i] == "I":
+        i += 1
+        args = []
+        while True:
+            m = re.match(r"L([ibjlm])(n?\d+)E", s[i:])
+            if not m:
+                break
+            v = m.group(2).replace("n", "-")
+            args.append(("true" if v == "1" else "false") if m.group(1) == "b" else v)
+            i += m.end()
+        name += "<" + ", ".join(args) + ">"
+    return name
+
+
 def short_name(name: str) -> str:
     """Kernel name without its argument list and return type."""
+    if name.startswith("_ZN"):
+        return _demangle_nested(name)
     n = name.replace("(anonymous namespace)", "anon")
     depth = 0
     for i, ch in enumerate(n):
@@ -65,7 +95,7 @@ def counter_means(path, counter):
 
 
 def pick(means, pattern):
-    hits = [(k, v) for k, v in means.items() if pattern in k]
+    hits = [(k, v) for k, v in means.items() if pattern in k or pattern in short_name(k)]
     if len(hits) != 1:
         raise SystemExit(f"pattern {pattern!r} matches {len(hits)} kernels: {[short_name(k) for k, _ in hits]}")
     return hits[0]
