@@ -106,6 +106,31 @@ def test_topk_ties_go_to_lower_index():
     _topk_case(128, 3, 1, 1, 8, 3000, 10, keys=keys, seed=12)
 
 
+def test_topk_ties_across_slices():
+    """Keys repeat every 300 positions over 60000 keys, so equal best scores
+    sit in many key slices: slices that see them late prune against a bound
+    other slices published, and ties at that bound must survive (the lowest
+    index wins)."""
+    print("case: topk ties across slices d=128 bits=3 n=60000 k=10", flush=True)
+    rng = np.random.default_rng(21)
+    base = rng.standard_normal((300, 128)).astype(np.float32)
+    keys = np.concatenate([base] * 200)[None]
+    _topk_case(128, 3, 1, 1, 8, 60000, 10, keys=keys, seed=22)
+
+
+@pytest.mark.parametrize("order", ["descending", "ascending"])
+def test_topk_norm_ordered_keys(order):
+    """Key norms sorted along the sequence: the best keys sit in the first
+    (or last) slices, so the shared bound is high from the start (or only at
+    the end) of the scan."""
+    print(f"case: topk norm-ordered keys ({order}) d=200 bits=4 n=50000 k=10", flush=True)
+    rng = np.random.default_rng(31)
+    keys = rng.standard_normal((1, 50000, 200)).astype(np.float32)
+    scale = np.geomspace(8.0, 0.125, 50000) if order == "descending" else np.geomspace(0.125, 8.0, 50000)
+    keys *= scale[None, :, None].astype(np.float32)
+    _topk_case(200, 4, 1, 1, 12, 50000, 10, keys=keys, seed=32)
+
+
 def test_topk_bf16_queries():
     print("case: topk bf16 d=128 bits=4 n=2500 k=10", flush=True)
     _topk_case(128, 4, 1, 2, 10, 2500, 10, bf16=True, seed=5)

@@ -213,6 +213,27 @@ __global__ void __launch_bounds__(256, (KK <= 16 && ((1 << (BP - 1)) + QJL) * ((
   // insertion rounds as the fullest queue holds.  The bounds a queued key
   // passed only rise until the lists take it, so the filter stays valid.
   int qn = 0;
+  // A key can only enter the query's top k if it ranks at least level with
+  // the query's current k-th best.  The largest of the 16 lanes' own k-th
+  // best scores is a lower bound of that (the lane alone holds k scores at
+  // least as large), so keys below it are skipped without touching the
+  // lists: insertions become rare.  A second bound: each of the 16 lanes
+  // holds j + 1 scores at least its entry j, so the smallest entry j over the
+  // lanes is at most the query's k-th best when 16 (j + 1) >= k.  With
+  // j = (k - 1) / 16 this takes the lanes' best scores, which rank near the
+  // query's top k (the first bound, a single lane's k-th best, ranks near its
+  // 16 k-th).  The bound changes only when the lists do, so it is refreshed
+  // after each bulk insertion (wave-uniform: the row reductions need every
+  // lane).
+  float tau = -INFINITY;
+  auto refresh = [&]() {
+    float kth = ls[0];
+#pragma unroll
+    for (int k = 1; k < KK; ++k)
+      if (k == topk - 1) kth = ls[k];
+    const float topj = (KK > 16 && topk > 16) ? ls[1] : ls[0];
+    tau = fmaxf(row_max16(kth), row_min16(topj));
+  };
   auto drain = [&]() {
 #pragma unroll 1
     for (int e = 0; e < kQueue; ++e) {
@@ -223,6 +244,7 @@ __global__ void __launch_bounds__(256, (KK <= 16 && ((1 << (BP - 1)) + QJL) * ((
       }
     }
     qn = 0;
+    refresh();
   };
 
   const uint32_t* cbase = codes + seq * n * WPK;
@@ -266,22 +288,6 @@ __global__ void __launch_bounds__(256, (KK <= 16 && ((1 << (BP - 1)) + QJL) * ((
     __syncthreads();                                          // ... and every wave's; slot of bi-1 free
     if (bi + P < nbat) issue(bi + P, slot == 0 ? NS - 1 : slot - 1);
     if (active) {
-      // A key can only enter the query's top k if it ranks at least level with
-      // the query's current k-th best.  The largest of the 16 lanes' own k-th
-      // best scores is a lower bound of that (the lane alone holds k scores at
-      // least as large), so keys below it are skipped without touching the
-      // lists: insertions become rare.
-      float kth = ls[0];
-#pragma unroll
-      for (int k = 1; k < KK; ++k)
-        if (k == topk - 1) kth = ls[k];
-      // A second bound: each of the 16 lanes holds j + 1 scores at least its
-      // entry j, so the smallest entry j over the lanes is at most the query's
-      // k-th best when 16 (j + 1) >= k.  With j = (k - 1) / 16 this takes the
-      // lanes' best scores, which rank near the query's top k (the first
-      // bound, a single lane's k-th best, ranks near its 16 k-th).
-      const float topj = (KK > 16 && topk > 16) ? ls[1] : ls[0];
-      const float tau = fmaxf(row_max16(kth), row_min16(topj));
       const uint32_t* kw = buf[slot];
       const float* kn = reinterpret_cast<const float*>(kw + BW);
       const int64_t k0 = k_begin + static_cast<int64_t>(bi) * kTopBlockKeys;
@@ -292,12 +298,14 @@ __global__ void __launch_bounds__(256, (KK <= 16 && ((1 << (BP - 1)) + QJL) * ((
         v4f aM = {0.f, 0.f, 0.f, 0.f}, aQ = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < C; ++c) {
+          // groups past the key's last one (gg >= GW) read the next key's
+          // words or the batch's norms, inside the slot: their fp4 values
+          // are finite and meet query coordinates >= 32 GW >= d, which the
+          // query operand holds as 0, so they add exactly 0
           const int gg = 4 * c + g;
           uint32_t w[5] = {0u, 0u, 0u, 0u, 0u};
-          if (gg < GW) {
 #pragma unroll
-            for (int p = 0; p < W; ++p) w[p] = kw[(kk * GW + gg) * W + p];
-          }
+          for (int p = 0; p < W; ++p) w[p] = kw[(kk * GW + gg) * W + p];
 #pragma unroll
           for (int t = 0; t < (1 << (BP - 1)); ++t)
             aM = mfma_fp8_fp4(A[t][c], bits_to_fp4(walsh_word<BP>(w, t)), aM);
