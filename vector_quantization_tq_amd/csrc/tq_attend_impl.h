@@ -245,8 +245,8 @@ __device__ __forceinline__ void attend_chunk_body(
         }
 #pragma unroll
         for (int t = 0; t < (1 << (BPK - 1)); ++t)
-          aM = mfma_fp8_fp4(AK[t][c], bits_to_fp4(walsh_word<BPK>(w, t)), aM);
-        if constexpr (QJL) aQ = mfma_fp8_fp4(AK[TK - 1][c], bits_to_fp4(w[BPK]), aQ);
+          aM = mfma_fp8_fp4(AK[t][c], key_bits_to_fp4(walsh_word<BPK>(w, t)), aM);
+        if constexpr (QJL) aQ = mfma_fp8_fp4(AK[TK - 1][c], key_bits_to_fp4(w[BPK]), aQ);
       }
       pin(aM);
       const float mse = fmaf(aM[0], cs[2], fmaf(aM[1], cs[3], fmaf(aM[2], cs[4], fmaf(aM[3], cs[5], cs[0]))));

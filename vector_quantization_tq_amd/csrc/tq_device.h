@@ -30,6 +30,22 @@ __device__ __forceinline__ v8i bits_to_fp4(uint32_t w) {
   return b;
 }
 
+// The same for key bits (logits, top-k and attention logits), one
+// instruction cheaper: dword 3 keeps bit 4i+3 where it is, as the sign of
+// 1.0 (nibble 0x2 or 0xA), so that slot's value is 1 - 2 bit.  The query
+// side takes the slot's A operand negated and halved and leaves those
+// coordinates out of its constant term (key_slot_value).
+__device__ __forceinline__ v8i key_bits_to_fp4(uint32_t w) {
+  // the 1.0 pattern lives in a vector register (an empty asm hides its
+  // value), so that mask-and-or is one v_and_or_b32: with both constants
+  // scalar it would break the one-scalar-operand limit and split in two
+  uint32_t one = 0x22222222u;
+  asm("" : "+v"(one));
+  v8i b = {static_cast<int>(w & 0x11111111u), static_cast<int>(w & 0x22222222u), static_cast<int>(w & 0x44444444u),
+           static_cast<int>((w & 0x88888888u) | one), 0, 0, 0, 0};
+  return b;
+}
+
 // The codebook of b' index bits is symmetric, so its centroids expand over
 // the odd Walsh functions of the bits: c[idx] = sum_t coef_t (2 x_t - 1) with
 // x_t the XOR of the index bits in mask t.  Word t of a packed group is that
@@ -117,6 +133,13 @@ __device__ __forceinline__ int ilogb_pos(float x) { return __builtin_amdgcn_frex
 
 // value of a set bit at element slot s = (K % 32) / 8
 __host__ __device__ __forceinline__ float fp4_slot_value(int s) { return s == 0 ? 0.5f : (s == 1 ? 1.f : 2.f); }
+// The divisor of a key-side A operand element at slot s: a set bit gives
+// 0.5 / 1 / 2 at slots 0-2; slot 3 gives 1 - 2 bit, so with the element
+// divided by -2 its product is (value) bit - (value) / 2, the constant half
+// of the Walsh term's 2 bit - 1 included.
+__host__ __device__ __forceinline__ float key_slot_value(int s) { return s == 3 ? -2.f : fp4_slot_value(s); }
+// coordinate j of a 32-coordinate word sits in slot j % 4 (bit 4i + s)
+__host__ __device__ __forceinline__ bool key_slot3_coord(int j) { return (j & 3) == 3; }
 
 // bit position inside the 32-bit word for MFMA K index within a 128 chunk
 __host__ __device__ __forceinline__ int k_to_bit(int k) { return 4 * (k & 7) + ((k & 31) >> 3); }

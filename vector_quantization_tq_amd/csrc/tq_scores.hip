@@ -13,7 +13,10 @@
 //   <s, sigma>   = <2 s, b_qjl> - sum(s),
 // where every b is a 0/1 vector read straight out of the packed words.  The
 // <value, 0/1 bits> products run on the 16x16x128 f8f6f4 MFMA: the key bits
-// are the fp4 B operand (a mask per nibble, no table lookup), the query side
+// are the fp4 B operand (a mask per nibble, no table lookup; the fourth of
+// every 4 coordinates is read as 1 - 2 bit, its A element negated and halved,
+// so that its half of the -1 rides in the MFMA and the constants above sum
+// the other coordinates only), the query side
 // is the fp8 A operand split into 4 limbs (rows), each limb carrying the
 // next 4 bits of the value with its own exponent, so the sum over limbs is
 // float-accurate per coordinate.  (The matrix core adds the products of a
@@ -145,14 +148,16 @@ __device__ __forceinline__ void query_prep_body(const void* __restrict__ queries
   if (valid) {
     for (int o = tid; o < dm; o += blockDim.x) {
       const float a = (pw[o] + pw[dm + o]) + (pw[2 * dm + o] + pw[3 * dm + o]);
+      // the constant terms sum the coordinates outside slot 3 (the MFMA's
+      // 1 - 2 bit slot carries its own half)
       if (o < d) {
         qh[o] = a;
         lmax_h = fmaxf(lmax_h, fabsf(a));
-        lsum_h += a;
+        if (!key_slot3_coord(o)) lsum_h += a;
       } else {
         sq[o - d] = a;
         lmax_s = fmaxf(lmax_s, fabsf(a));
-        lsum_s += a;
+        if (!key_slot3_coord(o - d)) lsum_s += a;
       }
     }
   }
@@ -203,7 +208,7 @@ __device__ __forceinline__ void query_prep_body(const void* __restrict__ queries
     float x = 0.f;
     if (valid && coord < (is_q ? m : d)) {
       const float coef = is_q ? alpha2 : 2.f * cb.coef[t];
-      const float v = coef * (is_q ? sq[coord] : qh[coord]) / fp4_slot_value((k & 31) >> 3);
+      const float v = coef * (is_q ? sq[coord] : qh[coord]) / key_slot_value((k & 31) >> 3);
       x = ldexpf(v, is_q ? E_q : E_m);
     }
     uint8_t* dst = base + (static_cast<int64_t>(t) * C + c) * tile_bytes + (4 * qi + 16 * g) * 32 + e;
@@ -401,8 +406,8 @@ __global__ void __launch_bounds__(256) scores_kernel(const uint32_t* __restrict_
         }
 #pragma unroll
         for (int t = 0; t < (1 << (BP - 1)); ++t)
-          accM = mfma_fp8_fp4(A[t][c], bits_to_fp4(walsh_word<BP>(w, t)), accM);
-        if constexpr (QJL) accQ = mfma_fp8_fp4(A[T - 1][c], bits_to_fp4(w[BP]), accQ);
+          accM = mfma_fp8_fp4(A[t][c], key_bits_to_fp4(walsh_word<BP>(w, t)), accM);
+        if constexpr (QJL) accQ = mfma_fp8_fp4(A[T - 1][c], key_bits_to_fp4(w[BP]), accQ);
       }
       pin(accM);
       const float mse = fmaf(accM[0], cs[2], fmaf(accM[1], cs[3], fmaf(accM[2], cs[4], fmaf(accM[3], cs[5], cs[0]))));

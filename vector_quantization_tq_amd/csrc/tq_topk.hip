@@ -308,8 +308,8 @@ __global__ void __launch_bounds__(256, (KK <= 16 && ((1 << (BP - 1)) + QJL) * ((
           for (int p = 0; p < W; ++p) w[p] = kw[(kk * GW + gg) * W + p];
 #pragma unroll
           for (int t = 0; t < (1 << (BP - 1)); ++t)
-            aM = mfma_fp8_fp4(A[t][c], bits_to_fp4(walsh_word<BP>(w, t)), aM);
-          if constexpr (QJL) aQ = mfma_fp8_fp4(A[T - 1][c], bits_to_fp4(w[BP]), aQ);
+            aM = mfma_fp8_fp4(A[t][c], key_bits_to_fp4(walsh_word<BP>(w, t)), aM);
+          if constexpr (QJL) aQ = mfma_fp8_fp4(A[T - 1][c], key_bits_to_fp4(w[BP]), aQ);
         }
         pin(aM);
         const float mse = fmaf(aM[0], cs[2], fmaf(aM[1], cs[3], fmaf(aM[2], cs[4], fmaf(aM[3], cs[5], cs[0]))));
