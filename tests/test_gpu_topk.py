@@ -131,6 +131,28 @@ def test_topk_norm_ordered_keys(order):
     _topk_case(200, 4, 1, 1, 12, 50000, 10, keys=keys, seed=32)
 
 
+@pytest.mark.parametrize("k", [1, 10, 12])
+def test_topk_identical_keys(k):
+    """Every key the same vector: all scores tie, so no key slice can bound
+    what it leaves out below the k-th best and the search falls back to the
+    exact scan for every query; the k lowest indices must come back."""
+    print(f"case: topk identical keys d=200 bits=4 n=5000 k={k}", flush=True)
+    rng = np.random.default_rng(41)
+    keys = np.repeat(rng.standard_normal((1, 1, 200)).astype(np.float32), 5000, axis=1)
+    _topk_case(200, 4, 1, 1, 9, 5000, k, keys=keys, seed=42)
+
+
+def test_topk_block_of_best_keys():
+    """A run of 40 copies of one strong key inside random keys: the slice
+    holding the run cannot certify its k-th best (more than k equal bounds),
+    other queries may; either way the lowest-indexed copies win."""
+    print("case: topk block of best keys d=200 bits=4 n=30000 k=10", flush=True)
+    rng = np.random.default_rng(51)
+    keys = rng.standard_normal((1, 30000, 200)).astype(np.float32)
+    keys[0, 12000:12040] = 6.0 * rng.standard_normal(200).astype(np.float32)
+    _topk_case(200, 4, 1, 1, 12, 30000, 10, keys=keys, seed=52)
+
+
 def test_topk_bf16_queries():
     print("case: topk bf16 d=128 bits=4 n=2500 k=10", flush=True)
     _topk_case(128, 4, 1, 2, 10, 2500, 10, bf16=True, seed=5)

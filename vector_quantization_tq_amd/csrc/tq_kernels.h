@@ -27,8 +27,9 @@ struct PrepSet {
 };
 hipError_t launch_query_prep_multi(const tq_quantizer* const* qs, void* const* ws, int nq, const void* queries,
                                    int q_dtype, int B, int Hq, int Hkv, hipStream_t st);
+// bound: also the limb bounds the bounded top-k scan reads (constants 10, 11)
 hipError_t launch_query_prep_ws(const tq_quantizer* q, const void* queries, int q_dtype, int B, int Hq, int Hkv,
-                                void* ws, hipStream_t st);
+                                void* ws, hipStream_t st, bool bound = false);
 hipError_t launch_scores_scan(const tq_quantizer* q, int B, int Hq, int Hkv, const uint32_t* codes, const float* norms,
                               const float* gammas, int64_t n, float* out, const void* ws, hipStream_t st);
 hipError_t launch_scores(const tq_quantizer* q, const void* queries, int q_dtype, int B, int Hq, int Hkv,

@@ -39,7 +39,11 @@ namespace tq {
 // The terms are the Walsh terms of the key codebook, then (prod keys) the
 // QJL term; MSE-only keys have no QJL term.
 // ---------------------------------------------------------------------------
-template <bool QBF16, bool ONE>
+// BOUND (the bounded top-k scan): also writes, in constants 10 and 11, bounds
+// of what limbs 2 and 3 add to the MSE and QJL sums of any key, so that a
+// scan over limbs 0 and 1 alone brackets the full score
+// (n (sum_k<2 sM_k C_M,k + cM +- E_M) + gamma (... +- E_Q)).
+template <bool QBF16, bool ONE, bool BOUND = false>
 __device__ __forceinline__ void query_prep_body(const void* __restrict__ queries, int q_dtype, int Hq, int Hkv, int G,
                                                 int RT, int d, int m, const float* __restrict__ qt, const Codebook& cb,
                                                 int qjl, int C, uint8_t* __restrict__ wsA, float* __restrict__ wsC) {
@@ -199,6 +203,10 @@ __device__ __forceinline__ void query_prep_body(const void* __restrict__ queries
   // residual is exact in float.
   const int64_t tile_bytes = 64 * 32;
   uint8_t* base = wsA + static_cast<int64_t>(gy) * T * C * tile_bytes;
+  // BOUND: per thread, sum over its elements of |limb value| x the largest
+  // |B| of the element's slot (0.5, 1, 2, 1), limbs 2-3 and all limbs, in
+  // the scaled units of limb 0 (each limb 16x finer than the one before)
+  float lo_m = 0.f, lo_q = 0.f, all_m = 0.f, all_q = 0.f;
   for (int idx = tid; idx < T * C * 128; idx += blockDim.x) {
     const int t = idx / (C * 128), c = (idx >> 7) - t * C, ge = idx & 127;
     const int g = ge >> 5, e = ge & 31;
@@ -212,12 +220,59 @@ __device__ __forceinline__ void query_prep_body(const void* __restrict__ queries
       x = ldexpf(v, is_q ? E_q : E_m);
     }
     uint8_t* dst = base + (static_cast<int64_t>(t) * C + c) * tile_bytes + (4 * qi + 16 * g) * 32 + e;
+    float lo = 0.f, all = 0.f;
 #pragma unroll
     for (int limb = 0; limb < 4; ++limb) {
       const uint32_t byte = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.f, 0, false)) & 0xFFu;
       dst[limb * 32] = static_cast<uint8_t>(byte);
-      x = (x - __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(byte), 0)) * 16.f;
+      const float lv = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(byte), 0);
+      x = (x - lv) * 16.f;
+      if constexpr (BOUND) {
+        const float a = fabsf(lv) * ldexpf(1.f, -4 * limb);
+        all += a;
+        if (limb >= 2) lo += a;
+      }
     }
+    if constexpr (BOUND) {
+      const int sl = (k & 31) >> 3;
+      const float bm = sl == 0 ? 0.5f : (sl == 2 ? 2.f : 1.f);
+      if (is_q) {
+        lo_q = fmaf(lo, bm, lo_q);
+        all_q = fmaf(all, bm, all_q);
+      } else {
+        lo_m = fmaf(lo, bm, lo_m);
+        all_m = fmaf(all, bm, all_m);
+      }
+    }
+  }
+  float e_m = 0.f, e_q = 0.f;
+  if constexpr (BOUND) {
+    for (int off = 32; off > 0; off >>= 1) {
+      lo_m += __shfl_xor(lo_m, off);
+      lo_q += __shfl_xor(lo_q, off);
+      all_m += __shfl_xor(all_m, off);
+      all_q += __shfl_xor(all_q, off);
+    }
+    __shared__ float bred[4][4];
+    if ((tid & 63) == 0) {
+      bred[tid >> 6][0] = lo_m;
+      bred[tid >> 6][1] = lo_q;
+      bred[tid >> 6][2] = all_m;
+      bred[tid >> 6][3] = all_q;
+    }
+    __syncthreads();
+    float s4[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w)
+      for (int j = 0; j < 4; ++j) s4[j] += bred[w][j];
+    // In real units (limb 0's scale 2^-E): the limbs 2-3 part of an MSE (QJL)
+    // sum is at most lo (the matrix core's own rounding only shrinks the
+    // products it truncates; 1% covers its aligned adds), and the float
+    // evaluation of either bracket differs from the full chain's by a few
+    // roundings of magnitudes below |constant| + all.
+    const float cm = valid ? fabsf(cb.coef_sum * sum_h) : 0.f;
+    const float cq = valid && qjl ? fabsf(0.5f * alpha2 * sum_s) : 0.f;
+    e_m = 1.01f * ldexpf(s4[0], -E_m) + 0x1p-17f * (cm + ldexpf(s4[2], -E_m));
+    e_q = 1.01f * ldexpf(s4[1], -E_q) + 0x1p-17f * (cq + ldexpf(s4[3], -E_q));
   }
   if (tid < 16) {
     float val = 0.f;
@@ -226,17 +281,19 @@ __device__ __forceinline__ void query_prep_body(const void* __restrict__ queries
       else if (tid == 1) val = qjl ? -0.5f * alpha2 * sum_s : 0.f;
       else if (tid < 6) val = ldexpf(1.f, -E_m - 4 * (tid - 2));
       else if (tid < 10) val = ldexpf(1.f, -E_q - 4 * (tid - 6));
+      else if (tid == 10) val = e_m;
+      else if (tid == 11) val = e_q;
     }
     wsC[(static_cast<int64_t>(gy) * 4 + qi) * 16 + tid] = val;
   }
 }
 
-template <bool QBF16, bool ONE>
+template <bool QBF16, bool ONE, bool BOUND>
 __global__ void __launch_bounds__(256) query_prep_kernel(const void* __restrict__ queries, int q_dtype, int Hq, int Hkv,
                                                          int G, int RT, int d, int m, const float* __restrict__ qt,
                                                          Codebook cb, int qjl, int C, uint8_t* __restrict__ wsA,
                                                          float* __restrict__ wsC) {
-  query_prep_body<QBF16, ONE>(queries, q_dtype, Hq, Hkv, G, RT, d, m, qt, cb, qjl, C, wsA, wsC);
+  query_prep_body<QBF16, ONE, BOUND>(queries, q_dtype, Hq, Hkv, G, RT, d, m, qt, cb, qjl, C, wsA, wsC);
 }
 
 // The query operands of several quantizers (the segments of one cache) in
@@ -454,7 +511,7 @@ int64_t scores_ws_bytes(const tq_quantizer* q, int B, int Hq, int Hkv) {
 }
 
 hipError_t launch_query_prep(const tq_quantizer* q, const void* queries, int q_dtype, int B, int Hq, int Hkv,
-                             uint8_t* wsA, float* wsC, hipStream_t st) {
+                             uint8_t* wsA, float* wsC, hipStream_t st, bool bound) {
   const int G = Hq / Hkv;
   const int RT = (G + 3) / 4;
   const int C = (q->d + 127) / 128;
@@ -462,13 +519,21 @@ hipError_t launch_query_prep(const tq_quantizer* q, const void* queries, int q_d
   dim3 grid(static_cast<unsigned>(static_cast<int64_t>(B) * Hkv * RT * 4));
   const int dm = q->d + q->m;
   const bool one = dm % 4 == 0 && dm <= 256 && q->d <= 128;
-#define TQ_QP(BF, ONE)                                                                                              \
-  hipLaunchKernelGGL((query_prep_kernel<BF, ONE>), grid, dim3(256), lds, st, queries, q_dtype, Hq, Hkv, G, RT, q->d, \
+#define TQ_QP(BF, ONE, BD)                                                                                            \
+  hipLaunchKernelGGL((query_prep_kernel<BF, ONE, BD>), grid, dim3(256), lds, st, queries, q_dtype, Hq, Hkv, G, RT, q->d, \
                      q->m, q->d_qt, key_codebook(q), key_qjl(q) ? 1 : 0, C, wsA, wsC)
-  if (q_dtype == 1) {
-    if (one) TQ_QP(true, true); else TQ_QP(true, false);
+  if (bound) {
+    if (q_dtype == 1) {
+      if (one) TQ_QP(true, true, true); else TQ_QP(true, false, true);
+    } else {
+      if (one) TQ_QP(false, true, true); else TQ_QP(false, false, true);
+    }
   } else {
-    if (one) TQ_QP(false, true); else TQ_QP(false, false);
+    if (q_dtype == 1) {
+      if (one) TQ_QP(true, true, false); else TQ_QP(true, false, false);
+    } else {
+      if (one) TQ_QP(false, true, false); else TQ_QP(false, false, false);
+    }
   }
 #undef TQ_QP
   return hipGetLastError();
@@ -508,7 +573,7 @@ hipError_t launch_query_prep_multi(const tq_quantizer* const* qs, void* const* w
 }
 
 hipError_t launch_query_prep_ws(const tq_quantizer* q, const void* queries, int q_dtype, int B, int Hq, int Hkv,
-                                void* ws, hipStream_t st) {
+                                void* ws, hipStream_t st, bool bound) {
   const int G = Hq / Hkv;
   const int RT = (G + 3) / 4;
   const int T = key_terms(q);
@@ -516,7 +581,7 @@ hipError_t launch_query_prep_ws(const tq_quantizer* q, const void* queries, int 
   const int64_t groups = static_cast<int64_t>(B) * Hkv * RT;
   uint8_t* wsA = static_cast<uint8_t*>(ws);
   float* wsC = reinterpret_cast<float*>(wsA + groups * T * C * 2048);
-  return launch_query_prep(q, queries, q_dtype, B, Hq, Hkv, wsA, wsC, st);
+  return launch_query_prep(q, queries, q_dtype, B, Hq, Hkv, wsA, wsC, st, bound);
 }
 
 hipError_t launch_scores_scan(const tq_quantizer* q, int B, int Hq, int Hkv, const uint32_t* codes, const float* norms,
