@@ -459,14 +459,14 @@ __global__ void __launch_bounds__(64) topk_merge_kernel(const float* __restrict_
 // (the logits' bits) and ranked.  A query whose ceiling reaches tau (ties,
 // repeated keys) is flagged and served by the exact scan and merge.
 // ---------------------------------------------------------------------------
-template <int BP, int GW, bool QJL>
+template <int BP, int GW, bool QJL, int KK>
 __global__ void __launch_bounds__(256, 2)
     topk_lb_scan_kernel(const uint32_t* __restrict__ codes, const float* __restrict__ norms,
                         const float* __restrict__ gammas, int64_t n, int RT, int64_t rg_per_seq, int64_t rg_count,
                         int64_t slices, int64_t slice_keys, int topk, const uint8_t* __restrict__ wsA,
                         const float* __restrict__ wsC, float* __restrict__ cand_l, int* __restrict__ cand_i,
                         float* __restrict__ cand_f) {
-  constexpr int KK = 12;
+  static_assert(KK >= 10 && KK <= 12, "lists of 10 or 12 entries (k <= KK)");
   constexpr int T = (1 << (BP - 1)) + (QJL ? 1 : 0);
   constexpr int W = BP + (QJL ? 1 : 0);
   constexpr int C = (GW + 3) / 4;
@@ -806,9 +806,15 @@ static hipError_t launch_topk_bounded(const TopkPlan& pl, const uint32_t* codes,
   } else {
     const int64_t blocks = (pl.slices + 7) / 8 * 8 * pl.rg_count;
     if (blocks > 0x7fffffff) return hipErrorNotSupported;
-    hipLaunchKernelGGL((topk_lb_scan_kernel<BPV, GWV, QV>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
-                       codes, norms, gammas, n, pl.RT, pl.rg_per_seq, pl.rg_count, pl.slices, pl.slice_keys, topk, wsA,
-                       wsC, ll, lix, lc);
+    // 10-entry lists where they hold k (fewer registers, cheaper insertions)
+    if (topk <= 10)
+      hipLaunchKernelGGL((topk_lb_scan_kernel<BPV, GWV, QV, 10>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
+                         codes, norms, gammas, n, pl.RT, pl.rg_per_seq, pl.rg_count, pl.slices, pl.slice_keys, topk,
+                         wsA, wsC, ll, lix, lc);
+    else
+      hipLaunchKernelGGL((topk_lb_scan_kernel<BPV, GWV, QV, 12>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
+                         codes, norms, gammas, n, pl.RT, pl.rg_per_seq, pl.rg_count, pl.slices, pl.slice_keys, topk,
+                         wsA, wsC, ll, lix, lc);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((topk_lb_merge_kernel<BPV, GWV, QV>), dim3(static_cast<unsigned>(static_cast<int64_t>(B) * Hq)),
