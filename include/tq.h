@@ -165,7 +165,8 @@ int64_t tq_code_words(const tq_quantizer* q, int mode, int64_t nseq, int64_t n);
  *   codes:  tq_code_words(q, mode, nseq, n) uint32 words, layout above
  *   norms:  [nseq][n] float;  gammas: [nseq][n] float (prod), NULL or
  *           ignored (TQ_MSE, TQ_MSE_KEYS: those use the bits-bit codebook)
- * nseq*n may be 0 (no launch). */
+ * nseq*n may be 0 (no launch).  Every d of a quantizer (3 <= d <= 1024);
+ * above 256 a general tile kernel (slower, fp32 matrix core). */
 int tq_encode(const tq_quantizer* q, int mode, const void* x, int dtype, int64_t nseq, int64_t n,
               uint32_t* codes, float* norms, float* gammas, void* stream);
 
@@ -189,7 +190,9 @@ int tq_decode(const tq_quantizer* q, int mode, const uint32_t* codes, const floa
  *   topk  > 0: out = the topk largest logits per query [B][Hq][topk] float,
  *              descending, ties by lower index; out_idx [B][Hq][topk] int64
  *              (1 <= topk <= 32)
- *   workspace: device scratch of at least tq_scores_workspace_bytes(...) */
+ *   workspace: device scratch of at least tq_scores_workspace_bytes(...)
+ *   d <= 256: the matrix-core scan; 256 < d <= 1024: logits only (topk == 0),
+ *             a vector-ALU scan; topk > 0 there returns TQ_EUNSUPPORTED */
 int64_t tq_scores_workspace_bytes(const tq_quantizer* q, int B, int Hq, int Hkv, int64_t n, int topk);
 
 /* The two halves of tq_scores (topk == 0), for callers that score several
@@ -197,7 +200,8 @@ int64_t tq_scores_workspace_bytes(const tq_quantizer* q, int B, int Hq, int Hkv,
  * tq_query_prep rotates and projects the queries once and writes the
  * query-side MFMA operands into `workspace` (a2a how-to-implement: the query
  * is pre-rotated once); tq_scores_from_prep streams the packed keys against
- * them.  The workspace must not change between the two calls. */
+ * them.  The workspace must not change between the two calls.  d <= 256
+ * (TQ_EUNSUPPORTED above: tq_scores covers those). */
 int tq_query_prep(const tq_quantizer* q, const void* queries, int q_dtype, int B, int Hq, int Hkv, void* workspace,
                   int64_t ws_bytes, void* stream);
 int tq_scores_from_prep(const tq_quantizer* q, int B, int Hq, int Hkv, const uint32_t* codes, const float* norms,

@@ -328,7 +328,7 @@ int tq_encode(const tq_quantizer* q, int mode, const void* x, int dtype, int64_t
   if (!x || !codes || !norms || (mode == TQ_PROD && !gammas)) return fail(TQ_EINVAL, "NULL array argument");
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(norms, 16) || (gammas && !aligned(gammas, 16)))
     return fail(TQ_EINVAL, "device pointers must be 16-byte aligned");
-  if (q->d > 256) return fail(TQ_EUNSUPPORTED, "encode supports d <= 256 (d=%d)", q->d);
+  if (q->d > tq::kMaxEncodeD) return fail(TQ_EUNSUPPORTED, "encode supports d <= %d (d=%d)", tq::kMaxEncodeD, q->d);
   if (nseq > 65535) return fail(TQ_EUNSUPPORTED, "nseq > 65535");
   DeviceGuard g(q->device);
   if (!g.ok) return fail(TQ_EHIP, "cannot select the quantizer's device");
@@ -382,7 +382,8 @@ int tq_scores(const tq_quantizer* q, const void* queries, int q_dtype, int B, in
   if (!aligned(queries, 16) || !aligned(codes, 16) || !aligned(norms, 16) || (gammas && !aligned(gammas, 16)) ||
       !aligned(out, 16) || (out_idx && !aligned(out_idx, 16)))
     return fail(TQ_EINVAL, "device pointers must be 16-byte aligned");
-  if (q->d > 256) return fail(TQ_EUNSUPPORTED, "scores support d <= 256 (d=%d)", q->d);
+  if (q->d > tq::kMaxEncodeD) return fail(TQ_EUNSUPPORTED, "scores support d <= %d (d=%d)", tq::kMaxEncodeD, q->d);
+  if (q->d > 256 && topk > 0) return fail(TQ_EUNSUPPORTED, "top-k supports d <= 256 (d=%d)", q->d);
   const int64_t need = tq_scores_workspace_bytes(q, B, Hq, Hkv, n, topk);
   if (need < 0) return TQ_EINVAL;
   if (!workspace || ws_bytes < need)
@@ -407,7 +408,7 @@ int tq_query_prep(const tq_quantizer* q, const void* queries, int q_dtype, int B
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return fail(TQ_EINVAL, "q_dtype must be TQ_F32 or TQ_BF16");
   if (!queries) return fail(TQ_EINVAL, "NULL queries");
   if (!aligned(queries, 16)) return fail(TQ_EINVAL, "device pointers must be 16-byte aligned");
-  if (q->d > 256) return fail(TQ_EUNSUPPORTED, "scores support d <= 256 (d=%d)", q->d);
+  if (q->d > 256) return fail(TQ_EUNSUPPORTED, "the split query-prep path supports d <= 256 (d=%d)", q->d);
   const int64_t need = tq::scores_ws_bytes(q, B, Hq, Hkv);
   if (!workspace || ws_bytes < need)
     return fail(TQ_EWORKSPACE, "workspace of %lld bytes needed", static_cast<long long>(need));
@@ -431,7 +432,7 @@ int tq_scores_from_prep(const tq_quantizer* q, int B, int Hq, int Hkv, const uin
   if (!codes || !norms || (tq::key_qjl(q) && !gammas) || !logits) return fail(TQ_EINVAL, "NULL array argument");
   if (!aligned(codes, 16) || !aligned(norms, 16) || (gammas && !aligned(gammas, 16)) || !aligned(logits, 16))
     return fail(TQ_EINVAL, "device pointers must be 16-byte aligned");
-  if (q->d > 256) return fail(TQ_EUNSUPPORTED, "scores support d <= 256 (d=%d)", q->d);
+  if (q->d > 256) return fail(TQ_EUNSUPPORTED, "the split query-prep path supports d <= 256 (d=%d)", q->d);
   const int64_t need = tq::scores_ws_bytes(q, B, Hq, Hkv);
   if (!workspace || ws_bytes < need)
     return fail(TQ_EWORKSPACE, "workspace of %lld bytes needed", static_cast<long long>(need));

@@ -294,6 +294,235 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(const void* __restrict
 }
 
 // ---------------------------------------------------------------------------
+// Encoder for 256 < d <= 1024: the general kernel's steps on tiles of ROWS
+// vectors (16 for keys; 32 for values, whose words hold 32 tokens), so that a
+// tile of d floats per row fits in LDS.  Same fp32 matrix-core contraction
+// (gemm_rows below), bucketize, residual, QJL projection and packing as
+// encode_kernel; Pi and S' are read from the L2-resident tables once per tile.
+// ---------------------------------------------------------------------------
+// acc[rt][j] = rows 16 rt .. 16 rt + 15 of xs times column tile w + 4 j of the
+// k-major Mt, for R row tiles and NTW column tiles per wave (column tiles at
+// or past NT compute on clamped columns and are never read).
+template <int R, int NTW>
+__device__ __forceinline__ void gemm_rows(const float* xs, int ld, const float* __restrict__ Mt, int ldm, int rows_m,
+                                          int d, int w, v4f (&acc)[R][NTW]) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, kq = lane >> 4;
+#pragma unroll
+  for (int rt = 0; rt < R; ++rt)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) acc[rt][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+  int colc[NTW];
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) colc[j] = min((w + 4 * j) * 16 + r, rows_m - 1);
+  for (int k0 = 0; k0 < d; k0 += 4) {
+    const int k = k0 + kq;
+    const bool kin = k < d;
+    const int kc = min(k, d - 1);
+    float b[NTW], a[R];
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) b[j] = Mt[static_cast<int64_t>(kc) * ldm + colc[j]];
+#pragma unroll
+    for (int rt = 0; rt < R; ++rt) {
+      const float v = xs[(16 * rt + r) * ld + kc];
+      a[rt] = kin ? v : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < NTW; ++j)
+#pragma unroll
+      for (int rt = 0; rt < R; ++rt) acc[rt][j] = mfma_f32(a[rt], b[j], acc[rt][j]);
+  }
+#pragma unroll
+  for (int rt = 0; rt < R; ++rt)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) pin(acc[rt][j]);
+}
+
+size_t encode_big_lds_bytes(int d, int rows, bool keys) {
+  const int DP = ((d + 15) / 16) * 16;
+  // x (then rho) [rows][DP + 1] floats, norms, centroids; keys add index and
+  // sign bytes [rows][DP] each (values keep their index bytes over x)
+  return sizeof(float) * (static_cast<size_t>(rows) * (DP + 1) + rows + kMaxLevels) +
+         (keys ? 2 * static_cast<size_t>(rows) * DP : 0);
+}
+
+template <int ROWS, int NTW>
+__global__ void __launch_bounds__(kThreads) encode_big_kernel(const void* __restrict__ x, int dtype, int64_t n, int d,
+                                                              int mode, const float* __restrict__ pit, int ldp,
+                                                              const float* __restrict__ spt, Codebook cb,
+                                                              uint32_t* __restrict__ codes, float* __restrict__ norms,
+                                                              float* __restrict__ gammas) {
+  constexpr int R = ROWS / 16;
+  constexpr int TPR = kThreads / ROWS;   // threads per row for the norms
+  const int NT = (d + 15) / 16;
+  const int DP = NT * 16, LD = DP + 1;
+  extern __shared__ float smem[];
+  float* xs = smem;                       // [ROWS][LD]
+  float* nrm = xs + ROWS * LD;            // [ROWS]
+  float* cen = nrm + ROWS;                // [kMaxLevels]
+  uint8_t* idxb = mode == 1 ? reinterpret_cast<uint8_t*>(xs) : reinterpret_cast<uint8_t*>(cen + kMaxLevels);
+  uint8_t* sgnb = idxb + ROWS * DP;       // keys only
+  __shared__ float part2[4][ROWS];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int64_t seq = blockIdx.y;
+  const int64_t v0 = static_cast<int64_t>(blockIdx.x) * ROWS;
+  const int rows = static_cast<int>(n - v0 < ROWS ? n - v0 : ROWS);
+  const int64_t base = seq * n + v0;
+
+  if (tid < kMaxLevels) cen[tid] = tid < cb.levels ? cb.c[tid] : 0.f;
+  for (int e = tid; e < ROWS * DP; e += kThreads) {
+    const int row = e / DP, col = e - row * DP;
+    float v = 0.f;
+    if (row < rows && col < d) v = load_elem(x, dtype, (base + row) * d + col);
+    xs[row * LD + col] = v;
+  }
+  __syncthreads();
+  {
+    const int row = tid / TPR, part = tid % TPR;
+    float s = 0.f;
+    for (int col = part; col < d; col += TPR) {
+      const float v = xs[row * LD + col];
+      s = fmaf(v, v, s);
+    }
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1) s += __shfl_xor(s, o);
+    if (part == 0) nrm[row] = sqrtf(s);
+  }
+  __syncthreads();
+
+  v4f acc[R][NTW];
+  gemm_rows<R, NTW>(xs, LD, pit, ldp, d, d, wave, acc);
+
+  const int col_in = lane & 15, rq = lane >> 4;
+  float inv_n[R][4], rho2[R][4];
+#pragma unroll
+  for (int rt = 0; rt < R; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float nv = nrm[16 * rt + 4 * rq + i];
+      inv_n[rt][i] = nv > 0.f ? 1.f / nv : 0.f;
+      rho2[rt][i] = 0.f;
+    }
+  const int kh = cb.levels >> 1;
+  // keys: index bytes go to their own array now and rho stays in acc; values:
+  // the index (as a float) stays in acc, since its bytes go over x
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) {
+    const int col = (wave + 4 * j) * 16 + col_in;
+#pragma unroll
+    for (int rt = 0; rt < R; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float y = acc[rt][j][i] * inv_n[rt][i];
+        const float ay = fabsf(y);
+        int jm = 0;
+#pragma unroll
+        for (int k = 0; k + 1 < kMaxLevels / 2; ++k)
+          if (k + 1 < kh) jm += (cb.t[kh + k] < ay) ? 1 : 0;
+        const int idx = col < d ? (y > 0.f ? kh + jm : kh - 1 - jm) : 0;
+        const float rho = col < d ? y - cen[idx] : 0.f;
+        rho2[rt][i] = fmaf(rho, rho, rho2[rt][i]);
+        if (mode != 1) {
+          if (wave + 4 * j < NT) idxb[(16 * rt + 4 * rq + i) * DP + col] = static_cast<uint8_t>(idx);
+          acc[rt][j][i] = rho;
+        } else {
+          acc[rt][j][i] = static_cast<float>(idx);
+        }
+      }
+  }
+  __syncthreads();   // every wave is done with x: rho (keys) or the index bytes (values) go over it
+#pragma unroll
+  for (int j = 0; j < NTW; ++j)
+    if (wave + 4 * j < NT) {
+#pragma unroll
+      for (int rt = 0; rt < R; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * rt + 4 * rq + i, col = (wave + 4 * j) * 16 + col_in;
+          if (mode != 1) xs[row * LD + col] = acc[rt][j][i];
+          else idxb[row * DP + col] = static_cast<uint8_t>(acc[rt][j][i]);
+        }
+    }
+
+  if (mode == 0) {
+#pragma unroll
+    for (int rt = 0; rt < R; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float sum = rho2[rt][i];
+        sum += __shfl_xor(sum, 1);
+        sum += __shfl_xor(sum, 2);
+        sum += __shfl_xor(sum, 4);
+        sum += __shfl_xor(sum, 8);
+        if (col_in == 0) part2[wave][16 * rt + 4 * rq + i] = sum;
+      }
+    __syncthreads();
+    gemm_rows<R, NTW>(xs, LD, spt, d, d, d, wave, acc);
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+      const int col = (wave + 4 * j) * 16 + col_in;
+      if (wave + 4 * j < NT) {
+#pragma unroll
+        for (int rt = 0; rt < R; ++rt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = 16 * rt + 4 * rq + i;
+            const bool bit = (acc[rt][j][i] >= 0.f) || (inv_n[rt][i] == 0.f);
+            sgnb[row * DP + col] = (col < d && bit) ? 1 : 0;
+          }
+      }
+    }
+    if (tid < rows) {
+      const float nv = nrm[tid];
+      norms[base + tid] = nv;
+      gammas[base + tid] = nv * sqrtf((part2[0][tid] + part2[1][tid]) + (part2[2][tid] + part2[3][tid]));
+    }
+  } else {
+    if (tid < rows) norms[base + tid] = nrm[tid];
+  }
+  __syncthreads();
+
+  const int bp = cb.bp;
+  if (mode != 1) {
+    const int G = (d + 31) >> 5;
+    const int W = bp + (mode == 0 ? 1 : 0);
+    for (int task = tid; task < ROWS * G; task += kThreads) {
+      const int row = task / G, g = task - row * G;
+      if (row >= rows) continue;
+      uint32_t w[5] = {0u, 0u, 0u, 0u, 0u};
+      const uint8_t* ib = idxb + row * DP + 32 * g;
+      const uint8_t* sb = sgnb + row * DP + 32 * g;
+      for (int i = 0; i < 32; ++i) {
+        if (32 * g + i >= DP) break;
+        const uint32_t iv = ib[i];
+        for (int p = 0; p < bp; ++p) w[p] |= ((iv >> p) & 1u) << i;
+        if (mode == 0) w[bp] |= static_cast<uint32_t>(sb[i]) << i;
+      }
+      uint32_t* out = codes + ((base + row) * G + g) * W;
+      for (int p = 0; p < W; ++p) out[p] = w[p];
+    }
+  } else {
+    // values: one 32-token block per tile (ROWS = 32), words [seq][blk][bp][d]
+    static_assert(ROWS == 32 || ROWS == 16, "tile rows");
+    const int64_t nb = (n + 31) >> 5;
+    const int64_t blk = v0 >> 5;
+    if (ROWS == 32 && blk < nb) {
+      for (int j = tid; j < d; j += kThreads) {
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        for (int i = 0; i < rows; ++i) {
+          const uint32_t iv = idxb[i * DP + j];
+          for (int p = 0; p < bp; ++p) w[p] |= ((iv >> p) & 1u) << i;
+        }
+        uint32_t* out = codes + ((seq * nb + blk) * bp) * d + j;
+        for (int p = 0; p < bp; ++p) out[static_cast<int64_t>(p) * d] = w[p];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Tile encoder for d <= 128 (the head dimensions of attention caches), on the
 // fp16 16x16x32 MFMA with split operands.
 //
@@ -1440,6 +1669,26 @@ hipError_t launch_encode(const tq_quantizer* q, int mode, const void* x, int dty
     return dtype == 1 ? launch_encode_wide_lk<1>(q, mode, x, dtype, nseq, n, codes, norms, gammas, st)
                       : launch_encode_wide_lk<2>(q, mode, x, dtype, nseq, n, codes, norms, gammas, st);
   }
+  if (q->d > kWideK) {
+    if (q->d > kMaxEncodeD) return hipErrorNotSupported;
+    // values: tiles of 32 (one token word); keys: 16
+    const int rows = mode == 1 ? 32 : 16;
+    const size_t lds = encode_big_lds_bytes(q->d, rows, mode != 1);
+    dim3 grid(static_cast<unsigned>((n + rows - 1) / rows), static_cast<unsigned>(nseq));
+    const float* spt = q->d_spt;
+    const Codebook& cb = q->cb[mode == 0 ? 0 : 1];
+    const int ntw = ((q->d + 15) / 16 + 3) / 4;
+#define TQ_BIG(ROWS, NTWV)                                                                                      \
+  hipLaunchKernelGGL((encode_big_kernel<ROWS, NTWV>), grid, dim3(kThreads), lds, st, x, dtype, n, q->d, mode, q->d_qt, \
+                     q->d + q->m, spt, cb, codes, norms, gammas)
+    if (rows == 32) {
+      if (ntw <= 8) TQ_BIG(32, 8); else TQ_BIG(32, 16);
+    } else {
+      if (ntw <= 8) TQ_BIG(16, 8); else TQ_BIG(16, 16);
+    }
+#undef TQ_BIG
+    return hipGetLastError();
+  }
   const int nt = (q->d + 15) / 16;
   switch (nt) {
 #define TQ_NT_CASE(N) \
@@ -1474,6 +1723,13 @@ hipError_t set_kernel_attributes() {
     TQ_ATTR(1) TQ_ATTR(2) TQ_ATTR(3) TQ_ATTR(4) TQ_ATTR(5) TQ_ATTR(6) TQ_ATTR(7) TQ_ATTR(8)
     TQ_ATTR(9) TQ_ATTR(10) TQ_ATTR(11) TQ_ATTR(12) TQ_ATTR(13) TQ_ATTR(14) TQ_ATTR(15) TQ_ATTR(16)
 #undef TQ_ATTR
+#define TQ_ATTR_BIG(ROWS, NTWV, KEYS)                                                                        \
+  if (e == hipSuccess)                                                                                       \
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&encode_big_kernel<ROWS, NTWV>),                   \
+                            hipFuncAttributeMaxDynamicSharedMemorySize,                                     \
+                            static_cast<int>(encode_big_lds_bytes(kMaxEncodeD, ROWS, KEYS)));
+    TQ_ATTR_BIG(16, 8, true) TQ_ATTR_BIG(16, 16, true) TQ_ATTR_BIG(32, 8, false) TQ_ATTR_BIG(32, 16, false)
+#undef TQ_ATTR_BIG
     return e;
   }();
   return once;

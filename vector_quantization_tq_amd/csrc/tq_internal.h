@@ -15,6 +15,7 @@ void qjl_matrix(int m, int d, uint64_t seed, double* s);
 int codebook(int d, int K, double* centroids, double* thresholds);
 
 constexpr int kMaxLevels = 16;
+constexpr int kMaxEncodeD = 1024;   // largest d of encode and logits (the host quantizer's bound)
 constexpr int kMaxTerms = 8;
 
 // One codebook as the kernels see it (passed by value as a kernel argument).

@@ -502,6 +502,8 @@ __global__ void __launch_bounds__(256) scores_kernel(const uint32_t* __restrict_
 }
 
 int64_t scores_ws_bytes(const tq_quantizer* q, int B, int Hq, int Hkv) {
+  // 256 < d: the float [Pi q; S q] of every query
+  if (q->d > 256) return static_cast<int64_t>(B) * Hq * (q->d + q->m) * 4 + 256;
   const int G = Hq / Hkv;
   const int RT = (G + 3) / 4;
   const int T = key_terms(q);
@@ -617,9 +619,109 @@ hipError_t launch_scores_scan(const tq_quantizer* q, int B, int Hq, int Hkv, con
   return hipErrorNotSupported;
 }
 
+// ---------------------------------------------------------------------------
+// Logits for 256 < d <= 1024, on the vector ALU: the operand layout of the
+// matrix-core scan holds at most 8 words per key in registers.  The prep
+// writes q^ = Pi q and s = S q of every query in float; the scan gives a
+// thread to a key, walks its packed words and accumulates
+//   logit = n <q^, c[idx]> + gamma sqrt(pi/2)/m <s, sigma>
+// (blog.hotdry.top "TurboQuant vector-search compression", QJL section) for
+// up to 4 queries of its KV group per pass, with their vectors in LDS.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) big_prep_kernel(const void* __restrict__ queries, int q_dtype, int d, int m,
+                                                       const float* __restrict__ qt, float* __restrict__ qs) {
+  __shared__ float qv[kMaxEncodeD];
+  const int64_t qh = blockIdx.x;   // b * Hq + h
+  const int tid = threadIdx.x;
+  for (int k = tid; k < d; k += 256) qv[k] = load_elem(queries, q_dtype, qh * d + k);
+  __syncthreads();
+  const int dm = d + m;
+  for (int o = tid; o < dm; o += 256) {
+    float a = 0.f;
+    for (int k = 0; k < d; ++k) a = fmaf(qt[static_cast<int64_t>(k) * dm + o], qv[k], a);
+    qs[qh * dm + o] = a;
+  }
+}
+
+constexpr int kBigQ = 4;   // queries per pass of the scan
+
+template <bool QJL>
+__global__ void __launch_bounds__(256) big_scores_kernel(const uint32_t* __restrict__ codes,
+                                                         const float* __restrict__ norms,
+                                                         const float* __restrict__ gammas, int64_t n, int d, int m,
+                                                         int Hq, int Hkv, const float* __restrict__ qs, Codebook cb,
+                                                         float* __restrict__ out) {
+  __shared__ float qsh[kBigQ][2 * kMaxEncodeD];
+  __shared__ float cen[kMaxLevels];
+  const int tid = threadIdx.x;
+  const int G = Hq / Hkv;
+  const int64_t seq = blockIdx.y;
+  const int64_t b = seq / Hkv;
+  const int kvh = static_cast<int>(seq - b * Hkv);
+  const int64_t key = static_cast<int64_t>(blockIdx.x) * 256 + tid;
+  const int dm = d + m;
+  const int GW = (d + 31) / 32, bp = cb.bp, W = bp + (QJL ? 1 : 0);
+  const float alpha = 1.2533141373155003f / static_cast<float>(m);   // sqrt(pi/2) / m
+  if (tid < kMaxLevels) cen[tid] = tid < cb.levels ? cb.c[tid] : 0.f;
+  for (int q0 = 0; q0 < G; q0 += kBigQ) {
+    const int nq = min(kBigQ, G - q0);
+    const int64_t qrow = b * Hq + static_cast<int64_t>(kvh) * G + q0;   // first query of the pass
+    __syncthreads();
+    for (int e = tid; e < nq * dm; e += 256) {
+      const int t = e / dm, o = e - t * dm;
+      qsh[t][o] = qs[(qrow + t) * dm + o];
+    }
+    __syncthreads();
+    if (key >= n) continue;
+    float am[kBigQ] = {0.f, 0.f, 0.f, 0.f}, aq[kBigQ] = {0.f, 0.f, 0.f, 0.f};
+    const uint32_t* kw = codes + (seq * n + key) * GW * W;
+    for (int gw = 0; gw < GW; ++gw) {
+      uint32_t w[5] = {0u, 0u, 0u, 0u, 0u};
+      for (int p = 0; p < W; ++p) w[p] = kw[gw * W + p];
+      const int nb = min(32, d - 32 * gw);
+      for (int bit = 0; bit < nb; ++bit) {
+        const int j = 32 * gw + bit;
+        int idx = 0;
+        for (int p = 0; p < bp; ++p) idx |= static_cast<int>((w[p] >> bit) & 1u) << p;
+        const float c = cen[idx];
+        const float sg = QJL ? (((w[bp] >> bit) & 1u) ? 1.f : -1.f) : 0.f;
+#pragma unroll
+        for (int t = 0; t < kBigQ; ++t) {
+          am[t] = fmaf(c, qsh[t][j], am[t]);
+          if constexpr (QJL) aq[t] = fmaf(sg, qsh[t][d + j], aq[t]);
+        }
+      }
+    }
+    const float nv = norms[seq * n + key];
+    const float gv = QJL ? gammas[seq * n + key] : 0.f;
+    for (int t = 0; t < nq; ++t)
+      out[(qrow + t) * n + key] = QJL ? fmaf(nv, am[t], gv * alpha * aq[t]) : nv * am[t];
+  }
+}
+
+static hipError_t launch_scores_big(const tq_quantizer* q, const void* queries, int q_dtype, int B, int Hq, int Hkv,
+                                    const uint32_t* codes, const float* norms, const float* gammas, int64_t n,
+                                    float* out, void* ws, hipStream_t st) {
+  if (q->d > kMaxEncodeD || q->m > kMaxEncodeD) return hipErrorNotSupported;
+  float* qs = static_cast<float*>(ws);
+  hipLaunchKernelGGL(big_prep_kernel, dim3(static_cast<unsigned>(static_cast<int64_t>(B) * Hq)), dim3(256), 0, st,
+                     queries, q_dtype, q->d, q->m, q->d_qt, qs);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid(static_cast<unsigned>((n + 255) / 256), static_cast<unsigned>(static_cast<int64_t>(B) * Hkv));
+  if (key_qjl(q))
+    hipLaunchKernelGGL((big_scores_kernel<true>), grid, dim3(256), 0, st, codes, norms, gammas, n, q->d, q->m, Hq, Hkv,
+                       qs, key_codebook(q), out);
+  else
+    hipLaunchKernelGGL((big_scores_kernel<false>), grid, dim3(256), 0, st, codes, norms, gammas, n, q->d, q->m, Hq,
+                       Hkv, qs, key_codebook(q), out);
+  return hipGetLastError();
+}
+
 hipError_t launch_scores(const tq_quantizer* q, const void* queries, int q_dtype, int B, int Hq, int Hkv,
                          const uint32_t* codes, const float* norms, const float* gammas, int64_t n, float* out,
                          void* ws, hipStream_t st) {
+  if (q->d > 256) return launch_scores_big(q, queries, q_dtype, B, Hq, Hkv, codes, norms, gammas, n, out, ws, st);
   hipError_t e = launch_query_prep_ws(q, queries, q_dtype, B, Hq, Hkv, ws, st);
   if (e != hipSuccess) return e;
   return launch_scores_scan(q, B, Hq, Hkv, codes, norms, gammas, n, out, ws, st);
