@@ -378,7 +378,10 @@ def run_gqa(args, torch, dev, tq, wl_fn, name, bits, n_tail=0):
             "bytes_per_key": rec_k + 4 * G,
         },
         "roofline_encode": {
-            "kernel": "encode_tile_kernel (tq_encode, %s)" % ("mse keys" if mse_keys else "prod"),
+            "kernel": "%s (tq_encode, %s)" % (
+                ("encode_wht_kernel" if args.rotation == "hadamard" else "encode_tile_kernel") if mse_keys
+                else ("encode_keys_split_kernel" if d == 128 and args.rotation == "haar" else "encode_tile_kernel"),
+                "mse keys" if mse_keys else "prod"),
             "bound": "mfma",
             "achieved": round(enc_flop / (enc_ms * 1e-3) / 1e12, 2),
             "peak": FP16_MFMA_PEAK_TFLOPS,

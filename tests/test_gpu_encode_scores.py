@@ -86,6 +86,24 @@ def test_encode_mse_shapes(d, bits, nseq, n, bf16):
         P.check_mse_codes(oq, xs[s], cw[s * per:(s + 1) * per], nn[s * n:(s + 1) * n])
 
 
+@pytest.mark.parametrize("bits,nseq,n,bf16", [
+    (2, 3, 40001, False), (3, 2, 33000, True), (4, 2, 40033, False), (4, 3, 21000, True)])
+def test_encode_prod_d128_many_tiles_per_workgroup(bits, nseq, n, bf16):
+    """d = 128 prod keys over hundreds of tiles, so every workgroup of the
+    persistent grid runs its pipeline (load, rotation, projection, store)
+    through several tiles; zero rows at tile edges and a ragged tail."""
+    print(f"case: prod d=128 bits={bits} nseq={nseq} n={n} bf16={bf16} (many tiles)", flush=True)
+    rng = np.random.default_rng(7000 + bits)
+    x = (rng.standard_normal((nseq, n, 128)) * np.exp(rng.uniform(0, math.log(50), (1, 1, 128)))).astype(np.float32)
+    for r in (0, 63, 64, 4095, n - 1):
+        x[nseq - 1, r] = 0.0
+    g, oq = _pair(128, bits)
+    xs, codes, norms, gam = _encode_prod(g, x, bf16)
+    P.check_prod_codes(oq, xs, codes, norms, gam)
+    zero = (nseq - 1) * n + np.array([0, 63, 64, 4095, n - 1])
+    assert np.all(norms[zero] == 0) and np.all(gam[zero] == 0)
+
+
 def test_encode_zero_vectors_and_empty():
     print("case: zero vectors", flush=True)
     g, oq = _pair(128, 3)

@@ -9,6 +9,9 @@
 //
 // Both products by a d x d matrix (Pi x and S' rho) are taken to fp32
 // accuracy, so the code decisions are taken on fp32-accurate values:
+//  * prod keys at d = 128 (encode_keys_split_kernel): the split products
+//    below, with the rotation and the QJL projection in different waves of
+//    one workgroup, pipelined one tile apart;
 //  * d <= 128 (encode_tile_kernel): the fp16 16x16x32 MFMA on split
 //    operands.  A float is written as hi + lo, two fp16 numbers (22
 //    significant bits), and the matrix core accumulates the products at fp32
@@ -27,6 +30,7 @@
 //  * the Hadamard rotation, values and MSE-only keys (encode_wht_kernel): the
 //    fast Walsh-Hadamard transform in registers, no matrix core.
 #include <algorithm>
+#include <type_traits>
 
 #include "tq_device.h"
 #include "tq_kernels.h"
@@ -1184,6 +1188,454 @@ __global__ void __launch_bounds__(64 * KS, KS == 4 ? 2 : 1)
 }
 
 // ---------------------------------------------------------------------------
+// Key encoder for d = 128 (prod mode, the Haar rotation) with the work split
+// by role between the eight waves of a workgroup, pipelined one tile apart:
+//  * rotation waves 0-3: wave w keeps rows 32w .. 32w + 31 of Pi in
+//    registers; for tile i it takes the rotation, decides the index bits, and
+//    writes the index words, the residual rho (hi and lo) and its partial
+//    ||rho||^2 to LDS;
+//  * projection waves 4-7: wave 4 + w keeps rows 32w .. 32w + 31 of S' (hi
+//    and lo); it puts tile i + 1 into LDS and fetches tile i + 2, stores the
+//    finished words, norms and gammas of tile i - 2, then projects the
+//    residual of tile i - 1 and writes its QJL words.
+// One barrier per tile.  A SIMD holds one wave of each role: while one
+// classifies (vector ALU), the other's products occupy the matrix core; the
+// projection waves do their vector work first, when the rotation waves start
+// on the matrix core, and both roles issue the products of their second
+// 32-key half inside the decisions on the first.  Every global access of an
+// iteration (the fetch, then the stores) is issued at its start: the stores
+// share the load counter, so the wait for the fetched tile one iteration
+// later also waits for them, and by then they are a whole iteration old.
+// Each role's stationary operands are live only in its own loop.
+//
+// The arithmetic per element is the tile kernel's: the same split fp16
+// products (rows scaled so that the largest element lies in [2^14, 2^15);
+// x (Pi_hi + Pi_lo), plus x_lo Pi_hi for fp32 keys; rho_hi S'_hi + rho_lo S'_hi
+// + rho_hi S'_lo) in the same order per accumulator, and the same decisions
+// and roundings.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ v4f mfma_x(const v8h& a, const v8h& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+template <int LK, int BP>
+__global__ void __launch_bounds__(512, 1)
+    encode_keys_split_kernel(const void* __restrict__ x, int64_t nseq, int64_t n, const float* __restrict__ pi,
+                             const float* __restrict__ sp, Codebook cb, uint32_t* __restrict__ codes,
+                             float* __restrict__ norms, float* __restrict__ gammas) {
+  static_assert(LK == 1 || LK == 2, "bf16 or fp32 rows in 16-byte chunks");
+  constexpr int D = 128;
+  constexpr int LDH = D + 8;             // LDS row stride in halves
+  constexpr bool XLO = LK == 2;          // fp32 keys carry x_lo (bf16 keys are exact in fp16)
+  constexpr int NSRC = XLO ? 2 : 1;      // parts of x in LDS
+  // rotation products: (x_hi, Pi_hi) (x_hi, Pi_lo), and (x_lo, Pi_hi) for fp32 keys
+  constexpr int NPASS = XLO ? 3 : 2;
+  constexpr int W = BP + 1;              // words per 32-coordinate group: index planes + QJL
+  constexpr int WPK = 4 * W;             // words per key
+  constexpr int esz = LK == 1 ? 2 : 4;
+  constexpr int CH = D * esz / 16;       // 16-byte chunks per row
+  constexpr int PREN = CH / 4;           // chunks per loader thread (4 threads per row)
+  constexpr int EPT = D / 4;             // elements per loader thread
+  __shared__ __attribute__((aligned(16))) uint16_t xs16[NSRC][2][kEncRows * LDH];   // x: fp16 hi (and lo)
+  __shared__ __attribute__((aligned(16))) _Float16 rh[2][kEncRows * LDH];
+  __shared__ __attribute__((aligned(16))) _Float16 rl[2][kEncRows * LDH];
+  __shared__ __attribute__((aligned(16))) float scl3[3][kEncRows];   // y 2^14 = acc * scl
+  __shared__ float nrm3[3][kEncRows];                                // n
+  __shared__ float part2[2][4][kEncRows];                            // ||rho||^2 per coordinate group
+  __shared__ __attribute__((aligned(16))) uint32_t ost[3][kEncRows * WPK];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
+  const int w = wv & 3;                  // coordinate group (rotation) or QJL row group (projection)
+  const int r16 = lane & 15, q = lane >> 4;
+  const int64_t tps = (n + kEncRows - 1) / kEncRows;   // tiles per sequence
+  const int64_t total = nseq * tps;
+  // tiles of this workgroup: blockIdx.x + k gridDim.x < total (the grid never exceeds the tiles)
+  const int T = static_cast<int>((total - blockIdx.x + gridDim.x - 1) / gridDim.x);
+
+  // A operand: rows 32h + 16h2 + r16 of an LDS tile, columns 32 s2 + 8q .. + 7
+  auto a_op = [&](const void* src, int h, int h2, int s2) {
+    return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + (32 * h + 16 * h2 + r16) * LDH +
+                                           32 * s2 + 8 * q);
+  };
+  auto zero_pin = [&](v4f (&acc)[2][2], bool zero) {
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        if (zero) acc[h2][ct] = (v4f){0.f, 0.f, 0.f, 0.f};
+        else pin(acc[h2][ct]);
+      }
+  };
+  // packed word of row 4q + i of a ballot pair (low 16 bits, high 16 bits)
+  auto halves = [&](uint64_t m0, uint64_t m1) {
+    return __builtin_amdgcn_perm(static_cast<uint32_t>(m1 >> (16 * q)), static_cast<uint32_t>(m0 >> (16 * q)),
+                                 0x05040100u);
+  };
+  // element (ct, s2, e) of this lane's stationary operand: row 32w + 16ct + r16
+  // of a matrix (output coordinate), column 32 s2 + 8q + e, times 2^8
+  auto mat_at = [&](const float* __restrict__ m, int ct, int s2, int e) {
+    return m[(32 * w + 16 * ct + r16) * D + 32 * s2 + 8 * q + e] * kPiScale;
+  };
+
+  if (wv < 4) {
+    // ======================= rotation waves =======================
+    v8h bP[2][2][4];   // Pi_hi, Pi_lo
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = mat_at(pi, ct, s2, e);
+          const _Float16 h0 = static_cast<_Float16>(v);
+          bP[0][ct][s2][e] = h0;
+          bP[1][ct][s2][e] = static_cast<_Float16>(v - static_cast<float>(h0));
+        }
+    // pass k: source part (x_hi, x_lo) and Pi part (hi, lo)
+    auto pass_src = [](int k) { return k == 2 ? 1 : 0; };
+    auto pass_op = [](int k) { return k == 1 ? 1 : 0; };
+    // symmetric codebook: sign = top index bit, |y| against the positive
+    // thresholds gives the others (as in the tile kernel)
+    constexpr int KH = 1 << (BP - 1);
+    float thp[KH > 1 ? KH - 1 : 1], cenS[KH];
+#pragma unroll
+    for (int k2 = 0; k2 + 1 < KH; ++k2) thp[k2] = cb.t[KH + k2] * kRhoScale;
+#pragma unroll
+    for (int k2 = 0; k2 < KH; ++k2) cenS[k2] = cb.c[KH + k2] * kRhoScale;
+    __syncthreads();   // tile 0 is in LDS
+    int s3 = 0;
+    for (int i = 0; i < T + 2; ++i, s3 = s3 == 2 ? 0 : s3 + 1) {
+      if (i < T) {
+        const int sb = i & 1;
+        const float* scl = scl3[s3];
+        v4f acc[2][2][2];
+        // A operands of one 32-key half: [source][s2][h2]
+        v8h av[NSRC][4][2];
+        auto load_half = [&](int h) {
+#pragma unroll
+          for (int sr = 0; sr < NSRC; ++sr)
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+              for (int h2 = 0; h2 < 2; ++h2) av[sr][s2][h2] = __builtin_bit_cast(v8h, a_op(xs16[sr][sb], h, h2, s2));
+        };
+        // sub-step k of half h: pass k / 4, contraction step k % 4 (per
+        // accumulator the products keep the order pass by pass, step by step)
+        auto rot = [&](int h, int k) {
+          const int ps = k >> 2, s2 = k & 3;
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+              acc[h][h2][ct] = mfma_x(av[pass_src(ps)][s2][h2], bP[pass_op(ps)][ct][s2], acc[h][h2][ct]);
+        };
+        load_half(0);
+        zero_pin(acc[0], true);
+#pragma unroll
+        for (int k = 0; k < 4 * NPASS; ++k) rot(0, k);
+        zero_pin(acc[0], false);
+        load_half(1);
+        zero_pin(acc[1], true);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if (h == 1) {
+            zero_pin(acc[1], false);
+          }
+          // lane holds vector 32h + 16h2 + 4q + i, coordinate 32w + 16ct + r16
+          float r2v[2][4];
+          uint32_t wdall[2][4][BP];
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const int vbase = 32 * h + 16 * h2 + 4 * q;
+            const float4 sc4 = *reinterpret_cast<const float4*>(scl + vbase);
+            const float scv[4] = {sc4.x, sc4.y, sc4.z, sc4.w};
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+              if (h == 0) {   // half 1's products, a few per classification step of half 0
+                const int st = 4 * h2 + i4;
+#pragma unroll
+                for (int k = (st * 4 * NPASS) / 8; k < ((st + 1) * 4 * NPASS) / 8; ++k) rot(1, k);
+              }
+              const float scS = scv[i4];
+              uint64_t ms[2], mj[2][BP > 1 ? BP - 1 : 1];
+              float r2 = 0.f;
+#pragma unroll
+              for (int ct = 0; ct < 2; ++ct) {
+                const int c = 32 * w + 16 * ct + r16;
+                const float a = acc[h][h2][ct][i4];
+                const bool pos = a > 0.f;
+                bool jb[BP > 1 ? BP - 1 : 1];
+                if constexpr (BP > 1) decide_bits<BP - 1, BP - 2>(fabsf(a * scS), thp, jb);
+                else jb[0] = false;
+                ms[ct] = __ballot(pos);
+#pragma unroll
+                for (int p = 0; p + 1 < BP; ++p) mj[ct][p] = __ballot(jb[p]);
+                float cabs;
+                if constexpr (BP > 1) cabs = pick_centroid<BP - 1>(cenS, jb);
+                else cabs = cenS[0];
+                // rho 2^14 = y 2^14 - c[idx] 2^14 in one rounding, split hi + lo
+                const float rs = fmaf(a, scS, pos ? -cabs : cabs);
+                r2 = fmaf(rs, rs, r2);
+                const _Float16 hh = static_cast<_Float16>(rs);
+                rh[sb][(vbase + i4) * LDH + c] = hh;
+                rl[sb][(vbase + i4) * LDH + c] = f16_remainder(rs, hh);
+              }
+              // sign plane [y > 0]; low planes [bit of j == sign]
+              const uint64_t s0 = ms[0], s1 = ms[1];
+              wdall[h2][i4][BP - 1] = halves(s0, s1);
+#pragma unroll
+              for (int p = 0; p + 1 < BP; ++p) wdall[h2][i4][p] = halves(~(mj[0][p] ^ s0), ~(mj[1][p] ^ s1));
+              r2v[h2][i4] = r2;
+            }
+          }
+          if (r16 == 0) {
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+              for (int i4 = 0; i4 < 4; ++i4)
+#pragma unroll
+                for (int p = 0; p < BP; ++p)
+                  ost[s3][(32 * h + 16 * h2 + 4 * q + i4) * WPK + w * W + p] = wdall[h2][i4][p];
+          }
+          // ||rho||^2 over this wave's 32 coordinates by the transposing
+          // butterfly of the tile kernel: lane r16 ends with row 16 b3 + 2 b2 + b0
+          // (lanes r16 and r16 ^ 2 hold the same sum and write the same word)
+          const bool b3 = (r16 & 8) != 0, b2 = (r16 & 4) != 0, b0 = (r16 & 1) != 0;
+          float a4[4], a2[2];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float lo = r2v[0][k], hi = r2v[1][k];
+            a4[k] = (b3 ? hi : lo) + dpp_f<0x128>(b3 ? lo : hi);
+          }
+#pragma unroll
+          for (int k = 0; k < 2; ++k) a2[k] = (b2 ? a4[k + 2] : a4[k]) + dpp_f<0x141>(b2 ? a4[k] : a4[k + 2]);
+          float t = (b0 ? a2[1] : a2[0]) + dpp_f<0xB1>(b0 ? a2[0] : a2[1]);
+          t += dpp_f<0x4E>(t);
+          part2[sb][w][32 * h + 16 * (b3 ? 1 : 0) + 4 * q + 2 * (b2 ? 1 : 0) + (b0 ? 1 : 0)] = t;
+        }
+      }
+      __syncthreads();
+    }
+  } else {
+    // ======================= projection waves =======================
+    const int tq = tid - 256;            // 0 .. 255
+    v8h bSh[2][4], bSl[2][4];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = mat_at(sp, ct, s2, e);
+          const _Float16 h0 = static_cast<_Float16>(v);
+          bSh[ct][s2][e] = h0;
+          bSl[ct][s2][e] = static_cast<_Float16>(v - static_cast<float>(h0));
+        }
+    const int lrow = tq >> 2, part = tq & 3;   // loader: 4 threads per row
+    uint4 pre[PREN];
+    struct TileAt { int64_t seq, r; };
+    auto advance = [&](TileAt a) {
+      a.r += gridDim.x;
+      if (a.r >= tps) {
+        if (a.r < 2 * tps) {
+          a.r -= tps;
+          ++a.seq;
+        } else {
+          const int64_t k = a.r / tps;
+          a.seq += k;
+          a.r -= k * tps;
+        }
+      }
+      return a;
+    };
+    auto rows_of = [&](TileAt a) { return static_cast<int>(min(static_cast<int64_t>(kEncRows), n - a.r * kEncRows)); };
+    auto fetch = [&](TileAt a) {
+      const int rows = rows_of(a);
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(x) +
+                                                        ((a.seq * n + a.r * kEncRows + lrow) * D) * esz);
+#pragma unroll
+      for (int j = 0; j < PREN; ++j) {
+        pre[j] = make_uint4(0u, 0u, 0u, 0u);   // rows past n read as 0
+        if (lrow < rows) pre[j] = src[part + 4 * j];
+      }
+    };
+    // the tile in `pre` -> LDS slot xsl, and its norms and scales
+    auto commit = [&](TileAt a, int xsl, float* scl, float* nrm) {
+      const int rows = rows_of(a);
+      float v[EPT];
+#pragma unroll
+      for (int j = 0; j < PREN; ++j) {
+        const uint32_t u[4] = {pre[j].x, pre[j].y, pre[j].z, pre[j].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (LK == 1) {
+            v[8 * j + 2 * e] = __uint_as_float(u[e] << 16);
+            v[8 * j + 2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
+          } else {
+            v[4 * j + e] = __uint_as_float(u[e]);
+          }
+        }
+      }
+      float ss = 0.f, mx = 0.f;
+#pragma unroll
+      for (int j = 0; j < EPT; ++j) {
+        ss = fmaf(v[j], v[j], ss);
+        mx = fmaxf(mx, fabsf(v[j]));
+      }
+#pragma unroll
+      for (int o = 1; o < 4; o <<= 1) {
+        ss += __shfl_xor(ss, o);
+        mx = fmaxf(mx, __shfl_xor(mx, o));
+      }
+      // power-of-two row scale putting the largest element in [2^14, 2^15)
+      const int sig = mx > 0.f ? 14 - ilogb_pos(mx) : 0;
+      uint16_t* row = xs16[0][xsl] + lrow * LDH;
+      if constexpr (LK == 1) {
+        // bf16 keys are exact in fp16 after the row scale: a chunk of 8 is one 16-byte row segment
+#pragma unroll
+        for (int j = 0; j < PREN; ++j) {
+          v8h hv;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) hv[e] = static_cast<_Float16>(ldexpf(v[8 * j + e], sig));
+          *reinterpret_cast<v8h*>(row + 8 * (part + 4 * j)) = hv;
+        }
+      } else {
+        typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+        uint16_t* rowl = xs16[NSRC - 1][xsl] + lrow * LDH;
+#pragma unroll
+        for (int j = 0; j < PREN; ++j) {
+          v4h hv, lv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float sv = ldexpf(v[4 * j + e], sig);
+            const _Float16 hh = static_cast<_Float16>(sv);
+            hv[e] = hh;
+            lv[e] = static_cast<_Float16>(sv - static_cast<float>(hh));
+          }
+          *reinterpret_cast<v4h*>(row + 4 * (part + 4 * j)) = hv;
+          *reinterpret_cast<v4h*>(rowl + 4 * (part + 4 * j)) = lv;
+        }
+      }
+      if (part == 0) {
+        const float nv = lrow < rows ? sqrtf(ss) : 0.f;
+        nrm[lrow] = nv;
+        // y 2^14 = acc * scl: the rotation of u, times 2^14 (Pi carries 2^8, the row 2^sig)
+        scl[lrow] = nv > 0.f ? ldexpf(1.f / nv, 6 - sig) : 0.f;
+      }
+    };
+    TileAt p2 = {0, 0}, p1 = {0, 0}, c0 = {static_cast<int64_t>(blockIdx.x) / tps, static_cast<int64_t>(blockIdx.x) % tps};
+    TileAt n1 = c0;
+    fetch(c0);
+    commit(c0, 0, scl3[0], nrm3[0]);
+    if (T > 1) {
+      n1 = advance(c0);
+      fetch(n1);
+    }
+    __syncthreads();   // tile 0 is in LDS
+    int s3 = 0;        // slot of tile i; i - 1 is s3 - 1, i - 2 and i + 1 are s3 + 1 (mod 3)
+    float nv_pend = 0.f, gv_pend = 0.f;   // norm and gamma of tile i - 2, row tq
+    for (int i = 0; i < T + 2; ++i, s3 = s3 == 2 ? 0 : s3 + 1) {
+      const int s3m1 = s3 == 0 ? 2 : s3 - 1, s3p1 = s3 == 2 ? 0 : s3 + 1;
+      TileAt nn = n1;
+      if (i + 1 < T) {
+        // ---- tile i + 1 into LDS; tile i + 2 in flight ----
+        commit(n1, (i + 1) & 1, scl3[s3p1], nrm3[s3p1]);
+        const TileAt n2 = advance(n1);
+        if (i + 2 < T) fetch(n2);
+        nn = n2;
+      }
+      if (i >= 2) {
+        // ---- tile i - 2 (finished in the previous iteration): words, norms, gammas ----
+        const int rows = rows_of(p2);
+        uint4* dst = reinterpret_cast<uint4*>(codes + (p2.seq * n + p2.r * kEncRows) * WPK);
+        const uint4* srcw = reinterpret_cast<const uint4*>(ost[s3p1]);
+        for (int e = tq; e < rows * (WPK / 4); e += 256) dst[e] = srcw[e];
+        if (tq < rows) {
+          const int64_t o = p2.seq * n + p2.r * kEncRows + tq;
+          norms[o] = nv_pend;
+          gammas[o] = gv_pend;
+        }
+      }
+      if (i >= 1 && i <= T) {
+        // ---- QJL of tile i - 1: z = S' rho (scaled), bit = [z >= 0] (all ones for a zero vector) ----
+        const int sbp = (i - 1) & 1;
+        const float* nrm = nrm3[s3m1];
+        // A operands of one 32-key half: [rho hi, rho lo][s2][h2]
+        v8h ra[2][4][2];
+        auto load_rho = [&](int h) {
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+              ra[0][s2][h2] = __builtin_bit_cast(v8h, a_op(rh[sbp], h, h2, s2));
+              ra[1][s2][h2] = __builtin_bit_cast(v8h, a_op(rl[sbp], h, h2, s2));
+            }
+        };
+        v4f qa[2][2][2];
+        // sub-step k of half h: products rho_hi S'_hi, rho_lo S'_hi, rho_hi S'_lo
+        // (k / 4), contraction step k % 4; the tile kernel's order per accumulator
+        auto proj = [&](int h, int k) {
+          const int ps = k >> 2, s2 = k & 3;
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+              qa[h][h2][ct] = mfma_x(ra[ps == 1 ? 1 : 0][s2][h2], ps == 2 ? bSl[ct][s2] : bSh[ct][s2], qa[h][h2][ct]);
+        };
+        load_rho(0);
+        zero_pin(qa[0], true);
+#pragma unroll
+        for (int k = 0; k < 12; ++k) proj(0, k);
+        zero_pin(qa[0], false);
+        load_rho(1);
+        zero_pin(qa[1], true);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if (h == 1) zero_pin(qa[1], false);
+          uint32_t wd[2][4];
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const int vbase = 32 * h + 16 * h2 + 4 * q;
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+              if (h == 0) {   // half 1's products, a few per step of half 0
+                const int st = 4 * h2 + i4;
+#pragma unroll
+                for (int k = (st * 12) / 8; k < ((st + 1) * 12) / 8; ++k) proj(1, k);
+              }
+              const uint64_t zm = __ballot(!(nrm[vbase + i4] > 0.f));
+              const uint64_t m0 = __ballot(qa[h][h2][0][i4] >= 0.f) | zm;
+              const uint64_t m1 = __ballot(qa[h][h2][1][i4] >= 0.f) | zm;
+              wd[h2][i4] = halves(m0, m1);
+            }
+          }
+          if (r16 == 0) {
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+              for (int i4 = 0; i4 < 4; ++i4) ost[s3m1][(32 * h + 16 * h2 + 4 * q + i4) * WPK + w * W + BP] = wd[h2][i4];
+          }
+        }
+        // norm and gamma of row tq, stored with the words in the next iteration
+        if (tq < kEncRows) {
+          nv_pend = nrm[tq];
+          float t = 0.f;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) t += part2[sbp][k][tq];
+          gv_pend = nv_pend * sqrtf(t) * (1.f / kRhoScale);
+        }
+      }
+      p2 = p1;
+      p1 = c0;
+      c0 = n1;
+      n1 = nn;
+      __syncthreads();
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Walsh-Hadamard encoder for the structured rotation Pi = H D / sqrt(d)
 // (TQ_ROT_HADAMARD; H the Sylvester-ordered Hadamard matrix, D the random
 // signs), values and MSE-only keys, d = 32 .. 256 a power of two.
@@ -1595,6 +2047,29 @@ hipError_t launch_encode_tile_m(const tq_quantizer* q, const void* x, int dtype,
   return hipGetLastError();
 }
 
+// Prod keys at d = 128 (Haar rotation, rows in 16-byte runs): the role-split
+// key encoder, one eight-wave workgroup per CU (its LDS holds two tiles of x
+// and of rho and three of words)
+template <int LK>
+hipError_t launch_encode_keys_split(const tq_quantizer* q, const void* x, int64_t nseq, int64_t n, uint32_t* codes,
+                                    float* norms, float* gammas, hipStream_t st) {
+  const int64_t tiles = nseq * ((n + kEncRows - 1) / kEncRows);
+  if (tiles == 0) return hipSuccess;
+  const Codebook& cb = q->cb[0];
+  const dim3 grid(static_cast<unsigned>(std::min<int64_t>(tiles, device_cu_count())));
+#define TQ_SPLIT(B)                                                                                                \
+  hipLaunchKernelGGL((encode_keys_split_kernel<LK, B>), grid, dim3(512), 0, st, x, nseq, n, q->d_pi, q->d_sp, cb, \
+                     codes, norms, gammas)
+  switch (cb.bp) {
+    case 1: TQ_SPLIT(1); break;
+    case 2: TQ_SPLIT(2); break;
+    case 3: TQ_SPLIT(3); break;
+    default: return hipErrorNotSupported;
+  }
+#undef TQ_SPLIT
+  return hipGetLastError();
+}
+
 template <int LK>
 hipError_t launch_encode_tile_lk(const tq_quantizer* q, int mode, const void* x, int dtype, int64_t nseq, int64_t n,
                                  uint32_t* codes, float* norms, float* gammas, hipStream_t st) {
@@ -1608,6 +2083,11 @@ hipError_t launch_encode_tile_lk(const tq_quantizer* q, int mode, const void* x,
     }
   }
   if (F && q->d == 128) {
+#ifndef TQ_NO_SPLIT_ENCODE
+    if constexpr (F) {
+      if (mode == 0) return launch_encode_keys_split<LK>(q, x, nseq, n, codes, norms, gammas, st);
+    }
+#endif
     if (mode == 0) return launch_encode_tile_m<4, LK, 0, F>(q, x, dtype, nseq, n, codes, norms, gammas, st);
     if (mode == 1) return launch_encode_tile_m<4, LK, 1, F>(q, x, dtype, nseq, n, codes, norms, gammas, st);
     return launch_encode_tile_m<4, LK, 2, F>(q, x, dtype, nseq, n, codes, norms, gammas, st);
@@ -1736,3 +2216,4 @@ hipError_t set_kernel_attributes() {
 }
 
 }  // namespace tq
+
