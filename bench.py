@@ -380,7 +380,7 @@ def run_gqa(args, torch, dev, tq, wl_fn, name, bits, n_tail=0):
         "roofline_encode": {
             "kernel": "%s (tq_encode, %s)" % (
                 ("encode_wht_kernel" if args.rotation == "hadamard" else "encode_tile_kernel") if mse_keys
-                else ("encode_keys_split_kernel" if d == 128 and args.rotation == "haar" else "encode_tile_kernel"),
+                else ("encode_keys_split_kernel" if d == 128 else "encode_tile_kernel"),
                 "mse keys" if mse_keys else "prod"),
             "bound": "mfma",
             "achieved": round(enc_flop / (enc_ms * 1e-3) / 1e12, 2),

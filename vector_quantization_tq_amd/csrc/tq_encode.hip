@@ -1188,7 +1188,7 @@ __global__ void __launch_bounds__(64 * KS, KS == 4 ? 2 : 1)
 }
 
 // ---------------------------------------------------------------------------
-// Key encoder for d = 128 (prod mode, the Haar rotation) with the work split
+// Key encoder for d = 128 (prod mode) with the work split
 // by role between the eight waves of a workgroup, pipelined one tile apart:
 //  * rotation waves 0-3: wave w keeps rows 32w .. 32w + 31 of Pi in
 //    registers; for tile i it takes the rotation, decides the index bits, and
@@ -1218,7 +1218,7 @@ __device__ __forceinline__ v4f mfma_x(const v8h& a, const v8h& b, const v4f& c) 
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-template <int LK, int BP>
+template <int LK, int BP, bool HAD>
 __global__ void __launch_bounds__(512, 1)
     encode_keys_split_kernel(const void* __restrict__ x, int64_t nseq, int64_t n, const float* __restrict__ pi,
                              const float* __restrict__ sp, Codebook cb, uint32_t* __restrict__ codes,
@@ -1228,8 +1228,10 @@ __global__ void __launch_bounds__(512, 1)
   constexpr int LDH = D + 8;             // LDS row stride in halves
   constexpr bool XLO = LK == 2;          // fp32 keys carry x_lo (bf16 keys are exact in fp16)
   constexpr int NSRC = XLO ? 2 : 1;      // parts of x in LDS
-  // rotation products: (x_hi, Pi_hi) (x_hi, Pi_lo), and (x_lo, Pi_hi) for fp32 keys
-  constexpr int NPASS = XLO ? 3 : 2;
+  // rotation products: (x_hi, Pi_hi) (x_hi, Pi_lo), and (x_lo, Pi_hi) for fp32 keys;
+  // HAD (Pi = H D / sqrt(d)): the operand sqrt(d) Pi 2^8 = +-2^8 is exact, so
+  // (x_hi, +-2^8), and (x_lo, +-2^8) for fp32 keys
+  constexpr int NPASS = HAD ? (XLO ? 2 : 1) : (XLO ? 3 : 2);
   constexpr int W = BP + 1;              // words per 32-coordinate group: index planes + QJL
   constexpr int WPK = 4 * W;             // words per key
   constexpr int esz = LK == 1 ? 2 : 4;
@@ -1280,7 +1282,7 @@ __global__ void __launch_bounds__(512, 1)
 
   if (wv < 4) {
     // ======================= rotation waves =======================
-    v8h bP[2][2][4];   // Pi_hi, Pi_lo
+    v8h bP[HAD ? 1 : 2][2][4];   // Pi_hi, Pi_lo (HAD: +-2^8 only)
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
@@ -1288,13 +1290,17 @@ __global__ void __launch_bounds__(512, 1)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float v = mat_at(pi, ct, s2, e);
-          const _Float16 h0 = static_cast<_Float16>(v);
-          bP[0][ct][s2][e] = h0;
-          bP[1][ct][s2][e] = static_cast<_Float16>(v - static_cast<float>(h0));
+          if constexpr (HAD) {
+            bP[0][ct][s2][e] = static_cast<_Float16>(v > 0.f ? kPiScale : v < 0.f ? -kPiScale : 0.f);
+          } else {
+            const _Float16 h0 = static_cast<_Float16>(v);
+            bP[0][ct][s2][e] = h0;
+            bP[HAD ? 0 : 1][ct][s2][e] = static_cast<_Float16>(v - static_cast<float>(h0));
+          }
         }
     // pass k: source part (x_hi, x_lo) and Pi part (hi, lo)
-    auto pass_src = [](int k) { return k == 2 ? 1 : 0; };
-    auto pass_op = [](int k) { return k == 1 ? 1 : 0; };
+    auto pass_src = [](int k) { return HAD ? k : (k == 2 ? 1 : 0); };
+    auto pass_op = [](int k) { return HAD ? 0 : (k == 1 ? 1 : 0); };
     // symmetric codebook: sign = top index bit, |y| against the positive
     // thresholds gives the others (as in the tile kernel)
     constexpr int KH = 1 << (BP - 1);
@@ -1521,7 +1527,11 @@ __global__ void __launch_bounds__(512, 1)
         const float nv = lrow < rows ? sqrtf(ss) : 0.f;
         nrm[lrow] = nv;
         // y 2^14 = acc * scl: the rotation of u, times 2^14 (Pi carries 2^8, the row 2^sig)
-        scl[lrow] = nv > 0.f ? ldexpf(1.f / nv, 6 - sig) : 0.f;
+        // (HAD: the operand is sqrt(d) Pi 2^8, so the scale also divides by sqrt(d))
+        if constexpr (HAD)
+          scl[lrow] = nv > 0.f ? ldexpf(1.f / (nv * sqrtf(static_cast<float>(D))), 6 - sig) : 0.f;
+        else
+          scl[lrow] = nv > 0.f ? ldexpf(1.f / nv, 6 - sig) : 0.f;
       }
     };
     TileAt p2 = {0, 0}, p1 = {0, 0}, c0 = {static_cast<int64_t>(blockIdx.x) / tps, static_cast<int64_t>(blockIdx.x) % tps};
@@ -2047,10 +2057,10 @@ hipError_t launch_encode_tile_m(const tq_quantizer* q, const void* x, int dtype,
   return hipGetLastError();
 }
 
-// Prod keys at d = 128 (Haar rotation, rows in 16-byte runs): the role-split
-// key encoder, one eight-wave workgroup per CU (its LDS holds two tiles of x
-// and of rho and three of words)
-template <int LK>
+// Prod keys at d = 128 (rows in 16-byte runs; HAD: the Hadamard rotation): the
+// role-split key encoder, one eight-wave workgroup per CU (its LDS holds two
+// tiles of x and of rho and three of words)
+template <int LK, bool HAD>
 hipError_t launch_encode_keys_split(const tq_quantizer* q, const void* x, int64_t nseq, int64_t n, uint32_t* codes,
                                     float* norms, float* gammas, hipStream_t st) {
   const int64_t tiles = nseq * ((n + kEncRows - 1) / kEncRows);
@@ -2058,7 +2068,7 @@ hipError_t launch_encode_keys_split(const tq_quantizer* q, const void* x, int64_
   const Codebook& cb = q->cb[0];
   const dim3 grid(static_cast<unsigned>(std::min<int64_t>(tiles, device_cu_count())));
 #define TQ_SPLIT(B)                                                                                                \
-  hipLaunchKernelGGL((encode_keys_split_kernel<LK, B>), grid, dim3(512), 0, st, x, nseq, n, q->d_pi, q->d_sp, cb, \
+  hipLaunchKernelGGL((encode_keys_split_kernel<LK, B, HAD>), grid, dim3(512), 0, st, x, nseq, n, q->d_pi, q->d_sp, cb, \
                      codes, norms, gammas)
   switch (cb.bp) {
     case 1: TQ_SPLIT(1); break;
@@ -2077,6 +2087,9 @@ hipError_t launch_encode_tile_lk(const tq_quantizer* q, int mode, const void* x,
   constexpr bool F = LK != 0;
   if constexpr (F) {
     if (q->d == 128 && q->rotation == 1) {   // TQ_ROT_HADAMARD: the exact +-1 rotation operand
+#ifndef TQ_NO_SPLIT_ENCODE
+      if (mode == 0) return launch_encode_keys_split<LK, true>(q, x, nseq, n, codes, norms, gammas, st);
+#endif
       if (mode == 0) return launch_encode_tile_m<4, LK, 0, true, true>(q, x, dtype, nseq, n, codes, norms, gammas, st);
       if (mode == 1) return launch_encode_tile_m<4, LK, 1, true, true>(q, x, dtype, nseq, n, codes, norms, gammas, st);
       return launch_encode_tile_m<4, LK, 2, true, true>(q, x, dtype, nseq, n, codes, norms, gammas, st);
@@ -2085,7 +2098,7 @@ hipError_t launch_encode_tile_lk(const tq_quantizer* q, int mode, const void* x,
   if (F && q->d == 128) {
 #ifndef TQ_NO_SPLIT_ENCODE
     if constexpr (F) {
-      if (mode == 0) return launch_encode_keys_split<LK>(q, x, nseq, n, codes, norms, gammas, st);
+      if (mode == 0) return launch_encode_keys_split<LK, false>(q, x, nseq, n, codes, norms, gammas, st);
     }
 #endif
     if (mode == 0) return launch_encode_tile_m<4, LK, 0, F>(q, x, dtype, nseq, n, codes, norms, gammas, st);
