@@ -38,7 +38,8 @@ def _keys(rng, nseq, n, d):
 
 @pytest.mark.parametrize("d,bits,nseq,n,bf16", [
     (128, 3, 2, 1000, True), (128, 4, 1, 777, False), (64, 2, 1, 300, True), (256, 3, 1, 200, False),
-    (16, 2, 2, 65, False)])
+    (16, 2, 2, 65, False),
+    (128, 2, 3, 20011, False)])   # fp32 keys over several tiles per workgroup of the persistent grid
 def test_encode_prod_hadamard(d, bits, nseq, n, bf16):
     print(f"case: hadamard prod encode d={d} bits={bits} nseq={nseq} n={n}", flush=True)
     g, oq = _pair(d, bits)
